@@ -1,0 +1,66 @@
+"""Work and memory accounting for the attention path (host-side arithmetic only).
+
+Counted FLOPs: per (batch, query head) the forward counts 4*Tq*Tk*d (two
+matrix products of 2*Tq*Tk*d) and the backward 10*Tq*Tk*d (five products:
+the score recompute, dP, dV, dK, dQ), both halved when causal.  This is the
+conventional count; the exact causal visible fraction is slightly above one
+half and is not what is reported.
+
+Retained-for-backward bytes: the recompute backward keeps Q, K, V, O (storage
+dtype) and the fp32 row statistic L, all linear in T.  The dense baseline
+keeps Q, K, V and the Tq x Tk probability matrix; for one head in fp32 this
+is (3*T*d + T*T) * 4 bytes, which reproduces the dense column of the
+measurement table on "What Ordinary Autograd Saves" (section "The
+measurement") exactly, and 3*T*d*4 bytes is the recomputed payload of the
+section "The way out is recomputation".
+"""
+
+from __future__ import annotations
+
+DTYPE_BYTES = {"fp32": 4, "bf16": 2}
+
+
+def flops(B, Hq, Tq, Tk, d, causal):
+    """(forward, backward) counted FLOPs."""
+    f = 4.0 * B * Hq * Tq * Tk * d
+    b = 10.0 * B * Hq * Tq * Tk * d
+    if causal:
+        f, b = f / 2, b / 2
+    return f, b
+
+
+def retained_bytes_recompute(B, Hq, Hkv, Tq, Tk, d, dtype):
+    """Q, K, V, O in the storage dtype plus fp32 L: what the backward keeps."""
+    e = DTYPE_BYTES[dtype]
+    return e * (2 * B * Hq * Tq * d + 2 * B * Hkv * Tk * d) + 4 * B * Hq * Tq
+
+
+def retained_bytes_dense(B, Hq, Hkv, Tq, Tk, d, dtype):
+    """Q, K, V plus the Tq x Tk probability matrix per query head, storage dtype."""
+    e = DTYPE_BYTES[dtype]
+    return e * (B * Hq * Tq * d + 2 * B * Hkv * Tk * d + B * Hq * Tq * Tk)
+
+
+def checkpoint_payload_bytes(T, d, dv, elem=4):
+    """Inputs only (Q, K, V of one head): the payload left when everything is recomputed."""
+    return elem * (2 * T * d + T * dv)
+
+
+def kv_block_bytes(heads, max_kv, d, elem=2):
+    """K and V for one block of `heads` expanded heads of max_kv keys (chunked-attention article)."""
+    return 2 * heads * max_kv * d * elem
+
+
+def min_hbm_bytes(B, Hq, Hkv, Tq, Tk, d, dtype):
+    """(forward, backward) compulsory HBM traffic.
+
+    Forward reads Q, K, V and writes O, L.  Backward reads Q, K, V, O, dO, L
+    and writes dQ, dK, dV.
+    """
+    e = DTYPE_BYTES[dtype]
+    q = B * Hq * Tq * d * e
+    kv = B * Hkv * Tk * d * e
+    lse = B * Hq * Tq * 4
+    fwd = q + 2 * kv + q + lse
+    bwd = 3 * q + 2 * kv + lse + q + 2 * kv
+    return fwd, bwd
