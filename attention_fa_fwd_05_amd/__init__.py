@@ -1,0 +1,9 @@
+"""Exact attention for MI355X (gfx950): tiled online-softmax forward that keeps
+O and the natural-log row logsumexp L, and a backward that rebuilds the score
+and probability tiles from Q, K, V, O and L.  The computation lives in
+libfa05.so (C ABI in include/fa.h); this package only marshals arguments.
+"""
+
+from ._binding import (EXPORTS, FA_DTYPE_BF16, FA_DTYPE_F32, LIB_PATH, STATUS, FaError,  # noqa: F401
+                       attention, backward, forward, load_library, status_string,
+                       workspace_bytes)

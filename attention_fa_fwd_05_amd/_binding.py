@@ -1,0 +1,188 @@
+"""ctypes binding of libfa05.so (include/fa.h): argument marshalling only.
+
+Torch provides device memory (outputs and the backward workspace are
+allocated here, outside the library) and the current HIP stream; every step
+of the computation runs in the library's kernels.  A missing library raises;
+there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfa05.so")
+
+FA_DTYPE_F32 = 0
+FA_DTYPE_BF16 = 1
+
+STATUS = {
+    0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_GQA_RATIO",
+    4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_DTYPE", 6: "FA_ERR_SCALE", 7: "FA_ERR_WORKSPACE",
+    8: "FA_ERR_ALIGNMENT", 9: "FA_ERR_TOO_LARGE", 10: "FA_ERR_HIP",
+}
+EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_hip_error_string",
+           "fa_abi_version"]
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        detail = status_string(status)
+        if status == 10:
+            detail += ": " + load_library().fa_hip_error_string().decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({detail})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa05.so and declare the C signatures (cached)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m attention_fa_fwd_05_amd.build`")
+    # The library shares torch's HIP runtime (same soname).  Its kernels must be
+    # registered after that runtime has initialised the device, or launches
+    # fail with "no ROCm-capable device", so bring torch's device up first.
+    import torch
+    if torch.cuda.is_available():
+        torch.cuda.init()
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                           i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_hip_error_string.argtypes = []
+    lib.fa_hip_error_string.restype = ctypes.c_char_p
+    lib.fa_abi_version.argtypes = []
+    lib.fa_abi_version.restype = i
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return FA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return FA_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t) -> int | None:
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+
+def _stream(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, d]")
+    B, Hq, Tq, d = q.shape
+    Bk, Hkv, Tk, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape) != (B, Hkv, Tk, d):
+        raise ValueError(f"inconsistent shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must share dtype and device")
+    return B, Hq, Hkv, Tq, Tk, d
+
+
+def workspace_bytes(B, Hq, Hkv, Tq, Tk, d, dtype_code) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(B, Hq, Hkv, Tq, Tk, d, dtype_code))
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """fa_fwd: returns (o, lse) with o like q and lse float32 [B, Hq, Tq]."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), B, Hq, Hkv, Tq, Tk, d,
+                    int(bool(causal)), scale, _dtype_code(q), _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_fwd")
+    return o, L
+
+
+def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
+             workspace=None, dq=None, dk=None, dv=None):
+    """fa_bwd: returns (dq, dk, dv) like q, k, v."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
+    for t, shape in ((o, q.shape), (do, q.shape)):
+        if tuple(t.shape) != tuple(shape) or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("o and do must match q")
+    if tuple(lse.shape) != (B, Hq, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be float32 [B, Hq, Tq]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    need = workspace_bytes(B, Hq, Hkv, Tq, Tk, d, code)
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                    _ptr(dv), ws.data_ptr(), ws.numel(), B, Hq, Hkv, Tq, Tk, d,
+                    int(bool(causal)), scale, code, _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def _autograd_function():
+    import torch
+
+    class FlashAttention(torch.autograd.Function):
+        """Autograd wrapper that saves exactly q, k, v, o and lse for the backward."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, causal, scale):
+            o, lse = forward(q, k, v, causal, scale)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.causal, ctx.scale = causal, scale
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, o, lse = ctx.saved_tensors
+            dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), ctx.causal, ctx.scale)
+            return dq, dk, dv, None, None
+
+    return FlashAttention
+
+
+_FN = None
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None):
+    """Differentiable attention through the library (retains q, k, v, o, lse only)."""
+    global _FN
+    if _FN is None:
+        _FN = _autograd_function()
+    return _FN.apply(q, k, v, causal, scale)

@@ -1,0 +1,70 @@
+"""Build libfa05.so in-tree with hipcc for gfx950.
+
+    python -m attention_fa_fwd_05_amd.build
+
+Every HIP source under csrc/ is compiled separately (in parallel) and linked
+into attention_fa_fwd_05_amd/libfa05.so.  Packed fp32 VALU instructions are
+disabled (-packed-fp32-ops) and float atomics use the hardware instruction
+(-munsafe-fp-atomics: the dQ accumulator lives in ordinary device memory).
+"""
+
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libfa05.so")
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.hip"]
+HEADERS = ["fa_common.h", "fa_kernels.h"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-munsafe-fp-atomics",
+    "-mcode-object-version=5",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libfa05.so)")
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-c",
+           os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    return obj
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    r = subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

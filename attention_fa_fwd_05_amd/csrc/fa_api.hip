@@ -1,0 +1,152 @@
+// C ABI entry points (include/fa.h): argument validation, workspace layout and
+// dispatch to the gfx950 kernels.  Every check runs before any HIP call; the
+// library allocates nothing and keeps no state.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr long long kMaxElems = 1LL << 40;          // element-count ceiling per tensor
+constexpr int kMaxSeq = 1 << 24;                     // Tq, Tk ceiling
+constexpr int kMaxGrid = 0x7fffffff;
+
+// Text of the HIP error behind the calling thread's most recent FA_ERR_HIP.
+thread_local const char* t_hip_error = "no HIP error";
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  t_hip_error = hipGetErrorString(e);
+  return FA_ERR_HIP;
+}
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int elem_bytes(int dtype) { return dtype == FA_DTYPE_BF16 ? 2 : 4; }
+
+// Shared shape checks; returns FA_OK or the first failing status.
+int check_common(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 0 || Tk < 0) return FA_ERR_BAD_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_GQA_RATIO;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (Tq > kMaxSeq || Tk > kMaxSeq) return FA_ERR_TOO_LARGE;
+  const long long q = (long long)B * Hq * Tq * d, kv = (long long)B * Hkv * Tk * d;
+  if (q > kMaxElems || kv > kMaxElems) return FA_ERR_TOO_LARGE;
+  // grid sizes: forward (Tq/128) * B * Hq, backward (Tk/128) * B * Hkv, rows/16
+  if ((long long)((Tq + 127) / 128) * B * Hq > kMaxGrid) return FA_ERR_TOO_LARGE;
+  if ((long long)((Tk + 127) / 128) * B * Hkv > kMaxGrid) return FA_ERR_TOO_LARGE;
+  if (((long long)B * Hq * Tq + 15) / 16 > kMaxGrid) return FA_ERR_TOO_LARGE;
+  if ((long long)B * Hq * Tq * d / 8 / 256 + 1 > kMaxGrid) return FA_ERR_TOO_LARGE;
+  return FA_OK;
+}
+
+// A tensor with elements needs a non-NULL, 16-byte aligned pointer.
+int check_ptr(const void* p, long long elems) {
+  if (elems == 0) return FA_OK;
+  if (p == nullptr) return FA_ERR_NULL_PTR;
+  if (misaligned(p)) return FA_ERR_ALIGNMENT;
+  return FA_OK;
+}
+
+struct WsLayout {
+  size_t dvec, lg, dqacc, total;
+};
+
+WsLayout ws_layout(int B, int Hq, int Tq, int d, int dtype) {
+  const size_t rows = (size_t)B * Hq * Tq;
+  WsLayout w;
+  w.dvec = 0;
+  w.lg = align_up(rows * 4);
+  w.dqacc = w.lg + align_up(rows * 4);
+  w.total = w.dqacc + (dtype == FA_DTYPE_BF16 ? align_up(rows * d * 4) : 0);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return (1 << 16) | 0; }
+
+const char* fa_hip_error_string(void) { return t_hip_error; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL_PTR: return "a required pointer is NULL";
+    case FA_ERR_BAD_SHAPE: return "bad shape: B, Hq, Hkv must be >= 1 and Tq, Tk >= 0";
+    case FA_ERR_GQA_RATIO: return "Hq must be a multiple of Hkv";
+    case FA_ERR_HEAD_DIM: return "unsupported head dimension (64 or 128)";
+    case FA_ERR_DTYPE: return "unsupported dtype (FA_DTYPE_F32 or FA_DTYPE_BF16)";
+    case FA_ERR_SCALE: return "scale must be finite";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_bwd_workspace_bytes";
+    case FA_ERR_ALIGNMENT: return "pointers must be 16-byte aligned";
+    case FA_ERR_TOO_LARGE: return "a size exceeds the library's index range";
+    case FA_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    default: return "unknown status";
+  }
+}
+
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
+           int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
+           int dtype, void* stream) {
+  int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
+  if (st != FA_OK) return st;
+  const long long nq = (long long)B * Hq * Tq * d, nkv = (long long)B * Hkv * Tk * d;
+  if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, nq)) || (st = check_ptr(K, nkv)) ||
+      (st = check_ptr(V, nkv)) || (st = check_ptr(L, (long long)B * Hq * Tq)))
+    return st;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (Tq == 0) return FA_OK;
+  fa::FwdArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype) {
+  if (check_common(B, Hq, Hkv, Tq, Tk, d, dtype) != FA_OK) return 0;
+  return ws_layout(B, Hq, Tq, d, dtype).total;
+}
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
+           const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+           int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
+           int dtype, void* stream) {
+  int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
+  if (st != FA_OK) return st;
+  const long long nq = (long long)B * Hq * Tq * d, nkv = (long long)B * Hkv * Tk * d;
+  const long long rows = (long long)B * Hq * Tq;
+  if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, nq)) || (st = check_ptr(dO, nq)) ||
+      (st = check_ptr(dQ, nq)) || (st = check_ptr(K, nkv)) || (st = check_ptr(V, nkv)) ||
+      (st = check_ptr(dK, nkv)) || (st = check_ptr(dV, nkv)) || (st = check_ptr(L, rows)))
+    return st;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const WsLayout ws = ws_layout(B, Hq, Tq, d, dtype);
+  if (ws.total > 0) {
+    if (workspace == nullptr || workspace_bytes < ws.total) return FA_ERR_WORKSPACE;
+    if (misaligned(workspace)) return FA_ERR_ALIGNMENT;
+  }
+  if (Tq == 0 && Tk == 0) return FA_OK;
+  char* wsb = static_cast<char*>(workspace);
+  fa::BwdArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L; a.dO = dO;
+  a.dQ = dQ; a.dK = dK; a.dV = dV;
+  a.Dvec = ws.total ? reinterpret_cast<float*>(wsb + ws.dvec) : nullptr;
+  a.Lg = ws.total ? reinterpret_cast<float*>(wsb + ws.lg) : nullptr;
+  a.dQacc = dtype == FA_DTYPE_BF16 ? (ws.total ? reinterpret_cast<float*>(wsb + ws.dqacc) : nullptr)
+                                   : static_cast<float*>(dQ);
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  return hip_status(fa::launch_bwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream));
+}
+
+}  // extern "C"

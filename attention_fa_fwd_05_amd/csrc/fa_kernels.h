@@ -1,0 +1,50 @@
+// Kernel argument blocks and launchers (host side of the kernels; no validation
+// here -- fa_api.hip checks every argument before calling these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* L;
+  int B, Hq, Hkv, Tq, Tk;
+  float scale_log2;   // scale * log2(e): scores are kept in the exp2 domain
+};
+
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const float* L;
+  const void* dO;
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* Dvec;        // [B*Hq*Tq] rowsum(dO * O)
+  float* Lg;          // [B*Hq*Tq] L * log2(e); +inf for rows without keys
+  float* dQacc;       // [B*Hq*Tq*d] fp32 dQ accumulator (== dQ for fp32)
+  int B, Hq, Hkv, Tq, Tk;
+  float scale;
+  float scale_log2;
+};
+
+// Launch a 256-thread kernel on a 1-D grid and return that launch's own status
+// (the thread's sticky last-error state is neither read nor cleared).
+template <typename... Params, typename... Args>
+inline hipError_t launch(void (*kernel)(Params...), long long blocks, hipStream_t stream, Args... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)blocks), dim3(256), argv, 0,
+                         stream);
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream);
+
+}  // namespace fa

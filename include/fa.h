@@ -1,0 +1,131 @@
+/*
+ * fa.h -- C ABI of the gfx950 (MI355X) exact-attention library (libfa05.so).
+ *
+ * The library computes exact softmax attention with a tiled forward pass that
+ * keeps only the output O and the natural-log row logsumexp L, and a backward
+ * pass that rebuilds the score and probability tiles from Q, K, V, O and L
+ * instead of storing them.
+ *
+ * Sources (web pages; cited by title and section):
+ *  - "What Ordinary Autograd Saves: Tiling the Forward Pass Is Only Half the
+ *    Algorithm", section "The implementation under test": the forward returns
+ *    O and L = m + ln(l) per row (max m, exponential sum l of the scaled
+ *    scores); scale = 1/sqrt(d) there.  Section "Why this is FlashAttention's
+ *    second idea": the backward keeps O and L and rebuilds the score and
+ *    probability tiles from them.
+ *  - "Backward Pass Implementation", sections "Limitations of PyTorch
+ *    Autograd" (S = Q K^T / sqrt(d), P = softmax(S), O = P V) and "The
+ *    Recomputation Strategy" (O(N) saved statistics; recompute S and P in the
+ *    backward); its introduction names arbitrary sequence lengths, causal
+ *    masking and GQA as features of the forward.
+ *  - "The Autograd Memory Trap: Diagnosing a Backward-Pass OOM in Chunked
+ *    Attention", sections "Tracing the Autograd Graph" (the backward of
+ *    repeating K/V heads is a sum over the repeats) and "The GQA Expansion
+ *    Question" (query heads share K/V heads, 32 over 8).
+ *
+ * Conventions shared by every entry point
+ *  - Layout: contiguous row-major.  Q, O, dO, dQ are [B][Hq][Tq][d]; K, V, dK,
+ *    dV are [B][Hkv][Tk][d]; L is [B][Hq][Tq], always float32, natural log.
+ *  - dtype: FA_DTYPE_F32 (float) or FA_DTYPE_BF16 (bfloat16 storage, float32
+ *    accumulation, outputs rounded to nearest even).  It applies to Q, K, V,
+ *    O, dO, dQ, dK, dV.
+ *  - d (head dimension, equal for Q/K and V): 64 or 128.
+ *  - GQA: Hq must be a multiple of Hkv; query head h reads K/V head
+ *    h / (Hq / Hkv).  dK and dV are summed over the query heads of a group.
+ *  - causal != 0: key j is visible to query i iff j <= i + (Tk - Tq)
+ *    (aligned at the end; j <= i when Tq == Tk).  Keys beyond Tk do not exist.
+ *  - A query row that sees no key (Tk == 0, or causal with i + Tk - Tq < 0)
+ *    gets O = 0, L = -inf and dQ = 0, and adds nothing to dK or dV.
+ *  - scale multiplies Q K^T; it must be finite (callers pass 1/sqrt(d)).
+ *  - Pointers are device pointers (or host-coherent memory the GPU can reach),
+ *    16-byte aligned, and must not alias one another.  A pointer may be NULL
+ *    only when the tensor it names has no elements.
+ *  - stream is a hipStream_t (NULL = the null stream).  All work is enqueued
+ *    on it; nothing synchronises the host, nothing prints, nothing allocates.
+ *  - Ownership: the caller owns every buffer.  The library keeps no state
+ *    between calls and may be called from several host threads at once.
+ *  - Outputs are overwritten, never accumulated into.
+ *  - Errors: arguments are validated before any HIP call and the first failing
+ *    check is returned; a failed launch returns FA_ERR_HIP.  No C++ exception
+ *    crosses this interface.  Tq == 0 is a successful no-op for fa_fwd.
+ */
+#ifndef FA05_FA_H
+#define FA05_FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL_PTR = 1,   /* a required pointer is NULL */
+  FA_ERR_BAD_SHAPE = 2,  /* B, Hq or Hkv < 1, Tq or Tk < 0 */
+  FA_ERR_GQA_RATIO = 3,  /* Hq is not a multiple of Hkv */
+  FA_ERR_HEAD_DIM = 4,   /* d is not 64 or 128 */
+  FA_ERR_DTYPE = 5,      /* dtype is not an fa_dtype value */
+  FA_ERR_SCALE = 6,      /* scale is NaN or infinite */
+  FA_ERR_WORKSPACE = 7,  /* workspace missing or smaller than fa_bwd_workspace_bytes */
+  FA_ERR_ALIGNMENT = 8,  /* a pointer is not 16-byte aligned */
+  FA_ERR_TOO_LARGE = 9,  /* a size exceeds the library's index range */
+  FA_ERR_HIP = 10        /* a HIP runtime call or kernel launch failed */
+} fa_status;
+
+typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
+
+/*
+ * Forward pass.  Computes, per (b, h) and query row i,
+ *   S_ij = scale * <Q_i, K_j>, over the visible keys j,
+ *   L_i  = ln sum_j exp(S_ij)             (written to L, float32),
+ *   O_i  = sum_j exp(S_ij - L_i) V_j      (written to O, dtype),
+ * with the online-softmax recurrence over key tiles (running max, running
+ * exponential sum, one rescale of the partial output when the max moves,
+ * normalisation once at the end).  Reads Q, K, V; writes O and L only.
+ */
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
+           int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
+           int dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes: float32 D and
+ * log2-domain L per query row, plus (bf16 only) a float32 dQ accumulator
+ * [B][Hq][Tq][d].  Each part starts on a 256-byte boundary.  Returns 0 for
+ * invalid arguments.  The workspace holds nothing between calls.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype);
+
+/*
+ * Backward pass: the gradients of sum(O * dO) with respect to Q, K and V
+ * (L receives no cotangent), rebuilt tile by tile from Q, K, V, O, L:
+ *   D_i   = sum_c dO_ic O_ic,
+ *   P_ij  = exp(scale <Q_i, K_j> - L_i)   (0 for invisible keys),
+ *   dP_ij = <dO_i, V_j>,  dS_ij = P_ij (dP_ij - D_i),
+ *   dQ_i  = scale sum_j dS_ij K_j,
+ *   dK_j  = scale sum_{h in group} sum_i dS_ij Q_i,
+ *   dV_j  = sum_{h in group} sum_i P_ij dO_i.
+ * O and L must be the outputs of fa_fwd for the same Q, K, V, sizes, causal
+ * and scale.  Writes dQ, dK, dV (dtype) and uses `workspace` (at least
+ * fa_bwd_workspace_bytes bytes, device memory, 256-byte aligned preferred)
+ * as scratch.  No T x T tensor is ever formed.
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
+           const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+           int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
+           int dtype, void* stream);
+
+/* Static English text for a status code (never NULL). */
+const char* fa_status_string(int status);
+
+/* Text of the HIP error behind the calling thread's most recent FA_ERR_HIP
+ * (static storage, never NULL; "no HIP error" before any).  Diagnostic only. */
+const char* fa_hip_error_string(void);
+
+/* Library ABI version: (major << 16) | minor. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA05_FA_H */

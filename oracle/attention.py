@@ -80,22 +80,27 @@ def _check_shapes(Q, K, V):
     return B, Hq, Hkv, Tq, Tk, d, V.shape[3]
 
 
-def head_forward(q, k, v, causal, scale):
+def head_forward(q, k, v, causal, scale, rows=None, Tq=None):
     """One query head against its key/value head, dense, fp64.
 
     Returns (O [Tq, dv], L [Tq], P [Tq, Tk]).  Steps as in standard attention:
     S = scale q k^T; masked scores do not exist (probability 0); per row
     m = max visible S, l = sum exp(S - m), L = m + ln l, P = exp(S - m) / l;
-    O = P v.
+    O = P v.  With ``rows`` given, q holds only those query rows of a head
+    with ``Tq`` rows (the causal mask needs their positions).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    Tq, Tk = q.shape[0], k.shape[0]
-    vis = visible(Tq, Tk, causal)
+    Tk = k.shape[0]
+    if rows is None:
+        Tq = q.shape[0]
+        vis = visible(Tq, Tk, causal)
+    else:
+        vis = visible(Tq, Tk, causal)[np.asarray(rows)]
     S = (q @ k.T) * scale
     Sm = np.where(vis, S, -np.inf)
-    m = Sm.max(axis=1) if Tk > 0 else np.full(Tq, -np.inf)
+    m = Sm.max(axis=1) if Tk > 0 else np.full(q.shape[0], -np.inf)
     has_key = np.isfinite(m)
     m_safe = np.where(has_key, m, 0.0)
     E = np.where(vis, np.exp(np.where(vis, S, 0.0) - m_safe[:, None]), 0.0)

@@ -1,0 +1,102 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes the workspace, and rejects bad arguments before any
+HIP call (all calls below fail validation, so nothing reaches the device)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import attention_fa_fwd_05_amd as fa
+from attention_fa_fwd_05_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        from attention_fa_fwd_05_amd import build
+        build.build(verbose=False)
+    return fa.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert header_functions() == sorted(_binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in range(11):
+        s = fa.status_string(code)
+        assert s and s != "unknown status"
+    assert fa.status_string(99) == "unknown status"
+    assert lib.fa_abi_version() >> 16 == 1
+
+
+def test_workspace_bytes(lib):
+    # bf16: D and L2 per row (256-aligned) + fp32 dQ accumulator
+    rows = 4 * 32 * 4096
+    want = rows * 4 + rows * 4 + rows * 128 * 4
+    assert fa.workspace_bytes(4, 32, 8, 4096, 4096, 128, fa.FA_DTYPE_BF16) == want
+    # fp32: no accumulator (dQ itself accumulates)
+    assert fa.workspace_bytes(1, 1, 1, 100, 100, 64, fa.FA_DTYPE_F32) == 512 + 512
+    assert fa.workspace_bytes(1, 1, 1, 0, 5, 64, fa.FA_DTYPE_BF16) == 0
+    # invalid arguments -> 0
+    assert fa.workspace_bytes(1, 3, 2, 10, 10, 64, fa.FA_DTYPE_BF16) == 0
+    assert fa.workspace_bytes(1, 1, 1, 10, 10, 96, fa.FA_DTYPE_BF16) == 0
+
+
+FAKE = 1 << 20   # aligned, never dereferenced: every call below fails validation first
+
+
+def fwd(lib, Q=FAKE, K=FAKE, V=FAKE, O=FAKE, L=FAKE, B=1, Hq=2, Hkv=1, Tq=16, Tk=16, d=64,
+        causal=0, scale=0.125, dtype=1):
+    return lib.fa_fwd(Q, K, V, O, L, B, Hq, Hkv, Tq, Tk, d, causal, scale, dtype, None)
+
+
+def bwd(lib, ws=FAKE, ws_bytes=1 << 30, Q=FAKE, dQ=FAKE, B=1, Hq=2, Hkv=1, Tq=16, Tk=16, d=64,
+        scale=0.125, dtype=1):
+    return lib.fa_bwd(Q, FAKE, FAKE, FAKE, FAKE, FAKE, dQ, FAKE, FAKE, ws, ws_bytes,
+                      B, Hq, Hkv, Tq, Tk, d, 0, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2), (dict(Tq=-1), 2), (dict(Tk=-5), 2),
+    (dict(Hq=3, Hkv=2), 3), (dict(d=96), 4), (dict(d=256), 4), (dict(dtype=7), 5),
+    (dict(scale=math.inf), 6), (dict(scale=math.nan), 6),
+    (dict(Q=None), 1), (dict(L=None), 1), (dict(V=FAKE + 4), 8), (dict(Tq=1 << 25), 9),
+])
+def test_fwd_rejects_bad_arguments(lib, kw, status):
+    assert fwd(lib, **kw) == status
+
+
+def test_fwd_null_pointers_allowed_for_empty_tensors(lib):
+    # Tq == 0: Q, O, L have no elements; a no-op that touches nothing
+    assert fwd(lib, Q=None, O=None, L=None, Tq=0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws=None), 7), (dict(ws_bytes=100), 7), (dict(ws=FAKE + 8), 8),
+    (dict(Q=None), 1), (dict(dQ=None), 1), (dict(Hq=4, Hkv=3), 3), (dict(scale=-math.inf), 6),
+])
+def test_bwd_rejects_bad_arguments(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        _binding.load_library(str(tmp_path / "nope.so"))

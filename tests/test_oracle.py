@@ -395,3 +395,15 @@ def test_flop_count_convention():
     f, b = accounting.flops(4, 32, 4096, 4096, 128, True)
     assert f == 2 * 4096 * 4096 * 128 * 128 and b == 5 * 4096 * 4096 * 128 * 128
     assert abs((f + b) / 1e9 - 1924.145) < 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_subset_matches_bruteforce(causal):
+    q, k, v = rnd((30, 6), 41), rnd((23, 6), 42), rnd((23, 5), 43)
+    rows = np.array([0, 3, 7, 8, 29])
+    O, L, _ = oa.head_forward(q[rows], k, v, causal, 0.5, rows=rows, Tq=30)
+    Ob, Lb = brute_forward(q.tolist(), k.tolist(), v.tolist(), causal, 0.5)
+    Ob, Lb = np.array(Ob)[rows], np.array(Lb)[rows]
+    assert np.array_equal(np.isneginf(L), np.isneginf(Lb))
+    fin = np.isfinite(Lb)
+    assert np.abs(O - Ob).max() < 1e-12 and np.abs(L[fin] - Lb[fin]).max() < 1e-12

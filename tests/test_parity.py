@@ -1,0 +1,285 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerance: maximum relative Frobenius error over O, L, dQ, dK, dV of 1e-4 for
+fp32 storage and 2e-2 for bf16 storage with fp32 accumulation.  L rows that
+are -inf in the oracle must be -inf on the GPU.
+
+Small and medium workloads are compared in full.  The three large bf16
+workloads run at full size in the launch configuration the benchmark times,
+and are compared on sampled (batch, K/V head) groups computed by the oracle in
+full (every output of the group) plus sampled query rows across all heads,
+and checked everywhere with exact invariants.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle.attention as oa
+from attention_fa_fwd_05_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def fa(require_gpu):
+    import attention_fa_fwd_05_amd as fa_mod
+    fa_mod.load_library()
+    return fa_mod
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(fa, w, inp):
+    import torch
+    q, k, v, do = wl.to_device(inp, w.dtype)
+    o, lse = fa.forward(q, k, v, w.causal, w.scale)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, w.causal, w.scale)
+    torch.cuda.synchronize()
+    return {n: t.float().cpu().numpy() for n, t in
+            (("O", o), ("L", lse), ("dQ", dq), ("dK", dk), ("dV", dv))}
+
+
+def errors_full(w, inp, out):
+    O, L, dQ, dK, dV = oa.attention_forward_backward(inp.q, inp.k, inp.v, inp.do, w.causal, w.scale)
+    return {"O": oa.relative_frobenius(out["O"], O),
+            "L": oa.relative_frobenius(out["L"], L, finite_only=True),
+            "dQ": oa.relative_frobenius(out["dQ"], dQ),
+            "dK": oa.relative_frobenius(out["dK"], dK),
+            "dV": oa.relative_frobenius(out["dV"], dV)}
+
+
+def check(w, errs):
+    log(f"{w.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= TOL[w.dtype]}
+    assert not bad, f"{w.name}: over tolerance {TOL[w.dtype]}: {bad}"
+
+
+def custom(name, B, Hq, Hkv, Tq, Tk, d, dtype, causal, seed=7, sigma=1.0):
+    return wl.Workload(name, B, Hq, Hkv, Tq, Tk, d, dtype, causal, seed, sigma)
+
+
+# ------------------------------------------------------------- full comparison
+
+SMALL = [wl.WORKLOADS[n] for n in (
+    "mha_fp32_T128_d64", "mha_fp32_T1000_d64", "mha_fp32_T1000_d64_causal",
+    "mha_fp32_T1000_d64_sigma3", "mha_fp32_T1000_d64_sigma3_causal")] + [
+    # several tiles plus ragged tails, GQA, both head dims, both dtypes
+    custom("gqa_bf16_T300_d128", 2, 4, 2, 300, 300, 128, "bf16", False),
+    custom("gqa_bf16_T300_d128_causal", 2, 4, 2, 300, 300, 128, "bf16", True),
+    custom("gqa_bf16_T300_d64_causal", 1, 8, 1, 300, 300, 64, "bf16", True),
+    custom("mha_bf16_T257_d64", 2, 2, 2, 257, 257, 64, "bf16", False),
+    custom("gqa_fp32_T200_d128_causal", 1, 4, 2, 200, 200, 128, "fp32", True),
+    custom("gqa_fp32_T130_d128", 2, 2, 1, 130, 130, 128, "fp32", False),
+    # end-aligned causal with Tq != Tk, including rows that see no key
+    custom("gqa_bf16_Tq200_Tk333_causal", 1, 4, 2, 200, 333, 128, "bf16", True),
+    custom("gqa_bf16_Tq333_Tk200_causal", 1, 4, 2, 333, 200, 128, "bf16", True),
+    custom("mha_fp32_Tq150_Tk40_causal", 1, 2, 2, 150, 40, 64, "fp32", True),
+    custom("mha_fp32_Tq40_Tk150", 1, 2, 2, 40, 150, 64, "fp32", False),
+    # a single query row
+    custom("mha_fp32_Tq1_Tk77_d64", 1, 2, 1, 1, 77, 64, "fp32", False),
+    custom("mha_bf16_Tq1_Tk300_d128", 1, 2, 1, 1, 300, 128, "bf16", False),
+    # large score spread (frequent running-max rescales) in bf16
+    custom("gqa_bf16_T512_d128_sigma3_causal", 1, 4, 1, 512, 512, 128, "bf16", True, 9, 3.0),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_parity_full(fa, w):
+    log(f"case {w.name}")
+    inp = wl.make_inputs(w)
+    out = run_gpu(fa, w, inp)
+    check(w, errors_full(w, inp, out))
+
+
+def test_non_default_scale(fa):
+    import torch
+    w = custom("gqa_bf16_T200_d128_causal_scale0.3", 1, 4, 2, 200, 200, 128, "bf16", True)
+    inp = wl.make_inputs(w)
+    q, k, v, do = wl.to_device(inp, w.dtype)
+    o, lse = fa.forward(q, k, v, True, 0.3)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, True, 0.3)
+    torch.cuda.synchronize()
+    got = [t.float().cpu().numpy() for t in (o, lse, dq, dk, dv)]
+    ref = oa.attention_forward_backward(inp.q, inp.k, inp.v, inp.do, True, 0.3)
+    check(w, {n: oa.relative_frobenius(g, r, finite_only=(n == "L"))
+              for n, g, r in zip(("O", "L", "dQ", "dK", "dV"), got, ref)})
+
+
+@pytest.mark.parametrize("w", [
+    custom("mha_bf16_T1_d128_causal", 1, 2, 2, 1, 1, 128, "bf16", True),
+    custom("mha_bf16_Tq70_Tk1_d128", 1, 4, 4, 70, 1, 128, "bf16", False),
+    custom("gqa_fp32_Tq70_Tk1_d64", 2, 4, 2, 70, 1, 64, "fp32", False),
+], ids=lambda w: w.name)
+def test_single_key_closed_form(fa, w):
+    """One visible key per row: O = V_0, L = scale q.k_0, dV_0 = sum dO and dQ = dK = 0.
+
+    dQ and dK vanish exactly, so their error is measured against the size of
+    the terms that cancel: scale * |dO| |V_0| |K_0| (Frobenius norms).
+    """
+    inp = wl.make_inputs(w)
+    out = run_gpu(fa, w, inp)
+    O, L, dQ, dK, dV = oa.attention_forward_backward(inp.q, inp.k, inp.v, inp.do, w.causal, w.scale)
+    assert np.abs(dQ).max() < 1e-12 and np.abs(dK).max() < 1e-12
+    errs = {"O": oa.relative_frobenius(out["O"], O),
+            "L": oa.relative_frobenius(out["L"], L, finite_only=True),
+            "dV": oa.relative_frobenius(out["dV"], dV)}
+    size = w.scale * np.linalg.norm(inp.do) * np.linalg.norm(inp.v) * np.linalg.norm(inp.k)
+    errs["dQ"] = float(np.linalg.norm(out["dQ"]) / size)
+    errs["dK"] = float(np.linalg.norm(out["dK"]) / size)
+    check(w, errs)
+
+
+# ------------------------------------------------------------- empty inputs
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_no_keys(fa, dtype):
+    import torch
+    tdt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    q = torch.randn(1, 4, 70, 64, device="cuda").to(tdt)
+    k = torch.empty(1, 2, 0, 64, device="cuda", dtype=tdt)
+    v = torch.empty(1, 2, 0, 64, device="cuda", dtype=tdt)
+    o, lse = fa.forward(q, k, v, False)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    do = torch.randn_like(q)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, False)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0) and dk.numel() == 0 and dv.numel() == 0
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_no_queries(fa, dtype):
+    import torch
+    tdt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    q = torch.empty(2, 4, 0, 128, device="cuda", dtype=tdt)
+    k = torch.randn(2, 2, 130, 128, device="cuda").to(tdt)
+    v = torch.randn(2, 2, 130, 128, device="cuda").to(tdt)
+    o, lse = fa.forward(q, k, v, True)
+    assert o.numel() == 0 and lse.numel() == 0
+    dk0 = torch.full_like(k, 7.0)
+    dv0 = torch.full_like(v, 7.0)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, torch.empty_like(q), True, dk=dk0, dv=dv0)
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+
+
+# ------------------------------------------------------------- large workloads
+
+LARGE = [wl.WORKLOADS[n] for n in ("mha_bf16_T2048_d128_causal", "gqa_bf16_T4096_d128_causal",
+                                   "gqa_bf16_T8000x8032_d128")]
+
+
+@pytest.mark.parametrize("w", LARGE, ids=[w.name for w in LARGE])
+def test_parity_large_sampled(fa, w):
+    log(f"case {w.name}: generating inputs")
+    inp = wl.make_inputs(w)
+    out = run_gpu(fa, w, inp)
+    log(f"case {w.name}: GPU done")
+    for name, arr in out.items():
+        fin = np.isfinite(arr) if name != "L" else ~np.isnan(arr)
+        assert fin.all(), f"{name} has non-finite values"
+    # full oracle on sampled (b, K/V head) groups: every output of the group
+    rng = np.random.default_rng(1234)
+    groups = [(0, 0), (w.B - 1, w.Hkv - 1)] if w.B * w.Hkv > 1 else [(0, 0)]
+    if w.B * w.Hkv > 2:
+        groups.append((int(rng.integers(w.B)), int(rng.integers(w.Hkv))))
+    G = w.G
+    for b, g in groups[:2 if w.Tq * w.Tk > 2e7 else 3]:
+        ref = oa.group_forward_backward(inp.q, inp.k, inp.v, inp.do, b, g, w.causal, w.scale)
+        errs = {"O": oa.relative_frobenius(out["O"][b, g * G:(g + 1) * G], ref["O"]),
+                "L": oa.relative_frobenius(out["L"][b, g * G:(g + 1) * G], ref["L"], finite_only=True),
+                "dQ": oa.relative_frobenius(out["dQ"][b, g * G:(g + 1) * G], ref["dQ"]),
+                "dK": oa.relative_frobenius(out["dK"][b, g], ref["dK"]),
+                "dV": oa.relative_frobenius(out["dV"][b, g], ref["dV"])}
+        check(w.with_(name=f"{w.name}[b={b},g={g}]"), errs)
+    # sampled query rows across every head: O and L
+    rows = np.unique(np.concatenate([[0, w.Tq - 1], rng.integers(0, w.Tq, 6)]))
+    Os, Ls, Or, Lr = [], [], [], []
+    for b in range(w.B):
+        for h in range(w.Hq):
+            o, lse, _ = oa.head_forward(inp.q[b, h, rows], inp.k[b, h // G], inp.v[b, h // G],
+                                        w.causal, w.scale, rows=rows, Tq=w.Tq)
+            Or.append(o), Lr.append(lse)
+            Os.append(out["O"][b, h, rows]), Ls.append(out["L"][b, h, rows])
+    check(w.with_(name=f"{w.name}[rows]"),
+          {"O": oa.relative_frobenius(np.stack(Os), np.stack(Or)),
+           "L": oa.relative_frobenius(np.stack(Ls), np.stack(Lr), finite_only=True)})
+    # exact invariants on every output: dK sums to zero over keys; dV sums to the
+    # group's summed cotangent (all rows see at least one key here)
+    dk_sum = out["dK"].sum(axis=2)
+    assert np.abs(dk_sum).max() <= 2e-2 * np.abs(out["dK"]).sum(axis=2).max()
+    do_sum = inp.do.astype(np.float64).reshape(w.B, w.Hkv, G, w.Tq, w.d).sum(axis=(2, 3))
+    dv_sum = out["dV"].astype(np.float64).sum(axis=2)
+    assert oa.relative_frobenius(dv_sum, do_sum) <= 2e-2
+
+
+# ------------------------------------------------------------- library behaviour
+
+def test_determinism_of_dk_dv(fa):
+    import torch
+    w = custom("gqa_bf16_T700_d128_causal", 2, 8, 2, 700, 700, 128, "bf16", True)
+    inp = wl.make_inputs(w)
+    q, k, v, do = wl.to_device(inp, w.dtype)
+    o, lse = fa.forward(q, k, v, True)
+    o2, lse2 = fa.forward(q, k, v, True)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    r1 = fa.backward(q, k, v, o, lse, do, True)
+    r2 = fa.backward(q, k, v, o, lse, do, True)
+    torch.cuda.synchronize()
+    assert torch.equal(r1[1], r2[1]) and torch.equal(r1[2], r2[2])
+    rel = (r1[0].float() - r2[0].float()).norm() / r1[0].float().norm()
+    assert rel <= 1e-2   # dQ: atomics may change the summation order
+
+
+def test_library_allocates_nothing(fa):
+    import torch
+    w = custom("gqa_bf16_T256_d128", 1, 4, 2, 256, 256, 128, "bf16", True)
+    inp = wl.make_inputs(w)
+    q, k, v, do = wl.to_device(inp, w.dtype)
+    o, lse = torch.empty_like(q), torch.empty(1, 4, 256, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.workspace_bytes(1, 4, 2, 256, 256, 128, fa.FA_DTYPE_BF16), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    fa.forward(q, k, v, True, out=o, lse=lse)
+    fa.backward(q, k, v, o, lse, do, True, workspace=ws, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == before
+
+
+def test_workspace_too_small_is_rejected(fa):
+    import torch
+    q = torch.randn(1, 2, 64, 128, device="cuda").to(torch.bfloat16)
+    k = torch.randn(1, 2, 64, 128, device="cuda").to(torch.bfloat16)
+    o, lse = fa.forward(q, k, k, False)
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(fa.FaError) as ei:
+        fa.backward(q, k, k, o, lse, torch.randn_like(q), False, workspace=ws)
+    assert ei.value.status == 7
+
+
+def test_autograd_wrapper_retains_linear_state(fa):
+    import torch
+    w = custom("mha_bf16_T512_d128", 1, 2, 2, 512, 512, 128, "bf16", True)
+    inp = wl.make_inputs(w)
+    q, k, v, do = (t.clone().requires_grad_(i < 3) for i, t in enumerate(wl.to_device(inp, w.dtype)))
+    saved = []
+
+    def pack(t):
+        saved.append((t.data_ptr(), t.numel() * t.element_size()))
+        return t
+
+    with torch.autograd.graph.saved_tensors_hooks(pack, lambda t: t):
+        o = fa.attention(q, k, v, True)
+    (o.float() * do.detach().float()).sum().backward()
+    total = sum(b for _, b in dict(saved).items())
+    from attention_fa_fwd_05_amd import accounting
+    assert total == accounting.retained_bytes_recompute(1, 2, 2, 512, 512, 128, "bf16")
+    O, L, dQ, dK, dV = oa.attention_forward_backward(inp.q, inp.k, inp.v, inp.do, True, w.scale)
+    assert oa.relative_frobenius(q.grad.float().cpu().numpy(), dQ) <= 2e-2
