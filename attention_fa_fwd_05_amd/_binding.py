@@ -21,10 +21,11 @@ FA_DTYPE_BF16 = 1
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_GQA_RATIO",
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_DTYPE", 6: "FA_ERR_SCALE", 7: "FA_ERR_WORKSPACE",
-    8: "FA_ERR_ALIGNMENT", 9: "FA_ERR_TOO_LARGE", 10: "FA_ERR_HIP",
+    8: "FA_ERR_ALIGNMENT", 9: "FA_ERR_TOO_LARGE", 10: "FA_ERR_HIP", 11: "FA_ERR_STAGES",
 }
-EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string", "fa_hip_error_string",
-           "fa_abi_version"]
+STAGE_PRE, STAGE_MAIN, STAGE_FINISH, STAGE_ALL = 1, 2, 4, 7
+EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_bwd_workspace_bytes", "fa_status_string",
+           "fa_hip_error_string", "fa_abi_version"]
 
 _lib = None
 
@@ -58,6 +59,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                            i, i, i, i, i, i, i, f, i, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_stages.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                  i, i, i, i, i, i, i, f, i, ctypes.c_uint, vp]
+    lib.fa_bwd_stages.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -128,8 +132,8 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
 
 
 def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
-             workspace=None, dq=None, dk=None, dv=None):
-    """fa_bwd: returns (dq, dk, dv) like q, k, v."""
+             workspace=None, dq=None, dk=None, dv=None, stages: int = STAGE_ALL):
+    """fa_bwd (fa_bwd_stages for a partial stage mask): returns (dq, dk, dv) like q, k, v."""
     import torch
     lib = load_library()
     B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
@@ -147,9 +151,12 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
-                    _ptr(dv), ws.data_ptr(), ws.numel(), B, Hq, Hkv, Tq, Tk, d,
-                    int(bool(causal)), scale, code, _stream(q))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+            _ptr(dv), ws.data_ptr(), ws.numel(), B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), scale, code)
+    if stages == STAGE_ALL:
+        st = lib.fa_bwd(*args, _stream(q))
+    else:
+        st = lib.fa_bwd_stages(*args, stages, _stream(q))
     if st != 0:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv

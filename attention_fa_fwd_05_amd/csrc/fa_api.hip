@@ -89,6 +89,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_ALIGNMENT: return "pointers must be 16-byte aligned";
     case FA_ERR_TOO_LARGE: return "a size exceeds the library's index range";
     case FA_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    case FA_ERR_STAGES: return "unknown backward stage bits";
     default: return "unknown status";
   }
 }
@@ -120,6 +121,14 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const flo
            const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
            int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
            int dtype, void* stream) {
+  return fa_bwd_stages(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq, Hkv, Tq, Tk, d,
+                       causal, scale, dtype, FA_BWD_STAGE_ALL, stream);
+}
+
+int fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                  const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                  int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
+                  int dtype, unsigned stages, void* stream) {
   int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
   if (st != FA_OK) return st;
   const long long nq = (long long)B * Hq * Tq * d, nkv = (long long)B * Hkv * Tk * d;
@@ -129,6 +138,7 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const flo
       (st = check_ptr(dK, nkv)) || (st = check_ptr(dV, nkv)) || (st = check_ptr(L, rows)))
     return st;
   if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (stages & ~(unsigned)FA_BWD_STAGE_ALL) return FA_ERR_STAGES;
   const WsLayout ws = ws_layout(B, Hq, Tq, d, dtype);
   if (ws.total > 0) {
     if (workspace == nullptr || workspace_bytes < ws.total) return FA_ERR_WORKSPACE;
@@ -146,7 +156,7 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const flo
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  return hip_status(fa::launch_bwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream));
+  return hip_status(fa::launch_bwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, stages, (hipStream_t)stream));
 }
 
 }  // extern "C"

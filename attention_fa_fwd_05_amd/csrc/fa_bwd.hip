@@ -212,27 +212,29 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
 }
 
 template <typename T, int D, bool CAUSAL>
-hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   const long long rows = (long long)a.B * a.Hq * a.Tq;
-  if (rows > 0) {
+  if ((stages & kStagePre) && rows > 0) {
     hipError_t e = launch(bwd_pre_kernel<T, D>, (rows + 15) / 16, stream, a);
     if (e != hipSuccess) return e;
   }
   const long long kblocks = (long long)((a.Tk + 127) / 128) * a.B * a.Hkv;
-  if (kblocks > 0) {
+  if ((stages & kStageMain) && kblocks > 0) {
     hipError_t e = launch(bwd_kernel<T, D, CAUSAL>, kblocks, stream, a);
     if (e != hipSuccess) return e;
   }
-  if (sizeof(T) == 2 && rows > 0) {
+  if ((stages & kStageFinish) && sizeof(T) == 2 && rows > 0) {
     const long long n8 = rows * D / 8;
     return launch(dq_convert_kernel, (n8 + 255) / 256, stream, (const float*)a.dQacc, (bf16*)a.dQ, n8);
   }
   return hipSuccess;
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream) {
-#define FA_BWD_CASE(T, DD)                                                              \
-  if (d == DD) return causal ? launch_bwd_t<T, DD, true>(a, stream) : launch_bwd_t<T, DD, false>(a, stream);
+hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int d, int causal, unsigned stages,
+                      hipStream_t stream) {
+#define FA_BWD_CASE(T, DD)                                                                         \
+  if (d == DD)                                                                                     \
+    return causal ? launch_bwd_t<T, DD, true>(a, stages, stream) : launch_bwd_t<T, DD, false>(a, stages, stream);
   if (dtype_bf16) {
     FA_BWD_CASE(bf16, 64)
     FA_BWD_CASE(bf16, 128)

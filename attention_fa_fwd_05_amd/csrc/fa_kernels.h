@@ -45,6 +45,9 @@ inline hipError_t launch(void (*kernel)(Params...), long long blocks, hipStream_
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream);
+// Backward stages (bit mask): preprocess, main kernel, dQ finish.
+constexpr unsigned kStagePre = 1u, kStageMain = 2u, kStageFinish = 4u;
+hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int d, int causal, unsigned stages,
+                      hipStream_t stream);
 
 }  // namespace fa

@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = the whole path over one batch: forward (O, L) then the backward
+(preprocess, main kernel, dQ finish) with a fixed cotangent dO.  Inputs are
+seeded synthetic tensors already resident in HBM; outputs and the workspace
+are allocated once, outside the timed region.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+Prints one JSON line: whole-step throughput in counted TFLOP/s (4*Tq*Tk*d
+forward + 10*Tq*Tk*d backward per query head, halved when causal), the
+roofline of the dominant kernel (its counted FLOPs per launch over its average
+launch time, from HIP events recorded on the stream the kernels run on), and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s & % bf16 MFMA peak, d=128 T=4096 GQA causal"
+# MI355X dense matrix peaks (TFLOP/s): 256 CUs x 2.4 GHz x 4096 bf16 flop/clk/CU.
+PEAK = {"bf16": 2516.6, "fp32": 157.3}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ["fa_common.h", "fa_kernels.h", "fa_fwd.hip", "fa_bwd.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "attention_fa_fwd_05_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload, {}).get(kernel)
+    if not entry or entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry["bytes_per_launch"]
+
+
+def cpu_baseline(w, inp, budget_s: float):
+    """Time the fp64 oracle on whole (batch, K/V head) groups until the budget is used."""
+    import numpy as np
+    import oracle.attention as oa
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    groups = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
+    rng = np.random.default_rng(0)
+    rng.shuffle(groups)
+    done, t0 = 0, time.perf_counter()
+    for b, g in groups:
+        oa.group_forward_backward(inp.q, inp.k, inp.v, inp.do, b, g, w.causal, w.scale)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    elapsed = time.perf_counter() - t0
+    f = (4.0 + 10.0) * w.G * w.Tq * w.Tk * w.d * (0.5 if w.causal else 1.0) * done
+    return {"value": f / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {len(groups)} (batch, K/V head) groups ({done * w.G} query heads), "
+                      f"dense fp64 forward+backward, {elapsed:.1f} s"}
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """A plain device copy of known size, for scaling rocprofv3 byte counters."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget for the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="run only a device copy of BYTES bytes (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the attention path here has no multi-GPU mode", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import attention_fa_fwd_05_amd as fa
+    from attention_fa_fwd_05_amd import accounting
+    from attention_fa_fwd_05_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, max(1, args.steps))
+        return 0
+
+    w = wl.WORKLOADS[args.workload or wl.HEADLINE]
+    fa.load_library()
+    inp = wl.make_inputs(w)
+    q, k, v, do = wl.to_device(inp, w.dtype)
+    code = fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_F32
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.Hq, w.Tq, dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(1, fa.workspace_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, code)),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.forward(q, k, v, w.causal, w.scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        for i, stage in enumerate((fa.STAGE_PRE, fa.STAGE_MAIN, fa.STAGE_FINISH)):
+            fa.backward(q, k, v, o, lse, do, w.causal, w.scale, workspace=ws, dq=dq, dk=dk, dv=dv,
+                        stages=stage)
+            if ev is not None:
+                ev[2 + i].record()
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    def avg_ms(a, b):
+        return sum(e[a].elapsed_time(e[b]) for e in events) / len(events)
+
+    ms_fwd, ms_pre, ms_main, ms_fin = avg_ms(0, 1), avg_ms(1, 2), avg_ms(2, 3), avg_ms(3, 4)
+    f_fwd, f_bwd = accounting.flops(w.B, w.Hq, w.Tq, w.Tk, w.d, w.causal)
+    ms_step = elapsed / args.steps * 1e3
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    peak = PEAK[w.dtype]
+    kernels = {"fwd_kernel": (f_fwd, ms_fwd), "bwd_kernel": (f_bwd, ms_main)}
+    dom = max(kernels, key=lambda n: kernels[n][1])
+    dom_flops, dom_ms = kernels[dom]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    ret = accounting.retained_bytes_recompute(w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, w.dtype)
+    dense = accounting.retained_bytes_dense(w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, w.dtype)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs and cotangent, rounded to bf16)" if w.dtype == "bf16"
+                else "synthetic (seeded N(0,1) inputs and cotangent)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Tq": w.Tq, "Tk": w.Tk,
+                   "d": w.d, "causal": w.causal, "scale": w.scale, "parallelism": "single GPU"},
+        "pct_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": stored_traffic(w.name, dom),
+                     "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 4)},
+        "breakdown_ms": {"fwd_kernel": round(ms_fwd, 4), "bwd_pre_kernel": round(ms_pre, 4),
+                         "bwd_kernel": round(ms_main, 4), "dq_convert_kernel": round(ms_fin, 4)},
+        "fwd_tflops": round(f_fwd / (ms_fwd * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(f_bwd / ((ms_pre + ms_main + ms_fin) * 1e-3) / 1e12, 2),
+        "retained_bytes": {"recompute_qkvoL": ret, "dense_qkv_plus_P": dense,
+                           "ratio": round(dense / ret, 2)},
+        "workspace_bytes": ws.numel(),
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

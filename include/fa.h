@@ -69,7 +69,8 @@ typedef enum {
   FA_ERR_WORKSPACE = 7,  /* workspace missing or smaller than fa_bwd_workspace_bytes */
   FA_ERR_ALIGNMENT = 8,  /* a pointer is not 16-byte aligned */
   FA_ERR_TOO_LARGE = 9,  /* a size exceeds the library's index range */
-  FA_ERR_HIP = 10        /* a HIP runtime call or kernel launch failed */
+  FA_ERR_HIP = 10,       /* a HIP runtime call or kernel launch failed */
+  FA_ERR_STAGES = 11     /* fa_bwd_stages: a bit outside FA_BWD_STAGE_ALL is set */
 } fa_status;
 
 typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
@@ -113,6 +114,26 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const flo
            const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
            int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
            int dtype, void* stream);
+
+/*
+ * The backward pass in three stages, for callers that time or schedule them
+ * separately.  Same arguments and semantics as fa_bwd, plus a bit mask:
+ *   FA_BWD_STAGE_PRE    D = rowsum(dO * O) and log2-domain L into the
+ *                       workspace; zero the fp32 dQ accumulator;
+ *   FA_BWD_STAGE_MAIN   recompute S and P tile by tile; write dK and dV;
+ *                       accumulate dQ (fp32);
+ *   FA_BWD_STAGE_FINISH (bf16) round the dQ accumulator into dQ; no-op for fp32.
+ * Stages read what earlier stages left in the workspace, so they must run in
+ * this order, on one stream, with identical arguments; fa_bwd runs all three.
+ */
+#define FA_BWD_STAGE_PRE 1u
+#define FA_BWD_STAGE_MAIN 2u
+#define FA_BWD_STAGE_FINISH 4u
+#define FA_BWD_STAGE_ALL 7u
+int fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                  const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                  int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
+                  int dtype, unsigned stages, void* stream);
 
 /* Static English text for a status code (never NULL). */
 const char* fa_status_string(int status);

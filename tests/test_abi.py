@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(11):
+    for code in range(12):
         s = fa.status_string(code)
         assert s and s != "unknown status"
     assert fa.status_string(99) == "unknown status"
@@ -95,6 +95,12 @@ def test_fwd_null_pointers_allowed_for_empty_tensors(lib):
 ])
 def test_bwd_rejects_bad_arguments(lib, kw, status):
     assert bwd(lib, **kw) == status
+
+
+def test_bwd_stages_rejects_unknown_bits(lib):
+    args = (FAKE,) * 10 + (1 << 30, 1, 2, 1, 16, 16, 64, 0, 0.125, 1)
+    assert lib.fa_bwd_stages(*args, 8, None) == 11
+    assert lib.fa_bwd_stages(*(args[:2] + (None,) + args[3:]), 2, None) == 1
 
 
 def test_missing_library_fails_loudly(tmp_path):
