@@ -8,13 +8,14 @@
 // statistic L = m + ln l is kept for the backward pass ("Why this is
 // FlashAttention's second idea").
 //
-// Mapping onto CDNA4.  One workgroup = 4 waves = 128 query rows of one (b, h);
+// Mapping onto CDNA4.  One workgroup = 8 waves = 256 query rows of one (b, h);
 // each wave owns 32 rows.  The wave computes the transposed score tile
 // S^T = K_j Q_i^T (keys x queries) so that one query row lives in one lane
 // column: the row max is an in-register reduction plus one exchange between
 // the two lane halves, and the probabilities feed O^T += V_j^T P^T straight
-// from registers.  K_j and V_j (64 keys) are staged in LDS in natural layout;
-// V^T operands are fetched with transposed LDS reads.  Softmax runs in the
+// from registers.  K_j and V_j (64 keys) are staged in LDS in natural layout,
+// double-buffered (the next tile's global loads are in flight while the
+// current one is computed); V^T operands are fetched with transposed LDS reads.  Softmax runs in the
 // exp2 domain (scores pre-multiplied by scale * log2 e); L is converted back
 // to a natural log at the end.
 #include "fa_common.h"
@@ -22,33 +23,99 @@
 
 namespace fa {
 
+// Work items in dispatch order.  Consecutive workgroup ids are spread over
+// the 8 XCDs round-robin; giving each XCD one contiguous range of the logical
+// order keeps every workgroup of a (batch, K/V head) group on one XCD, so the
+// group's K and V stay in that XCD's L2 while its query heads stream past.
+// Logical order: group, then query block (longest rows first when causal),
+// then query head within the group.
+struct FwdWork {
+  int b, hq, hk, qb;
+};
+
+__device__ inline FwdWork fwd_work(const FwdArgs& a, int nqb, bool causal) {
+  const int N = gridDim.x, p = blockIdx.x;
+  const int x = p & 7, slot = p >> 3, per = N >> 3, rem = N & 7;
+  const int logical = x * per + min(x, rem) + slot;
+  const int G = a.Hq / a.Hkv;
+  const int r = logical % G, t = logical / G;
+  const int qi = t % nqb, grp = t / nqb;
+  FwdWork w;
+  w.b = grp / a.Hkv;
+  w.hk = grp % a.Hkv;
+  w.hq = w.hk * G + r;
+  w.qb = causal ? nqb - 1 - qi : qi;
+  return w;
+}
+
+// Lazy rescale threshold (log2 units): the reference max m_run only moves when
+// a row's true max exceeds it by more than 2^TAU, so probabilities stay <= 2^8
+// and the O accumulator is rescaled only on the rare tiles where that happens.
+constexpr float kTau = 8.0f;
+
+// Waves per workgroup: 8 (256 query rows, two waves per SIMD), or 4 where the
+// fp32 d = 128 operands would not fit in 256 registers.
+template <typename T, int D>
+constexpr int fwd_waves() { return (sizeof(T) == 4 && D == 128) ? 4 : 8; }
+
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__((64 * fwd_waves<T, D>())) void fwd_kernel(FwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
-  constexpr int BQ = 128, BK = 64;
+  constexpr int NW = fwd_waves<T, D>(), BQ = 32 * NW, BK = 64;
   constexpr int KPER = M::KPER;
-  constexpr int LD = D + 16 / (int)sizeof(T);       // LDS row stride (elements)
+  constexpr int LD = D + 32 / (int)sizeof(T);       // 32-byte row padding
   constexpr int NSD = (D / 2) / KPER;               // steps over the head dim
   constexpr int NSK = (BK / 2) / KPER;              // steps over a key tile
   constexpr int NDT = D / 32;                       // 32-wide output tiles
-  __shared__ __attribute__((aligned(16))) T sK[BK * LD];
-  __shared__ __attribute__((aligned(16))) T sV[BK * LD];
+  constexpr int EPC = 16 / (int)sizeof(T);          // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;                      // chunks per row
+  constexpr int NCH = BK * CPR / (NW * 64);         // chunks per thread per tile
+  static_assert(NCH * NW * 64 == BK * CPR, "tile must split evenly");
+  __shared__ __attribute__((aligned(16))) T sK[2][BK * LD];
+  __shared__ __attribute__((aligned(16))) T sV[2][BK * LD];
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
-  const int BH = a.B * a.Hq;
   const int nqb = (a.Tq + BQ - 1) / BQ;
-  const int bh = blockIdx.x % BH;
-  int qb = blockIdx.x / BH;
-  if (CAUSAL) qb = nqb - 1 - qb;                    // longest rows first
-  const int b = bh / a.Hq, hq = bh % a.Hq, hk = hq / (a.Hq / a.Hkv);
-  const int q0 = qb * BQ, qw = q0 + 32 * w, myq = qw + n;
+  const FwdWork wk = fwd_work(a, nqb, CAUSAL);
+  const int bh = wk.b * a.Hq + wk.hq;
+  const int q0 = wk.qb * BQ, qw = q0 + 32 * w, myq = qw + n;
   const int off = a.Tk - a.Tq;
 
   const T* Qp = reinterpret_cast<const T*>(a.Q) + (size_t)bh * a.Tq * D;
-  const T* Kp = reinterpret_cast<const T*>(a.K) + (size_t)(b * a.Hkv + hk) * a.Tk * D;
-  const T* Vp = reinterpret_cast<const T*>(a.V) + (size_t)(b * a.Hkv + hk) * a.Tk * D;
+  const T* Kp = reinterpret_cast<const T*>(a.K) + (size_t)(wk.b * a.Hkv + wk.hk) * a.Tk * D;
+  const T* Vp = reinterpret_cast<const T*>(a.V) + (size_t)(wk.b * a.Hkv + wk.hk) * a.Tk * D;
+
+  int kend = a.Tk;
+  if (CAUSAL) kend = min(a.Tk, max(0, q0 + BQ + off));
+  const int ntiles = (kend + BK - 1) / BK;
+
+  // K/V tile staging: global -> registers (issued a tile ahead) -> LDS.
+  uint4 pk[NCH], pv[NCH];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int idx = i * NW * 64 + tid, row = idx / CPR, ch = idx % CPR;
+      const bool ok = k0 + row < a.Tk;
+      const size_t o = (size_t)(ok ? k0 + row : 0) * D + ch * EPC;
+      pk[i] = ld16(Kp + o);
+      pv[i] = ld16(Vp + o);
+      if (!ok) { pk[i] = uint4{0u, 0u, 0u, 0u}; pv[i] = uint4{0u, 0u, 0u, 0u}; }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int idx = i * NW * 64 + tid, row = idx / CPR, ch = idx % CPR;
+      st16(&sK[buf][row * LD + ch * EPC], pk[i]);
+      st16(&sV[buf][row * LD + ch * EPC], pv[i]);
+    }
+  };
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
 
   // Q^T operand for this lane: query myq, head-dim half h.
   Op qop[NSD];
@@ -61,71 +128,71 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       if (!ok) qop[s] = Op{};
     }
   }
+  __syncthreads();
 
   const float c = a.scale_log2;
-  float m = -INFINITY, lsum = 0.f;
+  float m_run = -INFINITY, lsum = 0.f;
   f32x16 o[NDT];
 #pragma unroll
   for (int t = 0; t < NDT; ++t) o[t] = f32x16{};
 
-  int kend = a.Tk;
-  if (CAUSAL) kend = min(a.Tk, max(0, q0 + BQ + off));
-  const int ntiles = (kend + BK - 1) / BK;
-
   for (int jt = 0; jt < ntiles; ++jt) {
-    const int k0 = jt * BK;
-    __syncthreads();
-    stage_tile<T, D, LD, BK>(sK, Kp + (size_t)k0 * D, a.Tk - k0);
-    stage_tile<T, D, LD, BK>(sV, Vp + (size_t)k0 * D, a.Tk - k0);
-    __syncthreads();
-    if (CAUSAL && k0 > qw + 31 + off) continue;     // every key hidden from this wave
+    const int k0 = jt * BK, buf = jt & 1;
+    const bool more = jt + 1 < ntiles;
+    if (more) gload(k0 + BK);
 
-    // S^T tile: 64 keys x 32 queries as two 32x32 accumulators.
-    f32x16 st[2];
+    if (!(CAUSAL && k0 > qw + 31 + off)) {          // some key of the tile visible to this wave
+      f32x16 st0 = f32x16{}, st1 = f32x16{};
+      const T* kr = &sK[buf][n * LD + h * (D / 2)];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      st[t] = f32x16{};
-      const T* krow = sK + (t * 32 + n) * LD + h * (D / 2);
+      for (int s = 0; s < NSD; ++s) {
+        st0 = M::mma(M::ld(kr + s * KPER), qop[s], st0);
+        st1 = M::mma(M::ld(kr + 32 * LD + s * KPER), qop[s], st1);
+      }
+      float x[32];
 #pragma unroll
-      for (int s = 0; s < NSD; ++s) st[t] = M::mma(M::ld(krow + s * KPER), qop[s], st[t]);
-    }
+      for (int i = 0; i < 16; ++i) { x[i] = st0[i]; x[16 + i] = st1[i]; }
+      if ((k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off)) {
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+          const int key = k0 + perm_index(h, r);
+          if (key >= a.Tk || (CAUSAL && key > myq + off)) x[r] = -INFINITY;
+        }
+      }
+      float mt = fmaxf(x[0], x[1]);
+#pragma unroll
+      for (int r = 2; r < 32; r += 2) mt = fmaxf(mt, fmaxf(x[r], x[r + 1]));
+      mt = wave_xor32_max(mt) * c;                   // row max, exp2 units
+      const bool need = mt > m_run + kTau;
+      if (__ballot(need)) {
+        const float m_new = need ? mt : m_run;
+        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+        lsum *= alpha;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) o[t] *= alpha;
+        m_run = m_new;
+      }
+      const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        x[r] = fast_exp2(__builtin_fmaf(x[r], c, nm));
+        ps += x[r];
+      }
+      lsum += ps;
 
-    float x[32];
-    const bool need_mask = (k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off);
+      Op pop[NSK];
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      x[r] = st[r >> 4][r & 15] * c;
-      if (need_mask) {
-        const int key = k0 + perm_index(h, r);
-        if (key >= a.Tk || (CAUSAL && key > myq + off)) x[r] = -INFINITY;
+      for (int s = 0; s < NSK; ++s) pop[s] = M::pack(x + s * KPER);
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) {
+#pragma unroll
+        for (int s = 0; s < NSK; ++s)
+          o[t] = M::mma(TrPerm<T>::ld(&sV[buf][0], LD, h, s, t * 32), pop[s], o[t]);
       }
     }
-    float mt = x[0];
-#pragma unroll
-    for (int r = 1; r < 32; ++r) mt = fmaxf(mt, x[r]);
-    mt = wave_xor32_max(mt);
-    const float m_new = fmaxf(m, mt);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    float ps = 0.f;
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      x[r] = fast_exp2(x[r] - m_use);
-      ps += x[r];
-    }
-    lsum = lsum * alpha + ps;
-    m = m_new;
-#pragma unroll
-    for (int t = 0; t < NDT; ++t) o[t] *= alpha;
-
-    Op pop[NSK];
-#pragma unroll
-    for (int s = 0; s < NSK; ++s) pop[s] = M::pack(x + s * KPER);
-#pragma unroll
-    for (int t = 0; t < NDT; ++t) {
-#pragma unroll
-      for (int s = 0; s < NSK; ++s) o[t] = M::mma(TrPerm<T>::ld(sV, LD, h, s, t * 32), pop[s], o[t]);
-    }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
   }
 
   const float ltot = wave_xor32_sum(lsum);
@@ -141,16 +208,20 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
                o[t][4 * g + 3] * inv);
       }
     }
-    if (h == 0) a.L[(size_t)bh * a.Tq + myq] = ltot > 0.f ? m * kLn2 + logf(ltot) : -INFINITY;
+    if (h == 0) {
+      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+      a.L[(size_t)bh * a.Tq + myq] = ltot > 0.f ? mref * kLn2 + logf(ltot) : -INFINITY;
+    }
   }
 }
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  const int nqb = (a.Tq + 127) / 128;
+  constexpr int NW = fwd_waves<T, D>();
+  const int nqb = (a.Tq + 32 * NW - 1) / (32 * NW);
   const long long blocks = (long long)nqb * a.B * a.Hq;
   if (blocks == 0) return hipSuccess;
-  return launch(fwd_kernel<T, D, CAUSAL>, blocks, stream, a);
+  return launch<64 * NW>(fwd_kernel<T, D, CAUSAL>, blocks, stream, a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream) {

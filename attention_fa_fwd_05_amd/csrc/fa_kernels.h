@@ -35,13 +35,14 @@ struct BwdArgs {
   float scale_log2;
 };
 
-// Launch a 256-thread kernel on a 1-D grid and return that launch's own status
-// (the thread's sticky last-error state is neither read nor cleared).
-template <typename... Params, typename... Args>
+// Launch a kernel of THREADS threads per workgroup on a 1-D grid and return
+// that launch's own status (the thread's sticky last-error state is neither
+// read nor cleared).
+template <int THREADS = 256, typename... Params, typename... Args>
 inline hipError_t launch(void (*kernel)(Params...), long long blocks, hipStream_t stream, Args... args) {
   void* argv[] = {static_cast<void*>(&args)...};
-  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)blocks), dim3(256), argv, 0,
-                         stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)blocks), dim3(THREADS), argv,
+                         0, stream);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream);
