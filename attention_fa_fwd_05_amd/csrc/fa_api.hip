@@ -4,7 +4,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/fa.h"
+#include "fa.h"
 #include "fa_kernels.h"
 
 namespace {
@@ -58,12 +58,15 @@ struct WsLayout {
   size_t dvec, lg, dqacc, total;
 };
 
+int padded_rows(int Tq) { return (Tq + 63) / 64 * 64; }
+
 WsLayout ws_layout(int B, int Hq, int Tq, int d, int dtype) {
   const size_t rows = (size_t)B * Hq * Tq;
+  const size_t prows = (size_t)B * Hq * padded_rows(Tq);
   WsLayout w;
   w.dvec = 0;
-  w.lg = align_up(rows * 4);
-  w.dqacc = w.lg + align_up(rows * 4);
+  w.lg = align_up(prows * 4);
+  w.dqacc = w.lg + align_up(prows * 4);
   w.total = w.dqacc + (dtype == FA_DTYPE_BF16 ? align_up(rows * d * 4) : 0);
   return w;
 }
@@ -154,6 +157,7 @@ int fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O, co
   a.dQacc = dtype == FA_DTYPE_BF16 ? (ws.total ? reinterpret_cast<float*>(wsb + ws.dqacc) : nullptr)
                                    : static_cast<float*>(dQ);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
+  a.Tqp = padded_rows(Tq);
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   return hip_status(fa::launch_bwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, stages, (hipStream_t)stream));

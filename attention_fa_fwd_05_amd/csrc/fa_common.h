@@ -116,6 +116,260 @@ template <int KC> struct TrNat<float, KC> {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Unpadded LDS tiles with XOR-swizzled 16-byte chunks.
+//
+// A [rows x D] tile of T is stored row-major without padding; chunk c of row r
+// (16 bytes) sits at slot c ^ fsw(r).  fsw takes 8 distinct values over any 8
+// consecutive rows (natural 16-byte operand reads of 8 rows hit 8 different
+// bank groups) and keeps the two chunks a transposed read touches in each of
+// 4 consecutive rows (aligned to 4) on 8 distinct slots.  The layout can be
+// filled by direct global->LDS loads, which write 64 consecutive 16-byte slots
+// per wave instruction.
+template <typename T, int D>
+struct SwzTile {
+  static constexpr int EPC = 16 / (int)sizeof(T);   // elements per chunk
+  static constexpr int NCH = D / EPC;               // chunks per row
+  static_assert(NCH == 8 || NCH == 16 || NCH == 32, "row must be 8, 16 or 32 chunks");
+  __device__ static inline int fsw(int r) {
+    return NCH >= 16 ? ((2 * (r & 7)) ^ ((r >> 3) & 1)) : ((2 * (r & 3)) ^ ((r >> 2) & 1));
+  }
+  // element index of (row, col)
+  __device__ static inline int elem(int r, int col) {
+    return r * D + (((col / EPC) ^ fsw(r)) * EPC) + (col % EPC);
+  }
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void global_void_t;
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Direct global->LDS loads, issued as inline assembly so the compiler neither
+// tracks them nor inserts waits for them: the caller orders them with
+// wait_vmcnt and a workgroup barrier.  M0 holds the wave-uniform LDS base;
+// lane l's data lands at base + size * l.
+__device__ inline void dma16(const void* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+__device__ inline void dma4(const void* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
+// Issue direct loads of global rows [g0, g0 + ROWS) (each clamped to
+// nrows - 1, which must be >= 0) into a swizzled tile.  NTHR threads take
+// part; each wave issues ROWS * NCH / NTHR instructions.
+template <typename T, int D, int ROWS, int NTHR>
+__device__ inline void dma_rows(T* tile, const T* g, int g0, int nrows) {
+  using TL = SwzTile<T, D>;
+  constexpr int SLOTS = ROWS * TL::NCH, NWV = NTHR / 64, PER = SLOTS / NTHR;
+  static_assert(PER * NTHR == SLOTS, "tile must split evenly over the threads");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t base = lds_addr(tile);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int blk = i * NWV + wave;                 // 64-slot block of this wave instruction
+    const int pos = blk * 64 + lane;
+    const int r = pos / TL::NCH, x = pos % TL::NCH;
+    const int gr = min(g0 + r, nrows - 1);
+    dma16(g + (size_t)gr * D + (x ^ TL::fsw(r)) * TL::EPC, base + blk * 1024);
+  }
+}
+
+// 4-byte direct loads of 64 consecutive floats by one wave.
+__device__ inline void dma_floats64(float* dst, const float* src) {
+  dma4(src + (threadIdx.x & 63), lds_addr(dst));
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt, lgkmcnt left
+// at their maxima, i.e. not waited on).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Natural operand from a swizzled tile: element e of step s is
+// tile[row][h * (D / 2) + s * KPER + e] (contraction over the row's columns).
+template <typename T, int D>
+__device__ inline typename MM<T>::Op ld_nat_swz(const T* tile, int row, int h, int s) {
+  return MM<T>::ld(tile + SwzTile<T, D>::elem(row, h * (D / 2) + s * MM<T>::KPER));
+}
+
+// Transposed bf16 operand from a swizzled tile: element 4 u + e4 comes from row
+// rows_u + e4 and column col0 + (lane % 32) (rows_u0, rows_u1 multiples of 4).
+template <int D>
+__device__ inline bf16x8 ld_tr_swz(const bf16* tile, int rows_u0, int rows_u1, int col0) {
+  using TL = SwzTile<bf16, D>;
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15;
+  const int c = col0 + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + TL::elem(rows_u0 + (i >> 2), c)));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + TL::elem(rows_u1 + (i >> 2), c)));
+  bf16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// Transposed operand, accumulator (perm_index) contraction order over rows.
+template <typename T, int D> struct TrPermSwz;
+template <int D> struct TrPermSwz<bf16, D> {
+  __device__ static inline bf16x8 ld(const bf16* tile, int h, int s, int col0) {
+    return ld_tr_swz<D>(tile, 16 * s + 4 * h, 16 * s + 8 + 4 * h, col0);
+  }
+};
+template <int D> struct TrPermSwz<float, D> {
+  __device__ static inline float ld(const float* tile, int h, int s, int col0) {
+    return tile[SwzTile<float, D>::elem(perm_index(h, s), col0 + (threadIdx.x & 31))];
+  }
+};
+
+// Transposed operand, natural contraction order over KC rows.
+template <typename T, int D, int KC> struct TrNatSwz;
+template <int D, int KC> struct TrNatSwz<bf16, D, KC> {
+  __device__ static inline bf16x8 ld(const bf16* tile, int h, int s, int col0) {
+    const int r0 = h * (KC / 2) + 8 * s;
+    return ld_tr_swz<D>(tile, r0, r0 + 4, col0);
+  }
+};
+template <int D, int KC> struct TrNatSwz<float, D, KC> {
+  __device__ static inline float ld(const float* tile, int h, int s, int col0) {
+    return tile[SwzTile<float, D>::elem(h * (KC / 2) + s, col0 + (threadIdx.x & 31))];
+  }
+};
+
+// Operand fetchers for swizzled tiles.  The swizzle is periodic in the row
+// (16 rows for >= 16-chunk rows, 8 rows otherwise), so every per-lane part of
+// an address can be tabulated once per kernel and every per-step part is a
+// compile-time byte offset.  Tables hold byte offsets from the tile base.
+
+// A value the optimiser must treat as freshly computed (keeps derived
+// addresses from being hoisted out of a loop into long-lived registers).
+__device__ inline int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ inline bf16x8 lds16(const void* base, int byte_off) {
+  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+__device__ inline bf16x4 lds_tr8(const void* base, int byte_off) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)(reinterpret_cast<const char*>(base) + byte_off));
+}
+__device__ inline bf16x8 cat(const bf16x4& lo, const bf16x4& hi) {
+  bf16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// Natural operand of lane row n (+ 32 t): element e of step s is
+// tile[32 t + n][h * D / 2 + s * KPER + e].
+template <typename T, int D> struct NatFetch;
+template <int D> struct NatFetch<bf16, D> {
+  using TL = SwzTile<bf16, D>;
+  static constexpr int NS = D / 16;                 // steps (one chunk each)
+  int off[NS];
+  __device__ void init(int n, int h) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) off[s] = 2 * TL::elem(n, h * (D / 2) + 8 * s);
+  }
+  __device__ bf16x8 ld(const bf16* tile, int t, int s) const { return lds16(tile + t * 32 * D, off[s]); }
+};
+template <int D> struct NatFetch<float, D> {
+  int n_, h_;
+  __device__ void init(int n, int h) { n_ = n; h_ = h; }
+  __device__ float ld(const float* tile, int t, int s) const {
+    return tile[32 * t * D + SwzTile<float, D>::elem(opaque(n_), h_ * (D / 2) + s)];
+  }
+};
+
+// Transposed operand in accumulator order over rows: element e of step s is
+// tile[perm_index(h, s * KPER + e)][32 t + lane % 32].
+template <typename T, int D> struct TrPermFetch;
+template <int D> struct TrPermFetch<bf16, D> {
+  using TL = SwzTile<bf16, D>;
+  static constexpr int NT = D / 32;
+  int off[2 * NT];                                  // (t, u): rows 8 u + 4 h + i / 4 of a 16-row period
+  __device__ void init(int lane) {
+    const int h = lane >> 5, i = lane & 15, g16 = (lane >> 4) & 1;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        off[2 * t + u] = 2 * TL::elem(8 * u + 4 * h + (i >> 2), 32 * t + 16 * g16 + 4 * (i & 3));
+  }
+  __device__ bf16x8 ld(const bf16* tile, int t, int s) const {
+    const bf16* base = tile + 16 * s * D;
+    return cat(lds_tr8(base, off[2 * t]), lds_tr8(base, off[2 * t + 1]));
+  }
+};
+template <int D> struct TrPermFetch<float, D> {
+  int lane_;
+  __device__ void init(int lane) { lane_ = lane; }
+  __device__ float ld(const float* tile, int t, int s) const {
+    const int l = opaque(lane_);
+    return tile[SwzTile<float, D>::elem(perm_index(l >> 5, s), 32 * t + (l & 31))];
+  }
+};
+
+// Transposed operand in natural order over KC rows: element e of step s is
+// tile[h * KC / 2 + s * KPER + e][32 dt + lane % 32], for one fixed d-tile dt.
+template <typename T, int D, int KC> struct TrNatFetch;
+template <int D, int KC> struct TrNatFetch<bf16, D, KC> {
+  using TL = SwzTile<bf16, D>;
+  static_assert((KC / 2) % 16 == 0, "half range must span whole swizzle periods");
+  int off[4];                                       // (s & 1, u): rows h*KC/2 + 8 (s&1) + 4 u + i / 4
+  __device__ void init(int lane, int dt) {
+    const int h = lane >> 5, i = lane & 15, g16 = (lane >> 4) & 1;
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        off[2 * p + u] = 2 * TL::elem(h * (KC / 2) + 8 * p + 4 * u + (i >> 2), 32 * dt + 16 * g16 + 4 * (i & 3));
+  }
+  __device__ bf16x8 ld(const bf16* tile, int s) const {
+    const bf16* base = tile + 16 * (s >> 1) * D;
+    return cat(lds_tr8(base, off[2 * (s & 1)]), lds_tr8(base, off[2 * (s & 1) + 1]));
+  }
+};
+template <int D, int KC> struct TrNatFetch<float, D, KC> {
+  int lane_, dt_;
+  __device__ void init(int lane, int dt) { lane_ = lane; dt_ = dt; }
+  __device__ float ld(const float* tile, int s) const {
+    const int l = opaque(lane_);
+    return tile[SwzTile<float, D>::elem((l >> 5) * (KC / 2) + s, 32 * dt_ + (l & 31))];
+  }
+};
+
+// Scheduling hint for a straight run of NMMA matrix instructions, each fed by
+// RPM LDS reads: issue the reads for the first AHEAD instructions, then
+// alternate one matrix instruction with the reads of a later one, so LDS
+// latency overlaps matrix work instead of stalling each instruction.
+template <int NMMA, int AHEAD, int RPM = 1>
+__device__ inline void sched_interleave() {
+  constexpr int kMfma = 0x008, kDsRead = 0x100;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, AHEAD * RPM, 0);
+#pragma unroll
+  for (int k = 0; k < NMMA - AHEAD; ++k) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, RPM, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD, 0);
+}
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline float wave_xor32_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }

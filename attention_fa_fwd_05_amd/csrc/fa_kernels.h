@@ -27,10 +27,11 @@ struct BwdArgs {
   void* dQ;
   void* dK;
   void* dV;
-  float* Dvec;        // [B*Hq*Tq] rowsum(dO * O)
-  float* Lg;          // [B*Hq*Tq] L * log2(e); +inf for rows without keys
+  float* Dvec;        // [B*Hq][Tqp] rowsum(dO * O); 0 in padding rows
+  float* Lg;          // [B*Hq][Tqp] L * log2(e); +inf for rows without keys and padding
   float* dQacc;       // [B*Hq*Tq*d] fp32 dQ accumulator (== dQ for fp32)
   int B, Hq, Hkv, Tq, Tk;
+  int Tqp;            // Tq rounded up to a multiple of 64
   float scale;
   float scale_log2;
 };

@@ -90,8 +90,9 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: float32 D and
- * log2-domain L per query row, plus (bf16 only) a float32 dQ accumulator
- * [B][Hq][Tq][d].  Each part starts on a 256-byte boundary.  Returns 0 for
+ * log2-domain L per query row (rows padded to a multiple of 64 per head),
+ * plus (bf16 only) a float32 dQ accumulator [B][Hq][Tq][d].  Each part starts
+ * on a 256-byte boundary.  Returns 0 for
  * invalid arguments.  The workspace holds nothing between calls.
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype);

@@ -52,7 +52,7 @@ def test_workspace_bytes(lib):
     rows = 4 * 32 * 4096
     want = rows * 4 + rows * 4 + rows * 128 * 4
     assert fa.workspace_bytes(4, 32, 8, 4096, 4096, 128, fa.FA_DTYPE_BF16) == want
-    # fp32: no accumulator (dQ itself accumulates)
+    # fp32: no accumulator (dQ itself accumulates); rows padded to 128 (multiple of 64)
     assert fa.workspace_bytes(1, 1, 1, 100, 100, 64, fa.FA_DTYPE_F32) == 512 + 512
     assert fa.workspace_bytes(1, 1, 1, 0, 5, 64, fa.FA_DTYPE_BF16) == 0
     # invalid arguments -> 0
