@@ -23,7 +23,7 @@ STATUS = {
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_DTYPE", 6: "FA_ERR_SCALE", 7: "FA_ERR_WORKSPACE",
     8: "FA_ERR_ALIGNMENT", 9: "FA_ERR_TOO_LARGE", 10: "FA_ERR_HIP", 11: "FA_ERR_STAGES",
 }
-STAGE_PRE, STAGE_MAIN, STAGE_FINISH, STAGE_ALL = 1, 2, 4, 7
+STAGE_PRE, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
 EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_bwd_workspace_bytes", "fa_status_string",
            "fa_hip_error_string", "fa_abi_version"]
 

@@ -29,6 +29,18 @@ def flops(B, Hq, Tq, Tk, d, causal):
     return f, b
 
 
+def kernel_flops(B, Hq, Tq, Tk, d, causal):
+    """Matrix FLOPs each kernel performs (halved when causal).
+
+    Per visible (query, key) pair: forward 4d (S and PV); dK/dV pass 8d (S, dP,
+    dV, dK); dQ pass 6d (S, dP, dQ).  The two backward passes together do 14d,
+    4d more than the 10d the backward is credited with, because each rebuilds
+    S and dP for itself.
+    """
+    pairs = B * Hq * Tq * Tk * (0.5 if causal else 1.0)
+    return {"fwd_kernel": 4.0 * d * pairs, "dkdv_kernel": 8.0 * d * pairs, "dq_kernel": 6.0 * d * pairs}
+
+
 def retained_bytes_recompute(B, Hq, Hkv, Tq, Tk, d, dtype):
     """Q, K, V, O in the storage dtype plus fp32 L: what the backward keeps."""
     e = DTYPE_BYTES[dtype]

@@ -55,7 +55,7 @@ int check_ptr(const void* p, long long elems) {
 }
 
 struct WsLayout {
-  size_t dvec, lg, dqacc, total;
+  size_t dvec, lg, total;
 };
 
 int padded_rows(int Tq) { return (Tq + 63) / 64 * 64; }
@@ -63,11 +63,13 @@ int padded_rows(int Tq) { return (Tq + 63) / 64 * 64; }
 WsLayout ws_layout(int B, int Hq, int Tq, int d, int dtype) {
   const size_t rows = (size_t)B * Hq * Tq;
   const size_t prows = (size_t)B * Hq * padded_rows(Tq);
+  (void)rows;
+  (void)d;
+  (void)dtype;
   WsLayout w;
   w.dvec = 0;
   w.lg = align_up(prows * 4);
-  w.dqacc = w.lg + align_up(prows * 4);
-  w.total = w.dqacc + (dtype == FA_DTYPE_BF16 ? align_up(rows * d * 4) : 0);
+  w.total = w.lg + align_up(prows * 4);
   return w;
 }
 
@@ -154,8 +156,6 @@ int fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O, co
   a.dQ = dQ; a.dK = dK; a.dV = dV;
   a.Dvec = ws.total ? reinterpret_cast<float*>(wsb + ws.dvec) : nullptr;
   a.Lg = ws.total ? reinterpret_cast<float*>(wsb + ws.lg) : nullptr;
-  a.dQacc = dtype == FA_DTYPE_BF16 ? (ws.total ? reinterpret_cast<float*>(wsb + ws.dqacc) : nullptr)
-                                   : static_cast<float*>(dQ);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
   a.Tqp = padded_rows(Tq);
   a.scale = scale;

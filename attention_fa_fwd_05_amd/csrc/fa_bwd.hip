@@ -4,23 +4,24 @@
 // rest; "Backward Pass Implementation", section "The Recomputation Strategy").
 //
 // Three launches on one stream:
-//  1. bwd_pre_kernel: D_i = rowsum(dO_i * O_i), L_i in log2 units (+inf for
-//     rows without keys, so their probabilities vanish), zero the fp32 dQ
-//     accumulator.  D and L2 rows are padded to a multiple of 64 per head
-//     (padding: D = 0, L2 = +inf), so query blocks load them without checks.
-//  2. bwd_kernel: one workgroup per (128-key block, b, K/V head).  Each of the
-//     4 waves owns 32 keys; their K and V rows sit in registers and dK, dV
+//  1. bwd_pre_kernel: D_i = rowsum(dO_i * O_i) and L_i in log2 units (+inf for
+//     rows without keys, so their probabilities vanish).  Rows are padded to a
+//     multiple of 64 per head (padding: D = 0, L2 = +inf).
+//  2. dkdv_kernel: one workgroup per (128-key block, b, K/V head); each of the
+//     4 waves owns 32 keys, whose K and V rows sit in registers, and dK, dV
 //     accumulate in registers across every query block of every query head of
 //     the group (the group sum of the GQA backward, "The Autograd Memory
-//     Trap", section "Tracing the Autograd Graph").  Q / dO / L / D blocks
-//     are double-buffered in LDS and filled by direct global->LDS loads issued
-//     one block ahead; LDS tiles are unpadded with XOR-swizzled 16-byte chunks.
-//     Per query block:
-//     S = Q K^T and dP = dO V^T (lane = key), P = exp2(S c - L2),
-//     dS = P (dP - D), dV^T += dO^T P, dK^T += Q^T dS (transposed LDS reads of
-//     the natural Q / dO tiles), dS goes through LDS and dQ = dS K is added to
-//     the fp32 accumulator with hardware float atomics.
-//  3. dq_convert_kernel (bf16 only): accumulator -> bf16 dQ.
+//     Trap", section "Tracing the Autograd Graph").  Per query block:
+//     S = Q K^T, dP = dO V^T (lane = key), P = exp2(S c - L2), dS = P (dP - D),
+//     dV^T += dO^T P, dK^T += Q^T dS.  Q / dO / L2 / D blocks are
+//     double-buffered in LDS and fetched by direct global->LDS loads one block
+//     ahead.
+//  3. dq_kernel: one workgroup per query block, the forward's structure: lane =
+//     query, S^T = K Q^T and dP^T = V dO^T per key tile, dS^T from L2 and D
+//     held per lane, dQ^T += K^T dS^T in registers, written once.
+// dQ is thus produced without atomics: the recompute of S and dP in the dQ
+// pass costs 3 extra matrix products per tile, but no fp32 accumulator has to
+// be zeroed, read-modify-written from every key block and converted.
 #include "fa_common.h"
 #include "fa_kernels.h"
 
@@ -45,31 +46,20 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int msk = 8; msk >= 1; msk >>= 1) acc += __shfl_xor(acc, msk, 64);
-  if (prow >= prows) return;
-  if (j == 0) {
-    const float l = ok ? a.L[row] : -INFINITY;
-    a.Dvec[prow] = acc;
-    a.Lg[prow] = (l == -INFINITY) ? INFINITY : l * kLog2e;
-  }
-  if (!ok) return;
-  float* z = a.dQacc + row * D + j * EPL;
-#pragma unroll
-  for (int e = 0; e < EPL; e += 4) store4(z + e, 0.f, 0.f, 0.f, 0.f);
+  if (prow >= prows || j != 0) return;
+  const float l = ok ? a.L[row] : -INFINITY;
+  a.Dvec[prow] = acc;
+  a.Lg[prow] = (l == -INFINITY) ? INFINITY : l * kLog2e;
 }
 
-// Dispatch order: each XCD (workgroup id mod 8) gets one contiguous range of
-// the logical order (group, then key block, heaviest first when causal), so
-// the key blocks of one (batch, K/V head) group share that XCD's L2 for the
-// group's Q / dO rows.
-struct BwdWork {
+// Key-block kernels: logical order = group, then key block (heaviest first
+// when causal: low key blocks see the most query blocks).
+struct KWork {
   int b, hk, kb;
 };
-
-__device__ inline BwdWork bwd_work(const BwdArgs& a, int nkb) {
-  const int N = gridDim.x, p = blockIdx.x;
-  const int x = p & 7, slot = p >> 3, per = N >> 3, rem = N & 7;
-  const int logical = x * per + min(x, rem) + slot;
-  BwdWork w;
+__device__ inline KWork kblock_work(const BwdArgs& a, int nkb) {
+  const int logical = xcd_logical_block();
+  KWork w;
   w.kb = logical % nkb;
   const int grp = logical / nkb;
   w.b = grp / a.Hkv;
@@ -78,35 +68,26 @@ __device__ inline BwdWork bwd_work(const BwdArgs& a, int nkb) {
 }
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   using M = MM<T>;
-  using TL = SwzTile<T, D>;
   typedef typename M::Op Op;
   constexpr int BK = 128;                           // keys per workgroup, 32 per wave
   constexpr int BQ = (sizeof(T) == 4 && D == 128) ? 32 : 64;
   constexpr int KPER = M::KPER;
-  constexpr int LDSS = BK + 32 / (int)sizeof(T);    // sdS row stride (32-byte padding)
   constexpr int NSD = (D / 2) / KPER;
   constexpr int NSQ = (BQ / 2) / KPER;
-  constexpr int NSK = (BK / 2) / KPER;
   constexpr int NDT = D / 32, NQT = BQ / 32;
-  constexpr int NT_W = NQT * NDT / 4;               // dQ tiles per wave
-  constexpr int NATOM = NT_W * 16;                  // dQ atomics per wave per query block
-  static_assert(NT_W * 4 == NQT * NDT, "dQ tiles must split evenly over the 4 waves");
-  static_assert(NATOM < 64, "vmcnt accounting");
-  // Q / dO / L / D blocks are double-buffered; the next block is loaded by
+  // Q / dO / L2 / D blocks are double-buffered; the next block is loaded by
   // direct global->LDS loads while the current one is processed.
-  __shared__ __attribute__((aligned(16))) T sK[BK * D];
   __shared__ __attribute__((aligned(16))) T sQ[2][BQ * D];
   __shared__ __attribute__((aligned(16))) T sdO[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) T sdS[BQ * LDSS];
   __shared__ __attribute__((aligned(16))) float sL[2][64];
   __shared__ __attribute__((aligned(16))) float sD[2][64];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
   const int nkb = (a.Tk + BK - 1) / BK;
-  const BwdWork wk = bwd_work(a, nkb);
+  const KWork wk = kblock_work(a, nkb);
   const int bhk = wk.b * a.Hkv + wk.hk, G = a.Hq / a.Hkv;
   const int k0 = wk.kb * BK, kw = k0 + 32 * w, mykey = kw + n;
   const int off = a.Tk - a.Tq;
@@ -117,7 +98,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
   const T* Vp = reinterpret_cast<const T*>(a.V) + (size_t)bhk * a.Tk * D;
 
   // Work list: every (query head of the group, query block that can see a key
-  // of this block); the next item's Q / dO / L / D are loaded during the current one.
+  // of this block); the next item's Q / dO / L2 / D are loaded during the current one.
   const int nqb = (a.Tq + BQ - 1) / BQ;
   const int qb0 = CAUSAL ? min(nqb, max(0, k0 - off) / BQ) : 0;
   const int per_head = nqb - qb0, total = G * per_head;
@@ -125,19 +106,17 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
     bh = wk.b * a.Hq + wk.hk * G + it / per_head;
     q0 = (qb0 + it % per_head) * BQ;
   };
-  // L2 and D rows are padded to 64 per head, so 64 floats can always be loaded.
+  // L2 and D rows are padded to 64 per head, so a 64-row window always loads.
   auto issue = [&](int it, int buf) {
     int bh, q0;
     item(it, bh, q0);
     const size_t qbase = (size_t)bh * a.Tq * D;
     dma_rows<T, D, BQ, 256>(sQ[buf], reinterpret_cast<const T*>(a.Q) + qbase, q0, a.Tq);
     dma_rows<T, D, BQ, 256>(sdO[buf], reinterpret_cast<const T*>(a.dO) + qbase, q0, a.Tq);
-    const int q64 = q0 & ~63;                       // 64-row aligned window holding this block
+    const int q64 = q0 & ~63;
     if (w == 0) dma_floats64(sL[buf], a.Lg + (size_t)bh * a.Tqp + q64);
     if (w == 1) dma_floats64(sD[buf], a.Dvec + (size_t)bh * a.Tqp + q64);
   };
-
-  dma_rows<T, D, BK, 256>(sK, Kp, k0, a.Tk);
   if (total > 0) issue(0, 0);
 
   Op kop[NSD], vop[NSD];
@@ -157,10 +136,6 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
   nat.init(n, h);
   TrPermFetch<T, D> trp;
   trp.init(lane);
-  // dQ tiles of this wave: idx = w + 4 j; with NDT | 4 the d-tile is the same for every j
-  static_assert(4 % NDT == 0, "one d-tile per wave");
-  TrNatFetch<T, D, BK> trk;
-  trk.init(lane, w % NDT);
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -222,8 +197,6 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
         pop[t * (16 / KPER) + s] = M::pack(p + s * KPER);
         dsop[t * (16 / KPER) + s] = M::pack(ds + s * KPER);
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sdS[perm_index(h, 16 * t + i) * LDSS + 32 * w + n] = (T)ds[i];
     }
 
 #pragma unroll
@@ -235,34 +208,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
       }
     }
     sched_interleave<2 * NDT * NSQ, 4, (sizeof(T) == 2 ? 2 : 1)>();
-    __syncthreads();
-
-    // dQ tiles of this wave: dQ[q0 + 32 qt .., 32 dt ..] += scale * dS K.
-    // Exactly NATOM atomics per wave (rows past Tq add 0 to the last row), so
-    // the wait below can count them.
-    float* dQp = a.dQacc + (size_t)bh * a.Tq * D;
-    f32x16 qacc[NT_W];
-#pragma unroll
-    for (int j = 0; j < NT_W; ++j) {
-      const int idx = w + 4 * j, qt = idx / NDT, dt = idx % NDT;
-      qacc[j] = f32x16{};
-      const T* arow = sdS + (qt * 32 + n) * LDSS + h * (BK / 2);
-#pragma unroll
-      for (int s = 0; s < NSK; ++s)
-        qacc[j] = M::mma(M::ld(arow + s * KPER), trk.ld(sK, s), qacc[j]);
-    }
-    sched_interleave<NT_W * NSK, 4, (sizeof(T) == 2 ? 3 : 2)>();
-#pragma unroll
-    for (int j = 0; j < NT_W; ++j) {
-      const int idx = w + 4 * j, qt = idx / NDT, dt = idx % NDT;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int q = q0 + qt * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        const bool ok = q < a.Tq;
-        unsafeAtomicAdd(dQp + (size_t)(ok ? q : a.Tq - 1) * D + dt * 32 + n, ok ? qacc[j][i] * a.scale : 0.f);
-      }
-    }
-    wait_vmcnt<NATOM>();                           // this wave's loads for the next item have landed
+    wait_vmcnt<0>();                               // this wave's loads of the next block have landed
     __syncthreads();
   }
 
@@ -283,34 +229,169 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
   }
 }
 
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ src, bf16* __restrict__ dst,
-                                                        long long n8) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const f32x4 lo = reinterpret_cast<const f32x4*>(src)[2 * i];
-  const f32x4 hi = reinterpret_cast<const f32x4*>(src)[2 * i + 1];
-  bf16x8 v;
+// Waves per dQ workgroup: 8 (256 query rows), or 4 where fp32 d = 128
+// operands would not fit in 256 registers.
+template <typename T, int D>
+constexpr int dq_waves() { return (sizeof(T) == 4 && D == 128) ? 4 : 8; }
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) {
+  using M = MM<T>;
+  typedef typename M::Op Op;
+  constexpr int NW = dq_waves<T, D>(), BQ = 32 * NW, BK = 64;
+  constexpr int KPER = M::KPER;
+  constexpr int LD = D + 32 / (int)sizeof(T);       // 32-byte row padding
+  constexpr int NSD = (D / 2) / KPER;
+  constexpr int NSK = (BK / 2) / KPER;
+  constexpr int NDT = D / 32;
+  constexpr int EPC = 16 / (int)sizeof(T);
+  constexpr int CPR = D / EPC;
+  constexpr int NCH = BK * CPR / (NW * 64);
+  static_assert(NCH * NW * 64 == BK * CPR, "tile must split evenly");
+  __shared__ __attribute__((aligned(16))) T sK[2][BK * LD];
+  __shared__ __attribute__((aligned(16))) T sV[2][BK * LD];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, n = lane & 31;
+  const int nqb = (a.Tq + BQ - 1) / BQ;
+  const QWork wk = qblock_work(a.B, a.Hq, a.Hkv, nqb, CAUSAL);
+  const int bh = wk.b * a.Hq + wk.hq;
+  const int q0 = wk.qb * BQ, qw = q0 + 32 * w, myq = qw + n;
+  const int off = a.Tk - a.Tq;
+  const bool q_ok = myq < a.Tq;
+
+  const T* Qp = reinterpret_cast<const T*>(a.Q) + (size_t)bh * a.Tq * D;
+  const T* dOp = reinterpret_cast<const T*>(a.dO) + (size_t)bh * a.Tq * D;
+  const T* Kp = reinterpret_cast<const T*>(a.K) + (size_t)(wk.b * a.Hkv + wk.hk) * a.Tk * D;
+  const T* Vp = reinterpret_cast<const T*>(a.V) + (size_t)(wk.b * a.Hkv + wk.hk) * a.Tk * D;
+
+  int kend = a.Tk;
+  if (CAUSAL) kend = min(a.Tk, max(0, q0 + BQ + off));
+  const int ntiles = (kend + BK - 1) / BK;
+
+  uint4 pk[NCH], pv[NCH];
+  auto gload = [&](int k0) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) { v[e] = (bf16)lo[e]; v[4 + e] = (bf16)hi[e]; }
-  reinterpret_cast<bf16x8*>(dst)[i] = v;
+    for (int i = 0; i < NCH; ++i) {
+      const int idx = i * NW * 64 + tid, row = idx / CPR, ch = idx % CPR;
+      const bool ok = k0 + row < a.Tk;
+      const size_t o = (size_t)(ok ? k0 + row : 0) * D + ch * EPC;
+      pk[i] = ld16(Kp + o);
+      pv[i] = ld16(Vp + o);
+      if (!ok) { pk[i] = uint4{0u, 0u, 0u, 0u}; pv[i] = uint4{0u, 0u, 0u, 0u}; }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int idx = i * NW * 64 + tid, row = idx / CPR, ch = idx % CPR;
+      st16(&sK[buf][row * LD + ch * EPC], pk[i]);
+      st16(&sV[buf][row * LD + ch * EPC], pv[i]);
+    }
+  };
+  if (ntiles > 0) {
+    gload(0);
+    lstore(0);
+  }
+
+  // Q^T and dO^T operands for this lane's query, L2 and D of that row.
+  Op qop[NSD], gop[NSD];
+  {
+    const size_t ro = (size_t)(q_ok ? myq : 0) * D + h * (D / 2);
+#pragma unroll
+    for (int s = 0; s < NSD; ++s) {
+      qop[s] = M::ld(Qp + ro + s * KPER);
+      gop[s] = M::ld(dOp + ro + s * KPER);
+      if (!q_ok) { qop[s] = Op{}; gop[s] = Op{}; }
+    }
+  }
+  const float l2 = q_ok ? a.Lg[(size_t)bh * a.Tqp + myq] : INFINITY;
+  const float dd = q_ok ? a.Dvec[(size_t)bh * a.Tqp + myq] : 0.f;
+  __syncthreads();
+
+  const float c = a.scale_log2;
+  f32x16 acc[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
+
+  for (int jt = 0; jt < ntiles; ++jt) {
+    const int k0 = jt * BK, buf = jt & 1;
+    const bool more = jt + 1 < ntiles;
+    if (more) gload(k0 + BK);
+
+    if (!(CAUSAL && k0 > qw + 31 + off)) {          // some key of the tile visible to this wave
+      // S^T = K Q^T and dP^T = V dO^T: 64 keys x 32 queries each.
+      f32x16 st0 = f32x16{}, st1 = f32x16{}, dp0 = f32x16{}, dp1 = f32x16{};
+      const T* kr = &sK[buf][n * LD + h * (D / 2)];
+      const T* vr = &sV[buf][n * LD + h * (D / 2)];
+#pragma unroll
+      for (int s = 0; s < NSD; ++s) {
+        st0 = M::mma(M::ld(kr + s * KPER), qop[s], st0);
+        st1 = M::mma(M::ld(kr + 32 * LD + s * KPER), qop[s], st1);
+        dp0 = M::mma(M::ld(vr + s * KPER), gop[s], dp0);
+        dp1 = M::mma(M::ld(vr + 32 * LD + s * KPER), gop[s], dp1);
+      }
+      sched_interleave<4 * NSD, 4>();
+      float ds[32];
+      const bool need_mask = (k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off);
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const float sv = r < 16 ? st0[r] : st1[r - 16];
+        const float dpv = r < 16 ? dp0[r] : dp1[r - 16];
+        float p = fast_exp2(__builtin_fmaf(sv, c, -l2));
+        if (need_mask) {
+          const int key = k0 + perm_index(h, r);
+          if (key >= a.Tk || (CAUSAL && key > myq + off)) p = 0.f;
+        }
+        ds[r] = p * (dpv - dd);
+      }
+      Op dsop[NSK];
+#pragma unroll
+      for (int s = 0; s < NSK; ++s) dsop[s] = M::pack(ds + s * KPER);
+      // dQ^T += K^T dS^T (K^T through transposed reads of the key tile).
+#pragma unroll
+      for (int t = 0; t < NDT; ++t) {
+#pragma unroll
+        for (int s = 0; s < NSK; ++s)
+          acc[t] = M::mma(TrPerm<T>::ld(&sK[buf][0], LD, h, s, t * 32), dsop[s], acc[t]);
+      }
+    }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  if (q_ok) {
+    T* qrow = reinterpret_cast<T*>(a.dQ) + ((size_t)bh * a.Tq + myq) * D;
+    const float sc = a.scale;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = t * 32 + 8 * g + 4 * h;
+        store4(qrow + d0, acc[t][4 * g] * sc, acc[t][4 * g + 1] * sc, acc[t][4 * g + 2] * sc,
+               acc[t][4 * g + 3] * sc);
+      }
+    }
+  }
 }
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t stream) {
-  const long long rows = (long long)a.B * a.Hq * a.Tq;
   const long long prows = (long long)a.B * a.Hq * a.Tqp;
-  if ((stages & kStagePre) && rows > 0) {
+  if ((stages & kStagePre) && prows > 0) {
     hipError_t e = launch(bwd_pre_kernel<T, D>, (prows + 15) / 16, stream, a);
     if (e != hipSuccess) return e;
   }
   const long long kblocks = (long long)((a.Tk + 127) / 128) * a.B * a.Hkv;
-  if ((stages & kStageMain) && kblocks > 0) {
-    hipError_t e = launch(bwd_kernel<T, D, CAUSAL>, kblocks, stream, a);
+  if ((stages & kStageDkDv) && kblocks > 0) {
+    hipError_t e = launch(dkdv_kernel<T, D, CAUSAL>, kblocks, stream, a);
     if (e != hipSuccess) return e;
   }
-  if ((stages & kStageFinish) && sizeof(T) == 2 && rows > 0) {
-    const long long n8 = rows * D / 8;
-    return launch(dq_convert_kernel, (n8 + 255) / 256, stream, (const float*)a.dQacc, (bf16*)a.dQ, n8);
+  constexpr int NW = dq_waves<T, D>();
+  const long long qblocks = (long long)((a.Tq + 32 * NW - 1) / (32 * NW)) * a.B * a.Hq;
+  if ((stages & kStageDq) && qblocks > 0) {
+    hipError_t e = launch<64 * NW>(dq_kernel<T, D, CAUSAL>, qblocks, stream, a);
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }

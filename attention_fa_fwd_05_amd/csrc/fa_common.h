@@ -102,20 +102,6 @@ template <> struct TrPerm<float> {
   }
 };
 
-// Transposed operand with natural contraction order over a length-KC range.
-template <typename T, int KC> struct TrNat;
-template <int KC> struct TrNat<bf16, KC> {
-  __device__ static inline bf16x8 ld(const bf16* tile, int stride, int h, int s, int col0) {
-    const int r0 = h * (KC / 2) + 8 * s;
-    return ld_tr_bf16(tile, stride, r0, r0 + 4, col0);
-  }
-};
-template <int KC> struct TrNat<float, KC> {
-  __device__ static inline float ld(const float* tile, int stride, int h, int s, int col0) {
-    return tile[(h * (KC / 2) + s) * stride + col0 + (threadIdx.x & 31)];
-  }
-};
-
 // ---------------------------------------------------------------------------
 // Unpadded LDS tiles with XOR-swizzled 16-byte chunks.
 //
@@ -197,57 +183,6 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Natural operand from a swizzled tile: element e of step s is
-// tile[row][h * (D / 2) + s * KPER + e] (contraction over the row's columns).
-template <typename T, int D>
-__device__ inline typename MM<T>::Op ld_nat_swz(const T* tile, int row, int h, int s) {
-  return MM<T>::ld(tile + SwzTile<T, D>::elem(row, h * (D / 2) + s * MM<T>::KPER));
-}
-
-// Transposed bf16 operand from a swizzled tile: element 4 u + e4 comes from row
-// rows_u + e4 and column col0 + (lane % 32) (rows_u0, rows_u1 multiples of 4).
-template <int D>
-__device__ inline bf16x8 ld_tr_swz(const bf16* tile, int rows_u0, int rows_u1, int col0) {
-  using TL = SwzTile<bf16, D>;
-  const int lane = threadIdx.x & 63;
-  const int i = lane & 15;
-  const int c = col0 + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + TL::elem(rows_u0 + (i >> 2), c)));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tile + TL::elem(rows_u1 + (i >> 2), c)));
-  bf16x8 r;
-  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-  return r;
-}
-
-// Transposed operand, accumulator (perm_index) contraction order over rows.
-template <typename T, int D> struct TrPermSwz;
-template <int D> struct TrPermSwz<bf16, D> {
-  __device__ static inline bf16x8 ld(const bf16* tile, int h, int s, int col0) {
-    return ld_tr_swz<D>(tile, 16 * s + 4 * h, 16 * s + 8 + 4 * h, col0);
-  }
-};
-template <int D> struct TrPermSwz<float, D> {
-  __device__ static inline float ld(const float* tile, int h, int s, int col0) {
-    return tile[SwzTile<float, D>::elem(perm_index(h, s), col0 + (threadIdx.x & 31))];
-  }
-};
-
-// Transposed operand, natural contraction order over KC rows.
-template <typename T, int D, int KC> struct TrNatSwz;
-template <int D, int KC> struct TrNatSwz<bf16, D, KC> {
-  __device__ static inline bf16x8 ld(const bf16* tile, int h, int s, int col0) {
-    const int r0 = h * (KC / 2) + 8 * s;
-    return ld_tr_swz<D>(tile, r0, r0 + 4, col0);
-  }
-};
-template <int D, int KC> struct TrNatSwz<float, D, KC> {
-  __device__ static inline float ld(const float* tile, int h, int s, int col0) {
-    return tile[SwzTile<float, D>::elem(h * (KC / 2) + s, col0 + (threadIdx.x & 31))];
-  }
-};
-
 // Operand fetchers for swizzled tiles.  The swizzle is periodic in the row
 // (16 rows for >= 16-chunk rows, 8 rows otherwise), so every per-lane part of
 // an address can be tabulated once per kernel and every per-step part is a
@@ -325,35 +260,6 @@ template <int D> struct TrPermFetch<float, D> {
   }
 };
 
-// Transposed operand in natural order over KC rows: element e of step s is
-// tile[h * KC / 2 + s * KPER + e][32 dt + lane % 32], for one fixed d-tile dt.
-template <typename T, int D, int KC> struct TrNatFetch;
-template <int D, int KC> struct TrNatFetch<bf16, D, KC> {
-  using TL = SwzTile<bf16, D>;
-  static_assert((KC / 2) % 16 == 0, "half range must span whole swizzle periods");
-  int off[4];                                       // (s & 1, u): rows h*KC/2 + 8 (s&1) + 4 u + i / 4
-  __device__ void init(int lane, int dt) {
-    const int h = lane >> 5, i = lane & 15, g16 = (lane >> 4) & 1;
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        off[2 * p + u] = 2 * TL::elem(h * (KC / 2) + 8 * p + 4 * u + (i >> 2), 32 * dt + 16 * g16 + 4 * (i & 3));
-  }
-  __device__ bf16x8 ld(const bf16* tile, int s) const {
-    const bf16* base = tile + 16 * (s >> 1) * D;
-    return cat(lds_tr8(base, off[2 * (s & 1)]), lds_tr8(base, off[2 * (s & 1) + 1]));
-  }
-};
-template <int D, int KC> struct TrNatFetch<float, D, KC> {
-  int lane_, dt_;
-  __device__ void init(int lane, int dt) { lane_ = lane; dt_ = dt; }
-  __device__ float ld(const float* tile, int s) const {
-    const int l = opaque(lane_);
-    return tile[SwzTile<float, D>::elem((l >> 5) * (KC / 2) + s, 32 * dt_ + (l & 31))];
-  }
-};
-
 // Scheduling hint for a straight run of NMMA matrix instructions, each fed by
 // RPM LDS reads: issue the reads for the first AHEAD instructions, then
 // alternate one matrix instruction with the reads of a later one, so LDS
@@ -368,6 +274,34 @@ __device__ inline void sched_interleave() {
     __builtin_amdgcn_sched_group_barrier(kDsRead, RPM, 0);
   }
   __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD, 0);
+}
+
+// Work items in dispatch order.  Consecutive workgroup ids are spread over
+// the 8 XCDs round-robin; giving each XCD one contiguous range of the logical
+// order keeps the workgroups of a (batch, K/V head) group on one XCD, so the
+// group's tiles stay in that XCD's L2.
+__device__ inline int xcd_logical_block() {
+  const int N = gridDim.x, p = blockIdx.x;
+  const int x = p & 7, slot = p >> 3, per = N >> 3, rem = N & 7;
+  return x * per + min(x, rem) + slot;
+}
+
+// Query-block kernels (forward, dQ): logical order = group, then query block
+// (longest rows first when causal), then query head within the group.
+struct QWork {
+  int b, hq, hk, qb;
+};
+__device__ inline QWork qblock_work(int B, int Hq, int Hkv, int nqb, bool causal) {
+  const int logical = xcd_logical_block();
+  const int G = Hq / Hkv;
+  const int r = logical % G, t = logical / G;
+  const int qi = t % nqb, grp = t / nqb;
+  QWork w;
+  w.b = grp / Hkv;
+  w.hk = grp % Hkv;
+  w.hq = w.hk * G + r;
+  w.qb = causal ? nqb - 1 - qi : qi;
+  return w;
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -387,23 +321,6 @@ __device__ inline void store4(bf16* p, float a, float b, float c, float d) {
   bf16x4 v;
   v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
   *reinterpret_cast<bf16x4*>(p) = v;
-}
-
-// Copy a [rows x D] tile of T from global (row stride D) into LDS (row stride
-// LD), rows >= nvalid filled with zeros.  All 256 threads take part.
-template <typename T, int D, int LD, int ROWS>
-__device__ inline void stage_tile(T* lds, const T* g, int nvalid) {
-  constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
-  constexpr int TOTAL = ROWS * CPR;
-  static_assert(TOTAL % 256 == 0, "tile must split evenly over 256 threads");
-#pragma unroll
-  for (int it = 0; it < TOTAL / 256; ++it) {
-    const int idx = it * 256 + threadIdx.x;
-    const int row = idx / CPR, ch = idx % CPR;
-    uint4 v = {0u, 0u, 0u, 0u};
-    if (row < nvalid) v = ld16(g + (size_t)row * D + ch * (16 / sizeof(T)));
-    st16(lds + row * LD + ch * (16 / sizeof(T)), v);
-  }
 }
 
 }  // namespace fa

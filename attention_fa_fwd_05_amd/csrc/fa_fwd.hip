@@ -23,31 +23,6 @@
 
 namespace fa {
 
-// Work items in dispatch order.  Consecutive workgroup ids are spread over
-// the 8 XCDs round-robin; giving each XCD one contiguous range of the logical
-// order keeps every workgroup of a (batch, K/V head) group on one XCD, so the
-// group's K and V stay in that XCD's L2 while its query heads stream past.
-// Logical order: group, then query block (longest rows first when causal),
-// then query head within the group.
-struct FwdWork {
-  int b, hq, hk, qb;
-};
-
-__device__ inline FwdWork fwd_work(const FwdArgs& a, int nqb, bool causal) {
-  const int N = gridDim.x, p = blockIdx.x;
-  const int x = p & 7, slot = p >> 3, per = N >> 3, rem = N & 7;
-  const int logical = x * per + min(x, rem) + slot;
-  const int G = a.Hq / a.Hkv;
-  const int r = logical % G, t = logical / G;
-  const int qi = t % nqb, grp = t / nqb;
-  FwdWork w;
-  w.b = grp / a.Hkv;
-  w.hk = grp % a.Hkv;
-  w.hq = w.hk * G + r;
-  w.qb = causal ? nqb - 1 - qi : qi;
-  return w;
-}
-
 // Lazy rescale threshold (log2 units): the reference max m_run only moves when
 // a row's true max exceeds it by more than 2^TAU, so probabilities stay <= 2^8
 // and the O accumulator is rescaled only on the rare tiles where that happens.
@@ -78,7 +53,7 @@ __global__ __launch_bounds__((64 * fwd_waves<T, D>())) void fwd_kernel(FwdArgs a
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
   const int nqb = (a.Tq + BQ - 1) / BQ;
-  const FwdWork wk = fwd_work(a, nqb, CAUSAL);
+  const QWork wk = qblock_work(a.B, a.Hq, a.Hkv, nqb, CAUSAL);
   const int bh = wk.b * a.Hq + wk.hq;
   const int q0 = wk.qb * BQ, qw = q0 + 32 * w, myq = qw + n;
   const int off = a.Tk - a.Tq;

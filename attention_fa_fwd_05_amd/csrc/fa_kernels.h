@@ -29,7 +29,6 @@ struct BwdArgs {
   void* dV;
   float* Dvec;        // [B*Hq][Tqp] rowsum(dO * O); 0 in padding rows
   float* Lg;          // [B*Hq][Tqp] L * log2(e); +inf for rows without keys and padding
-  float* dQacc;       // [B*Hq*Tq*d] fp32 dQ accumulator (== dQ for fp32)
   int B, Hq, Hkv, Tq, Tk;
   int Tqp;            // Tq rounded up to a multiple of 64
   float scale;
@@ -47,8 +46,8 @@ inline hipError_t launch(void (*kernel)(Params...), long long blocks, hipStream_
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream);
-// Backward stages (bit mask): preprocess, main kernel, dQ finish.
-constexpr unsigned kStagePre = 1u, kStageMain = 2u, kStageFinish = 4u;
+// Backward stages (bit mask): preprocess, dK/dV kernel, dQ kernel.
+constexpr unsigned kStagePre = 1u, kStageDkDv = 2u, kStageDq = 4u;
 hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int d, int causal, unsigned stages,
                       hipStream_t stream);
 

@@ -90,10 +90,10 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: float32 D and
- * log2-domain L per query row (rows padded to a multiple of 64 per head),
- * plus (bf16 only) a float32 dQ accumulator [B][Hq][Tq][d].  Each part starts
- * on a 256-byte boundary.  Returns 0 for
- * invalid arguments.  The workspace holds nothing between calls.
+ * log2-domain L per query row, rows padded to a multiple of 64 per head, each
+ * part starting on a 256-byte boundary (8 * B * Hq * ceil(Tq / 64) * 64 bytes
+ * plus alignment).  Returns 0 for invalid arguments.  The workspace holds
+ * nothing between calls.
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype);
 
@@ -108,8 +108,10 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int
  *   dV_j  = sum_{h in group} sum_i P_ij dO_i.
  * O and L must be the outputs of fa_fwd for the same Q, K, V, sizes, causal
  * and scale.  Writes dQ, dK, dV (dtype) and uses `workspace` (at least
- * fa_bwd_workspace_bytes bytes, device memory, 256-byte aligned preferred)
- * as scratch.  No T x T tensor is ever formed.
+ * fa_bwd_workspace_bytes bytes, device memory, 16-byte aligned) as scratch.
+ * No T x T tensor is ever formed and no atomics are used: dK, dV come from a
+ * pass over key blocks, dQ from a pass over query blocks, each of which
+ * rebuilds the score and probability tiles it needs.
  */
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const float* L,
            const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
@@ -119,17 +121,16 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const flo
 /*
  * The backward pass in three stages, for callers that time or schedule them
  * separately.  Same arguments and semantics as fa_bwd, plus a bit mask:
- *   FA_BWD_STAGE_PRE    D = rowsum(dO * O) and log2-domain L into the
- *                       workspace; zero the fp32 dQ accumulator;
- *   FA_BWD_STAGE_MAIN   recompute S and P tile by tile; write dK and dV;
- *                       accumulate dQ (fp32);
- *   FA_BWD_STAGE_FINISH (bf16) round the dQ accumulator into dQ; no-op for fp32.
- * Stages read what earlier stages left in the workspace, so they must run in
- * this order, on one stream, with identical arguments; fa_bwd runs all three.
+ *   FA_BWD_STAGE_PRE   D = rowsum(dO * O) and log2-domain L into the workspace;
+ *   FA_BWD_STAGE_DKDV  rebuild S and P per key block; write dK and dV;
+ *   FA_BWD_STAGE_DQ    rebuild S and P per query block; write dQ.
+ * DKDV and DQ read what PRE left in the workspace (and nothing else of each
+ * other), so PRE must run first on the same stream with identical arguments;
+ * fa_bwd runs all three.
  */
 #define FA_BWD_STAGE_PRE 1u
-#define FA_BWD_STAGE_MAIN 2u
-#define FA_BWD_STAGE_FINISH 4u
+#define FA_BWD_STAGE_DKDV 2u
+#define FA_BWD_STAGE_DQ 4u
 #define FA_BWD_STAGE_ALL 7u
 int fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O, const float* L,
                   const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,

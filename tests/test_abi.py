@@ -48,12 +48,11 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    # bf16: D and L2 per row (256-aligned) + fp32 dQ accumulator
+    # D and L2 per query row, rows padded to a multiple of 64 per head, 256-byte aligned parts
     rows = 4 * 32 * 4096
-    want = rows * 4 + rows * 4 + rows * 128 * 4
-    assert fa.workspace_bytes(4, 32, 8, 4096, 4096, 128, fa.FA_DTYPE_BF16) == want
-    # fp32: no accumulator (dQ itself accumulates); rows padded to 128 (multiple of 64)
+    assert fa.workspace_bytes(4, 32, 8, 4096, 4096, 128, fa.FA_DTYPE_BF16) == 2 * rows * 4
     assert fa.workspace_bytes(1, 1, 1, 100, 100, 64, fa.FA_DTYPE_F32) == 512 + 512
+    assert fa.workspace_bytes(3, 1, 1, 1, 100, 64, fa.FA_DTYPE_BF16) == 768 + 768
     assert fa.workspace_bytes(1, 1, 1, 0, 5, 64, fa.FA_DTYPE_BF16) == 0
     # invalid arguments -> 0
     assert fa.workspace_bytes(1, 3, 2, 10, 10, 64, fa.FA_DTYPE_BF16) == 0
