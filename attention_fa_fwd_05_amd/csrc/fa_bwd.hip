@@ -238,18 +238,13 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
-  constexpr int NW = dq_waves<T, D>(), BQ = 32 * NW, BK = 64;
+  constexpr int NW = dq_waves<T, D>(), NTHR = 64 * NW, BQ = 32 * NW, BK = 64;
   constexpr int KPER = M::KPER;
-  constexpr int LD = D + 32 / (int)sizeof(T);       // 32-byte row padding
   constexpr int NSD = (D / 2) / KPER;
   constexpr int NSK = (BK / 2) / KPER;
   constexpr int NDT = D / 32;
-  constexpr int EPC = 16 / (int)sizeof(T);
-  constexpr int CPR = D / EPC;
-  constexpr int NCH = BK * CPR / (NW * 64);
-  static_assert(NCH * NW * 64 == BK * CPR, "tile must split evenly");
-  __shared__ __attribute__((aligned(16))) T sK[2][BK * LD];
-  __shared__ __attribute__((aligned(16))) T sV[2][BK * LD];
+  __shared__ __attribute__((aligned(16))) T sK[2][BK * D];
+  __shared__ __attribute__((aligned(16))) T sV[2][BK * D];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
@@ -269,30 +264,12 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   if (CAUSAL) kend = min(a.Tk, max(0, q0 + BQ + off));
   const int ntiles = (kend + BK - 1) / BK;
 
-  uint4 pk[NCH], pv[NCH];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int idx = i * NW * 64 + tid, row = idx / CPR, ch = idx % CPR;
-      const bool ok = k0 + row < a.Tk;
-      const size_t o = (size_t)(ok ? k0 + row : 0) * D + ch * EPC;
-      pk[i] = ld16(Kp + o);
-      pv[i] = ld16(Vp + o);
-      if (!ok) { pk[i] = uint4{0u, 0u, 0u, 0u}; pv[i] = uint4{0u, 0u, 0u, 0u}; }
-    }
+  // Rows past Tk are loaded as copies of the last key; their scores are masked.
+  auto issue = [&](int k0, int buf) {
+    dma_rows<T, D, BK, NTHR>(sK[buf], Kp, k0, a.Tk);
+    dma_rows<T, D, BK, NTHR>(sV[buf], Vp, k0, a.Tk);
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int idx = i * NW * 64 + tid, row = idx / CPR, ch = idx % CPR;
-      st16(&sK[buf][row * LD + ch * EPC], pk[i]);
-      st16(&sV[buf][row * LD + ch * EPC], pv[i]);
-    }
-  };
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
+  if (ntiles > 0) issue(0, 0);
 
   // Q^T and dO^T operands for this lane's query, L2 and D of that row.
   Op qop[NSD], gop[NSD];
@@ -307,6 +284,11 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   }
   const float l2 = q_ok ? a.Lg[(size_t)bh * a.Tqp + myq] : INFINITY;
   const float dd = q_ok ? a.Dvec[(size_t)bh * a.Tqp + myq] : 0.f;
+  NatFetch<T, D> nat;
+  nat.init(n, h);
+  TrPermFetch<T, D> trp;
+  trp.init(lane);
+  wait_vmcnt<0>();
   __syncthreads();
 
   const float c = a.scale_log2;
@@ -316,20 +298,19 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
 
   for (int jt = 0; jt < ntiles; ++jt) {
     const int k0 = jt * BK, buf = jt & 1;
-    const bool more = jt + 1 < ntiles;
-    if (more) gload(k0 + BK);
+    if (jt + 1 < ntiles) issue(k0 + BK, buf ^ 1);
+    const T* cK = sK[buf];
+    const T* cV = sV[buf];
 
     if (!(CAUSAL && k0 > qw + 31 + off)) {          // some key of the tile visible to this wave
       // S^T = K Q^T and dP^T = V dO^T: 64 keys x 32 queries each.
       f32x16 st0 = f32x16{}, st1 = f32x16{}, dp0 = f32x16{}, dp1 = f32x16{};
-      const T* kr = &sK[buf][n * LD + h * (D / 2)];
-      const T* vr = &sV[buf][n * LD + h * (D / 2)];
 #pragma unroll
       for (int s = 0; s < NSD; ++s) {
-        st0 = M::mma(M::ld(kr + s * KPER), qop[s], st0);
-        st1 = M::mma(M::ld(kr + 32 * LD + s * KPER), qop[s], st1);
-        dp0 = M::mma(M::ld(vr + s * KPER), gop[s], dp0);
-        dp1 = M::mma(M::ld(vr + 32 * LD + s * KPER), gop[s], dp1);
+        st0 = M::mma(nat.ld(cK, 0, s), qop[s], st0);
+        st1 = M::mma(nat.ld(cK, 1, s), qop[s], st1);
+        dp0 = M::mma(nat.ld(cV, 0, s), gop[s], dp0);
+        dp1 = M::mma(nat.ld(cV, 1, s), gop[s], dp1);
       }
       sched_interleave<4 * NSD, 4>();
       float ds[32];
@@ -352,11 +333,11 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
 #pragma unroll
       for (int t = 0; t < NDT; ++t) {
 #pragma unroll
-        for (int s = 0; s < NSK; ++s)
-          acc[t] = M::mma(TrPerm<T>::ld(&sK[buf][0], LD, h, s, t * 32), dsop[s], acc[t]);
+        for (int s = 0; s < NSK; ++s) acc[t] = M::mma(trp.ld(cK, t, s), dsop[s], acc[t]);
       }
+      sched_interleave<NDT * NSK, 4, (sizeof(T) == 2 ? 2 : 1)>();
     }
-    if (more) lstore(buf ^ 1);
+    wait_vmcnt<0>();                                 // this wave's loads of the next tile have landed
     __syncthreads();
   }
 

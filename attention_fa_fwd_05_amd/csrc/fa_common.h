@@ -106,10 +106,16 @@ template <> struct TrPerm<float> {
 // Unpadded LDS tiles with XOR-swizzled 16-byte chunks.
 //
 // A [rows x D] tile of T is stored row-major without padding; chunk c of row r
-// (16 bytes) sits at slot c ^ fsw(r).  fsw takes 8 distinct values over any 8
-// consecutive rows (natural 16-byte operand reads of 8 rows hit 8 different
-// bank groups) and keeps the two chunks a transposed read touches in each of
-// 4 consecutive rows (aligned to 4) on 8 distinct slots.  The layout can be
+// (16 bytes = 4 of the 64 LDS banks) sits at slot c ^ fsw(r).  For 256-byte
+// rows fsw(r) = 4 (r & 3) + ((r >> 2) & 3):
+//  * it takes 16 distinct values over any 16 consecutive rows, so 16 lanes
+//    reading one chunk of 16 rows (a natural operand) hit 16 different slots;
+//  * the 4 rows of an aligned 4-row group differ in bits 2-3, so the 4-chunk
+//    run {c .. c+3} (c a multiple of 4) that 32 lanes of a transposed read take
+//    from each of the 4 rows lands on 16 distinct slots.
+// For 128-byte rows (two rows per bank sweep) the same holds with
+// fsw(r) = 4 ((r >> 1) & 1) + ((r >> 2) & 3).  fsw depends on r & 15 only, so
+// per-lane offsets can be tabulated over a 16-row period.  The layout can be
 // filled by direct global->LDS loads, which write 64 consecutive 16-byte slots
 // per wave instruction.
 template <typename T, int D>
@@ -118,7 +124,7 @@ struct SwzTile {
   static constexpr int NCH = D / EPC;               // chunks per row
   static_assert(NCH == 8 || NCH == 16 || NCH == 32, "row must be 8, 16 or 32 chunks");
   __device__ static inline int fsw(int r) {
-    return NCH >= 16 ? ((2 * (r & 7)) ^ ((r >> 3) & 1)) : ((2 * (r & 3)) ^ ((r >> 2) & 1));
+    return NCH >= 16 ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
   }
   // element index of (row, col)
   __device__ static inline int elem(int r, int col) {

@@ -13,9 +13,9 @@
 // S^T = K_j Q_i^T (keys x queries) so that one query row lives in one lane
 // column: the row max is an in-register reduction plus one exchange between
 // the two lane halves, and the probabilities feed O^T += V_j^T P^T straight
-// from registers.  K_j and V_j (64 keys) are staged in LDS in natural layout,
-// double-buffered (the next tile's global loads are in flight while the
-// current one is computed); V^T operands are fetched with transposed LDS reads.  Softmax runs in the
+// from registers.  K_j and V_j (64 keys) are staged in LDS as swizzled
+// row-major tiles, double-buffered and filled by direct global->LDS loads one
+// tile ahead; V^T operands are fetched with transposed LDS reads.  Softmax runs in the
 // exp2 domain (scores pre-multiplied by scale * log2 e); L is converted back
 // to a natural log at the end.
 #include "fa_common.h"
@@ -37,18 +37,15 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__((64 * fwd_waves<T, D>())) void fwd_kernel(FwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
-  constexpr int NW = fwd_waves<T, D>(), BQ = 32 * NW, BK = 64;
+  constexpr int NW = fwd_waves<T, D>(), NTHR = 64 * NW, BQ = 32 * NW, BK = 64;
   constexpr int KPER = M::KPER;
-  constexpr int LD = D + 32 / (int)sizeof(T);       // 32-byte row padding
   constexpr int NSD = (D / 2) / KPER;               // steps over the head dim
   constexpr int NSK = (BK / 2) / KPER;              // steps over a key tile
   constexpr int NDT = D / 32;                       // 32-wide output tiles
-  constexpr int EPC = 16 / (int)sizeof(T);          // elements per 16-byte chunk
-  constexpr int CPR = D / EPC;                      // chunks per row
-  constexpr int NCH = BK * CPR / (NW * 64);         // chunks per thread per tile
-  static_assert(NCH * NW * 64 == BK * CPR, "tile must split evenly");
-  __shared__ __attribute__((aligned(16))) T sK[2][BK * LD];
-  __shared__ __attribute__((aligned(16))) T sV[2][BK * LD];
+  // K / V tiles, swizzled, double-buffered; the next tile is fetched by direct
+  // global->LDS loads while the current one is used.
+  __shared__ __attribute__((aligned(16))) T sK[2][BK * D];
+  __shared__ __attribute__((aligned(16))) T sV[2][BK * D];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
@@ -66,31 +63,12 @@ __global__ __launch_bounds__((64 * fwd_waves<T, D>())) void fwd_kernel(FwdArgs a
   if (CAUSAL) kend = min(a.Tk, max(0, q0 + BQ + off));
   const int ntiles = (kend + BK - 1) / BK;
 
-  // K/V tile staging: global -> registers (issued a tile ahead) -> LDS.
-  uint4 pk[NCH], pv[NCH];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int idx = i * NW * 64 + tid, row = idx / CPR, ch = idx % CPR;
-      const bool ok = k0 + row < a.Tk;
-      const size_t o = (size_t)(ok ? k0 + row : 0) * D + ch * EPC;
-      pk[i] = ld16(Kp + o);
-      pv[i] = ld16(Vp + o);
-      if (!ok) { pk[i] = uint4{0u, 0u, 0u, 0u}; pv[i] = uint4{0u, 0u, 0u, 0u}; }
-    }
+  // Rows past Tk are loaded as copies of the last key; their scores are masked.
+  auto issue = [&](int k0, int buf) {
+    dma_rows<T, D, BK, NTHR>(sK[buf], Kp, k0, a.Tk);
+    dma_rows<T, D, BK, NTHR>(sV[buf], Vp, k0, a.Tk);
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int idx = i * NW * 64 + tid, row = idx / CPR, ch = idx % CPR;
-      st16(&sK[buf][row * LD + ch * EPC], pk[i]);
-      st16(&sV[buf][row * LD + ch * EPC], pv[i]);
-    }
-  };
-  if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
+  if (ntiles > 0) issue(0, 0);
 
   // Q^T operand for this lane: query myq, head-dim half h.
   Op qop[NSD];
@@ -103,6 +81,11 @@ __global__ __launch_bounds__((64 * fwd_waves<T, D>())) void fwd_kernel(FwdArgs a
       if (!ok) qop[s] = Op{};
     }
   }
+  NatFetch<T, D> nat;
+  nat.init(n, h);
+  TrPermFetch<T, D> trp;
+  trp.init(lane);
+  wait_vmcnt<0>();
   __syncthreads();
 
   const float c = a.scale_log2;
@@ -113,17 +96,18 @@ __global__ __launch_bounds__((64 * fwd_waves<T, D>())) void fwd_kernel(FwdArgs a
 
   for (int jt = 0; jt < ntiles; ++jt) {
     const int k0 = jt * BK, buf = jt & 1;
-    const bool more = jt + 1 < ntiles;
-    if (more) gload(k0 + BK);
+    if (jt + 1 < ntiles) issue(k0 + BK, buf ^ 1);
+    const T* cK = sK[buf];
+    const T* cV = sV[buf];
 
     if (!(CAUSAL && k0 > qw + 31 + off)) {          // some key of the tile visible to this wave
       f32x16 st0 = f32x16{}, st1 = f32x16{};
-      const T* kr = &sK[buf][n * LD + h * (D / 2)];
 #pragma unroll
       for (int s = 0; s < NSD; ++s) {
-        st0 = M::mma(M::ld(kr + s * KPER), qop[s], st0);
-        st1 = M::mma(M::ld(kr + 32 * LD + s * KPER), qop[s], st1);
+        st0 = M::mma(nat.ld(cK, 0, s), qop[s], st0);
+        st1 = M::mma(nat.ld(cK, 1, s), qop[s], st1);
       }
+      sched_interleave<2 * NSD, 4>();
       float x[32];
 #pragma unroll
       for (int i = 0; i < 16; ++i) { x[i] = st0[i]; x[16 + i] = st1[i]; }
@@ -162,11 +146,11 @@ __global__ __launch_bounds__((64 * fwd_waves<T, D>())) void fwd_kernel(FwdArgs a
 #pragma unroll
       for (int t = 0; t < NDT; ++t) {
 #pragma unroll
-        for (int s = 0; s < NSK; ++s)
-          o[t] = M::mma(TrPerm<T>::ld(&sV[buf][0], LD, h, s, t * 32), pop[s], o[t]);
+        for (int s = 0; s < NSK; ++s) o[t] = M::mma(trp.ld(cV, t, s), pop[s], o[t]);
       }
+      sched_interleave<NDT * NSK, 4, (sizeof(T) == 2 ? 2 : 1)>();
     }
-    if (more) lstore(buf ^ 1);
+    wait_vmcnt<0>();                                 // this wave's loads of the next tile have landed
     __syncthreads();
   }
 
