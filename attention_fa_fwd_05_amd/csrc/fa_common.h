@@ -270,13 +270,16 @@ template <int D> struct TrPermFetch<float, D> {
 // RPM LDS reads: issue the reads for the first AHEAD instructions, then
 // alternate one matrix instruction with the reads of a later one, so LDS
 // latency overlaps matrix work instead of stalling each instruction.
-template <int NMMA, int AHEAD, int RPM = 1>
+// MPR matrix instructions may share one operand read (MPR consecutive
+// instructions per RPM reads).
+template <int NMMA, int AHEAD, int RPM = 1, int MPR = 1>
 __device__ inline void sched_interleave() {
   constexpr int kMfma = 0x008, kDsRead = 0x100;
-  __builtin_amdgcn_sched_group_barrier(kDsRead, AHEAD * RPM, 0);
+  static_assert(NMMA % MPR == 0 && AHEAD % MPR == 0, "groups of MPR matrix instructions");
+  __builtin_amdgcn_sched_group_barrier(kDsRead, AHEAD / MPR * RPM, 0);
 #pragma unroll
-  for (int k = 0; k < NMMA - AHEAD; ++k) {
-    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+  for (int k = 0; k < (NMMA - AHEAD) / MPR; ++k) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, MPR, 0);
     __builtin_amdgcn_sched_group_barrier(kDsRead, RPM, 0);
   }
   __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD, 0);
@@ -308,6 +311,26 @@ __device__ inline QWork qblock_work(int B, int Hq, int Hkv, int nqb, bool causal
   w.hq = w.hk * G + r;
   w.qb = causal ? nqb - 1 - qi : qi;
   return w;
+}
+
+// Scheduling hint for matrix work that should hide independent vector-ALU
+// work: after AHEAD operand reads, each matrix instruction is followed by up
+// to VPM vector-ALU instructions and the read of a later operand.
+template <int NMMA, int AHEAD, int VPM>
+__device__ inline void sched_interleave_valu() {
+  constexpr int kValu = 0x002 | 0x400, kMfma = 0x008, kDsRead = 0x100;  // VALU incl. transcendental
+  __builtin_amdgcn_sched_group_barrier(kDsRead, AHEAD, 0);
+#pragma unroll
+  for (int k = 0; k < NMMA - AHEAD; ++k) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kValu, VPM, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < AHEAD; ++k) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kValu, VPM, 0);
+  }
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

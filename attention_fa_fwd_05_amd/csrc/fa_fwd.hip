@@ -28,16 +28,24 @@ namespace fa {
 // and the O accumulator is rescaled only on the rare tiles where that happens.
 constexpr float kTau = 8.0f;
 
-// Waves per workgroup: 8 (256 query rows, two waves per SIMD), or 4 where the
-// fp32 d = 128 operands would not fit in 256 registers.
-template <typename T, int D>
-constexpr int fwd_waves() { return (sizeof(T) == 4 && D == 128) ? 4 : 8; }
+// Workgroup shape.  Each wave owns QT 32-row query tiles; with QT = 2 every
+// K / V operand read from LDS feeds two matrix instructions, but a wave then
+// needs the whole register file (one wave per SIMD) and its softmax no longer
+// overlaps another wave's matrix work, which costs more than the LDS saving:
+// QT = 1 with 8 waves (two per SIMD) is faster.  fp32 d = 128 uses 4 waves so
+// its operands fit.
+template <typename T, int D> struct FwdShape {
+  static constexpr int QT = 1;
+  static constexpr int NW = (sizeof(T) == 4 && D == 128) ? 4 : 8;
+  static constexpr int BQ = 32 * QT * NW;
+};
 
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__((64 * fwd_waves<T, D>())) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
-  constexpr int NW = fwd_waves<T, D>(), NTHR = 64 * NW, BQ = 32 * NW, BK = 64;
+  using SH = FwdShape<T, D>;
+  constexpr int QT = SH::QT, NW = SH::NW, NTHR = 64 * NW, BQ = SH::BQ, BK = 64;
   constexpr int KPER = M::KPER;
   constexpr int NSD = (D / 2) / KPER;               // steps over the head dim
   constexpr int NSK = (BK / 2) / KPER;              // steps over a key tile
@@ -52,7 +60,7 @@ __global__ __launch_bounds__((64 * fwd_waves<T, D>())) void fwd_kernel(FwdArgs a
   const int nqb = (a.Tq + BQ - 1) / BQ;
   const QWork wk = qblock_work(a.B, a.Hq, a.Hkv, nqb, CAUSAL);
   const int bh = wk.b * a.Hq + wk.hq;
-  const int q0 = wk.qb * BQ, qw = q0 + 32 * w, myq = qw + n;
+  const int q0 = wk.qb * BQ, qw = q0 + 32 * QT * w;  // this wave's rows: qw .. qw + 32 QT - 1
   const int off = a.Tk - a.Tq;
 
   const T* Qp = reinterpret_cast<const T*>(a.Q) + (size_t)bh * a.Tq * D;
@@ -70,15 +78,17 @@ __global__ __launch_bounds__((64 * fwd_waves<T, D>())) void fwd_kernel(FwdArgs a
   };
   if (ntiles > 0) issue(0, 0);
 
-  // Q^T operand for this lane: query myq, head-dim half h.
-  Op qop[NSD];
-  {
-    const bool ok = myq < a.Tq;
-    const T* qrow = Qp + (size_t)(ok ? myq : 0) * D + h * (D / 2);
+  // Q^T operands for this lane's queries qw + 32 u + n, head-dim half h.
+  Op qop[QT][NSD];
+#pragma unroll
+  for (int u = 0; u < QT; ++u) {
+    const int q = qw + 32 * u + n;
+    const bool ok = q < a.Tq;
+    const T* qrow = Qp + (size_t)(ok ? q : 0) * D + h * (D / 2);
 #pragma unroll
     for (int s = 0; s < NSD; ++s) {
-      qop[s] = M::ld(qrow + s * KPER);
-      if (!ok) qop[s] = Op{};
+      qop[u][s] = M::ld(qrow + s * KPER);
+      if (!ok) qop[u][s] = Op{};
     }
   }
   NatFetch<T, D> nat;
@@ -89,10 +99,15 @@ __global__ __launch_bounds__((64 * fwd_waves<T, D>())) void fwd_kernel(FwdArgs a
   __syncthreads();
 
   const float c = a.scale_log2;
-  float m_run = -INFINITY, lsum = 0.f;
-  f32x16 o[NDT];
+  float m_run[QT], lsum[QT];
+  f32x16 o[QT][NDT];
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) o[t] = f32x16{};
+  for (int u = 0; u < QT; ++u) {
+    m_run[u] = -INFINITY;
+    lsum[u] = 0.f;
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) o[u][t] = f32x16{};
+  }
 
   for (int jt = 0; jt < ntiles; ++jt) {
     const int k0 = jt * BK, buf = jt & 1;
@@ -100,87 +115,109 @@ __global__ __launch_bounds__((64 * fwd_waves<T, D>())) void fwd_kernel(FwdArgs a
     const T* cK = sK[buf];
     const T* cV = sV[buf];
 
-    if (!(CAUSAL && k0 > qw + 31 + off)) {          // some key of the tile visible to this wave
-      f32x16 st0 = f32x16{}, st1 = f32x16{};
+    if (!(CAUSAL && k0 > qw + 32 * QT - 1 + off)) {   // some key of the tile visible to this wave
+      // S^T = K Q^T: 2 key sub-tiles x QT query tiles; each K operand feeds QT products.
+      f32x16 st[QT][2];
+#pragma unroll
+      for (int u = 0; u < QT; ++u) { st[u][0] = f32x16{}; st[u][1] = f32x16{}; }
 #pragma unroll
       for (int s = 0; s < NSD; ++s) {
-        st0 = M::mma(nat.ld(cK, 0, s), qop[s], st0);
-        st1 = M::mma(nat.ld(cK, 1, s), qop[s], st1);
-      }
-      sched_interleave<2 * NSD, 4>();
-      float x[32];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) { x[i] = st0[i]; x[16 + i] = st1[i]; }
-      if ((k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off)) {
+        for (int kt = 0; kt < 2; ++kt) {
+          const Op kop = nat.ld(cK, kt, s);
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
-          const int key = k0 + perm_index(h, r);
-          if (key >= a.Tk || (CAUSAL && key > myq + off)) x[r] = -INFINITY;
+          for (int u = 0; u < QT; ++u) st[u][kt] = M::mma(kop, qop[u][s], st[u][kt]);
         }
       }
-      float mt = fmaxf(x[0], x[1]);
-#pragma unroll
-      for (int r = 2; r < 32; r += 2) mt = fmaxf(mt, fmaxf(x[r], x[r + 1]));
-      mt = wave_xor32_max(mt) * c;                   // row max, exp2 units
-      const bool need = mt > m_run + kTau;
-      if (__ballot(need)) {
-        const float m_new = need ? mt : m_run;
-        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
-        lsum *= alpha;
-#pragma unroll
-        for (int t = 0; t < NDT; ++t) o[t] *= alpha;
-        m_run = m_new;
-      }
-      const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
-      float ps = 0.f;
-#pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        x[r] = fast_exp2(__builtin_fmaf(x[r], c, nm));
-        ps += x[r];
-      }
-      lsum += ps;
+      sched_interleave<2 * NSD * QT, 4 * QT, 1, QT>();
 
-      Op pop[NSK];
+      const bool need_mask = (k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off);
+      Op pop[QT][NSK];
 #pragma unroll
-      for (int s = 0; s < NSK; ++s) pop[s] = M::pack(x + s * KPER);
+      for (int u = 0; u < QT; ++u) {
+        const int myq = qw + 32 * u + n;
+        float x[32];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { x[i] = st[u][0][i]; x[16 + i] = st[u][1][i]; }
+        if (need_mask) {
+#pragma unroll
+          for (int r = 0; r < 32; ++r) {
+            const int key = k0 + perm_index(h, r);
+            if (key >= a.Tk || (CAUSAL && key > myq + off)) x[r] = -INFINITY;
+          }
+        }
+        float mt = fmaxf(x[0], x[1]);
+#pragma unroll
+        for (int r = 2; r < 32; r += 2) mt = fmaxf(mt, fmaxf(x[r], x[r + 1]));
+        mt = wave_xor32_max(mt) * c;                 // row max, exp2 units
+        const bool need = mt > m_run[u] + kTau;
+        if (__ballot(need)) {
+          const float m_new = need ? mt : m_run[u];
+          const float alpha = need ? fast_exp2(m_run[u] - m_new) : 1.f;
+          lsum[u] *= alpha;
+#pragma unroll
+          for (int t = 0; t < NDT; ++t) o[u][t] *= alpha;
+          m_run[u] = m_new;
+        }
+        const float nm = (m_run[u] == -INFINITY) ? 0.f : -m_run[u];
+        float ps = 0.f;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+          x[r] = fast_exp2(__builtin_fmaf(x[r], c, nm));
+          ps += x[r];
+        }
+        lsum[u] += ps;
+#pragma unroll
+        for (int s = 0; s < NSK; ++s) pop[u][s] = M::pack(x + s * KPER);
+      }
+
+      // O^T += V^T P^T; each V^T operand feeds QT products.
 #pragma unroll
       for (int t = 0; t < NDT; ++t) {
 #pragma unroll
-        for (int s = 0; s < NSK; ++s) o[t] = M::mma(trp.ld(cV, t, s), pop[s], o[t]);
+        for (int s = 0; s < NSK; ++s) {
+          const Op vop = trp.ld(cV, t, s);
+#pragma unroll
+          for (int u = 0; u < QT; ++u) o[u][t] = M::mma(vop, pop[u][s], o[u][t]);
+        }
       }
-      sched_interleave<NDT * NSK, 4, (sizeof(T) == 2 ? 2 : 1)>();
+      sched_interleave<NDT * NSK * QT, 4 * QT, (sizeof(T) == 2 ? 2 : 1), QT>();
     }
     wait_vmcnt<0>();                                 // this wave's loads of the next tile have landed
     __syncthreads();
   }
 
-  const float ltot = wave_xor32_sum(lsum);
-  if (myq < a.Tq) {
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    T* orow = reinterpret_cast<T*>(a.O) + ((size_t)bh * a.Tq + myq) * D;
 #pragma unroll
-    for (int t = 0; t < NDT; ++t) {
+  for (int u = 0; u < QT; ++u) {
+    const int myq = qw + 32 * u + n;
+    const float ltot = wave_xor32_sum(lsum[u]);
+    if (myq < a.Tq) {
+      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+      T* orow = reinterpret_cast<T*>(a.O) + ((size_t)bh * a.Tq + myq) * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = t * 32 + 8 * g + 4 * h;
-        store4(orow + d0, o[t][4 * g] * inv, o[t][4 * g + 1] * inv, o[t][4 * g + 2] * inv,
-               o[t][4 * g + 3] * inv);
+      for (int t = 0; t < NDT; ++t) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = t * 32 + 8 * g + 4 * h;
+          store4(orow + d0, o[u][t][4 * g] * inv, o[u][t][4 * g + 1] * inv, o[u][t][4 * g + 2] * inv,
+                 o[u][t][4 * g + 3] * inv);
+        }
       }
-    }
-    if (h == 0) {
-      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-      a.L[(size_t)bh * a.Tq + myq] = ltot > 0.f ? mref * kLn2 + logf(ltot) : -INFINITY;
+      if (h == 0) {
+        const float mref = (m_run[u] == -INFINITY) ? 0.f : m_run[u];
+        a.L[(size_t)bh * a.Tq + myq] = ltot > 0.f ? mref * kLn2 + logf(ltot) : -INFINITY;
+      }
     }
   }
 }
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  constexpr int NW = fwd_waves<T, D>();
-  const int nqb = (a.Tq + 32 * NW - 1) / (32 * NW);
+  using SH = FwdShape<T, D>;
+  const int nqb = (a.Tq + SH::BQ - 1) / SH::BQ;
   const long long blocks = (long long)nqb * a.B * a.Hq;
   if (blocks == 0) return hipSuccess;
-  return launch<64 * NW>(fwd_kernel<T, D, CAUSAL>, blocks, stream, a);
+  return launch<64 * SH::NW>(fwd_kernel<T, D, CAUSAL>, blocks, stream, a);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream) {
