@@ -4,9 +4,10 @@
 // rest; "Backward Pass Implementation", section "The Recomputation Strategy").
 //
 // Three launches on one stream:
-//  1. bwd_pre_kernel: D_i = rowsum(dO_i * O_i) and L_i in log2 units (+inf for
-//     rows without keys, so their probabilities vanish).  Rows are padded to a
-//     multiple of 64 per head (padding: D = 0, L2 = +inf).
+//  1. bwd_pre_kernel: -D_i = -rowsum(dO_i * O_i) and L_i in log2 units (+inf
+//     for rows without keys, so their probabilities vanish).  Rows are padded
+//     to a multiple of 64 per head (padding: -D = 0, L2 = +inf).  The negated
+//     D seeds the dP accumulators, which then hold dP - D directly.
 //  2. dkdv_kernel: one workgroup per (128-key block, b, K/V head); each of the
 //     4 waves owns 32 keys, whose K and V rows sit in registers, and dK, dV
 //     accumulate in registers across every query block of every query head of
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   for (int msk = 8; msk >= 1; msk >>= 1) acc += __shfl_xor(acc, msk, 64);
   if (prow >= prows || j != 0) return;
   const float l = ok ? a.L[row] : -INFINITY;
-  a.Dvec[prow] = acc;
+  a.Dvec[prow] = -acc;
   a.Lg[prow] = (l == -INFINITY) ? INFINITY : l * kLog2e;
 }
 
@@ -67,22 +68,63 @@ __device__ inline KWork kblock_work(const BwdArgs& a, int nkb) {
   return w;
 }
 
+// Position of the m-th instruction of a phase that interleaves NA products of
+// kind A with NB of kind B as evenly as possible: true when it is of kind B.
+__host__ __device__ constexpr bool interleave_is_b(int m, int na, int nb) {
+  return ((m + 1) * nb) / (na + nb) > (m * nb) / (na + nb);
+}
+__host__ __device__ constexpr int interleave_rank(int m, int na, int nb) {
+  // index of instruction m within its own kind
+  return interleave_is_b(m, na, nb) ? (m * nb) / (na + nb) : m - ((m + 1) * nb) / (na + nb);
+}
+
+template <int V> struct IC { static constexpr int value = V; };
+
+__device__ inline void zero_elem(bf16x8& x, int e) { x[e] = (bf16)0.f; }
+__device__ inline void zero_elem(float& x, int) { x = 0.f; }
+
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
   constexpr int BK = 128;                           // keys per workgroup, 32 per wave
-  constexpr int BQ = (sizeof(T) == 4 && D == 128) ? 32 : 64;
+  constexpr int BQ = 64;                            // queries per block: two 32-query tiles
   constexpr int KPER = M::KPER;
-  constexpr int NSD = (D / 2) / KPER;
-  constexpr int NSQ = (BQ / 2) / KPER;
-  constexpr int NDT = D / 32, NQT = BQ / 32;
-  // Q / dO / L2 / D blocks are double-buffered; the next block is loaded by
-  // direct global->LDS loads while the current one is processed.
-  __shared__ __attribute__((aligned(16))) T sQ[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) T sdO[2][BQ * D];
-  __shared__ __attribute__((aligned(16))) float sL[2][64];
-  __shared__ __attribute__((aligned(16))) float sD[2][64];
+  constexpr int NSD = (D / 2) / KPER;               // contraction steps over d
+  constexpr int NSQ = (BQ / 2) / KPER;              // contraction steps over a query block
+  constexpr int NDT = D / 32;
+  constexpr int NSH = NSQ / 2;                      // steps per 32-query tile
+  // Three LDS buffers let block i+2 load while blocks i and i+1 are read;
+  // fp32 with d = 128 fits two, and then loads without overlap.
+  constexpr int NB = (sizeof(T) == 4 && D == 128) ? 2 : 3;
+  // Software pipeline over the query blocks of the work list, iteration i:
+  //   phase 1a: S, dP of block i+1 tile 0  |  dV, dK of block i, first quarter
+  //             of its steps  |  P, dS of block i tile 1 (vector ALU);
+  //   phase 1b: S, dP of block i+1 tile 1  |  dV, dK of block i, second quarter;
+  //   phase 2:  dV, dK of block i, second half  |  P, dS of block i+1 tile 0.
+  // P, dS of a tile are written over those of the same tile of the previous
+  // block once its last product has been issued.  Products and LDS reads go
+  // out in a fixed order with a fixed number of operands in flight, and the
+  // loop is unrolled over the buffers so that every LDS address is a lane
+  // offset plus a constant.
+  constexpr int NS1 = 2 * NSD;                      // S and dP products per tile
+  constexpr int NDQ = (NSH / 2) * 2 * NDT;          // dV/dK products per quarter of the steps
+  constexpr int NDH = NSH * 2 * NDT;                // ... per half
+  constexpr int NPA = NS1 + NDQ;                    // products in phase 1a (and 1b)
+  constexpr int AHEAD = 4;                          // operands in flight
+  constexpr int EPS1 = (16 + NPA - 1) / NPA;        // probabilities per product, phase 1a
+  constexpr int EPS2 = (16 + NDH - 1) / NDH;        // ... phase 2
+  constexpr int LAST_PROB1 = (16 + EPS1 - 1) / EPS1 - 1;   // last phase-1a step with one
+  // step of phase 1a that seeds tile 1's dP accumulator: after its last
+  // probability and before tile 1's first operand read
+  constexpr int SEED1 = LAST_PROB1 > NPA - AHEAD - 1 ? LAST_PROB1 : NPA - AHEAD - 1;
+  static_assert(NSH % 2 == 0, "quarters of the query steps");
+  static_assert(SEED1 < NPA, "seed step inside phase 1a");
+  static_assert(NPA % AHEAD == 0, "operand ring slots line up across phases");
+  __shared__ __attribute__((aligned(16))) float sL[NB][64];
+  __shared__ __attribute__((aligned(16))) float sD[NB][64];    // -D
+  __shared__ __attribute__((aligned(16))) T sQ[NB][BQ * D];
+  __shared__ __attribute__((aligned(16))) T sdO[NB][BQ * D];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
@@ -93,31 +135,29 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   const int off = a.Tk - a.Tq;
   const float c = a.scale_log2;
   const bool key_ok = mykey < a.Tk;
+  const bool ragged = k0 + BK > a.Tk;               // uniform: this block holds the key end
 
   const T* Kp = reinterpret_cast<const T*>(a.K) + (size_t)bhk * a.Tk * D;
   const T* Vp = reinterpret_cast<const T*>(a.V) + (size_t)bhk * a.Tk * D;
 
   // Work list: every (query head of the group, query block that can see a key
-  // of this block); the next item's Q / dO / L2 / D are loaded during the current one.
+  // of this block).
   const int nqb = (a.Tq + BQ - 1) / BQ;
   const int qb0 = CAUSAL ? min(nqb, max(0, k0 - off) / BQ) : 0;
   const int per_head = nqb - qb0, total = G * per_head;
-  auto item = [&](int it, int& bh, int& q0) {
-    bh = wk.b * a.Hq + wk.hk * G + it / per_head;
-    q0 = (qb0 + it % per_head) * BQ;
-  };
+  auto item_q0 = [&](int it) { return (qb0 + it % per_head) * BQ; };
   // L2 and D rows are padded to 64 per head, so a 64-row window always loads.
   auto issue = [&](int it, int buf) {
-    int bh, q0;
-    item(it, bh, q0);
+    const int bh = wk.b * a.Hq + wk.hk * G + it / per_head;
+    const int q0 = item_q0(it);
     const size_t qbase = (size_t)bh * a.Tq * D;
     dma_rows<T, D, BQ, 256>(sQ[buf], reinterpret_cast<const T*>(a.Q) + qbase, q0, a.Tq);
     dma_rows<T, D, BQ, 256>(sdO[buf], reinterpret_cast<const T*>(a.dO) + qbase, q0, a.Tq);
-    const int q64 = q0 & ~63;
-    if (w == 0) dma_floats64(sL[buf], a.Lg + (size_t)bh * a.Tqp + q64);
-    if (w == 1) dma_floats64(sD[buf], a.Dvec + (size_t)bh * a.Tqp + q64);
+    if (w == 0) dma_floats64(sL[buf], a.Lg + (size_t)bh * a.Tqp + q0);
+    if (w == 1) dma_floats64(sD[buf], a.Dvec + (size_t)bh * a.Tqp + q0);
   };
   if (total > 0) issue(0, 0);
+  if (total > 1) issue(1, 1);
 
   Op kop[NSD], vop[NSD];
   {
@@ -136,80 +176,162 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   nat.init(n, h);
   TrPermFetch<T, D> trp;
   trp.init(lane);
+
+  f32x16 sacc[2], dpacc[2];                         // S and dP - D of one block (lane = key)
+  Op pop[NSQ], dsop[NSQ];                           // P, dS as operands, by query step
+
+  // Seed of tile t's dP accumulator: -D of the tile's queries (register i
+  // holds query 32 t + 8 (i / 4) + 4 h + i % 4).
+  auto seed_dp = [&](const float* nd, int t) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(nd + 32 * t + 8 * g + 4 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dpacc[t][4 * g + e] = v[e];
+    }
+  };
+  // S / dP product m of tile t: step m / 2, Q (even) or dO (odd).
+  auto s_mma = [&](int t, int m, const Op& x) {
+    if (m & 1) dpacc[t] = M::mma(x, vop[m >> 1], dpacc[t]);
+    else sacc[t] = M::mma(x, kop[m >> 1], sacc[t]);
+  };
+  // dV / dK product m (0 .. NSQ * 2 * NDT): query step m / (2 NDT) outermost,
+  // then d tile, then dV (even) or dK (odd).
+  auto d_mma = [&](int m, const Op& x) {
+    const int s = m / (2 * NDT), t = (m >> 1) % NDT;
+    if (m & 1) dk[t] = M::mma(x, dsop[s], dk[t]);
+    else dv[t] = M::mma(x, pop[s], dv[t]);
+  };
+  // P = exp2(S c - L2) and dS = P (dP - D) of register i of tile t, packed
+  // KPER at a time into the operands of query step (16 t + i) / KPER.
+  float pe[KPER], dse[KPER];
+  f32x4 l4;
+  auto prob = [&](const float* lg, int t, int i) {
+    if (i % 4 == 0) l4 = *reinterpret_cast<const f32x4*>(lg + 32 * t + 8 * (i >> 2) + 4 * h);
+    const float p = fast_exp2(__builtin_fmaf(sacc[t][i], c, -l4[i & 3]));
+    pe[i % KPER] = p;
+    dse[i % KPER] = dpacc[t][i] * p;
+    if ((i + 1) % KPER == 0) {
+      const int s = (16 * t + i) / KPER;
+      pop[s] = M::pack(pe);
+      dsop[s] = M::pack(dse);
+    }
+  };
+  // Causal diagonal and ragged key end, only on the blocks that have them:
+  // P and dS of pairs the key may not see are cleared in the packed operands.
+  // Register i of tile t holds query q0 + 32 t + 4 h + 8 (i / 4) + i % 4.
+  auto mask_tile = [&](int q0, int t) {
+    if (ragged || (CAUSAL && k0 + BK - 1 > q0 + 32 * t + off)) {
+      const int thr = !key_ok ? INT_MAX : (CAUSAL ? mykey - off - q0 - 32 * t - 4 * h : INT_MIN);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (8 * (i >> 2) + (i & 3) < thr) {
+          const int s = (16 * t + i) / KPER;
+          zero_elem(pop[s], i % KPER);
+          zero_elem(dsop[s], i % KPER);
+        }
+      }
+    }
+  };
+
   wait_vmcnt<0>();
   __syncthreads();
-
-  for (int it = 0; it < total; ++it) {
-    const int buf = it & 1;
-    if (it + 1 < total) issue(it + 1, buf ^ 1);
-    int bh, q0;
-    item(it, bh, q0);
-    const T* cQ = sQ[buf];
-    const T* cdO = sdO[buf];
-    const float* cL = sL[buf] + (q0 & 63);          // this block's rows within the 64-row window
-    const float* cD = sD[buf] + (q0 & 63);
-
-    // S = Q K^T and dP = dO V^T for 32-query tiles x this wave's 32 keys.
-    f32x16 sacc[NQT], dpacc[NQT];
+  if (total > 0) {                                  // block 0: S, dP and tile 0's P, dS
 #pragma unroll
-    for (int t = 0; t < NQT; ++t) {
+    for (int t = 0; t < 2; ++t) {
       sacc[t] = f32x16{};
-      dpacc[t] = f32x16{};
+      seed_dp(sD[0], t);
 #pragma unroll
-      for (int s = 0; s < NSD; ++s) {
-        sacc[t] = M::mma(nat.ld(cQ, t, s), kop[s], sacc[t]);
-        dpacc[t] = M::mma(nat.ld(cdO, t, s), vop[s], dpacc[t]);
-      }
+      for (int m = 0; m < NS1; ++m) s_mma(t, m, nat.ld((m & 1) ? sdO[0] : sQ[0], t, m >> 1));
     }
-    sched_interleave<2 * NQT * NSD, 4>();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) prob(sL[0], 0, i);
+    mask_tile(item_q0(0), 0);
+  }
 
-    // P = exp2(S c - L2) and dS = P (dP - D), one 32-query tile at a time.
-    // Padding query rows carry L2 = +inf, so only the diagonal and the ragged
-    // key end need explicit masks.
-    const bool need_mask = !key_ok || (CAUSAL && k0 + BK - 1 > q0 + off);
-    Op pop[NSQ], dsop[NSQ];
+  // One iteration with block i in buffer CUR, block i+1 in the next buffer.
+  auto iteration = [&](auto cur_c, int it) {
+    constexpr int cur = decltype(cur_c)::value;
+    constexpr int nxt = (cur + 1) % NB, nn = (cur + 2) % NB;
+    if (NB == 3 && it + 2 < total) issue(it + 2, nn);
+    // On the last item buffer nxt holds stale rows: its products are computed
+    // and discarded, which keeps the sequence free of branches.
+    const int q0 = item_q0(it), nq0 = item_q0(it + 1);
+    const T* cQ = sQ[cur];
+    const T* cdO = sdO[cur];
+    const T* nQ = sQ[nxt];
+    const T* ndO = sdO[nxt];
+
+    // S / dP operand of product m of tile t (block i+1), dV / dK operand of
+    // product m (block i).
+    auto s_fetch = [&](int t, int m) -> Op { return nat.ld((m & 1) ? ndO : nQ, t, m >> 1); };
+    auto d_fetch = [&](int m) -> Op {
+      const int s = m / (2 * NDT), t = (m >> 1) % NDT;
+      return trp.ld((m & 1) ? cQ : cdO, t, s);
+    };
+    // Phases 1a and 1b: tile u of block i+1's S, dP interleaved with quarter u
+    // of block i's dV, dK.
+    auto p1_fetch = [&](int u, int m) -> Op {
+      return interleave_is_b(m, NS1, NDQ) ? d_fetch(u * NDQ + interleave_rank(m, NS1, NDQ))
+                                          : s_fetch(u, interleave_rank(m, NS1, NDQ));
+    };
+    Op ring[AHEAD];
+    sacc[0] = f32x16{};
+    seed_dp(sD[nxt], 0);
 #pragma unroll
-    for (int t = 0; t < NQT; ++t) {
-      float p[16], ds[16];
+    for (int m = 0; m < AHEAD; ++m) ring[m] = p1_fetch(0, m);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qg = 32 * t + 8 * g + 4 * h;      // queries of registers 4g .. 4g+3
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&cL[qg]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&cD[qg]);
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g + e;
-          p[i] = fast_exp2(__builtin_fmaf(sacc[t][i], c, -l4[e]));
-          ds[i] = dpacc[t][i] - d4[e];
+      for (int m = 0; m < NPA; ++m) {
+        const Op x = ring[m % AHEAD];
+        if (m + AHEAD < NPA) ring[m % AHEAD] = p1_fetch(u, m + AHEAD);
+        else if (u == 0) ring[m % AHEAD] = p1_fetch(1, m + AHEAD - NPA);
+        else ring[m % AHEAD] = d_fetch(NDH + (m + AHEAD - NPA));
+        if (interleave_is_b(m, NS1, NDQ)) d_mma(u * NDQ + interleave_rank(m, NS1, NDQ), x);
+        else s_mma(u, interleave_rank(m, NS1, NDQ), x);
+        if (u == 0) {
+          // tile 1 of block i: its 16 probabilities, all done by step SEED1
+#pragma unroll
+          for (int j = 0; j < EPS1; ++j)
+            if (m * EPS1 + j < 16) prob(sL[cur], 1, m * EPS1 + j);
+          if (m == SEED1) {                        // tile 1 of block i is done with S, dP
+            sacc[1] = f32x16{};
+            seed_dp(sD[nxt], 1);
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (need_mask) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = q0 + 32 * t + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (!key_ok || (CAUSAL && mykey > q + off)) p[i] = 0.f;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) ds[i] *= p[i];
-#pragma unroll
-      for (int s = 0; s < 16 / KPER; ++s) {
-        pop[t * (16 / KPER) + s] = M::pack(p + s * KPER);
-        dsop[t * (16 / KPER) + s] = M::pack(ds + s * KPER);
-      }
+      if (u == 0) mask_tile(q0, 1);
     }
 
+    // Phase 2: the second half of block i's dV, dK, each product followed by
+    // its share of block i+1's tile-0 probabilities.
 #pragma unroll
-    for (int t = 0; t < NDT; ++t) {
+    for (int m = 0; m < NDH; ++m) {
+      const Op x = ring[(2 * NPA + m) % AHEAD];
+      if (m + AHEAD < NDH) ring[(2 * NPA + m) % AHEAD] = d_fetch(NDH + m + AHEAD);
+      d_mma(NDH + m, x);
 #pragma unroll
-      for (int s = 0; s < NSQ; ++s) {
-        dv[t] = M::mma(trp.ld(cdO, t, s), pop[s], dv[t]);
-        dk[t] = M::mma(trp.ld(cQ, t, s), dsop[s], dk[t]);
-      }
+      for (int j = 0; j < EPS2; ++j)
+        if (m * EPS2 + j < 16) prob(sL[nxt], 0, m * EPS2 + j);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    sched_interleave<2 * NDT * NSQ, 4, (sizeof(T) == 2 ? 2 : 1)>();
-    wait_vmcnt<0>();                               // this wave's loads of the next block have landed
-    __syncthreads();
+    mask_tile(nq0, 0);
+    if (NB == 3) {
+      wait_vmcnt<0>();                             // this wave's loads of block i+2 have landed
+      __syncthreads();
+    } else {
+      __syncthreads();                             // block i's buffer is free
+      if (it + 2 < total) issue(it + 2, cur);
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+  };
+  for (int it = 0; it < total; it += NB) {
+    iteration(IC<0>{}, it);
+    if (it + 1 < total) iteration(IC<1>{}, it + 1);
+    if (NB == 3 && it + 2 < total) iteration(IC<NB - 1>{}, it + 2);
   }
 
   if (key_ok) {
@@ -283,7 +405,7 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
     }
   }
   const float l2 = q_ok ? a.Lg[(size_t)bh * a.Tqp + myq] : INFINITY;
-  const float dd = q_ok ? a.Dvec[(size_t)bh * a.Tqp + myq] : 0.f;
+  const float ndd = q_ok ? a.Dvec[(size_t)bh * a.Tqp + myq] : 0.f;   // -D of this lane's query
   NatFetch<T, D> nat;
   nat.init(n, h);
   TrPermFetch<T, D> trp;
@@ -324,7 +446,7 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
           const int key = k0 + perm_index(h, r);
           if (key >= a.Tk || (CAUSAL && key > myq + off)) p = 0.f;
         }
-        ds[r] = p * (dpv - dd);
+        ds[r] = p * (dpv + ndd);
       }
       Op dsop[NSK];
 #pragma unroll
