@@ -4,8 +4,7 @@
 
 Every HIP source under csrc/ is compiled separately (in parallel) and linked
 into attention_fa_fwd_05_amd/libfa05.so.  Packed fp32 VALU instructions are
-disabled (-packed-fp32-ops) and float atomics use the hardware instruction
-(-munsafe-fp-atomics: the dQ accumulator lives in ordinary device memory).
+disabled (-packed-fp32-ops).
 """
 
 from __future__ import annotations
@@ -27,7 +26,6 @@ HEADERS = ["fa_common.h", "fa_kernels.h"]
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics",
     "-mcode-object-version=5",
 ]
 

@@ -81,7 +81,7 @@ __host__ __device__ constexpr int interleave_rank(int m, int na, int nb) {
 template <int V> struct IC { static constexpr int value = V; };
 
 __device__ inline void zero_elem(bf16x8& x, int e) { x[e] = (bf16)0.f; }
-__device__ inline void zero_elem(float& x, int) { x = 0.f; }
+__device__ inline void zero_elem(f32x4& x, int e) { x[e] = 0.f; }
 
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
@@ -99,28 +99,28 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   constexpr int NB = (sizeof(T) == 4 && D == 128) ? 2 : 3;
   // Software pipeline over the query blocks of the work list, iteration i:
   //   phase 1a: S, dP of block i+1 tile 0  |  dV, dK of block i, first quarter
-  //             of its steps  |  P, dS of block i tile 1 (vector ALU);
-  //   phase 1b: S, dP of block i+1 tile 1  |  dV, dK of block i, second quarter;
-  //   phase 2:  dV, dK of block i, second half  |  P, dS of block i+1 tile 0.
-  // P, dS of a tile are written over those of the same tile of the previous
-  // block once its last product has been issued.  Products and LDS reads go
-  // out in a fixed order with a fixed number of operands in flight, and the
-  // loop is unrolled over the buffers so that every LDS address is a lane
-  // offset plus a constant.
+  //             of its query steps  |  P, dS of block i tile 1;
+  //   phase 1b: S, dP of block i+1 tile 1  |  dV, dK of block i, second
+  //             quarter  |  P, dS of block i+1 tile 0, first half;
+  //   phase 2:  dV, dK of block i, second half  |  P, dS of block i+1 tile 0,
+  //             second half.
+  // The vector work of an element runs in three stages on successive product
+  // steps (x = S c - L2; P = exp2 x; dS = P (dP - D) and packing), so that a
+  // step's vector instructions never wait on one another and the in-order
+  // issue keeps feeding the matrix unit.  P, dS of a tile overwrite those of
+  // the same tile of the previous block once its last product has been
+  // issued.  Products and LDS reads go out in a fixed order with a fixed
+  // number of operands in flight; the loop is unrolled over the buffers so
+  // every LDS address is a lane offset plus a constant.
   constexpr int NS1 = 2 * NSD;                      // S and dP products per tile
   constexpr int NDQ = (NSH / 2) * 2 * NDT;          // dV/dK products per quarter of the steps
   constexpr int NDH = NSH * 2 * NDT;                // ... per half
   constexpr int NPA = NS1 + NDQ;                    // products in phase 1a (and 1b)
-  constexpr int AHEAD = 4;                          // operands in flight
-  constexpr int EPS1 = (16 + NPA - 1) / NPA;        // probabilities per product, phase 1a
-  constexpr int EPS2 = (16 + NDH - 1) / NDH;        // ... phase 2
-  constexpr int LAST_PROB1 = (16 + EPS1 - 1) / EPS1 - 1;   // last phase-1a step with one
-  // step of phase 1a that seeds tile 1's dP accumulator: after its last
-  // probability and before tile 1's first operand read
-  constexpr int SEED1 = LAST_PROB1 > NPA - AHEAD - 1 ? LAST_PROB1 : NPA - AHEAD - 1;
+  constexpr int AHEAD = (sizeof(T) == 2 && NPA % 8 == 0) ? 8 : 4;   // operands in flight
   static_assert(NSH % 2 == 0, "quarters of the query steps");
-  static_assert(SEED1 < NPA, "seed step inside phase 1a");
   static_assert(NPA % AHEAD == 0, "operand ring slots line up across phases");
+  static_assert(NPA >= 12 && NDH >= 8, "room for the vector stages");
+  static_assert(NB == 2 || 2 * (2 * DmaRows<T, D, BQ, 256>::PER + 1) <= NPA, "loads fit in phase 1b");
   __shared__ __attribute__((aligned(16))) float sL[NB][64];
   __shared__ __attribute__((aligned(16))) float sD[NB][64];    // -D
   __shared__ __attribute__((aligned(16))) T sQ[NB][BQ * D];
@@ -158,6 +158,52 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   };
   if (total > 0) issue(0, 0);
   if (total > 1) issue(1, 1);
+  // The same loads split into single instructions, spread over phase 1b (the
+  // phase with the least vector work) so that no step issues a burst and the
+  // address unit is never backed up: NDMA pieces, Q rows, dO rows, then L2
+  // and -D.
+  using DR = DmaRows<T, D, BQ, 256>;
+  constexpr int NDMA = 2 * DR::PER + 1;
+  uint32_t src_off[DR::PER];                        // per-lane source byte offsets, one per instruction
+#pragma unroll
+  for (int j = 0; j < DR::PER; ++j) src_off[j] = DR::src_off(j);
+  // Uniform description of one block's loads (computed once per iteration).
+  struct Src {
+    const char* q;                                  // Q row q0 of the head
+    const char* o;                                  // dO row q0 of the head
+    const float* l;
+    const float* d;
+    int q0;
+    bool whole;                                     // all BQ rows exist: no clamping
+  };
+  auto block_src = [&](int it) {
+    Src r;
+    const int bh = wk.b * a.Hq + wk.hk * G + it / per_head;
+    r.q0 = item_q0(it);
+    const size_t row = (size_t)bh * a.Tq + r.q0;
+    r.q = reinterpret_cast<const char*>(a.Q) + row * D * sizeof(T);
+    r.o = reinterpret_cast<const char*>(a.dO) + row * D * sizeof(T);
+    r.l = a.Lg + (size_t)bh * a.Tqp + r.q0;
+    r.d = a.Dvec + (size_t)bh * a.Tqp + r.q0;
+    r.whole = r.q0 + BQ <= a.Tq;
+    return r;
+  };
+  auto dma_piece = [&](const Src& src, int buf, int j) {
+    if (j < 2 * DR::PER) {
+      const int i = j % DR::PER;
+      T* tile = j < DR::PER ? sQ[buf] : sdO[buf];
+      const char* base = j < DR::PER ? src.q : src.o;
+      if (src.whole) {
+        dma16s(base, src_off[i], lds_addr(tile) + DR::lds_off(i));
+      } else {                                      // ragged end of the queries: clamped rows
+        const T* g = reinterpret_cast<const T*>(base) - (size_t)src.q0 * D;
+        DR::one(tile, g, src.q0, a.Tq, i);
+      }
+    } else {
+      if (w == 0) dma_floats64(sL[buf], src.l);
+      if (w == 1) dma_floats64(sD[buf], src.d);
+    }
+  };
 
   Op kop[NSD], vop[NSD];
   {
@@ -167,6 +213,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       kop[s] = M::ld(Kp + ro + s * KPER);
       vop[s] = M::ld(Vp + ro + s * KPER);
       if (!key_ok) { kop[s] = Op{}; vop[s] = Op{}; }
+      // K and V only feed matrix instructions: keep them in accumulation
+      // registers, leaving the vector registers to the softmax work.
+      if constexpr (sizeof(T) == 2) {
+        asm volatile("" : "+a"(kop[s]));
+        asm volatile("" : "+a"(vop[s]));
+      }
     }
   }
   f32x16 dk[NDT], dv[NDT];
@@ -190,10 +242,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) dpacc[t][4 * g + e] = v[e];
     }
   };
-  // S / dP product m of tile t: step m / 2, Q (even) or dO (odd).
+  // S / dP product m of tile t: the NSD products of S = Q K^T first, then
+  // those of dP = dO V^T (their seed then has time to arrive).
   auto s_mma = [&](int t, int m, const Op& x) {
-    if (m & 1) dpacc[t] = M::mma(x, vop[m >> 1], dpacc[t]);
-    else sacc[t] = M::mma(x, kop[m >> 1], sacc[t]);
+    if (m < NSD) sacc[t] = M::mma(x, kop[m], sacc[t]);
+    else dpacc[t] = M::mma(x, vop[m - NSD], dpacc[t]);
   };
   // dV / dK product m (0 .. NSQ * 2 * NDT): query step m / (2 NDT) outermost,
   // then d tile, then dV (even) or dK (odd).
@@ -202,21 +255,55 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     if (m & 1) dk[t] = M::mma(x, dsop[s], dk[t]);
     else dv[t] = M::mma(x, pop[s], dv[t]);
   };
-  // P = exp2(S c - L2) and dS = P (dP - D) of register i of tile t, packed
-  // KPER at a time into the operands of query step (16 t + i) / KPER.
-  float pe[KPER], dse[KPER];
-  f32x4 l4;
-  auto prob = [&](const float* lg, int t, int i) {
-    if (i % 4 == 0) l4 = *reinterpret_cast<const f32x4*>(lg + 32 * t + 8 * (i >> 2) + 4 * h);
-    const float p = fast_exp2(__builtin_fmaf(sacc[t][i], c, -l4[i & 3]));
-    pe[i % KPER] = p;
-    dse[i % KPER] = dpacc[t][i] * p;
-    if ((i + 1) % KPER == 0) {
-      const int s = (16 * t + i) / KPER;
-      pop[s] = M::pack(pe);
-      dsop[s] = M::pack(dse);
+  // L2 of one tile's queries in accumulator order.
+  f32x4 lt[4];
+  auto load_l = [&](const float* lg, int t) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) lt[g] = *reinterpret_cast<const f32x4*>(lg + 32 * t + 8 * g + 4 * h);
+  };
+  // The three vector stages of register e of tile t.
+  float xa[16], pa[16];
+  bf16x2 ppk[8], dpk[8];                            // packed pairs (bf16 operands)
+  auto st1 = [&](int t, int e) { xa[e] = __builtin_fmaf(sacc[t][e], c, -lt[e >> 2][e & 3]); };
+  auto st2 = [&](int e) { pa[e] = fast_exp2(xa[e]); };
+  auto st3 = [&](int t, int e) {
+    if constexpr (sizeof(T) == 4) {
+      if ((e & 3) == 3) {
+        const int s = (16 * t + e) / 4;
+        pop[s] = f32x4{pa[e - 3], pa[e - 2], pa[e - 1], pa[e]};
+        dsop[s] = f32x4{dpacc[t][e - 3] * pa[e - 3], dpacc[t][e - 2] * pa[e - 2],
+                        dpacc[t][e - 1] * pa[e - 1], dpacc[t][e] * pa[e]};
+      }
+    } else if (e & 1) {
+      ppk[e >> 1] = bf16x2{(bf16)pa[e - 1], (bf16)pa[e]};
+      dpk[e >> 1] = bf16x2{(bf16)(dpacc[t][e - 1] * pa[e - 1]), (bf16)(dpacc[t][e] * pa[e])};
+      if ((e & 7) == 7) {
+        const int s = (16 * t + e) / 8, j = (e >> 1) - 3;
+        const bf16x4 p0 = __builtin_shufflevector(ppk[j], ppk[j + 1], 0, 1, 2, 3);
+        const bf16x4 p1 = __builtin_shufflevector(ppk[j + 2], ppk[j + 3], 0, 1, 2, 3);
+        const bf16x4 d0 = __builtin_shufflevector(dpk[j], dpk[j + 1], 0, 1, 2, 3);
+        const bf16x4 d1 = __builtin_shufflevector(dpk[j + 2], dpk[j + 3], 0, 1, 2, 3);
+        pop[s] = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
+        dsop[s] = __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
     }
   };
+  // Stages due at step m of a schedule whose element e (e0 <= e < e1) starts
+  // at step (e - e0) * span / (e1 - e0).
+  auto stages = [&](int t, int m, int e0, int e1, int span) {
+#pragma unroll
+    for (int e = e0; e < e1; ++e) {
+      const int f = (e - e0) * span / (e1 - e0);
+      if (f + 2 == m) st3(t, e);
+      if (f + 1 == m) st2(e);
+      if (f == m) st1(t, e);
+    }
+  };
+  constexpr int SPAN1A = NPA - 4;                   // tile 1 of block i over phase 1a
+  constexpr int SPAN1B = NPA - 3;                   // tile 0, registers 0..7, over phase 1b
+  constexpr int SPAN2 = NDH - 3;                    // tile 0, registers 8..15, over phase 2
+  constexpr int LOADL0 = 15 * SPAN1A / 16 + 1;      // after tile 1's last stage 1
+  static_assert(15 * SPAN1A / 16 + 2 < NPA - 1, "tile 1 done before its reseed");
   // Causal diagonal and ragged key end, only on the blocks that have them:
   // P and dS of pairs the key may not see are cleared in the packed operands.
   // Register i of tile t holds query q0 + 32 t + 4 h + 8 (i / 4) + i % 4.
@@ -242,18 +329,22 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       sacc[t] = f32x16{};
       seed_dp(sD[0], t);
 #pragma unroll
-      for (int m = 0; m < NS1; ++m) s_mma(t, m, nat.ld((m & 1) ? sdO[0] : sQ[0], t, m >> 1));
+      for (int m = 0; m < NS1; ++m) s_mma(t, m, nat.ld(m < NSD ? sQ[0] : sdO[0], t, m % NSD));
     }
+    load_l(sL[0], 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) prob(sL[0], 0, i);
+    for (int m = 0; m < 18; ++m) stages(0, m, 0, 16, 16);
     mask_tile(item_q0(0), 0);
+    load_l(sL[0], 1);
   }
 
   // One iteration with block i in buffer CUR, block i+1 in the next buffer.
   auto iteration = [&](auto cur_c, int it) {
     constexpr int cur = decltype(cur_c)::value;
     constexpr int nxt = (cur + 1) % NB, nn = (cur + 2) % NB;
-    if (NB == 3 && it + 2 < total) issue(it + 2, nn);
+    // Block i+2 goes to buffer nn (free since the last barrier); past the end
+    // of the list the last block is loaded again, harmlessly.
+    const Src dsrc = block_src(min(it + 2, total - 1));
     // On the last item buffer nxt holds stale rows: its products are computed
     // and discarded, which keeps the sequence free of branches.
     const int q0 = item_q0(it), nq0 = item_q0(it + 1);
@@ -264,7 +355,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 
     // S / dP operand of product m of tile t (block i+1), dV / dK operand of
     // product m (block i).
-    auto s_fetch = [&](int t, int m) -> Op { return nat.ld((m & 1) ? ndO : nQ, t, m >> 1); };
+    auto s_fetch = [&](int t, int m) -> Op { return nat.ld(m < NSD ? nQ : ndO, t, m % NSD); };
     auto d_fetch = [&](int m) -> Op {
       const int s = m / (2 * NDT), t = (m >> 1) % NDT;
       return trp.ld((m & 1) ? cQ : cdO, t, s);
@@ -280,8 +371,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     seed_dp(sD[nxt], 0);
 #pragma unroll
     for (int m = 0; m < AHEAD; ++m) ring[m] = p1_fetch(0, m);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    // Half u as a compile-time constant: the phase is one straight sequence.
+    auto phase1 = [&](auto u_c) {
+      constexpr int u = decltype(u_c)::value;
 #pragma unroll
       for (int m = 0; m < NPA; ++m) {
         const Op x = ring[m % AHEAD];
@@ -290,34 +382,36 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
         else ring[m % AHEAD] = d_fetch(NDH + (m + AHEAD - NPA));
         if (interleave_is_b(m, NS1, NDQ)) d_mma(u * NDQ + interleave_rank(m, NS1, NDQ), x);
         else s_mma(u, interleave_rank(m, NS1, NDQ), x);
+        if (NB == 3 && u == 1 && m % 2 == 1 && m / 2 < NDMA) dma_piece(dsrc, nn, m / 2);
         if (u == 0) {
-          // tile 1 of block i: its 16 probabilities, all done by step SEED1
-#pragma unroll
-          for (int j = 0; j < EPS1; ++j)
-            if (m * EPS1 + j < 16) prob(sL[cur], 1, m * EPS1 + j);
-          if (m == SEED1) {                        // tile 1 of block i is done with S, dP
+          stages(1, m, 0, 16, SPAN1A);             // tile 1 of block i
+          if (m == LOADL0) load_l(sL[nxt], 0);     // L2 of block i+1's tile 0
+          if (m == NPA - 1) {                      // tile 1 of block i is done with S, dP
             sacc[1] = f32x16{};
             seed_dp(sD[nxt], 1);
           }
+        } else {
+          stages(0, m, 0, 8, SPAN1B);              // tile 0 of block i+1, first half
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (u == 0) mask_tile(q0, 1);
-    }
+    };
+    phase1(IC<0>{});
+    mask_tile(q0, 1);
+    phase1(IC<1>{});
 
-    // Phase 2: the second half of block i's dV, dK, each product followed by
-    // its share of block i+1's tile-0 probabilities.
+    // Phase 2: the second half of block i's dV, dK, with the second half of
+    // block i+1's tile-0 probabilities.
 #pragma unroll
     for (int m = 0; m < NDH; ++m) {
       const Op x = ring[(2 * NPA + m) % AHEAD];
       if (m + AHEAD < NDH) ring[(2 * NPA + m) % AHEAD] = d_fetch(NDH + m + AHEAD);
       d_mma(NDH + m, x);
-#pragma unroll
-      for (int j = 0; j < EPS2; ++j)
-        if (m * EPS2 + j < 16) prob(sL[nxt], 0, m * EPS2 + j);
+      stages(0, m, 8, 16, SPAN2);
       __builtin_amdgcn_sched_barrier(0);
     }
     mask_tile(nq0, 0);
+    load_l(sL[nxt], 1);                            // for block i+1's tile-1 probabilities
     if (NB == 3) {
       wait_vmcnt<0>();                             // this wave's loads of block i+2 have landed
       __syncthreads();

@@ -59,47 +59,20 @@ template <> struct MM<bf16> {
   }
 };
 
+// fp32: an operand is 4 consecutive contraction elements per lane, consumed by
+// four chained 32x32x2 products (element e feeds the e-th), so that operands
+// are 16-byte LDS reads as for bf16.
 template <> struct MM<float> {
-  static constexpr int KPER = 1;
-  typedef float Op;
-  __device__ static inline f32x16 mma(Op a, Op b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  static constexpr int KPER = 4;
+  typedef f32x4 Op;
+  __device__ static inline f32x16 mma(const Op& a, const Op& b, const f32x16& c) {
+    f32x16 d = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], b[0], c, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1], b[1], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_32x32x2f32(a[2], b[2], d, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a[3], b[3], d, 0, 0, 0);
   }
-  __device__ static inline Op ld(const float* p) { return *p; }
-  __device__ static inline Op pack(const float* v) { return v[0]; }
-};
-
-// Transposed bf16 operand for step s from a row-major LDS tile: element
-// 4 u + e4 comes from row row_of(u) + e4 and column col0 + (lane % 32).
-// rows_u0 / rows_u1: first row of the four rows read by halves u = 0 / 1.
-__device__ inline bf16x8 ld_tr_bf16(const bf16* tile, int stride, int rows_u0, int rows_u1, int col0) {
-  const int lane = threadIdx.x & 63;
-  const int i = lane & 15;
-  const int c = col0 + 16 * ((lane >> 4) & 1) + 4 * (i & 3);
-  const bf16* p0 = tile + (rows_u0 + (i >> 2)) * stride + c;
-  const bf16* p1 = tile + (rows_u1 + (i >> 2)) * stride + c;
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
-  bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p1));
-  bf16x8 r;
-  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-  return r;
-}
-
-// Transposed operand whose contraction index follows accumulator order
-// (perm_index): step s of lane half h covers registers r = s * KPER + e.
-template <typename T> struct TrPerm;
-template <> struct TrPerm<bf16> {
-  __device__ static inline bf16x8 ld(const bf16* tile, int stride, int h, int s, int col0) {
-    // registers s*8 + 4u + e4 hold index 16 s + 8 u + 4 h + e4
-    return ld_tr_bf16(tile, stride, 16 * s + 4 * h, 16 * s + 8 + 4 * h, col0);
-  }
-};
-template <> struct TrPerm<float> {
-  __device__ static inline float ld(const float* tile, int stride, int h, int s, int col0) {
-    return tile[perm_index(h, s) * stride + col0 + (threadIdx.x & 31)];
-  }
+  __device__ static inline Op ld(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+  __device__ static inline Op pack(const float* v) { return f32x4{v[0], v[1], v[2], v[3]}; }
 };
 
 // ---------------------------------------------------------------------------
@@ -149,6 +122,16 @@ __device__ inline void dma16(const void* gsrc, uint32_t lds_base) {
                "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory", "m0");
 }
+// The same with a wave-uniform 64-bit base (scalar registers) and a 32-bit
+// per-lane byte offset: no per-lane address arithmetic at the call site.
+__device__ inline void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb),
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
 __device__ inline void dma4(const void* gsrc, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc),
                "s"(__builtin_amdgcn_readfirstlane(lds_base))
@@ -159,20 +142,33 @@ __device__ inline void dma4(const void* gsrc, uint32_t lds_base) {
 // nrows - 1, which must be >= 0) into a swizzled tile.  NTHR threads take
 // part; each wave issues ROWS * NCH / NTHR instructions.
 template <typename T, int D, int ROWS, int NTHR>
-__device__ inline void dma_rows(T* tile, const T* g, int g0, int nrows) {
+struct DmaRows {
   using TL = SwzTile<T, D>;
-  constexpr int SLOTS = ROWS * TL::NCH, NWV = NTHR / 64, PER = SLOTS / NTHR;
+  static constexpr int SLOTS = ROWS * TL::NCH, NWV = NTHR / 64, PER = SLOTS / NTHR;
   static_assert(PER * NTHR == SLOTS, "tile must split evenly over the threads");
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint32_t base = lds_addr(tile);
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
+  // Instruction i (0 <= i < PER) of this wave.
+  __device__ static inline void one(T* tile, const T* g, int g0, int nrows, int i) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int blk = i * NWV + wave;                 // 64-slot block of this wave instruction
     const int pos = blk * 64 + lane;
     const int r = pos / TL::NCH, x = pos % TL::NCH;
     const int gr = min(g0 + r, nrows - 1);
-    dma16(g + (size_t)gr * D + (x ^ TL::fsw(r)) * TL::EPC, base + blk * 1024);
+    dma16(g + (size_t)gr * D + (x ^ TL::fsw(r)) * TL::EPC, lds_addr(tile) + blk * 1024);
   }
+  // Byte offset from row 0 of the tile's source rows for instruction i of this
+  // lane (rows not clamped), and the LDS byte offset of its 64-slot block.
+  __device__ static inline uint32_t src_off(int i) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int pos = (i * NWV + wave) * 64 + lane;
+    const int r = pos / TL::NCH, x = pos % TL::NCH;
+    return (uint32_t)((r * D + (x ^ TL::fsw(r)) * TL::EPC) * (int)sizeof(T));
+  }
+  __device__ static inline uint32_t lds_off(int i) { return (uint32_t)((i * NWV + (threadIdx.x >> 6)) * 1024); }
+};
+template <typename T, int D, int ROWS, int NTHR>
+__device__ inline void dma_rows(T* tile, const T* g, int g0, int nrows) {
+#pragma unroll
+  for (int i = 0; i < DmaRows<T, D, ROWS, NTHR>::PER; ++i) DmaRows<T, D, ROWS, NTHR>::one(tile, g, g0, nrows, i);
 }
 
 // 4-byte direct loads of 64 consecutive floats by one wave.
@@ -230,10 +226,11 @@ template <int D> struct NatFetch<bf16, D> {
   __device__ bf16x8 ld(const bf16* tile, int t, int s) const { return lds16(tile + t * 32 * D, off[s]); }
 };
 template <int D> struct NatFetch<float, D> {
+  using TL = SwzTile<float, D>;
   int n_, h_;
   __device__ void init(int n, int h) { n_ = n; h_ = h; }
-  __device__ float ld(const float* tile, int t, int s) const {
-    return tile[32 * t * D + SwzTile<float, D>::elem(opaque(n_), h_ * (D / 2) + s)];
+  __device__ f32x4 ld(const float* tile, int t, int s) const {
+    return *reinterpret_cast<const f32x4*>(tile + 32 * t * D + TL::elem(opaque(n_), h_ * (D / 2) + 4 * s));
   }
 };
 
@@ -260,9 +257,12 @@ template <int D> struct TrPermFetch<bf16, D> {
 template <int D> struct TrPermFetch<float, D> {
   int lane_;
   __device__ void init(int lane) { lane_ = lane; }
-  __device__ float ld(const float* tile, int t, int s) const {
-    const int l = opaque(lane_);
-    return tile[SwzTile<float, D>::elem(perm_index(l >> 5, s), 32 * t + (l & 31))];
+  __device__ f32x4 ld(const float* tile, int t, int s) const {
+    const int l = opaque(lane_), h = l >> 5, col = 32 * t + (l & 31);
+    f32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = tile[SwzTile<float, D>::elem(perm_index(h, 4 * s + e), col)];
+    return r;
   }
 };
 
