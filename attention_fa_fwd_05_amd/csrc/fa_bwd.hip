@@ -140,15 +140,20 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   const T* Kp = reinterpret_cast<const T*>(a.K) + (size_t)bhk * a.Tk * D;
   const T* Vp = reinterpret_cast<const T*>(a.V) + (size_t)bhk * a.Tk * D;
 
-  // Work list: every (query head of the group, query block that can see a key
-  // of this block).
+  // Work list: every (query block that can see a key of this block, query
+  // head of the group), query blocks from the last one down and heads
+  // innermost.  All key blocks of a group run at once on one XCD and step
+  // through the same query blocks in lockstep (each stops at its diagonal), so
+  // every Q / dO block is fetched into that XCD's L2 once, not once per key
+  // block.
   const int nqb = (a.Tq + BQ - 1) / BQ;
   const int qb0 = CAUSAL ? min(nqb, max(0, k0 - off) / BQ) : 0;
-  const int per_head = nqb - qb0, total = G * per_head;
-  auto item_q0 = [&](int it) { return (qb0 + it % per_head) * BQ; };
+  const int total = G * (nqb - qb0);
+  auto item_q0 = [&](int it) { return (nqb - 1 - it / G) * BQ; };
+  auto item_bh = [&](int it) { return wk.b * a.Hq + wk.hk * G + it % G; };
   // L2 and D rows are padded to 64 per head, so a 64-row window always loads.
   auto issue = [&](int it, int buf) {
-    const int bh = wk.b * a.Hq + wk.hk * G + it / per_head;
+    const int bh = item_bh(it);
     const int q0 = item_q0(it);
     const size_t qbase = (size_t)bh * a.Tq * D;
     dma_rows<T, D, BQ, 256>(sQ[buf], reinterpret_cast<const T*>(a.Q) + qbase, q0, a.Tq);
@@ -178,7 +183,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   };
   auto block_src = [&](int it) {
     Src r;
-    const int bh = wk.b * a.Hq + wk.hk * G + it / per_head;
+    const int bh = item_bh(it);
     r.q0 = item_q0(it);
     const size_t row = (size_t)bh * a.Tq + r.q0;
     r.q = reinterpret_cast<const char*>(a.Q) + row * D * sizeof(T);
