@@ -126,7 +126,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) T sQ[NB][BQ * D];
   __shared__ __attribute__((aligned(16))) T sdO[NB][BQ * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The wave index is uniform across a wave; readfirstlane tells the compiler,
+  // so conditions built from it become scalar branches.
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, n = lane & 31;
   const int nkb = (a.Tk + BK - 1) / BK;
   const KWork wk = kblock_work(a, nkb);
@@ -464,10 +466,16 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   constexpr int NSD = (D / 2) / KPER;
   constexpr int NSK = (BK / 2) / KPER;
   constexpr int NDT = D / 32;
-  __shared__ __attribute__((aligned(16))) T sK[2][BK * D];
-  __shared__ __attribute__((aligned(16))) T sV[2][BK * D];
+  // Three K/V buffers: tile j+2 loads while tile j is read, so the wait at the
+  // end of a tile only covers loads issued a whole tile earlier.  fp32 with
+  // d = 128 fits two (its loads then wait within the tile).
+  constexpr int NBUF = (sizeof(T) == 4 && D == 128) ? 2 : 3;
+  __shared__ __attribute__((aligned(16))) T sK[NBUF][BK * D];
+  __shared__ __attribute__((aligned(16))) T sV[NBUF][BK * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The wave index is uniform across a wave; readfirstlane tells the compiler,
+  // so conditions built from it become scalar branches.
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, n = lane & 31;
   const int nqb = (a.Tq + BQ - 1) / BQ;
   const QWork wk = qblock_work(a.B, a.Hq, a.Hkv, nqb, CAUSAL);
@@ -490,7 +498,10 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
     dma_rows<T, D, BK, NTHR>(sK[buf], Kp, k0, a.Tk);
     dma_rows<T, D, BK, NTHR>(sV[buf], Vp, k0, a.Tk);
   };
+  // Direct-load instructions per wave for one tile (K and V).
+  constexpr int NLD = 2 * DmaRows<T, D, BK, NTHR>::PER;
   if (ntiles > 0) issue(0, 0);
+  if (NBUF == 3 && ntiles > 1) issue(BK, 1);
 
   // Q^T and dO^T operands for this lane's query, L2 and D of that row.
   Op qop[NSD], gop[NSD];
@@ -517,9 +528,13 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
 #pragma unroll
   for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
 
+  int buf = 0;
   for (int jt = 0; jt < ntiles; ++jt) {
-    const int k0 = jt * BK, buf = jt & 1;
-    if (jt + 1 < ntiles) issue(k0 + BK, buf ^ 1);
+    const int k0 = jt * BK;
+    constexpr int ahead = NBUF - 1;                  // tiles in flight beyond this one
+    const int lbuf = buf + ahead >= NBUF ? buf + ahead - NBUF : buf + ahead;
+    const bool issued = jt + ahead < ntiles;
+    if (issued) issue(k0 + ahead * BK, lbuf);
     const T* cK = sK[buf];
     const T* cV = sV[buf];
 
@@ -535,17 +550,19 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
       }
       sched_interleave<4 * NSD, 4>();
       float ds[32];
-      const bool need_mask = (k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off);
 #pragma unroll
       for (int r = 0; r < 32; ++r) {
         const float sv = r < 16 ? st0[r] : st1[r - 16];
         const float dpv = r < 16 ? dp0[r] : dp1[r - 16];
-        float p = fast_exp2(__builtin_fmaf(sv, c, -l2));
-        if (need_mask) {
-          const int key = k0 + perm_index(h, r);
-          if (key >= a.Tk || (CAUSAL && key > myq + off)) p = 0.f;
-        }
-        ds[r] = p * (dpv + ndd);
+        ds[r] = fast_exp2(__builtin_fmaf(sv, c, -l2)) * (dpv + ndd);
+      }
+      // Only the diagonal tiles and the ragged key end (a uniform test) clear
+      // dS of the keys this query may not see; every value above is finite.
+      if ((k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off)) {
+        const int lim = min(a.Tk - 1, CAUSAL ? myq + off : a.Tk - 1) - k0;   // last visible key offset
+#pragma unroll
+        for (int r = 0; r < 32; ++r)
+          if (perm_index(h, r) > lim) ds[r] = 0.f;
       }
       Op dsop[NSK];
 #pragma unroll
@@ -558,8 +575,13 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
       }
       sched_interleave<NDT * NSK, 4, (sizeof(T) == 2 ? 2 : 1)>();
     }
-    wait_vmcnt<0>();                                 // this wave's loads of the next tile have landed
+    // This wave's loads of tile j+1 have landed (those of tile j+2, issued
+    // last, may still be in flight); the barrier makes every wave's share
+    // visible and frees buffer buf for the loads issued next.
+    if (NBUF == 3 && issued) wait_vmcnt<NLD>();
+    else wait_vmcnt<0>();
     __syncthreads();
+    buf = buf + 1 == NBUF ? 0 : buf + 1;
   }
 
   if (q_ok) {
