@@ -78,8 +78,6 @@ __host__ __device__ constexpr int interleave_rank(int m, int na, int nb) {
   return interleave_is_b(m, na, nb) ? (m * nb) / (na + nb) : m - ((m + 1) * nb) / (na + nb);
 }
 
-template <int V> struct IC { static constexpr int value = V; };
-
 __device__ inline void zero_elem(bf16x8& x, int e) { x[e] = (bf16)0.f; }
 __device__ inline void zero_elem(f32x4& x, int e) { x[e] = 0.f; }
 

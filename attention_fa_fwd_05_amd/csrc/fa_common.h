@@ -197,6 +197,16 @@ __device__ inline int opaque(int x) {
   return x;
 }
 
+// A compile-time constant as a type (for generic lambdas).
+template <auto V> struct IC { static constexpr auto value = V; };
+
+// The same for a wave-uniform value, kept in a scalar register.
+__device__ inline int opaque_s(int x) {
+  x = __builtin_amdgcn_readfirstlane(x);
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
 __device__ inline bf16x8 lds16(const void* base, int byte_off) {
   return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(base) + byte_off);
 }
