@@ -13,10 +13,11 @@
 // S^T = K_j Q_i^T (keys x queries) so that one query row lives in one lane
 // column: the row max is an in-register reduction plus one exchange between
 // the two lane halves, and the probabilities feed O^T += V_j^T P^T straight
-// from registers.  K_j and V_j (64 keys) are staged in LDS as swizzled
-// row-major tiles, double-buffered and filled by direct global->LDS loads one
-// tile ahead; V^T operands are fetched with transposed LDS reads.  Softmax runs in the
-// exp2 domain (scores pre-multiplied by scale * log2 e); L is converted back
+// from registers.  K_j and V_j are staged in LDS as swizzled row-major tiles
+// (128 keys; 64 for fp32 with d = 128), double-buffered and filled by direct
+// global->LDS loads one tile ahead; V^T operands are fetched with transposed
+// LDS reads.  Softmax runs in the exp2 domain (scores pre-multiplied by
+// scale * log2 e); L is converted back
 // to a natural log at the end.
 #include "fa_common.h"
 #include "fa_kernels.h"
@@ -34,10 +35,13 @@ constexpr float kTau = 8.0f;
 // overlaps another wave's matrix work, which costs more than the LDS saving:
 // QT = 1 with 8 waves (two per SIMD) is faster.  fp32 d = 128 uses 4 waves so
 // its operands fit.
+// Keys per tile: 128, so a workgroup meets one barrier per 128 keys; fp32 with
+// d = 128 keeps 64 (two 128-key K / V buffers of it would exceed the LDS).
 template <typename T, int D> struct FwdShape {
   static constexpr int QT = 1;
   static constexpr int NW = (sizeof(T) == 4 && D == 128) ? 4 : 8;
   static constexpr int BQ = 32 * QT * NW;
+  static constexpr int BK = (sizeof(T) == 4 && D == 128) ? 64 : 128;
 };
 
 template <typename T, int D, bool CAUSAL>
@@ -45,7 +49,9 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
   using M = MM<T>;
   typedef typename M::Op Op;
   using SH = FwdShape<T, D>;
-  constexpr int QT = SH::QT, NW = SH::NW, NTHR = 64 * NW, BQ = SH::BQ, BK = 64;
+  constexpr int QT = SH::QT, NW = SH::NW, NTHR = 64 * NW, BQ = SH::BQ, BK = SH::BK;
+  constexpr int NKT = BK / 32;                      // 32-key sub-tiles per key tile
+  constexpr int NE = 16 * NKT;                      // scores per lane per query tile
   constexpr int KPER = M::KPER;
   constexpr int NSD = (D / 2) / KPER;               // steps over the head dim
   constexpr int NSK = (BK / 2) / KPER;              // steps over a key tile
@@ -116,39 +122,41 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
     const T* cV = sV[buf];
 
     if (!(CAUSAL && k0 > qw + 32 * QT - 1 + off)) {   // some key of the tile visible to this wave
-      // S^T = K Q^T: 2 key sub-tiles x QT query tiles; each K operand feeds QT products.
-      f32x16 st[QT][2];
+      // S^T = K Q^T: NKT key sub-tiles x QT query tiles; each K operand feeds QT products.
+      f32x16 st[QT][NKT];
 #pragma unroll
-      for (int u = 0; u < QT; ++u) { st[u][0] = f32x16{}; st[u][1] = f32x16{}; }
+      for (int u = 0; u < QT; ++u)
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) st[u][kt] = f32x16{};
 #pragma unroll
       for (int s = 0; s < NSD; ++s) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < NKT; ++kt) {
           const Op kop = nat.ld(cK, kt, s);
 #pragma unroll
           for (int u = 0; u < QT; ++u) st[u][kt] = M::mma(kop, qop[u][s], st[u][kt]);
         }
       }
-      sched_interleave<2 * NSD * QT, 4 * QT, 1, QT>();
+      sched_interleave<NKT * NSD * QT, 4 * QT, 1, QT>();
 
       const bool need_mask = (k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off);
       Op pop[QT][NSK];
 #pragma unroll
       for (int u = 0; u < QT; ++u) {
         const int myq = qw + 32 * u + n;
-        float x[32];
+        float x[NE];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { x[i] = st[u][0][i]; x[16 + i] = st[u][1][i]; }
+        for (int r = 0; r < NE; ++r) x[r] = st[u][r >> 4][r & 15];
         if (need_mask) {
 #pragma unroll
-          for (int r = 0; r < 32; ++r) {
+          for (int r = 0; r < NE; ++r) {
             const int key = k0 + perm_index(h, r);
             if (key >= a.Tk || (CAUSAL && key > myq + off)) x[r] = -INFINITY;
           }
         }
         float mt = fmaxf(x[0], x[1]);
 #pragma unroll
-        for (int r = 2; r < 32; r += 2) mt = fmaxf(mt, fmaxf(x[r], x[r + 1]));
+        for (int r = 2; r < NE; r += 2) mt = fmaxf(mt, fmaxf(x[r], x[r + 1]));
         mt = wave_xor32_max(mt) * c;                 // row max, exp2 units
         const bool need = mt > m_run[u] + kTau;
         if (__ballot(need)) {
@@ -162,7 +170,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
         const float nm = (m_run[u] == -INFINITY) ? 0.f : -m_run[u];
         float ps = 0.f;
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
+        for (int r = 0; r < NE; ++r) {
           x[r] = fast_exp2(__builtin_fmaf(x[r], c, nm));
           ps += x[r];
         }
