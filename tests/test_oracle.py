@@ -407,3 +407,21 @@ def test_row_subset_matches_bruteforce(causal):
     assert np.array_equal(np.isneginf(L), np.isneginf(Lb))
     fin = np.isfinite(Lb)
     assert np.abs(O - Ob).max() < 1e-12 and np.abs(L[fin] - Lb[fin]).max() < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_subset_dq_matches_full_backward(causal):
+    """dQ of a query row depends only on that row's P, dP and D, so the backward
+    applied to a row subset (as the long-sequence GPU check does) gives exactly
+    those rows of the full head's dQ (itself pinned by finite differences and
+    torch autograd above).  Rows 0..3 of a causal Tq > Tk head see no key."""
+    Tq, Tk = 40, 31
+    q, k, v, dO = rnd((Tq, 6), 51), rnd((Tk, 6), 52), rnd((Tk, 6), 53), rnd((Tq, 6), 54)
+    O, L, P = oa.head_forward(q, k, v, causal, 0.7)
+    dq_full, _, _ = oa.head_backward(q, k, v, dO, O, P, 0.7)
+    rows = np.array([0, 2, 9, 10, 27, 39])
+    Or, Lr, Pr = oa.head_forward(q[rows], k, v, causal, 0.7, rows=rows, Tq=Tq)
+    dq_rows, _, _ = oa.head_backward(q[rows], k, v, dO[rows], Or, Pr, 0.7)
+    assert np.abs(dq_rows - dq_full[rows]).max() < 1e-12
+    if causal:
+        assert np.all(dq_rows[0] == 0.0)
