@@ -4,7 +4,9 @@
 
 Every HIP source under csrc/ is compiled separately (in parallel) and linked
 into attention_fa_fwd_05_amd/libfa05.so.  Packed fp32 VALU instructions are
-disabled (-packed-fp32-ops).
+disabled (-packed-fp32-ops).  NaNs are not honoured (-fno-honor-nans): inputs are
+assumed free of them, and the kernels make none (masked scores are -inf), so
+maxima need no NaN-quieting instructions.
 """
 
 from __future__ import annotations
@@ -24,7 +26,7 @@ SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.hip"]
 HEADERS = ["fa_common.h", "fa_kernels.h"]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fno-honor-nans",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mcode-object-version=5",
 ]

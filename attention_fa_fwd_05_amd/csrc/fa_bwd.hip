@@ -467,9 +467,11 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   // Three K/V buffers: tile j+2 loads while tile j is read, so the wait at the
   // end of a tile only covers loads issued a whole tile earlier.  fp32 with
   // d = 128 fits two (its loads then wait within the tile).
-  constexpr int NBUF = (sizeof(T) == 4 && D == 128) ? 2 : 3;
-  __shared__ __attribute__((aligned(16))) T sK[NBUF][BK * D];
-  __shared__ __attribute__((aligned(16))) T sV[NBUF][BK * D];
+  constexpr int NBUF = NW == 8 ? 3 : 2;
+  constexpr int AHEAD = NBUF - 1;                   // tiles loaded beyond the current one
+  constexpr int TILE = BK * D;                      // elements of one K or V tile
+  // Buffer b: K tile, then V tile; 4096-byte alignment for XorFetch.
+  __shared__ __attribute__((aligned(4096))) T sKV[NBUF][2 * TILE];
 
   // The wave index is uniform across a wave; readfirstlane tells the compiler,
   // so conditions built from it become scalar branches.
@@ -491,15 +493,33 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   if (CAUSAL) kend = min(a.Tk, max(0, q0 + BQ + off));
   const int ntiles = (kend + BK - 1) / BK;
 
-  // Rows past Tk are loaded as copies of the last key; their scores are masked.
+  // A whole tile is addressed from a wave-uniform base plus per-lane offsets
+  // tabulated once; in the tile holding the key end, rows past Tk are loaded
+  // as copies of the last key (their scores are masked).
+  using DR = DmaRows<T, D, BK, NTHR>;
+  uint32_t src_off[DR::PER];
+#pragma unroll
+  for (int i = 0; i < DR::PER; ++i) src_off[i] = DR::src_off(i);
   auto issue = [&](int k0, int buf) {
-    dma_rows<T, D, BK, NTHR>(sK[buf], Kp, k0, a.Tk);
-    dma_rows<T, D, BK, NTHR>(sV[buf], Vp, k0, a.Tk);
+    T* tk = sKV[buf];
+    T* tv = sKV[buf] + TILE;
+    if (k0 + BK <= a.Tk) {
+      const T* kb = Kp + (size_t)k0 * D;
+      const T* vb = Vp + (size_t)k0 * D;
+#pragma unroll
+      for (int i = 0; i < DR::PER; ++i) dma16s(kb, src_off[i], lds_addr(tk) + DR::lds_off(i));
+#pragma unroll
+      for (int i = 0; i < DR::PER; ++i) dma16s(vb, src_off[i], lds_addr(tv) + DR::lds_off(i));
+    } else {
+      dma_rows<T, D, BK, NTHR>(tk, Kp, k0, a.Tk);
+      dma_rows<T, D, BK, NTHR>(tv, Vp, k0, a.Tk);
+    }
   };
   // Direct-load instructions per wave for one tile (K and V).
-  constexpr int NLD = 2 * DmaRows<T, D, BK, NTHR>::PER;
-  if (ntiles > 0) issue(0, 0);
-  if (NBUF == 3 && ntiles > 1) issue(BK, 1);
+  constexpr int NLD = 2 * DR::PER;
+#pragma unroll
+  for (int j = 0; j < AHEAD; ++j)
+    if (j < ntiles) issue(j * BK, j);
 
   // Q^T and dO^T operands for this lane's query, L2 and D of that row.
   Op qop[NSD], gop[NSD];
@@ -514,10 +534,33 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   }
   const float l2 = q_ok ? a.Lg[(size_t)bh * a.Tqp + myq] : INFINITY;
   const float ndd = q_ok ? a.Dvec[(size_t)bh * a.Tqp + myq] : 0.f;   // -D of this lane's query
+  // Operand fetch: bf16 from one base register per tile (XorFetch); fp32
+  // (test shapes only) from offset tables.
+  XorFetch<D> xf;
   NatFetch<T, D> nat;
-  nat.init(n, h);
   TrPermFetch<T, D> trp;
-  trp.init(lane);
+  if constexpr (sizeof(T) == 2) {
+    xf.init(lane);
+  } else {
+    nat.init(n, h);
+    trp.init(lane);
+  }
+  // Natural K (kv = 0) or V (kv = 1) operand of key sub-tile t, step s, and
+  // transposed K operand of d tile t, step s, from buffer buf.
+  auto ld_nat = [&](int buf, int kv, int t, int s) -> Op {
+    if constexpr (sizeof(T) == 2) {
+      return XorFetch<D>::nat(lds_addr(sKV[buf]) + xf.nat0 + kv * TILE * 2, t, s);
+    } else {
+      return nat.ld(sKV[buf] + kv * TILE, t, s);
+    }
+  };
+  auto ld_tr = [&](int buf, int t, int s) -> Op {
+    if constexpr (sizeof(T) == 2) {
+      return XorFetch<D>::tr(lds_addr(sKV[buf]) + xf.tr0, t, s);
+    } else {
+      return trp.ld(sKV[buf], t, s);
+    }
+  };
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -525,58 +568,66 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   f32x16 acc[NDT];
 #pragma unroll
   for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
+  // S^T = K Q^T and dP^T = V dO^T of one tile: 64 keys x 32 queries each.
+  f32x16 st0, st1, dp0, dp1;
 
-  int buf = 0;
-  for (int jt = 0; jt < ntiles; ++jt) {
-    const int k0 = jt * BK;
-    constexpr int ahead = NBUF - 1;                  // tiles in flight beyond this one
-    const int lbuf = buf + ahead >= NBUF ? buf + ahead - NBUF : buf + ahead;
-    const bool issued = jt + ahead < ntiles;
-    if (issued) issue(k0 + ahead * BK, lbuf);
-    const T* cK = sK[buf];
-    const T* cV = sV[buf];
-
-    if (!(CAUSAL && k0 > qw + 31 + off)) {          // some key of the tile visible to this wave
-      // S^T = K Q^T and dP^T = V dO^T: 64 keys x 32 queries each.
-      f32x16 st0 = f32x16{}, st1 = f32x16{}, dp0 = f32x16{}, dp1 = f32x16{};
+  // Some key of tile j is visible to this wave's queries.
+  auto visible = [&](int j) { return !(CAUSAL && j * BK > qw + 31 + off); };
+  auto s_phase = [&](int buf) {
+    st0 = f32x16{}; st1 = f32x16{}; dp0 = f32x16{}; dp1 = f32x16{};
 #pragma unroll
-      for (int s = 0; s < NSD; ++s) {
-        st0 = M::mma(nat.ld(cK, 0, s), qop[s], st0);
-        st1 = M::mma(nat.ld(cK, 1, s), qop[s], st1);
-        dp0 = M::mma(nat.ld(cV, 0, s), gop[s], dp0);
-        dp1 = M::mma(nat.ld(cV, 1, s), gop[s], dp1);
-      }
-      sched_interleave<4 * NSD, 4>();
-      float ds[32];
-#pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        const float sv = r < 16 ? st0[r] : st1[r - 16];
-        const float dpv = r < 16 ? dp0[r] : dp1[r - 16];
-        ds[r] = fast_exp2(__builtin_fmaf(sv, c, -l2)) * (dpv + ndd);
-      }
-      // Only the diagonal tiles and the ragged key end (a uniform test) clear
-      // dS of the keys this query may not see; every value above is finite.
-      if ((k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off)) {
-        const int lim = min(a.Tk - 1, CAUSAL ? myq + off : a.Tk - 1) - k0;   // last visible key offset
-#pragma unroll
-        for (int r = 0; r < 32; ++r)
-          if (perm_index(h, r) > lim) ds[r] = 0.f;
-      }
-      Op dsop[NSK];
-#pragma unroll
-      for (int s = 0; s < NSK; ++s) dsop[s] = M::pack(ds + s * KPER);
-      // dQ^T += K^T dS^T (K^T through transposed reads of the key tile).
-#pragma unroll
-      for (int t = 0; t < NDT; ++t) {
-#pragma unroll
-        for (int s = 0; s < NSK; ++s) acc[t] = M::mma(trp.ld(cK, t, s), dsop[s], acc[t]);
-      }
-      sched_interleave<NDT * NSK, 4, (sizeof(T) == 2 ? 2 : 1)>();
+    for (int s = 0; s < NSD; ++s) {
+      st0 = M::mma(ld_nat(buf, 0, 0, s), qop[s], st0);
+      st1 = M::mma(ld_nat(buf, 0, 1, s), qop[s], st1);
+      dp0 = M::mma(ld_nat(buf, 1, 0, s), gop[s], dp0);
+      dp1 = M::mma(ld_nat(buf, 1, 1, s), gop[s], dp1);
     }
-    // This wave's loads of tile j+1 have landed (those of tile j+2, issued
-    // last, may still be in flight); the barrier makes every wave's share
+    sched_interleave<4 * NSD, 4>();
+  };
+  // dS^T from the tile's S^T, dP^T, then dQ^T += K^T dS^T (K^T through
+  // transposed reads of the key tile).
+  auto dq_phase = [&](int j, int buf) {
+    const int k0 = j * BK;
+    float ds[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const float sv = r < 16 ? st0[r] : st1[r - 16];
+      const float dpv = r < 16 ? dp0[r] : dp1[r - 16];
+      ds[r] = fast_exp2(__builtin_fmaf(sv, c, -l2)) * (dpv + ndd);
+    }
+    // Only the diagonal tiles and the ragged key end (a uniform test) clear
+    // dS of the keys this query may not see; every value above is finite.
+    if ((k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off)) {
+      // Last visible key offset, less this lane half's 4 h, against the
+      // compile-time part of perm_index (no per-lane index table).
+      const int lim = min(a.Tk - 1, CAUSAL ? myq + off : a.Tk - 1) - k0 - 4 * h;
+#pragma unroll
+      for (int r = 0; r < 32; ++r)
+        if (perm_index(0, r) > lim) ds[r] = 0.f;
+    }
+    Op dsop[NSK];
+#pragma unroll
+    for (int s = 0; s < NSK; ++s) dsop[s] = M::pack(ds + s * KPER);
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) {
+#pragma unroll
+      for (int s = 0; s < NSK; ++s) acc[t] = M::mma(ld_tr(buf, t, s), dsop[s], acc[t]);
+    }
+    sched_interleave<NDT * NSK, 4, (sizeof(T) == 2 ? 2 : 1)>();
+  };
+
+  int buf = 0;                                      // buffer of tile jt
+  for (int jt = 0; jt < ntiles; ++jt) {
+    const bool issued = jt + AHEAD < ntiles;
+    if (issued) issue((jt + AHEAD) * BK, buf + AHEAD >= NBUF ? buf + AHEAD - NBUF : buf + AHEAD);
+    if (visible(jt)) {
+      s_phase(buf);
+      dq_phase(jt, buf);
+    }
+    // This wave's loads of tile jt+1 have landed (those of tile jt+2, issued
+    // just now, may still be in flight); the barrier makes every wave's share
     // visible and frees buffer buf for the loads issued next.
-    if (NBUF == 3 && issued) wait_vmcnt<NLD>();
+    if (AHEAD == 2 && issued) wait_vmcnt<NLD>();
     else wait_vmcnt<0>();
     __syncthreads();
     buf = buf + 1 == NBUF ? 0 : buf + 1;

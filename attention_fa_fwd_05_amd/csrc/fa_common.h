@@ -276,6 +276,40 @@ template <int D> struct TrPermFetch<float, D> {
   }
 };
 
+// Loads from a 32-bit LDS byte address.
+__device__ inline bf16x8 lds16_at(uint32_t addr) {
+  typedef __attribute__((address_space(3))) bf16x8 lds_t;
+  return *(const lds_t*)addr;
+}
+__device__ inline bf16x4 lds_tr8_at(uint32_t addr) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_t;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_t*)addr);
+}
+
+// Register-lean form of the two bf16 fetchers above, for tiles whose buffer is
+// chosen at run time.  In a swizzled tile, a lane's natural-operand offset for
+// step s is its step-0 offset XOR 16 s, and its transposed-read offset for
+// column tile t and row group u is the (0, 0) offset XOR 64 t + (32 + 16 D) u.
+// These XOR constants stay below 4096, so with 4096-byte aligned tiles the XOR
+// can follow the addition of the tile address.  A wave keeps one base
+// register per tile instead of a table of offsets, and spends one v_xor per
+// distinct step; the step's row offset is an immediate.
+template <int D> struct XorFetch {
+  using TL = SwzTile<bf16, D>;
+  uint32_t nat0, tr0;                               // byte offsets within a tile
+  __device__ void init(int lane) {
+    const int h = lane >> 5, n = lane & 31, i = lane & 15, g16 = (lane >> 4) & 1;
+    nat0 = 2 * TL::elem(n, h * (D / 2));
+    tr0 = 2 * TL::elem(4 * h + (i >> 2), 16 * g16 + 4 * (i & 3));
+  }
+  // vn = tile address + nat0: tile[32 t + n][h D / 2 + 8 s .. + 7]
+  __device__ static bf16x8 nat(uint32_t vn, int t, int s) { return lds16_at((vn ^ (16 * s)) + t * 64 * D); }
+  // vt = tile address + tr0: as TrPermFetch::ld
+  __device__ static bf16x8 tr(uint32_t vt, int t, int s) {
+    return cat(lds_tr8_at((vt ^ (64 * t)) + 32 * s * D), lds_tr8_at((vt ^ (64 * t + 32 + 16 * D)) + 32 * s * D));
+  }
+};
+
 // Scheduling hint for a straight run of NMMA matrix instructions, each fed by
 // RPM LDS reads: issue the reads for the first AHEAD instructions, then
 // alternate one matrix instruction with the reads of a later one, so LDS
@@ -346,6 +380,31 @@ __device__ inline void sched_interleave_valu() {
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline float wave_xor32_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
+
+// Maximum of N values as a tree of three-input maxima (v_max3_f32 once NaNs
+// need not be propagated, which the library's build assumes).
+template <int N>
+__device__ inline float max_tree(const float* v) {
+  if constexpr (N == 1) {
+    return v[0];
+  } else if constexpr (N == 2) {
+    return fmaxf(v[0], v[1]);
+  } else {
+    constexpr int A = N / 3, B = (N - A) / 2, C = N - A - B;
+    return fmaxf(fmaxf(max_tree<A>(v), max_tree<B>(v + A)), max_tree<C>(v + A + B));
+  }
+}
+
+// Sum of the 8 bf16 values of an operand, accumulated in fp32 by two-element
+// dot products with (1, 1): the sum of exactly the rounded values the matrix
+// unit multiplies.
+__device__ inline void sum_bf16x8(const bf16x8& p, float* acc4) {
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+  acc4[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), one, acc4[0], false);
+  acc4[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), one, acc4[1], false);
+  acc4[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), one, acc4[2], false);
+  acc4[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), one, acc4[3], false);
+}
 __device__ inline float wave_xor32_sum(float v) { return v + __shfl_xor(v, 32, 64); }
 
 // 16-byte global <-> LDS copy helpers.

@@ -77,10 +77,25 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
   if (CAUSAL) kend = min(a.Tk, max(0, q0 + BQ + off));
   const int ntiles = (kend + BK - 1) / BK;
 
-  // Rows past Tk are loaded as copies of the last key; their scores are masked.
+  // A whole tile is addressed from a wave-uniform base plus per-lane offsets
+  // tabulated once; in the tile holding the key end, rows past Tk are loaded
+  // as copies of the last key (their scores are masked).
+  using DR = DmaRows<T, D, BK, NTHR>;
+  uint32_t src_off[DR::PER];
+#pragma unroll
+  for (int i = 0; i < DR::PER; ++i) src_off[i] = DR::src_off(i);
   auto issue = [&](int k0, int buf) {
-    dma_rows<T, D, BK, NTHR>(sK[buf], Kp, k0, a.Tk);
-    dma_rows<T, D, BK, NTHR>(sV[buf], Vp, k0, a.Tk);
+    if (k0 + BK <= a.Tk) {
+      const T* kb = Kp + (size_t)k0 * D;
+      const T* vb = Vp + (size_t)k0 * D;
+#pragma unroll
+      for (int i = 0; i < DR::PER; ++i) dma16s(kb, src_off[i], lds_addr(sK[buf]) + DR::lds_off(i));
+#pragma unroll
+      for (int i = 0; i < DR::PER; ++i) dma16s(vb, src_off[i], lds_addr(sV[buf]) + DR::lds_off(i));
+    } else {
+      dma_rows<T, D, BK, NTHR>(sK[buf], Kp, k0, a.Tk);
+      dma_rows<T, D, BK, NTHR>(sV[buf], Vp, k0, a.Tk);
+    }
   };
   if (ntiles > 0) issue(0, 0);
 
@@ -148,16 +163,13 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
 #pragma unroll
         for (int r = 0; r < NE; ++r) x[r] = st[u][r >> 4][r & 15];
         if (need_mask) {
+          // Key k0 + perm_index(h, r) is visible iff perm_index(0, r) <= lim.
+          const int lim = min(a.Tk - 1, CAUSAL ? myq + off : a.Tk - 1) - k0 - 4 * h;
 #pragma unroll
-          for (int r = 0; r < NE; ++r) {
-            const int key = k0 + perm_index(h, r);
-            if (key >= a.Tk || (CAUSAL && key > myq + off)) x[r] = -INFINITY;
-          }
+          for (int r = 0; r < NE; ++r)
+            if (perm_index(0, r) > lim) x[r] = -INFINITY;
         }
-        float mt = fmaxf(x[0], x[1]);
-#pragma unroll
-        for (int r = 2; r < NE; r += 2) mt = fmaxf(mt, fmaxf(x[r], x[r + 1]));
-        mt = wave_xor32_max(mt) * c;                 // row max, exp2 units
+        float mt = wave_xor32_max(max_tree<NE>(x)) * c;   // row max, exp2 units
         const bool need = mt > m_run[u] + kTau;
         if (__ballot(need)) {
           const float m_new = need ? mt : m_run[u];
@@ -168,15 +180,21 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
           m_run[u] = m_new;
         }
         const float nm = (m_run[u] == -INFINITY) ? 0.f : -m_run[u];
-        float ps = 0.f;
 #pragma unroll
-        for (int r = 0; r < NE; ++r) {
-          x[r] = fast_exp2(__builtin_fmaf(x[r], c, nm));
-          ps += x[r];
-        }
-        lsum[u] += ps;
+        for (int r = 0; r < NE; ++r) x[r] = fast_exp2(__builtin_fmaf(x[r], c, nm));
 #pragma unroll
         for (int s = 0; s < NSK; ++s) pop[u][s] = M::pack(x + s * KPER);
+        // Row sum: of the rounded bf16 probabilities (two per instruction), so
+        // the normaliser is the sum of exactly what the PV product weighs.
+        float ps4[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int s = 0; s < NSK; ++s) sum_bf16x8(pop[u][s], ps4);
+        } else {
+#pragma unroll
+          for (int r = 0; r < NE; ++r) ps4[r & 3] += x[r];
+        }
+        lsum[u] += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
       }
 
       // O^T += V^T P^T; each V^T operand feeds QT products.
