@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   };
   // The three vector stages of register e of tile t.
   float xa[16], pa[16];
-  bf16x2 ppk[8], dpk[8];                            // packed pairs (bf16 operands)
+  uint32_t ppk[8], dpk[8];                          // packed bf16 pairs (bf16 operands)
   auto st1 = [&](int t, int e) { xa[e] = __builtin_fmaf(sacc[t][e], c, -lt[e >> 2][e & 3]); };
   auto st2 = [&](int e) { pa[e] = fast_exp2(xa[e]); };
   auto st3 = [&](int t, int e) {
@@ -280,16 +280,15 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
                         dpacc[t][e - 1] * pa[e - 1], dpacc[t][e] * pa[e]};
       }
     } else if (e & 1) {
-      ppk[e >> 1] = bf16x2{(bf16)pa[e - 1], (bf16)pa[e]};
-      dpk[e >> 1] = bf16x2{(bf16)(dpacc[t][e - 1] * pa[e - 1]), (bf16)(dpacc[t][e] * pa[e])};
+      // Whole 32-bit words (one v_cvt_pk_bf16_f32 each) assembled into the
+      // operand as words, so no 16-bit lane shuffles are generated.
+      ppk[e >> 1] = __builtin_bit_cast(uint32_t, bf16x2{(bf16)pa[e - 1], (bf16)pa[e]});
+      dpk[e >> 1] = __builtin_bit_cast(uint32_t, bf16x2{(bf16)(dpacc[t][e - 1] * pa[e - 1]),
+                                                         (bf16)(dpacc[t][e] * pa[e])});
       if ((e & 7) == 7) {
         const int s = (16 * t + e) / 8, j = (e >> 1) - 3;
-        const bf16x4 p0 = __builtin_shufflevector(ppk[j], ppk[j + 1], 0, 1, 2, 3);
-        const bf16x4 p1 = __builtin_shufflevector(ppk[j + 2], ppk[j + 3], 0, 1, 2, 3);
-        const bf16x4 d0 = __builtin_shufflevector(dpk[j], dpk[j + 1], 0, 1, 2, 3);
-        const bf16x4 d1 = __builtin_shufflevector(dpk[j + 2], dpk[j + 3], 0, 1, 2, 3);
-        pop[s] = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
-        dsop[s] = __builtin_shufflevector(d0, d1, 0, 1, 2, 3, 4, 5, 6, 7);
+        pop[s] = __builtin_bit_cast(bf16x8, u32x4{ppk[j], ppk[j + 1], ppk[j + 2], ppk[j + 3]});
+        dsop[s] = __builtin_bit_cast(bf16x8, u32x4{dpk[j], dpk[j + 1], dpk[j + 2], dpk[j + 3]});
       }
     }
   };
