@@ -35,7 +35,14 @@ Readings where the pages are silent (each is listed in the design notes):
   and V (L receives no cotangent), written out as the textbook softmax/matmul
   derivative: dP = dO V^T, D = rowsum(dO * O), dS = P * (dP - D),
   dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO;
-* the scale is an argument whose default is 1/sqrt(d).
+* the scale is an argument whose default is 1/sqrt(d);
+* a sliding window of ``window`` keys (the chunked-attention article's
+  sliding-window layers, section "The Reasoning: A Deep Dive into Autograd
+  Memory" and its list of subtle mistakes: such layers see a much smaller key
+  span than the full-attention layer) lets query i see only keys
+  j > i + (Tk - Tq) - window, i.e. at most ``window`` keys ending at its
+  end-aligned diagonal position; it combines with the causal bound, and
+  window <= 0 means no window.
 
 Layouts: Q, dO are [B, Hq, Tq, d]; K is [B, Hkv, Tk, d]; V is [B, Hkv, Tk, dv];
 O is [B, Hq, Tq, dv]; L is [B, Hq, Tq].  Query head h reads key/value head
@@ -59,13 +66,20 @@ def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
 
-def visible(Tq: int, Tk: int, causal: bool) -> np.ndarray:
-    """Boolean [Tq, Tk] visibility: all True, or end-aligned causal j <= i + Tk - Tq."""
-    if not causal:
-        return np.ones((Tq, Tk), dtype=bool)
+def visible(Tq: int, Tk: int, causal: bool, window: int = 0) -> np.ndarray:
+    """Boolean [Tq, Tk] visibility of key j to query i.
+
+    All True, narrowed by the end-aligned causal bound j <= i + Tk - Tq when
+    causal, and by the sliding window j > i + Tk - Tq - window when window > 0.
+    """
     i = np.arange(Tq)[:, None]
     j = np.arange(Tk)[None, :]
-    return j <= i + (Tk - Tq)
+    vis = np.ones((Tq, Tk), dtype=bool)
+    if causal:
+        vis &= j <= i + (Tk - Tq)
+    if window > 0:
+        vis &= j > i + (Tk - Tq) - window
+    return vis
 
 
 def _check_shapes(Q, K, V):
@@ -80,7 +94,7 @@ def _check_shapes(Q, K, V):
     return B, Hq, Hkv, Tq, Tk, d, V.shape[3]
 
 
-def head_forward(q, k, v, causal, scale, rows=None, Tq=None):
+def head_forward(q, k, v, causal, scale, rows=None, Tq=None, window=0):
     """One query head against its key/value head, dense, fp64.
 
     Returns (O [Tq, dv], L [Tq], P [Tq, Tk]).  Steps as in standard attention:
@@ -95,9 +109,9 @@ def head_forward(q, k, v, causal, scale, rows=None, Tq=None):
     Tk = k.shape[0]
     if rows is None:
         Tq = q.shape[0]
-        vis = visible(Tq, Tk, causal)
+        vis = visible(Tq, Tk, causal, window)
     else:
-        vis = visible(Tq, Tk, causal)[np.asarray(rows)]
+        vis = visible(Tq, Tk, causal, window)[np.asarray(rows)]
     S = (q @ k.T) * scale
     Sm = np.where(vis, S, -np.inf)
     m = Sm.max(axis=1) if Tk > 0 else np.full(q.shape[0], -np.inf)
@@ -131,7 +145,7 @@ def head_backward(q, k, v, dO, O, P, scale):
     return dq, dk, dv
 
 
-def attention_forward(Q, K, V, causal=False, scale=None):
+def attention_forward(Q, K, V, causal=False, scale=None, window=0):
     """Dense exact attention with GQA: returns O [B,Hq,Tq,dv] and L [B,Hq,Tq] (fp64)."""
     B, Hq, Hkv, Tq, Tk, d, dv = _check_shapes(Q, K, V)
     if scale is None:
@@ -142,11 +156,11 @@ def attention_forward(Q, K, V, causal=False, scale=None):
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            O[b, h], L[b, h], _ = head_forward(Q[b, h], K[b, g], V[b, g], causal, scale)
+            O[b, h], L[b, h], _ = head_forward(Q[b, h], K[b, g], V[b, g], causal, scale, window=window)
     return O, L
 
 
-def group_forward_backward(Q, K, V, dO, b, g, causal=False, scale=None):
+def group_forward_backward(Q, K, V, dO, b, g, causal=False, scale=None, window=0):
     """Everything for one (batch b, key/value head g): the G query heads of the group.
 
     Returns dict with O [G,Tq,dv], L [G,Tq], dQ [G,Tq,d], dK [Tk,d], dV [Tk,dv]
@@ -169,7 +183,7 @@ def group_forward_backward(Q, K, V, dO, b, g, causal=False, scale=None):
     for r in range(G):
         h = g * G + r
         q = np.asarray(Q[b, h], dtype=np.float64)
-        o, lse, p = head_forward(q, kg, vg, causal, scale)
+        o, lse, p = head_forward(q, kg, vg, causal, scale, window=window)
         dq, dk, dvv = head_backward(q, kg, vg, dO[b, h], o, p, scale)
         out["O"][r], out["L"][r], out["dQ"][r] = o, lse, dq
         out["dK"] += dk
@@ -177,7 +191,7 @@ def group_forward_backward(Q, K, V, dO, b, g, causal=False, scale=None):
     return out
 
 
-def attention_forward_backward(Q, K, V, dO, causal=False, scale=None):
+def attention_forward_backward(Q, K, V, dO, causal=False, scale=None, window=0):
     """Full dense forward and backward: (O, L, dQ, dK, dV), all fp64."""
     B, Hq, Hkv, Tq, Tk, d, dv = _check_shapes(Q, K, V)
     if scale is None:
@@ -190,7 +204,7 @@ def attention_forward_backward(Q, K, V, dO, causal=False, scale=None):
     dV = np.zeros((B, Hkv, Tk, dv))
     for b in range(B):
         for g in range(Hkv):
-            r = group_forward_backward(Q, K, V, dO, b, g, causal, scale)
+            r = group_forward_backward(Q, K, V, dO, b, g, causal, scale, window)
             O[b, g * G:(g + 1) * G] = r["O"]
             L[b, g * G:(g + 1) * G] = r["L"]
             dQ[b, g * G:(g + 1) * G] = r["dQ"]
@@ -199,7 +213,7 @@ def attention_forward_backward(Q, K, V, dO, causal=False, scale=None):
     return O, L, dQ, dK, dV
 
 
-def tiled_head_forward(q, k, v, block_q, block_k, causal, scale):
+def tiled_head_forward(q, k, v, block_q, block_k, causal, scale, window=0):
     """The online-softmax recurrence of the printed tiled forward, in fp64.
 
     Outer loop over query blocks, inner loop over key blocks (the last ones may
@@ -229,7 +243,9 @@ def tiled_head_forward(q, k, v, block_q, block_k, causal, scale):
             cols = np.arange(j, j + kj.shape[0])[None, :]
             vis = np.ones((nq, kj.shape[0]), dtype=bool)
             if causal:
-                vis = cols <= rows + (Tk - Tq)
+                vis &= cols <= rows + (Tk - Tq)
+            if window > 0:
+                vis &= cols > rows + (Tk - Tq) - window
             S = np.where(vis, (qi @ kj.T) * scale, -np.inf)
             m_new = np.maximum(m, S.max(axis=1))
             alpha = np.zeros(nq)
@@ -247,7 +263,7 @@ def tiled_head_forward(q, k, v, block_q, block_k, causal, scale):
     return O, L
 
 
-def tiled_forward(Q, K, V, block_q=32, block_k=32, causal=False, scale=None):
+def tiled_forward(Q, K, V, block_q=32, block_k=32, causal=False, scale=None, window=0):
     """tiled_head_forward over every (b, h) with GQA head mapping; fp64 O and L."""
     B, Hq, Hkv, Tq, Tk, d, dv = _check_shapes(Q, K, V)
     if scale is None:
@@ -258,7 +274,7 @@ def tiled_forward(Q, K, V, block_q=32, block_k=32, causal=False, scale=None):
     for b in range(B):
         for h in range(Hq):
             O[b, h], L[b, h] = tiled_head_forward(Q[b, h], K[b, h // G], V[b, h // G],
-                                                  block_q, block_k, causal, scale)
+                                                  block_q, block_k, causal, scale, window)
     return O, L
 
 

@@ -310,12 +310,12 @@ def _mutant_backward_sign(q, k, v, dO, O, P, scale):
     return scale * (dS @ k), scale * (dS.T @ q), P.T @ dO
 
 
-def _mutant_forward_log2(q, k, v, causal, scale):
-    O, L, P = _ORIG_HEAD_FORWARD(q, k, v, causal, scale)
+def _mutant_forward_log2(q, k, v, causal, scale, rows=None, Tq=None, window=0):
+    O, L, P = _ORIG_HEAD_FORWARD(q, k, v, causal, scale, rows, Tq, window=window)
     return O, L / math.log(2.0), P                # L in log2
 
 
-def _mutant_visible_start_aligned(Tq, Tk, causal):
+def _mutant_visible_start_aligned(Tq, Tk, causal, window=0):
     if not causal:
         return np.ones((Tq, Tk), dtype=bool)
     return np.arange(Tk)[None, :] <= np.arange(Tq)[:, None]
@@ -324,14 +324,15 @@ def _mutant_visible_start_aligned(Tq, Tk, causal):
 _ORIG_HEAD_FORWARD = oa.head_forward
 
 
-def _mutant_gqa_modulo(Q, K, V, causal=False, scale=None):
+def _mutant_gqa_modulo(Q, K, V, causal=False, scale=None, window=0):
     B, Hq, Hkv, Tq, Tk, d, dv = oa._check_shapes(Q, K, V)
     scale = oa.default_scale(d) if scale is None else scale
     O = np.zeros((B, Hq, Tq, dv))
     L = np.zeros((B, Hq, Tq))
     for b in range(B):
         for h in range(Hq):
-            O[b, h], L[b, h], _ = oa.head_forward(Q[b, h], K[b, h % Hkv], V[b, h % Hkv], causal, scale)
+            O[b, h], L[b, h], _ = oa.head_forward(Q[b, h], K[b, h % Hkv], V[b, h % Hkv], causal, scale,
+                                                  window=window)
     return O, L
 
 
