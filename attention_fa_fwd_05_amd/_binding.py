@@ -24,8 +24,8 @@ STATUS = {
     8: "FA_ERR_ALIGNMENT", 9: "FA_ERR_TOO_LARGE", 10: "FA_ERR_HIP", 11: "FA_ERR_STAGES",
 }
 STAGE_PRE, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
-EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_bwd_workspace_bytes", "fa_status_string",
-           "fa_hip_error_string", "fa_abi_version"]
+EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_window", "fa_bwd_window",
+           "fa_bwd_workspace_bytes", "fa_status_string", "fa_hip_error_string", "fa_abi_version"]
 
 _lib = None
 
@@ -62,6 +62,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_stages.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                   i, i, i, i, i, i, i, f, i, ctypes.c_uint, vp]
     lib.fa_bwd_stages.restype = i
+    lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_window.restype = i
+    lib.fa_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                  i, i, i, i, i, i, i, i, f, i, ctypes.c_uint, vp]
+    lib.fa_bwd_window.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -116,24 +121,30 @@ def workspace_bytes(B, Hq, Hkv, Tq, Tk, d, dtype_code) -> int:
     return int(load_library().fa_bwd_workspace_bytes(B, Hq, Hkv, Tq, Tk, d, dtype_code))
 
 
-def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
-    """fa_fwd: returns (o, lse) with o like q and lse float32 [B, Hq, Tq]."""
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+            window: int = 0):
+    """fa_fwd (fa_fwd_window when window > 0): returns (o, lse), o like q, lse float32 [B, Hq, Tq]."""
     import torch
     lib = load_library()
     B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
-    st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), B, Hq, Hkv, Tq, Tk, d,
-                    int(bool(causal)), scale, _dtype_code(q), _stream(q))
+    if window > 0:
+        st = lib.fa_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), B, Hq, Hkv, Tq, Tk, d,
+                               int(bool(causal)), int(window), scale, _dtype_code(q), _stream(q))
+    else:
+        st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), B, Hq, Hkv, Tq, Tk, d,
+                        int(bool(causal)), scale, _dtype_code(q), _stream(q))
     if st != 0:
-        raise FaError(st, "fa_fwd")
+        raise FaError(st, "fa_fwd_window" if window > 0 else "fa_fwd")
     return o, L
 
 
 def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
-             workspace=None, dq=None, dk=None, dv=None, stages: int = STAGE_ALL):
-    """fa_bwd (fa_bwd_stages for a partial stage mask): returns (dq, dk, dv) like q, k, v."""
+             workspace=None, dq=None, dk=None, dv=None, stages: int = STAGE_ALL, window: int = 0):
+    """fa_bwd (fa_bwd_stages for a partial stage mask, fa_bwd_window when window > 0):
+    returns (dq, dk, dv) like q, k, v."""
     import torch
     lib = load_library()
     B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
@@ -152,7 +163,13 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
-            _ptr(dv), ws.data_ptr(), ws.numel(), B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), scale, code)
+            _ptr(dv), ws.data_ptr(), ws.numel(), B, Hq, Hkv, Tq, Tk, d, int(bool(causal)))
+    if window > 0:
+        st = lib.fa_bwd_window(*args, int(window), scale, code, stages, _stream(q))
+        if st != 0:
+            raise FaError(st, "fa_bwd_window")
+        return dq, dk, dv
+    args = args + (scale, code)
     if stages == STAGE_ALL:
         st = lib.fa_bwd(*args, _stream(q))
     else:
@@ -169,17 +186,18 @@ def _autograd_function():
         """Autograd wrapper that saves exactly q, k, v, o and lse for the backward."""
 
         @staticmethod
-        def forward(ctx, q, k, v, causal, scale):
-            o, lse = forward(q, k, v, causal, scale)
+        def forward(ctx, q, k, v, causal, scale, window):
+            o, lse = forward(q, k, v, causal, scale, window=window)
             ctx.save_for_backward(q, k, v, o, lse)
-            ctx.causal, ctx.scale = causal, scale
+            ctx.causal, ctx.scale, ctx.window = causal, scale, window
             return o
 
         @staticmethod
         def backward(ctx, do):
             q, k, v, o, lse = ctx.saved_tensors
-            dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), ctx.causal, ctx.scale)
-            return dq, dk, dv, None, None
+            dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), ctx.causal, ctx.scale,
+                                  window=ctx.window)
+            return dq, dk, dv, None, None, None
 
     return FlashAttention
 
@@ -187,9 +205,9 @@ def _autograd_function():
 _FN = None
 
 
-def attention(q, k, v, causal: bool = False, scale: float | None = None):
+def attention(q, k, v, causal: bool = False, scale: float | None = None, window: int = 0):
     """Differentiable attention through the library (retains q, k, v, o, lse only)."""
     global _FN
     if _FN is None:
         _FN = _autograd_function()
-    return _FN.apply(q, k, v, causal, scale)
+    return _FN.apply(q, k, v, causal, scale, window)

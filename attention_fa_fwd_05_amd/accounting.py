@@ -29,16 +29,43 @@ def flops(B, Hq, Tq, Tk, d, causal):
     return f, b
 
 
-def kernel_flops(B, Hq, Tq, Tk, d, causal):
-    """Matrix FLOPs each kernel performs (halved when causal).
+def kernel_flops(B, Hq, Tq, Tk, d, causal, window=0):
+    """Matrix FLOPs each kernel performs (halved when causal; exactly counted
+    visible pairs under a sliding window).
 
     Per visible (query, key) pair: forward 4d (S and PV); dK/dV pass 8d (S, dP,
     dV, dK); dQ pass 6d (S, dP, dQ).  The two backward passes together do 14d,
     4d more than the 10d the backward is credited with, because each rebuilds
     S and dP for itself.
     """
-    pairs = B * Hq * Tq * Tk * (0.5 if causal else 1.0)
+    if window > 0:
+        pairs = float(B * Hq * visible_pairs(Tq, Tk, causal, window))
+    else:
+        pairs = B * Hq * Tq * Tk * (0.5 if causal else 1.0)
     return {"fwd_kernel": 4.0 * d * pairs, "dkdv_kernel": 8.0 * d * pairs, "dq_kernel": 6.0 * d * pairs}
+
+
+def visible_pairs(Tq, Tk, causal, window=0):
+    """Exact number of visible (query, key) pairs of one head.
+
+    Query i sees keys lo(i) .. hi(i) with hi = min(Tk - 1, i + Tk - Tq) when
+    causal (else Tk - 1) and lo = max(0, i + Tk - Tq - window + 1) for a
+    sliding window (else 0).
+    """
+    import numpy as np
+    i = np.arange(Tq, dtype=np.int64)
+    off = Tk - Tq
+    hi = np.minimum(Tk - 1, i + off) if causal else np.full(Tq, Tk - 1, dtype=np.int64)
+    lo = np.maximum(0, i + off - window + 1) if window > 0 else np.zeros(Tq, dtype=np.int64)
+    return int(np.maximum(0, hi - lo + 1).sum())
+
+
+def window_flops(B, Hq, Tq, Tk, d, causal, window):
+    """(forward, backward) FLOPs of a sliding-window workload: 4d and 10d per
+    exactly visible pair (the causal-halving convention has no analogue for a
+    window, so the pairs are counted)."""
+    p = float(B * Hq * visible_pairs(Tq, Tk, causal, window))
+    return 4.0 * d * p, 10.0 * d * p
 
 
 def retained_bytes_recompute(B, Hq, Hkv, Tq, Tk, d, dtype):

@@ -77,7 +77,7 @@ WsLayout ws_layout(int B, int Hq, int Tq, int d, int dtype) {
 
 extern "C" {
 
-int fa_abi_version(void) { return (1 << 16) | 0; }
+int fa_abi_version(void) { return (1 << 16) | 1; }
 
 const char* fa_hip_error_string(void) { return t_hip_error; }
 
@@ -102,6 +102,12 @@ const char* fa_status_string(int status) {
 int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
            int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
            int dtype, void* stream) {
+  return fa_fwd_window(Q, K, V, O, L, B, Hq, Hkv, Tq, Tk, d, causal, 0, scale, dtype, stream);
+}
+
+int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* L,
+                  int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int window, float scale,
+                  int dtype, void* stream) {
   int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
   if (st != FA_OK) return st;
   const long long nq = (long long)B * Hq * Tq * d, nkv = (long long)B * Hkv * Tk * d;
@@ -113,6 +119,7 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
   fa::FwdArgs a;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
+  a.window = window > 0 ? window : 0;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream));
 }
@@ -133,6 +140,14 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const flo
 int fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O, const float* L,
                   const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
                   int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
+                  int dtype, unsigned stages, void* stream) {
+  return fa_bwd_window(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, B, Hq, Hkv, Tq, Tk, d,
+                       causal, 0, scale, dtype, stages, stream);
+}
+
+int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                  const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                  int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int window, float scale,
                   int dtype, unsigned stages, void* stream) {
   int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
   if (st != FA_OK) return st;
@@ -158,6 +173,7 @@ int fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O, co
   a.Lg = ws.total ? reinterpret_cast<float*>(wsb + ws.lg) : nullptr;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
   a.Tqp = padded_rows(Tq);
+  a.window = window > 0 ? window : 0;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   return hip_status(fa::launch_bwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, stages, (hipStream_t)stream));

@@ -146,10 +146,15 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   // through the same query blocks in lockstep (each stops at its diagonal), so
   // every Q / dO block is fetched into that XCD's L2 once, not once per key
   // block.
+  // Query blocks qb0 .. qb1 see some key of this block: none before the
+  // causal bound of its first key, none past the window of its last.
   const int nqb = (a.Tq + BQ - 1) / BQ;
+  const int W = a.window;
   const int qb0 = CAUSAL ? min(nqb, max(0, k0 - off) / BQ) : 0;
-  const int total = G * (nqb - qb0);
-  auto item_q0 = [&](int it) { return (nqb - 1 - it / G) * BQ; };
+  const int qlast = W > 0 ? min(a.Tq - 1, k0 + BK - 1 - off + W - 1) : a.Tq - 1;   // last query seeing a key
+  const int qb1 = qlast < 0 ? -1 : qlast / BQ;
+  const int total = G * max(0, qb1 - qb0 + 1);
+  auto item_q0 = [&](int it) { return (qb1 - it / G) * BQ; };
   auto item_bh = [&](int it) { return wk.b * a.Hq + wk.hk * G + it % G; };
   // L2 and D rows are padded to 64 per head, so a 64-row window always loads.
   auto issue = [&](int it, int buf) {
@@ -311,12 +316,14 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   // Causal diagonal and ragged key end, only on the blocks that have them:
   // P and dS of pairs the key may not see are cleared in the packed operands.
   // Register i of tile t holds query q0 + 32 t + 4 h + 8 (i / 4) + i % 4.
+  // The sliding window clears pairs whose query is past the key's window.
   auto mask_tile = [&](int q0, int t) {
-    if (ragged || (CAUSAL && k0 + BK - 1 > q0 + 32 * t + off)) {
+    if (ragged || (CAUSAL && k0 + BK - 1 > q0 + 32 * t + off) || (W > 0 && q0 + 32 * t + 31 > k0 - off + W - 1)) {
       const int thr = !key_ok ? INT_MAX : (CAUSAL ? mykey - off - q0 - 32 * t - 4 * h : INT_MIN);
+      const int thr_hi = W > 0 ? mykey - off + W - 1 - q0 - 32 * t - 4 * h : INT_MAX;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (8 * (i >> 2) + (i & 3) < thr) {
+        if (8 * (i >> 2) + (i & 3) < thr || 8 * (i >> 2) + (i & 3) > thr_hi) {
           const int s = (16 * t + i) / KPER;
           zero_elem(pop[s], i % KPER);
           zero_elem(dsop[s], i % KPER);
@@ -488,9 +495,13 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   const T* Kp = reinterpret_cast<const T*>(a.K) + (size_t)(wk.b * a.Hkv + wk.hk) * a.Tk * D;
   const T* Vp = reinterpret_cast<const T*>(a.V) + (size_t)(wk.b * a.Hkv + wk.hk) * a.Tk * D;
 
+  // Key tiles jt0 .. ntiles - 1 (before the window of the block's first
+  // query, or after the causal bound of its last, nothing is visible).
+  const int W = a.window;
   int kend = a.Tk;
   if (CAUSAL) kend = min(a.Tk, max(0, q0 + BQ + off));
   const int ntiles = (kend + BK - 1) / BK;
+  const int jt0 = W > 0 ? min(ntiles, max(0, q0 + off - W + 1) / BK) : 0;
 
   // A whole tile is addressed from a wave-uniform base plus per-lane offsets
   // tabulated once; in the tile holding the key end, rows past Tk are loaded
@@ -518,7 +529,7 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   constexpr int NLD = 2 * DR::PER;
 #pragma unroll
   for (int j = 0; j < AHEAD; ++j)
-    if (j < ntiles) issue(j * BK, j);
+    if (jt0 + j < ntiles) issue((jt0 + j) * BK, j);
 
   // Q^T and dO^T operands for this lane's query, L2 and D of that row.
   Op qop[NSD], gop[NSD];
@@ -571,7 +582,9 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   f32x16 st0, st1, dp0, dp1;
 
   // Some key of tile j is visible to this wave's queries.
-  auto visible = [&](int j) { return !(CAUSAL && j * BK > qw + 31 + off); };
+  auto visible = [&](int j) {
+    return !(CAUSAL && j * BK > qw + 31 + off) && !(W > 0 && j * BK + BK - 1 < qw + off - W + 1);
+  };
   auto s_phase = [&](int buf) {
     st0 = f32x16{}; st1 = f32x16{}; dp0 = f32x16{}; dp1 = f32x16{};
 #pragma unroll
@@ -596,13 +609,14 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
     }
     // Only the diagonal tiles and the ragged key end (a uniform test) clear
     // dS of the keys this query may not see; every value above is finite.
-    if ((k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off)) {
-      // Last visible key offset, less this lane half's 4 h, against the
-      // compile-time part of perm_index (no per-lane index table).
+    if ((k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off) || (W > 0 && k0 < qw + 31 + off - W + 1)) {
+      // First and last visible key offsets, less this lane half's 4 h,
+      // against the compile-time part of perm_index (no per-lane table).
       const int lim = min(a.Tk - 1, CAUSAL ? myq + off : a.Tk - 1) - k0 - 4 * h;
+      const int lo = W > 0 ? myq + off - W + 1 - k0 - 4 * h : INT_MIN;
 #pragma unroll
       for (int r = 0; r < 32; ++r)
-        if (perm_index(0, r) > lim) ds[r] = 0.f;
+        if (perm_index(0, r) > lim || perm_index(0, r) < lo) ds[r] = 0.f;
     }
     Op dsop[NSK];
 #pragma unroll
@@ -616,7 +630,7 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   };
 
   int buf = 0;                                      // buffer of tile jt
-  for (int jt = 0; jt < ntiles; ++jt) {
+  for (int jt = jt0; jt < ntiles; ++jt) {
     const bool issued = jt + AHEAD < ntiles;
     if (issued) issue((jt + AHEAD) * BK, buf + AHEAD >= NBUF ? buf + AHEAD - NBUF : buf + AHEAD);
     if (visible(jt)) {

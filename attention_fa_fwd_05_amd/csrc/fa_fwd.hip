@@ -73,9 +73,14 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
   const T* Kp = reinterpret_cast<const T*>(a.K) + (size_t)(wk.b * a.Hkv + wk.hk) * a.Tk * D;
   const T* Vp = reinterpret_cast<const T*>(a.V) + (size_t)(wk.b * a.Hkv + wk.hk) * a.Tk * D;
 
+  // Key tiles jt0 .. ntiles - 1: those before the sliding window of the
+  // block's first query, and those after the causal bound of its last, are
+  // never loaded.
+  const int W = a.window;
   int kend = a.Tk;
   if (CAUSAL) kend = min(a.Tk, max(0, q0 + BQ + off));
   const int ntiles = (kend + BK - 1) / BK;
+  const int jt0 = W > 0 ? min(ntiles, max(0, q0 + off - W + 1) / BK) : 0;
 
   // A whole tile is addressed from a wave-uniform base plus per-lane offsets
   // tabulated once; in the tile holding the key end, rows past Tk are loaded
@@ -97,7 +102,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
       dma_rows<T, D, BK, NTHR>(sV[buf], Vp, k0, a.Tk);
     }
   };
-  if (ntiles > 0) issue(0, 0);
+  if (jt0 < ntiles) issue(jt0 * BK, 0);
 
   // Q^T operands for this lane's queries qw + 32 u + n, head-dim half h.
   Op qop[QT][NSD];
@@ -130,13 +135,15 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
     for (int t = 0; t < NDT; ++t) o[u][t] = f32x16{};
   }
 
-  for (int jt = 0; jt < ntiles; ++jt) {
-    const int k0 = jt * BK, buf = jt & 1;
+  for (int jt = jt0; jt < ntiles; ++jt) {
+    const int k0 = jt * BK, buf = (jt - jt0) & 1;
     if (jt + 1 < ntiles) issue(k0 + BK, buf ^ 1);
     const T* cK = sK[buf];
     const T* cV = sV[buf];
 
-    if (!(CAUSAL && k0 > qw + 32 * QT - 1 + off)) {   // some key of the tile visible to this wave
+    // Some key of the tile is visible to this wave: not all after the causal
+    // bound of its last row, nor all before the window of its first.
+    if (!(CAUSAL && k0 > qw + 32 * QT - 1 + off) && !(W > 0 && k0 + BK - 1 < qw + off - W + 1)) {
       // S^T = K Q^T: NKT key sub-tiles x QT query tiles; each K operand feeds QT products.
       f32x16 st[QT][NKT];
 #pragma unroll
@@ -154,7 +161,8 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
       }
       sched_interleave<NKT * NSD * QT, 4 * QT, 1, QT>();
 
-      const bool need_mask = (k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off);
+      const bool need_mask = (k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off) ||
+                             (W > 0 && k0 < qw + 32 * QT - 1 + off - W + 1);
       Op pop[QT][NSK];
 #pragma unroll
       for (int u = 0; u < QT; ++u) {
@@ -163,11 +171,12 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
 #pragma unroll
         for (int r = 0; r < NE; ++r) x[r] = st[u][r >> 4][r & 15];
         if (need_mask) {
-          // Key k0 + perm_index(h, r) is visible iff perm_index(0, r) <= lim.
+          // Key k0 + perm_index(h, r) is visible iff lo <= perm_index(0, r) <= lim.
           const int lim = min(a.Tk - 1, CAUSAL ? myq + off : a.Tk - 1) - k0 - 4 * h;
+          const int lo = W > 0 ? myq + off - W + 1 - k0 - 4 * h : INT_MIN;
 #pragma unroll
           for (int r = 0; r < NE; ++r)
-            if (perm_index(0, r) > lim) x[r] = -INFINITY;
+            if (perm_index(0, r) > lim || perm_index(0, r) < lo) x[r] = -INFINITY;
         }
         float mt = wave_xor32_max(max_tree<NE>(x)) * c;   // row max, exp2 units
         const bool need = mt > m_run[u] + kTau;

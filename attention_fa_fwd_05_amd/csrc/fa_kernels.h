@@ -14,6 +14,7 @@ struct FwdArgs {
   void* O;
   float* L;
   int B, Hq, Hkv, Tq, Tk;
+  int window;         // > 0: query i sees keys j > i + Tk - Tq - window; else no window
   float scale_log2;   // scale * log2(e): scores are kept in the exp2 domain
 };
 
@@ -31,6 +32,7 @@ struct BwdArgs {
   float* Lg;          // [B*Hq][Tqp] L * log2(e); +inf for rows without keys and padding
   int B, Hq, Hkv, Tq, Tk;
   int Tqp;            // Tq rounded up to a multiple of 64
+  int window;         // as FwdArgs::window
   float scale;
   float scale_log2;
 };

@@ -32,6 +32,7 @@ class Workload:
     causal: bool
     seed: int
     sigma_qk: float = 1.0
+    window: int = 0      # > 0: sliding window of that many keys (query i sees j > i + Tk - Tq - window)
 
     @property
     def G(self) -> int:
@@ -60,6 +61,9 @@ WORKLOADS = {
         Workload("mha_bf16_T2048_d128_causal", 8, 16, 16, 2048, 2048, 128, "bf16", True, 3),
         Workload("gqa_bf16_T4096_d128_causal", 4, 32, 8, 4096, 4096, 128, "bf16", True, 4),
         Workload("gqa_bf16_T8000x8032_d128", 1, 32, 8, 8000, 8032, 128, "bf16", False, 5),
+        # the same shape under the article's sliding-window layers: 2080 keys per query
+        Workload("gqa_bf16_T8000x8032_d128_causal_window2080", 1, 32, 8, 8000, 8032, 128, "bf16", True, 6,
+                 window=2080),
     ]
 }
 

@@ -69,12 +69,16 @@ def cpu_baseline(w, inp, budget_s: float):
     rng.shuffle(groups)
     done, t0 = 0, time.perf_counter()
     for b, g in groups:
-        oa.group_forward_backward(inp.q, inp.k, inp.v, inp.do, b, g, w.causal, w.scale)
+        oa.group_forward_backward(inp.q, inp.k, inp.v, inp.do, b, g, w.causal, w.scale, window=w.window)
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     elapsed = time.perf_counter() - t0
-    f = (4.0 + 10.0) * w.G * w.Tq * w.Tk * w.d * (0.5 if w.causal else 1.0) * done
+    from attention_fa_fwd_05_amd import accounting
+    if w.window > 0:
+        f = sum(accounting.window_flops(1, w.G, w.Tq, w.Tk, w.d, w.causal, w.window)) * done
+    else:
+        f = (4.0 + 10.0) * w.G * w.Tq * w.Tk * w.d * (0.5 if w.causal else 1.0) * done
     return {"value": f / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done} of {len(groups)} (batch, K/V head) groups ({done * w.G} query heads), "
                       f"dense fp64 forward+backward, {elapsed:.1f} s"}
@@ -136,12 +140,12 @@ def main() -> int:
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        fa.forward(q, k, v, w.causal, w.scale, out=o, lse=lse)
+        fa.forward(q, k, v, w.causal, w.scale, out=o, lse=lse, window=w.window)
         if ev is not None:
             ev[1].record()
         for i, stage in enumerate((fa.STAGE_PRE, fa.STAGE_DKDV, fa.STAGE_DQ)):
             fa.backward(q, k, v, o, lse, do, w.causal, w.scale, workspace=ws, dq=dq, dk=dk, dv=dv,
-                        stages=stage)
+                        stages=stage, window=w.window)
             if ev is not None:
                 ev[2 + i].record()
 
@@ -159,13 +163,16 @@ def main() -> int:
         return sum(e[a].elapsed_time(e[b]) for e in events) / len(events)
 
     ms_fwd, ms_pre, ms_dkdv, ms_dq = avg_ms(0, 1), avg_ms(1, 2), avg_ms(2, 3), avg_ms(3, 4)
-    f_fwd, f_bwd = accounting.flops(w.B, w.Hq, w.Tq, w.Tk, w.d, w.causal)
+    if w.window > 0:
+        f_fwd, f_bwd = accounting.window_flops(w.B, w.Hq, w.Tq, w.Tk, w.d, w.causal, w.window)
+    else:
+        f_fwd, f_bwd = accounting.flops(w.B, w.Hq, w.Tq, w.Tk, w.d, w.causal)
     ms_step = elapsed / args.steps * 1e3
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
     peak = PEAK[w.dtype]
     # Each kernel's own matrix work per visible (query, key) pair: forward 4d
     # (S, PV), dK/dV pass 8d (S, dP, dV, dK), dQ pass 6d (S, dP, dQ).
-    kf = accounting.kernel_flops(w.B, w.Hq, w.Tq, w.Tk, w.d, w.causal)
+    kf = accounting.kernel_flops(w.B, w.Hq, w.Tq, w.Tk, w.d, w.causal, w.window)
     kernels = {"fwd_kernel": (kf["fwd_kernel"], ms_fwd), "dkdv_kernel": (kf["dkdv_kernel"], ms_dkdv),
                "dq_kernel": (kf["dq_kernel"], ms_dq)}
     dom = max(kernels, key=lambda n: kernels[n][1])
@@ -188,7 +195,8 @@ def main() -> int:
         "data": "synthetic (seeded N(0,1) inputs and cotangent, rounded to bf16)" if w.dtype == "bf16"
                 else "synthetic (seeded N(0,1) inputs and cotangent)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Tq": w.Tq, "Tk": w.Tk,
-                   "d": w.d, "causal": w.causal, "scale": w.scale, "parallelism": "single GPU"},
+                   "d": w.d, "causal": w.causal, "window": w.window, "scale": w.scale,
+                   "parallelism": "single GPU"},
         "pct_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),

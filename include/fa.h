@@ -137,6 +137,30 @@ int fa_bwd_stages(const void* Q, const void* K, const void* V, const void* O, co
                   int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
                   int dtype, unsigned stages, void* stream);
 
+/*
+ * Sliding-window attention ("The Autograd Memory Trap: Diagnosing a
+ * Backward-Pass OOM in Chunked Attention": its sliding-window layers attend
+ * over a much smaller key span, 2080 keys, than the full-attention layer's
+ * 8032).  With window > 0, query i sees key j only if
+ *   j > i + (Tk - Tq) - window,
+ * i.e. at most `window` keys ending at its end-aligned diagonal position; this
+ * narrows the causal bound when causal != 0 and applies on its own otherwise.
+ * window <= 0 means no window, and the calls are then identical to fa_fwd and
+ * fa_bwd_stages.  Rows left with no visible key get O = 0, L = -inf, dQ = 0.
+ * Key tiles entirely outside a query block's window are neither loaded nor
+ * computed, so the work scales with Tq * window instead of Tq * Tk.  All other
+ * arguments, layouts, ownership and error behaviour are those of fa_fwd and
+ * fa_bwd_stages; O and L passed to fa_bwd_window must come from fa_fwd_window
+ * with the same window.
+ */
+int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* L,
+                  int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int window, float scale,
+                  int dtype, void* stream);
+int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                  const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                  int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int window, float scale,
+                  int dtype, unsigned stages, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* fa_status_string(int status);
 
