@@ -6,4 +6,5 @@ libfa05.so (C ABI in include/fa.h); this package only marshals arguments.
 
 from ._binding import (EXPORTS, FA_DTYPE_BF16, FA_DTYPE_F32, LIB_PATH, STAGE_ALL,  # noqa: F401
                        STAGE_DKDV, STAGE_DQ, STAGE_PRE, STATUS, FaError, attention, backward, forward,
-                       load_library, status_string, workspace_bytes)
+                       forward_splitk, load_library, splitk_workspace_bytes, status_string,
+                       workspace_bytes)

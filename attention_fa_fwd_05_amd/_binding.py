@@ -24,8 +24,9 @@ STATUS = {
     8: "FA_ERR_ALIGNMENT", 9: "FA_ERR_TOO_LARGE", 10: "FA_ERR_HIP", 11: "FA_ERR_STAGES",
 }
 STAGE_PRE, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
-EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_window", "fa_bwd_window",
-           "fa_bwd_workspace_bytes", "fa_status_string", "fa_hip_error_string", "fa_abi_version"]
+EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_window", "fa_bwd_window", "fa_fwd_splitk",
+           "fa_fwd_splitk_workspace_bytes", "fa_bwd_workspace_bytes", "fa_status_string",
+           "fa_hip_error_string", "fa_abi_version"]
 
 _lib = None
 
@@ -67,6 +68,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                   i, i, i, i, i, i, i, i, f, i, ctypes.c_uint, vp]
     lib.fa_bwd_window.restype = i
+    lib.fa_fwd_splitk.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_splitk.restype = i
+    lib.fa_fwd_splitk_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+    lib.fa_fwd_splitk_workspace_bytes.restype = sz
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -138,6 +143,30 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
                         int(bool(causal)), scale, _dtype_code(q), _stream(q))
     if st != 0:
         raise FaError(st, "fa_fwd_window" if window > 0 else "fa_fwd")
+    return o, L
+
+
+def splitk_workspace_bytes(B, Hq, Hkv, Tq, Tk, d, dtype_code, nsplit=0) -> int:
+    return int(load_library().fa_fwd_splitk_workspace_bytes(B, Hq, Hkv, Tq, Tk, d, dtype_code, nsplit))
+
+
+def forward_splitk(q, k, v, causal: bool = False, scale: float | None = None, window: int = 0,
+                   nsplit: int = 0, workspace=None, out=None, lse=None):
+    """fa_fwd_splitk: the forward split over key slices and merged; returns (o, lse)."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    need = splitk_workspace_bytes(B, Hq, Hkv, Tq, Tk, d, code, nsplit)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = lib.fa_fwd_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), ws.data_ptr(), ws.numel(),
+                           B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), int(window), scale, code, int(nsplit),
+                           _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_fwd_splitk")
     return o, L
 
 

@@ -73,6 +73,34 @@ WsLayout ws_layout(int B, int Hq, int Tq, int d, int dtype) {
   return w;
 }
 
+// All Tq rows of a K/V group's G query heads fit one forward workgroup.
+int fwd_pack(int Hq, int Hkv, int Tq, int d, int dtype) {
+  const int nw = fa::fwd_waves(dtype == FA_DTYPE_BF16, d), G = Hq / Hkv;
+  return (G <= nw && Tq <= 32 * (nw / G)) ? 1 : 0;
+}
+
+// Key slices of a split forward: the requested count, or (nsplit <= 0) enough
+// slices for about two workgroups per compute unit, each of at least two key
+// tiles, at most 64.
+int fwd_splits(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int nsplit) {
+  if (nsplit > 0) return nsplit;
+  const int nw = fa::fwd_waves(dtype == FA_DTYPE_BF16, d), bk = fa::fwd_block_keys(dtype == FA_DTYPE_BF16, d);
+  const long long items = fwd_pack(Hq, Hkv, Tq, d, dtype) ? (long long)B * Hkv
+                                                          : (long long)((Tq + 32 * nw - 1) / (32 * nw)) * B * Hq;
+  const long long tiles = (Tk + bk - 1) / bk;
+  long long ns = items > 0 ? (512 + items - 1) / items : 1;
+  ns = ns < tiles / 2 ? ns : tiles / 2;
+  ns = ns < 64 ? ns : 64;
+  return ns < 1 ? 1 : (int)ns;
+}
+
+constexpr int kMaxSplits = 1024;
+
+size_t splitk_ws_bytes(int B, int Hq, int Tq, int d, int ns) {
+  const size_t rows = (size_t)B * Hq * Tq;
+  return align_up((size_t)ns * rows * d * 4) + align_up((size_t)ns * rows * 4);
+}
+
 }  // namespace
 
 extern "C" {
@@ -121,7 +149,47 @@ int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* L
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
   a.window = window > 0 ? window : 0;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.pack = fwd_pack(Hq, Hkv, Tq, d, dtype);
+  a.Opart = nullptr;
+  a.Lpart = nullptr;
   return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream));
+}
+
+size_t fa_fwd_splitk_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int nsplit) {
+  if (check_common(B, Hq, Hkv, Tq, Tk, d, dtype) != FA_OK) return 0;
+  const int ns = fwd_splits(B, Hq, Hkv, Tq, Tk, d, dtype, nsplit);
+  if (ns > kMaxSplits) return 0;
+  return splitk_ws_bytes(B, Hq, Tq, d, ns);
+}
+
+int fa_fwd_splitk(const void* Q, const void* K, const void* V, void* O, float* L, void* workspace,
+                  size_t workspace_bytes, int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal,
+                  int window, float scale, int dtype, int nsplit, void* stream) {
+  int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
+  if (st != FA_OK) return st;
+  const long long nq = (long long)B * Hq * Tq * d, nkv = (long long)B * Hkv * Tk * d;
+  if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, nq)) || (st = check_ptr(K, nkv)) ||
+      (st = check_ptr(V, nkv)) || (st = check_ptr(L, (long long)B * Hq * Tq)))
+    return st;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const int ns = fwd_splits(B, Hq, Hkv, Tq, Tk, d, dtype, nsplit);
+  if (ns > kMaxSplits) return FA_ERR_TOO_LARGE;
+  const size_t need = splitk_ws_bytes(B, Hq, Tq, d, ns);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (misaligned(workspace)) return FA_ERR_ALIGNMENT;
+  }
+  if (Tq == 0) return FA_OK;
+  char* wsb = static_cast<char*>(workspace);
+  fa::FwdArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
+  a.window = window > 0 ? window : 0;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.pack = fwd_pack(Hq, Hkv, Tq, d, dtype);
+  a.Opart = reinterpret_cast<float*>(wsb);
+  a.Lpart = reinterpret_cast<float*>(wsb + align_up((size_t)ns * B * Hq * Tq * d * 4));
+  return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream, ns));
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype) {

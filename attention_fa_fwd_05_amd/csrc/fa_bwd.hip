@@ -81,7 +81,7 @@ __host__ __device__ constexpr int interleave_rank(int m, int na, int nb) {
 __device__ inline void zero_elem(bf16x8& x, int e) { x[e] = (bf16)0.f; }
 __device__ inline void zero_elem(f32x4& x, int e) { x[e] = 0.f; }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   // Query blocks qb0 .. qb1 see some key of this block: none before the
   // causal bound of its first key, none past the window of its last.
   const int nqb = (a.Tq + BQ - 1) / BQ;
-  const int W = a.window;
+  const int W = WIN ? a.window : 0;               // compile-time 0 without a window
   const int qb0 = CAUSAL ? min(nqb, max(0, k0 - off) / BQ) : 0;
   const int qlast = W > 0 ? min(a.Tq - 1, k0 + BK - 1 - off + W - 1) : a.Tq - 1;   // last query seeing a key
   const int qb1 = qlast < 0 ? -1 : qlast / BQ;
@@ -461,7 +461,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 template <typename T, int D>
 constexpr int dq_waves() { return (sizeof(T) == 4 && D == 128) ? 4 : 8; }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
@@ -497,7 +497,7 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
 
   // Key tiles jt0 .. ntiles - 1 (before the window of the block's first
   // query, or after the causal bound of its last, nothing is visible).
-  const int W = a.window;
+  const int W = WIN ? a.window : 0;               // compile-time 0 without a window
   int kend = a.Tk;
   if (CAUSAL) kend = min(a.Tk, max(0, q0 + BQ + off));
   const int ntiles = (kend + BK - 1) / BK;
@@ -670,13 +670,15 @@ hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   }
   const long long kblocks = (long long)((a.Tk + 127) / 128) * a.B * a.Hkv;
   if ((stages & kStageDkDv) && kblocks > 0) {
-    hipError_t e = launch(dkdv_kernel<T, D, CAUSAL>, kblocks, stream, a);
+    hipError_t e = a.window > 0 ? launch(dkdv_kernel<T, D, CAUSAL, true>, kblocks, stream, a)
+                                : launch(dkdv_kernel<T, D, CAUSAL, false>, kblocks, stream, a);
     if (e != hipSuccess) return e;
   }
   constexpr int NW = dq_waves<T, D>();
   const long long qblocks = (long long)((a.Tq + 32 * NW - 1) / (32 * NW)) * a.B * a.Hq;
   if ((stages & kStageDq) && qblocks > 0) {
-    hipError_t e = launch<64 * NW>(dq_kernel<T, D, CAUSAL>, qblocks, stream, a);
+    hipError_t e = a.window > 0 ? launch<64 * NW>(dq_kernel<T, D, CAUSAL, true>, qblocks, stream, a)
+                                : launch<64 * NW>(dq_kernel<T, D, CAUSAL, false>, qblocks, stream, a);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

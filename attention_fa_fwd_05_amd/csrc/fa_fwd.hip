@@ -44,7 +44,7 @@ template <typename T, int D> struct FwdShape {
   static constexpr int BK = (sizeof(T) == 4 && D == 128) ? 64 : 128;
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool WIN>
 __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
@@ -61,26 +61,57 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
   __shared__ __attribute__((aligned(16))) T sK[2][BK * D];
   __shared__ __attribute__((aligned(16))) T sV[2][BK * D];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, n = lane & 31;
-  const int nqb = (a.Tq + BQ - 1) / BQ;
-  const QWork wk = qblock_work(a.B, a.Hq, a.Hkv, nqb, CAUSAL);
-  const int bh = wk.b * a.Hq + wk.hq;
-  const int q0 = wk.qb * BQ, qw = q0 + 32 * QT * w;  // this wave's rows: qw .. qw + 32 QT - 1
+  const int G = a.Hq / a.Hkv;
+  // Work of this workgroup and wave.  Usually one (b, query head, block of BQ
+  // rows), 32 rows per wave.  Packed (few query rows, as when one block of
+  // new tokens attends to a long prefix): one (b, K/V head) with all Tq rows
+  // of each of its G query heads, NW / G waves per head, so every K/V tile is
+  // loaded once for the whole group.
+  int b, hk, hq, q0, qlast, qw;
+  bool active;
+  if (a.pack) {
+    const int grp = xcd_logical_block();
+    const int wph = NW / G, r = w / wph;
+    b = grp / a.Hkv;
+    hk = grp % a.Hkv;
+    hq = hk * G + min(r, G - 1);
+    q0 = 0;
+    qlast = a.Tq - 1;
+    qw = 32 * QT * (w % wph);
+    active = r < G && qw < a.Tq;
+  } else {
+    const int nqb = (a.Tq + BQ - 1) / BQ;
+    const QWork wk = qblock_work(a.B, a.Hq, a.Hkv, nqb, CAUSAL);
+    b = wk.b;
+    hk = wk.hk;
+    hq = wk.hq;
+    q0 = wk.qb * BQ;
+    qlast = min(a.Tq - 1, q0 + BQ - 1);
+    qw = q0 + 32 * QT * w;                          // this wave's rows: qw .. qw + 32 QT - 1
+    active = qw < a.Tq;
+  }
+  const int bh = b * a.Hq + hq;
   const int off = a.Tk - a.Tq;
 
   const T* Qp = reinterpret_cast<const T*>(a.Q) + (size_t)bh * a.Tq * D;
-  const T* Kp = reinterpret_cast<const T*>(a.K) + (size_t)(wk.b * a.Hkv + wk.hk) * a.Tk * D;
-  const T* Vp = reinterpret_cast<const T*>(a.V) + (size_t)(wk.b * a.Hkv + wk.hk) * a.Tk * D;
+  const T* Kp = reinterpret_cast<const T*>(a.K) + (size_t)(b * a.Hkv + hk) * a.Tk * D;
+  const T* Vp = reinterpret_cast<const T*>(a.V) + (size_t)(b * a.Hkv + hk) * a.Tk * D;
 
   // Key tiles jt0 .. ntiles - 1: those before the sliding window of the
   // block's first query, and those after the causal bound of its last, are
-  // never loaded.
-  const int W = a.window;
+  // never loaded.  Split over keys, slice blockIdx.y takes an equal share.
+  const int W = WIN ? a.window : 0;               // compile-time 0 without a window
   int kend = a.Tk;
-  if (CAUSAL) kend = min(a.Tk, max(0, q0 + BQ + off));
-  const int ntiles = (kend + BK - 1) / BK;
-  const int jt0 = W > 0 ? min(ntiles, max(0, q0 + off - W + 1) / BK) : 0;
+  if (CAUSAL) kend = min(a.Tk, max(0, qlast + 1 + off));
+  int ntiles = (kend + BK - 1) / BK;
+  int jt0 = W > 0 ? min(ntiles, max(0, q0 + off - W + 1) / BK) : 0;
+  if (gridDim.y > 1) {
+    const int per = (ntiles - jt0 + (int)gridDim.y - 1) / (int)gridDim.y;
+    jt0 = min(ntiles, jt0 + (int)blockIdx.y * per);
+    ntiles = min(ntiles, jt0 + per);
+  }
 
   // A whole tile is addressed from a wave-uniform base plus per-lane offsets
   // tabulated once; in the tile holding the key end, rows past Tk are loaded
@@ -143,7 +174,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
 
     // Some key of the tile is visible to this wave: not all after the causal
     // bound of its last row, nor all before the window of its first.
-    if (!(CAUSAL && k0 > qw + 32 * QT - 1 + off) && !(W > 0 && k0 + BK - 1 < qw + off - W + 1)) {
+    if (active && !(CAUSAL && k0 > qw + 32 * QT - 1 + off) && !(W > 0 && k0 + BK - 1 < qw + off - W + 1)) {
       // S^T = K Q^T: NKT key sub-tiles x QT query tiles; each K operand feeds QT products.
       f32x16 st[QT][NKT];
 #pragma unroll
@@ -226,7 +257,28 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
   for (int u = 0; u < QT; ++u) {
     const int myq = qw + 32 * u + n;
     const float ltot = wave_xor32_sum(lsum[u]);
-    if (myq < a.Tq) {
+    if (a.Opart != nullptr) {                         // a key slice: fp32 partials
+      if (active && myq < a.Tq) {
+        const size_t row = (size_t)blockIdx.y * ((size_t)a.B * a.Hq * a.Tq) + (size_t)bh * a.Tq + myq;
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        float* orow = a.Opart + row * D;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int d0 = t * 32 + 8 * g + 4 * h;
+            store4(orow + d0, o[u][t][4 * g] * inv, o[u][t][4 * g + 1] * inv, o[u][t][4 * g + 2] * inv,
+                   o[u][t][4 * g + 3] * inv);
+          }
+        }
+        if (h == 0) {
+          const float mref = (m_run[u] == -INFINITY) ? 0.f : m_run[u];
+          a.Lpart[row] = ltot > 0.f ? mref * kLn2 + logf(ltot) : -INFINITY;
+        }
+      }
+      continue;
+    }
+    if (active && myq < a.Tq) {
       const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
       T* orow = reinterpret_cast<T*>(a.O) + ((size_t)bh * a.Tq + myq) * D;
 #pragma unroll
@@ -246,18 +298,73 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
   }
 }
 
-template <typename T, int D, bool CAUSAL>
-hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  using SH = FwdShape<T, D>;
-  const int nqb = (a.Tq + SH::BQ - 1) / SH::BQ;
-  const long long blocks = (long long)nqb * a.B * a.Hq;
-  if (blocks == 0) return hipSuccess;
-  return launch<64 * SH::NW>(fwd_kernel<T, D, CAUSAL>, blocks, stream, a);
+// Merge of the key slices' partials, one row per 16 lanes: with m the largest
+// slice logsumexp and w_s = exp(L_s - m), L = m + ln sum_s w_s and
+// O = sum_s w_s O_s / sum_s w_s (slices without a visible key have L_s = -inf
+// and weigh nothing; a row without any gets O = 0, L = -inf).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a, int nsplit) {
+  constexpr int EPL = D / 16;
+  const long long rows = (long long)a.B * a.Hq * a.Tq;
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int j = threadIdx.x & 15;
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, a.Lpart[s * rows + row]);
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < nsplit; ++s) {
+      const float ls = a.Lpart[s * rows + row];
+      if (ls == -INFINITY) continue;
+      const float wt = __expf(ls - m);
+      wsum += wt;
+      const float* op = a.Opart + (s * rows + row) * D + j * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(op + e);
+        acc[e] += wt * v[0];
+        acc[e + 1] += wt * v[1];
+        acc[e + 2] += wt * v[2];
+        acc[e + 3] += wt * v[3];
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  T* orow = reinterpret_cast<T*>(a.O) + row * D + j * EPL;
+#pragma unroll
+  for (int e = 0; e < EPL; e += 4) store4(orow + e, acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+  if (j == 0) a.L[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream) {
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream, int nsplit) {
+  using SH = FwdShape<T, D>;
+  const int nqb = (a.Tq + SH::BQ - 1) / SH::BQ;
+  const long long blocks = a.pack ? (long long)a.B * a.Hkv : (long long)nqb * a.B * a.Hq;
+  if (blocks == 0) return hipSuccess;
+  hipError_t e = a.window > 0 ? launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, true>, blocks, nsplit, stream, a)
+                              : launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, false>, blocks, nsplit, stream, a);
+  if (e != hipSuccess || a.Opart == nullptr) return e;
+  const long long rows = (long long)a.B * a.Hq * a.Tq;
+  return launch(fwd_merge_kernel<T, D>, (rows + 15) / 16, stream, a, nsplit);
+}
+
+int fwd_waves(int dtype_bf16, int d) {
+  return dtype_bf16 ? (d == 64 ? FwdShape<bf16, 64>::NW : FwdShape<bf16, 128>::NW)
+                    : (d == 64 ? FwdShape<float, 64>::NW : FwdShape<float, 128>::NW);
+}
+int fwd_block_keys(int dtype_bf16, int d) {
+  return dtype_bf16 ? (d == 64 ? FwdShape<bf16, 64>::BK : FwdShape<bf16, 128>::BK)
+                    : (d == 64 ? FwdShape<float, 64>::BK : FwdShape<float, 128>::BK);
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream, int nsplit) {
 #define FA_FWD_CASE(T, DD)                                                              \
-  if (d == DD) return causal ? launch_fwd_t<T, DD, true>(a, stream) : launch_fwd_t<T, DD, false>(a, stream);
+  if (d == DD)                                                                          \
+    return causal ? launch_fwd_t<T, DD, true>(a, stream, nsplit) : launch_fwd_t<T, DD, false>(a, stream, nsplit);
   if (dtype_bf16) {
     FA_FWD_CASE(bf16, 64)
     FA_FWD_CASE(bf16, 128)

@@ -16,6 +16,12 @@ struct FwdArgs {
   int B, Hq, Hkv, Tq, Tk;
   int window;         // > 0: query i sees keys j > i + Tk - Tq - window; else no window
   float scale_log2;   // scale * log2(e): scores are kept in the exp2 domain
+  int pack;           // 1: a workgroup holds all Tq rows of every query head of a K/V group
+  // Split over keys (gridDim.y > 1 or Opart set): workgroup slice s = blockIdx.y
+  // of the key tiles writes its normalised partial output and row logsumexp,
+  // fp32, to Opart[s][row][d] and Lpart[s][row]; fwd_merge combines them.
+  float* Opart;
+  float* Lpart;
 };
 
 struct BwdArgs {
@@ -47,7 +53,20 @@ inline hipError_t launch(void (*kernel)(Params...), long long blocks, hipStream_
                          0, stream);
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream);
+// Launch on a 2-D grid (blocks x ny).
+template <int THREADS = 256, typename... Params, typename... Args>
+inline hipError_t launch2(void (*kernel)(Params...), long long blocks, int ny, hipStream_t stream, Args... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3((unsigned)blocks, (unsigned)ny),
+                         dim3(THREADS), argv, 0, stream);
+}
+
+// Forward over nsplit key slices (nsplit >= 1; with Opart/Lpart set, the
+// slices' partials are merged into O and L by a second kernel).
+hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream, int nsplit = 1);
+// Waves per forward workgroup for a dtype and head dim (pack needs G <= waves).
+int fwd_waves(int dtype_bf16, int d);
+int fwd_block_keys(int dtype_bf16, int d);
 // Backward stages (bit mask): preprocess, dK/dV kernel, dQ kernel.
 constexpr unsigned kStagePre = 1u, kStageDkDv = 2u, kStageDq = 4u;
 hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int d, int causal, unsigned stages,

@@ -61,6 +61,9 @@ WORKLOADS = {
         Workload("mha_bf16_T2048_d128_causal", 8, 16, 16, 2048, 2048, 128, "bf16", True, 3),
         Workload("gqa_bf16_T4096_d128_causal", 4, 32, 8, 4096, 4096, 128, "bf16", True, 4),
         Workload("gqa_bf16_T8000x8032_d128", 1, 32, 8, 8000, 8032, 128, "bf16", False, 5),
+        # 16 blocks of 32 new positions, each against its own 8000 + 32 key prefix
+        # (the article's drafter block shape), forward only
+        Workload("gqa_bf16_B16_Tq32_Tk8032_d128_causal", 16, 32, 8, 32, 8032, 128, "bf16", True, 7),
         # the same shape under the article's sliding-window layers: 2080 keys per query
         Workload("gqa_bf16_T8000x8032_d128_causal_window2080", 1, 32, 8, 8000, 8032, 128, "bf16", True, 6,
                  window=2080),

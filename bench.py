@@ -84,6 +84,58 @@ def cpu_baseline(w, inp, budget_s: float):
                       f"dense fp64 forward+backward, {elapsed:.1f} s"}
 
 
+def decode_bench(args, fa, accounting, wl):
+    """Forward only, split over key slices and merged (fa_fwd_splitk, automatic
+    slice count), for few query rows against a long key prefix.  HBM-bound:
+    the roofline is the algorithmic bytes (Q, K, V read; O, L written) over the
+    launch pair's time against 8 TB/s."""
+    import torch
+    w = wl.WORKLOADS[args.workload or "gqa_bf16_B16_Tq32_Tk8032_d128_causal"]
+    inp = wl.make_inputs(w)
+    q, k, v, _ = wl.to_device(inp, w.dtype)
+    code = fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_F32
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.Hq, w.Tq, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, fa.splitk_workspace_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, code, 0)),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        fa.forward_splitk(q, k, v, w.causal, w.scale, window=w.window, workspace=ws, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for _ in range(args.steps):
+        step()
+    ev[1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    if w.window > 0:
+        f_fwd, _ = accounting.window_flops(w.B, w.Hq, w.Tq, w.Tk, w.d, w.causal, w.window)
+    else:
+        f_fwd = 4.0 * w.d * w.B * w.Hq * accounting.visible_pairs(w.Tq, w.Tk, w.causal, w.window)
+    e = 2 if w.dtype == "bf16" else 4
+    algo_bytes = e * (2 * w.B * w.Hq * w.Tq * w.d + 2 * w.B * w.Hkv * w.Tk * w.d) + 4 * w.B * w.Hq * w.Tq
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
+    out = {"metric": "decode-shaped forward (key-split, merged): TFLOP/s and HBM GB/s",
+           "value": round(f_fwd / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+           "data": "synthetic (seeded N(0,1) inputs, rounded to bf16)",
+           "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Tq": w.Tq, "Tk": w.Tk,
+                      "d": w.d, "causal": w.causal, "window": w.window, "nsplit": "auto",
+                      "workspace_bytes": ws.numel()},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                        "frac": round(gbs / 8000.0, 4), "traffic": None,
+                        "algorithmic_bytes_per_launch": algo_bytes, "avg_launch_ms": round(ms, 4)}}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def copy_calibration(nbytes: int, reps: int):
     """A plain device copy of known size, for scaling rocprofv3 byte counters."""
     import torch
@@ -103,6 +155,8 @@ def main() -> int:
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the CPU oracle baseline (0 disables it)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the key-split forward on a decode-shaped workload instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run only a device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -126,8 +180,10 @@ def main() -> int:
         copy_calibration(args.copy_calibration, max(1, args.steps))
         return 0
 
-    w = wl.WORKLOADS[args.workload or wl.HEADLINE]
     fa.load_library()
+    if args.decode:
+        return decode_bench(args, fa, accounting, wl)
+    w = wl.WORKLOADS[args.workload or wl.HEADLINE]
     inp = wl.make_inputs(w)
     q, k, v, do = wl.to_device(inp, w.dtype)
     code = fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_F32

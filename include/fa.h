@@ -161,6 +161,31 @@ int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, co
                   int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int window, float scale,
                   int dtype, unsigned stages, void* stream);
 
+/*
+ * Forward split over the keys, for few query rows against many keys: one
+ * block of new tokens attending to a long prefix ("The Autograd Memory Trap",
+ * section "The Scene": 32 new positions against an 8000-key prefix, 8032 keys
+ * in all; inference stashes nothing for a backward, "What Ordinary Autograd
+ * Saves", section "Why this is FlashAttention's second idea").  The key tiles
+ * each workgroup would visit are divided into `nsplit` slices run side by
+ * side; slice s writes its normalised partial output O_s and row logsumexp L_s
+ * (float32) to the workspace, and a merge writes
+ *   L = ln sum_s exp(L_s),  O = sum_s exp(L_s - L) O_s,
+ * which is exactly the attention over the union of the slices (a row whose
+ * keys all lie outside a slice has L_s = -inf there).  Results equal fa_fwd /
+ * fa_fwd_window up to rounding.  nsplit <= 0 picks a count that fills the GPU
+ * (about two workgroups per compute unit, at least two key tiles per slice,
+ * at most 64).  The workspace (device memory, 16-byte aligned, at least
+ * fa_fwd_splitk_workspace_bytes for the same nsplit) holds nsplit * B * Hq *
+ * Tq * (d + 1) floats; it carries nothing between calls.  Errors as fa_fwd,
+ * plus FA_ERR_WORKSPACE and FA_ERR_TOO_LARGE (more than 1024 slices);
+ * fa_fwd_splitk_workspace_bytes returns 0 for invalid arguments.
+ */
+size_t fa_fwd_splitk_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int nsplit);
+int fa_fwd_splitk(const void* Q, const void* K, const void* V, void* O, float* L, void* workspace,
+                  size_t workspace_bytes, int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal,
+                  int window, float scale, int dtype, int nsplit, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* fa_status_string(int status);
 
