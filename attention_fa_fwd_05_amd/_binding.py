@@ -25,8 +25,8 @@ STATUS = {
 }
 STAGE_PRE, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
 EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_window", "fa_bwd_window", "fa_fwd_splitk",
-           "fa_fwd_splitk_workspace_bytes", "fa_bwd_workspace_bytes", "fa_status_string",
-           "fa_hip_error_string", "fa_abi_version"]
+           "fa_fwd_splitk_workspace_bytes", "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_workspace_bytes",
+           "fa_status_string", "fa_hip_error_string", "fa_abi_version"]
 
 _lib = None
 
@@ -72,6 +72,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_splitk.restype = i
     lib.fa_fwd_splitk_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
     lib.fa_fwd_splitk_workspace_bytes.restype = sz
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_varlen.restype = i
+    lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp,
+                                  i, i, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_varlen.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -168,6 +173,63 @@ def forward_splitk(q, k, v, causal: bool = False, scale: float | None = None, wi
     if st != 0:
         raise FaError(st, "fa_fwd_splitk")
     return o, L
+
+
+def _varlen_shapes(q, k, v, cu_q, cu_k):
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("varlen q, k, v must be [H, total, d]")
+    Hq, total_q, d = q.shape
+    Hkv, total_k, dk = k.shape
+    if dk != d or tuple(v.shape) != (Hkv, total_k, d):
+        raise ValueError(f"inconsistent shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    for t in (q, k, v):
+        if not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must be contiguous and share dtype and device")
+    for c in (cu_q, cu_k):
+        if c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous() or c.device != q.device:
+            raise ValueError("cu_seqlens must be contiguous int32 [B + 1] on q's device")
+    if cu_q.numel() != cu_k.numel() or cu_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 >= 2 offsets")
+    return cu_q.numel() - 1, Hq, Hkv, total_q, total_k, d
+
+
+def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                   causal: bool = False, scale: float | None = None, window: int = 0, out=None, lse=None):
+    """fa_fwd_varlen: q [Hq, total_q, d], k, v [Hkv, total_k, d] packed head-major; returns
+    (o like q, lse float32 [Hq, total_q])."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, total_q, total_k, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    L = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), cu_seqlens_q.data_ptr(),
+                           cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q),
+                           int(max_seqlen_k), d, int(bool(causal)), int(window), scale, _dtype_code(q), _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_fwd_varlen")
+    return o, L
+
+
+def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    causal: bool = False, scale: float | None = None, window: int = 0, workspace=None):
+    """fa_bwd_varlen: returns (dq, dk, dv) like q, k, v (packed head-major)."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, total_q, total_k, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    need = workspace_bytes(B, Hq, Hkv, int(max_seqlen_q), int(max_seqlen_k), d, code)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = lib.fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                           _ptr(dv), ws.data_ptr(), ws.numel(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                           B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), d,
+                           int(bool(causal)), int(window), scale, code, _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_bwd_varlen")
+    return dq, dk, dv
 
 
 def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,

@@ -96,6 +96,24 @@ int fwd_splits(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int nsp
 
 constexpr int kMaxSplits = 1024;
 
+// Variable-length batch arguments: offsets present and 4-byte aligned, sizes
+// non-negative, the longest sequence within the totals.  The offsets
+// themselves live in device memory and are not read here; the kernels clamp
+// each sequence into the packed tensors.
+int check_varlen(const int* cu_q, const int* cu_k, int total_q, int total_k, int max_q, int max_k) {
+  if (cu_q == nullptr || cu_k == nullptr) return FA_ERR_NULL_PTR;
+  if ((reinterpret_cast<uintptr_t>(cu_q) & 3u) || (reinterpret_cast<uintptr_t>(cu_k) & 3u)) return FA_ERR_ALIGNMENT;
+  if (total_q < 0 || total_k < 0 || max_q < 0 || max_k < 0) return FA_ERR_BAD_SHAPE;
+  if (max_q > total_q || max_k > total_k) return FA_ERR_BAD_SHAPE;
+  if (total_q > kMaxSeq * 64 || total_k > kMaxSeq * 64) return FA_ERR_TOO_LARGE;
+  return FA_OK;
+}
+
+int bwd_core(const void* Q, const void* K, const void* V, const void* O, const float* L,
+             const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+             const int* cu_q, const int* cu_k, int B, int Hq, int Hkv, int total_q, int total_k, int Tq,
+             int Tk, int d, int causal, int window, float scale, int dtype, unsigned stages, void* stream);
+
 size_t splitk_ws_bytes(int B, int Hq, int Tq, int d, int ns) {
   const size_t rows = (size_t)B * Hq * Tq;
   return align_up((size_t)ns * rows * d * 4) + align_up((size_t)ns * rows * 4);
@@ -152,6 +170,37 @@ int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* L
   a.pack = fwd_pack(Hq, Hkv, Tq, d, dtype);
   a.Opart = nullptr;
   a.Lpart = nullptr;
+  a.cu_q = a.cu_k = nullptr;
+  a.total_q = a.total_k = 0;
+  return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream));
+}
+
+int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L, const int* cu_seqlens_q,
+                  const int* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                  int max_seqlen_k, int d, int causal, int window, float scale, int dtype, void* stream) {
+  int st = check_common(B, Hq, Hkv, max_seqlen_q, max_seqlen_k, d, dtype);
+  if (st != FA_OK) return st;
+  if ((st = check_varlen(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max_seqlen_k)) != FA_OK)
+    return st;
+  const long long nq = (long long)Hq * total_q * d, nkv = (long long)Hkv * total_k * d;
+  if (nq > kMaxElems || nkv > kMaxElems) return FA_ERR_TOO_LARGE;
+  if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, nq)) || (st = check_ptr(K, nkv)) ||
+      (st = check_ptr(V, nkv)) || (st = check_ptr(L, (long long)Hq * total_q)))
+    return st;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (max_seqlen_q == 0 || total_q == 0) return FA_OK;
+  fa::FwdArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = max_seqlen_q; a.Tk = max_seqlen_k;
+  a.window = window > 0 ? window : 0;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.pack = fwd_pack(Hq, Hkv, max_seqlen_q, d, dtype);
+  a.Opart = nullptr;
+  a.Lpart = nullptr;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
   return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream));
 }
 
@@ -187,6 +236,8 @@ int fa_fwd_splitk(const void* Q, const void* K, const void* V, void* O, float* L
   a.window = window > 0 ? window : 0;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.pack = fwd_pack(Hq, Hkv, Tq, d, dtype);
+  a.cu_q = a.cu_k = nullptr;
+  a.total_q = a.total_k = 0;
   a.Opart = reinterpret_cast<float*>(wsb);
   a.Lpart = reinterpret_cast<float*>(wsb + align_up((size_t)ns * B * Hq * Tq * d * 4));
   return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream, ns));
@@ -217,10 +268,37 @@ int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, co
                   const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
                   int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int window, float scale,
                   int dtype, unsigned stages, void* stream) {
+  return bwd_core(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, nullptr, nullptr, B, Hq, Hkv,
+                  0, 0, Tq, Tk, d, causal, window, scale, dtype, stages, stream);
+}
+
+int fa_bwd_varlen(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                  const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv, int total_q,
+                  int total_k, int max_seqlen_q, int max_seqlen_k, int d, int causal, int window,
+                  float scale, int dtype, void* stream) {
+  int st = check_varlen(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max_seqlen_k);
+  if (st != FA_OK) return st;
+  return bwd_core(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, cu_seqlens_q, cu_seqlens_k, B,
+                  Hq, Hkv, total_q, total_k, max_seqlen_q, max_seqlen_k, d, causal, window, scale, dtype,
+                  FA_BWD_STAGE_ALL, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int bwd_core(const void* Q, const void* K, const void* V, const void* O, const float* L,
+             const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+             const int* cu_q, const int* cu_k, int B, int Hq, int Hkv, int total_q, int total_k, int Tq,
+             int Tk, int d, int causal, int window, float scale, int dtype, unsigned stages, void* stream) {
   int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
   if (st != FA_OK) return st;
-  const long long nq = (long long)B * Hq * Tq * d, nkv = (long long)B * Hkv * Tk * d;
-  const long long rows = (long long)B * Hq * Tq;
+  const bool varlen = cu_q != nullptr;
+  const long long nq = varlen ? (long long)Hq * total_q * d : (long long)B * Hq * Tq * d;
+  const long long nkv = varlen ? (long long)Hkv * total_k * d : (long long)B * Hkv * Tk * d;
+  if (nq > kMaxElems || nkv > kMaxElems) return FA_ERR_TOO_LARGE;
+  const long long rows = varlen ? (long long)Hq * total_q : (long long)B * Hq * Tq;
   if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, nq)) || (st = check_ptr(dO, nq)) ||
       (st = check_ptr(dQ, nq)) || (st = check_ptr(K, nkv)) || (st = check_ptr(V, nkv)) ||
       (st = check_ptr(dK, nkv)) || (st = check_ptr(dV, nkv)) || (st = check_ptr(L, rows)))
@@ -233,6 +311,7 @@ int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, co
     if (misaligned(workspace)) return FA_ERR_ALIGNMENT;
   }
   if (Tq == 0 && Tk == 0) return FA_OK;
+  if (varlen && total_q == 0 && total_k == 0) return FA_OK;
   char* wsb = static_cast<char*>(workspace);
   fa::BwdArgs a;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L; a.dO = dO;
@@ -242,9 +321,13 @@ int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, co
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
   a.Tqp = padded_rows(Tq);
   a.window = window > 0 ? window : 0;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   return hip_status(fa::launch_bwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, stages, (hipStream_t)stream));
 }
 
-}  // extern "C"
+}  // namespace

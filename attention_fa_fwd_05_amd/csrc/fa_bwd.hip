@@ -34,10 +34,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   const long long prows = (long long)a.B * a.Hq * a.Tqp;
   const long long prow = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int j = threadIdx.x & 15;
-  const long long bh = prow / a.Tqp;
-  const int q = (int)(prow - bh * a.Tqp);
-  const bool ok = prow < prows && q < a.Tq;        // a real query row (else padding)
-  const long long row = bh * a.Tq + q;
+  // 32-bit index arithmetic: B * Hq * Tqp is bounded by the grid limits.  A
+  // workgroup's 16 rows lie in one (b, h), since Tqp is a multiple of 64.
+  const int prow32 = (int)min(prow, prows - 1);
+  const int bh = prow32 / a.Tqp;
+  const int q = prow32 - bh * a.Tqp;
+  const int b = bh / a.Hq, hq = bh - b * a.Hq;
+  const SeqView sq = seq_view(a, b);
+  const bool ok = prow < prows && q < sq.Tq;       // a real query row (else padding)
+  const long long row = (long long)sq.q_row(hq) + q;
   float acc = 0.f;
   if (ok) {
     const T* o = reinterpret_cast<const T*>(a.O) + row * D + j * EPL;
@@ -130,15 +135,22 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   const int h = lane >> 5, n = lane & 31;
   const int nkb = (a.Tk + BK - 1) / BK;
   const KWork wk = kblock_work(a, nkb);
-  const int bhk = wk.b * a.Hkv + wk.hk, G = a.Hq / a.Hkv;
+  const int G = a.Hq / a.Hkv;
   const int k0 = wk.kb * BK, kw = k0 + 32 * w, mykey = kw + n;
-  const int off = a.Tk - a.Tq;
+  // This workgroup's sequence (a variable-length batch has its own lengths
+  // and rows; the grid covers the longest).  No key of it here: leave before
+  // any barrier (uniform).
+  const SeqView sq = seq_view(a, wk.b);
+  const int Tq = sq.Tq, Tk = sq.Tk;
+  if (k0 >= Tk) return;
+  const size_t krow0 = sq.k_row(wk.hk);  // row of key 0 of (b, hk) in K, V, dK, dV
+  const int off = Tk - Tq;
   const float c = a.scale_log2;
-  const bool key_ok = mykey < a.Tk;
-  const bool ragged = k0 + BK > a.Tk;               // uniform: this block holds the key end
+  const bool key_ok = mykey < Tk;
+  const bool ragged = k0 + BK > Tk;                 // uniform: this block holds the key end
 
-  const T* Kp = reinterpret_cast<const T*>(a.K) + (size_t)bhk * a.Tk * D;
-  const T* Vp = reinterpret_cast<const T*>(a.V) + (size_t)bhk * a.Tk * D;
+  const T* Kp = reinterpret_cast<const T*>(a.K) + krow0 * D;
+  const T* Vp = reinterpret_cast<const T*>(a.V) + krow0 * D;
 
   // Work list: every (query block that can see a key of this block, query
   // head of the group), query blocks from the last one down and heads
@@ -148,21 +160,22 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   // block.
   // Query blocks qb0 .. qb1 see some key of this block: none before the
   // causal bound of its first key, none past the window of its last.
-  const int nqb = (a.Tq + BQ - 1) / BQ;
+  const int nqb = (Tq + BQ - 1) / BQ;
   const int W = WIN ? a.window : 0;               // compile-time 0 without a window
   const int qb0 = CAUSAL ? min(nqb, max(0, k0 - off) / BQ) : 0;
-  const int qlast = W > 0 ? min(a.Tq - 1, k0 + BK - 1 - off + W - 1) : a.Tq - 1;   // last query seeing a key
+  const int qlast = W > 0 ? min(Tq - 1, k0 + BK - 1 - off + W - 1) : Tq - 1;   // last query seeing a key
   const int qb1 = qlast < 0 ? -1 : qlast / BQ;
   const int total = G * max(0, qb1 - qb0 + 1);
   auto item_q0 = [&](int it) { return (qb1 - it / G) * BQ; };
-  auto item_bh = [&](int it) { return wk.b * a.Hq + wk.hk * G + it % G; };
+  auto item_bh = [&](int it) { return wk.b * a.Hq + wk.hk * G + it % G; };   // workspace rows (padded)
+  auto item_qrow = [&](int it) { return sq.q_row(wk.hk * G + it % G); };   // Q, dO rows
   // L2 and D rows are padded to 64 per head, so a 64-row window always loads.
   auto issue = [&](int it, int buf) {
     const int bh = item_bh(it);
     const int q0 = item_q0(it);
-    const size_t qbase = (size_t)bh * a.Tq * D;
-    dma_rows<T, D, BQ, 256>(sQ[buf], reinterpret_cast<const T*>(a.Q) + qbase, q0, a.Tq);
-    dma_rows<T, D, BQ, 256>(sdO[buf], reinterpret_cast<const T*>(a.dO) + qbase, q0, a.Tq);
+    const size_t qbase = item_qrow(it) * D;
+    dma_rows<T, D, BQ, 256>(sQ[buf], reinterpret_cast<const T*>(a.Q) + qbase, q0, Tq);
+    dma_rows<T, D, BQ, 256>(sdO[buf], reinterpret_cast<const T*>(a.dO) + qbase, q0, Tq);
     if (w == 0) dma_floats64(sL[buf], a.Lg + (size_t)bh * a.Tqp + q0);
     if (w == 1) dma_floats64(sD[buf], a.Dvec + (size_t)bh * a.Tqp + q0);
   };
@@ -190,12 +203,12 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     Src r;
     const int bh = item_bh(it);
     r.q0 = item_q0(it);
-    const size_t row = (size_t)bh * a.Tq + r.q0;
+    const size_t row = item_qrow(it) + r.q0;
     r.q = reinterpret_cast<const char*>(a.Q) + row * D * sizeof(T);
     r.o = reinterpret_cast<const char*>(a.dO) + row * D * sizeof(T);
     r.l = a.Lg + (size_t)bh * a.Tqp + r.q0;
     r.d = a.Dvec + (size_t)bh * a.Tqp + r.q0;
-    r.whole = r.q0 + BQ <= a.Tq;
+    r.whole = r.q0 + BQ <= Tq;
     return r;
   };
   auto dma_piece = [&](const Src& src, int buf, int j) {
@@ -207,7 +220,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
         dma16s(base, src_off[i], lds_addr(tile) + DR::lds_off(i));
       } else {                                      // ragged end of the queries: clamped rows
         const T* g = reinterpret_cast<const T*>(base) - (size_t)src.q0 * D;
-        DR::one(tile, g, src.q0, a.Tq, i);
+        DR::one(tile, g, src.q0, Tq, i);
       }
     } else {
       if (w == 0) dma_floats64(sL[buf], src.l);
@@ -440,8 +453,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   }
 
   if (key_ok) {
-    T* dKr = reinterpret_cast<T*>(a.dK) + ((size_t)bhk * a.Tk + mykey) * D;
-    T* dVr = reinterpret_cast<T*>(a.dV) + ((size_t)bhk * a.Tk + mykey) * D;
+    T* dKr = reinterpret_cast<T*>(a.dK) + (krow0 + mykey) * D;
+    T* dVr = reinterpret_cast<T*>(a.dV) + (krow0 + mykey) * D;
     const float sc = a.scale;
 #pragma unroll
     for (int t = 0; t < NDT; ++t) {
@@ -485,21 +498,28 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   const int h = lane >> 5, n = lane & 31;
   const int nqb = (a.Tq + BQ - 1) / BQ;
   const QWork wk = qblock_work(a.B, a.Hq, a.Hkv, nqb, CAUSAL);
-  const int bh = wk.b * a.Hq + wk.hq;
+  const int bh = wk.b * a.Hq + wk.hq;               // workspace rows (padded per head)
   const int q0 = wk.qb * BQ, qw = q0 + 32 * w, myq = qw + n;
-  const int off = a.Tk - a.Tq;
-  const bool q_ok = myq < a.Tq;
+  // This workgroup's sequence (its own lengths and rows in a variable-length
+  // batch).  No query of it here: leave before any barrier (uniform).
+  const SeqView sq = seq_view(a, wk.b);
+  const int Tq = sq.Tq, Tk = sq.Tk;
+  if (q0 >= Tq) return;
+  const size_t qrow0 = sq.q_row(wk.hq);  // row of query 0 of (b, hq) in Q, dO, dQ
+  const size_t krow0 = sq.k_row(wk.hk);
+  const int off = Tk - Tq;
+  const bool q_ok = myq < Tq;
 
-  const T* Qp = reinterpret_cast<const T*>(a.Q) + (size_t)bh * a.Tq * D;
-  const T* dOp = reinterpret_cast<const T*>(a.dO) + (size_t)bh * a.Tq * D;
-  const T* Kp = reinterpret_cast<const T*>(a.K) + (size_t)(wk.b * a.Hkv + wk.hk) * a.Tk * D;
-  const T* Vp = reinterpret_cast<const T*>(a.V) + (size_t)(wk.b * a.Hkv + wk.hk) * a.Tk * D;
+  const T* Qp = reinterpret_cast<const T*>(a.Q) + qrow0 * D;
+  const T* dOp = reinterpret_cast<const T*>(a.dO) + qrow0 * D;
+  const T* Kp = reinterpret_cast<const T*>(a.K) + krow0 * D;
+  const T* Vp = reinterpret_cast<const T*>(a.V) + krow0 * D;
 
   // Key tiles jt0 .. ntiles - 1 (before the window of the block's first
   // query, or after the causal bound of its last, nothing is visible).
   const int W = WIN ? a.window : 0;               // compile-time 0 without a window
-  int kend = a.Tk;
-  if (CAUSAL) kend = min(a.Tk, max(0, q0 + BQ + off));
+  int kend = Tk;
+  if (CAUSAL) kend = min(Tk, max(0, q0 + BQ + off));
   const int ntiles = (kend + BK - 1) / BK;
   const int jt0 = W > 0 ? min(ntiles, max(0, q0 + off - W + 1) / BK) : 0;
 
@@ -513,7 +533,7 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   auto issue = [&](int k0, int buf) {
     T* tk = sKV[buf];
     T* tv = sKV[buf] + TILE;
-    if (k0 + BK <= a.Tk) {
+    if (k0 + BK <= Tk) {
       const T* kb = Kp + (size_t)k0 * D;
       const T* vb = Vp + (size_t)k0 * D;
 #pragma unroll
@@ -521,8 +541,8 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
 #pragma unroll
       for (int i = 0; i < DR::PER; ++i) dma16s(vb, src_off[i], lds_addr(tv) + DR::lds_off(i));
     } else {
-      dma_rows<T, D, BK, NTHR>(tk, Kp, k0, a.Tk);
-      dma_rows<T, D, BK, NTHR>(tv, Vp, k0, a.Tk);
+      dma_rows<T, D, BK, NTHR>(tk, Kp, k0, Tk);
+      dma_rows<T, D, BK, NTHR>(tv, Vp, k0, Tk);
     }
   };
   // Direct-load instructions per wave for one tile (K and V).
@@ -609,10 +629,10 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
     }
     // Only the diagonal tiles and the ragged key end (a uniform test) clear
     // dS of the keys this query may not see; every value above is finite.
-    if ((k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off) || (W > 0 && k0 < qw + 31 + off - W + 1)) {
+    if ((k0 + BK > Tk) || (CAUSAL && k0 + BK - 1 > qw + off) || (W > 0 && k0 < qw + 31 + off - W + 1)) {
       // First and last visible key offsets, less this lane half's 4 h,
       // against the compile-time part of perm_index (no per-lane table).
-      const int lim = min(a.Tk - 1, CAUSAL ? myq + off : a.Tk - 1) - k0 - 4 * h;
+      const int lim = min(Tk - 1, CAUSAL ? myq + off : Tk - 1) - k0 - 4 * h;
       const int lo = W > 0 ? myq + off - W + 1 - k0 - 4 * h : INT_MIN;
 #pragma unroll
       for (int r = 0; r < 32; ++r)
@@ -647,7 +667,7 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   }
 
   if (q_ok) {
-    T* qrow = reinterpret_cast<T*>(a.dQ) + ((size_t)bh * a.Tq + myq) * D;
+    T* qrow = reinterpret_cast<T*>(a.dQ) + (qrow0 + myq) * D;
     const float sc = a.scale;
 #pragma unroll
     for (int t = 0; t < NDT; ++t) {

@@ -92,19 +92,27 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
     qw = q0 + 32 * QT * w;                          // this wave's rows: qw .. qw + 32 QT - 1
     active = qw < a.Tq;
   }
-  const int bh = b * a.Hq + hq;
-  const int off = a.Tk - a.Tq;
+  // This workgroup's sequence (a variable-length batch: its own lengths and
+  // rows; the grid covers the longest).  Nothing of it here: leave before
+  // any barrier (uniform).
+  const SeqView sq = seq_view(a, b);
+  const int Tq = sq.Tq, Tk = sq.Tk;
+  if (q0 >= Tq) return;
+  active = active && qw < Tq;
+  qlast = min(qlast, Tq - 1);
+  const size_t qrow0 = sq.q_row(hq);       // row of query 0 of (b, hq) in Q, O, L
+  const int off = Tk - Tq;
 
-  const T* Qp = reinterpret_cast<const T*>(a.Q) + (size_t)bh * a.Tq * D;
-  const T* Kp = reinterpret_cast<const T*>(a.K) + (size_t)(b * a.Hkv + hk) * a.Tk * D;
-  const T* Vp = reinterpret_cast<const T*>(a.V) + (size_t)(b * a.Hkv + hk) * a.Tk * D;
+  const T* Qp = reinterpret_cast<const T*>(a.Q) + qrow0 * D;
+  const T* Kp = reinterpret_cast<const T*>(a.K) + sq.k_row(hk) * D;
+  const T* Vp = reinterpret_cast<const T*>(a.V) + sq.k_row(hk) * D;
 
   // Key tiles jt0 .. ntiles - 1: those before the sliding window of the
   // block's first query, and those after the causal bound of its last, are
   // never loaded.  Split over keys, slice blockIdx.y takes an equal share.
   const int W = WIN ? a.window : 0;               // compile-time 0 without a window
-  int kend = a.Tk;
-  if (CAUSAL) kend = min(a.Tk, max(0, qlast + 1 + off));
+  int kend = Tk;
+  if (CAUSAL) kend = min(Tk, max(0, qlast + 1 + off));
   int ntiles = (kend + BK - 1) / BK;
   int jt0 = W > 0 ? min(ntiles, max(0, q0 + off - W + 1) / BK) : 0;
   if (gridDim.y > 1) {
@@ -121,7 +129,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
 #pragma unroll
   for (int i = 0; i < DR::PER; ++i) src_off[i] = DR::src_off(i);
   auto issue = [&](int k0, int buf) {
-    if (k0 + BK <= a.Tk) {
+    if (k0 + BK <= Tk) {
       const T* kb = Kp + (size_t)k0 * D;
       const T* vb = Vp + (size_t)k0 * D;
 #pragma unroll
@@ -129,8 +137,8 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
 #pragma unroll
       for (int i = 0; i < DR::PER; ++i) dma16s(vb, src_off[i], lds_addr(sV[buf]) + DR::lds_off(i));
     } else {
-      dma_rows<T, D, BK, NTHR>(sK[buf], Kp, k0, a.Tk);
-      dma_rows<T, D, BK, NTHR>(sV[buf], Vp, k0, a.Tk);
+      dma_rows<T, D, BK, NTHR>(sK[buf], Kp, k0, Tk);
+      dma_rows<T, D, BK, NTHR>(sV[buf], Vp, k0, Tk);
     }
   };
   if (jt0 < ntiles) issue(jt0 * BK, 0);
@@ -140,7 +148,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
 #pragma unroll
   for (int u = 0; u < QT; ++u) {
     const int q = qw + 32 * u + n;
-    const bool ok = q < a.Tq;
+    const bool ok = q < Tq;
     const T* qrow = Qp + (size_t)(ok ? q : 0) * D + h * (D / 2);
 #pragma unroll
     for (int s = 0; s < NSD; ++s) {
@@ -192,7 +200,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
       }
       sched_interleave<NKT * NSD * QT, 4 * QT, 1, QT>();
 
-      const bool need_mask = (k0 + BK > a.Tk) || (CAUSAL && k0 + BK - 1 > qw + off) ||
+      const bool need_mask = (k0 + BK > Tk) || (CAUSAL && k0 + BK - 1 > qw + off) ||
                              (W > 0 && k0 < qw + 32 * QT - 1 + off - W + 1);
       Op pop[QT][NSK];
 #pragma unroll
@@ -203,7 +211,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
         for (int r = 0; r < NE; ++r) x[r] = st[u][r >> 4][r & 15];
         if (need_mask) {
           // Key k0 + perm_index(h, r) is visible iff lo <= perm_index(0, r) <= lim.
-          const int lim = min(a.Tk - 1, CAUSAL ? myq + off : a.Tk - 1) - k0 - 4 * h;
+          const int lim = min(Tk - 1, CAUSAL ? myq + off : Tk - 1) - k0 - 4 * h;
           const int lo = W > 0 ? myq + off - W + 1 - k0 - 4 * h : INT_MIN;
 #pragma unroll
           for (int r = 0; r < NE; ++r)
@@ -258,8 +266,9 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
     const int myq = qw + 32 * u + n;
     const float ltot = wave_xor32_sum(lsum[u]);
     if (a.Opart != nullptr) {                         // a key slice: fp32 partials
-      if (active && myq < a.Tq) {
-        const size_t row = (size_t)blockIdx.y * ((size_t)a.B * a.Hq * a.Tq) + (size_t)bh * a.Tq + myq;
+      if (active && myq < Tq) {
+        const size_t rows_all = (a.cu_q != nullptr) ? (size_t)a.Hq * a.total_q : (size_t)a.B * a.Hq * a.Tq;
+        const size_t row = (size_t)blockIdx.y * rows_all + qrow0 + myq;
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
         float* orow = a.Opart + row * D;
 #pragma unroll
@@ -278,9 +287,9 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
       }
       continue;
     }
-    if (active && myq < a.Tq) {
+    if (active && myq < Tq) {
       const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-      T* orow = reinterpret_cast<T*>(a.O) + ((size_t)bh * a.Tq + myq) * D;
+      T* orow = reinterpret_cast<T*>(a.O) + (qrow0 + myq) * D;
 #pragma unroll
       for (int t = 0; t < NDT; ++t) {
 #pragma unroll
@@ -292,7 +301,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
       }
       if (h == 0) {
         const float mref = (m_run[u] == -INFINITY) ? 0.f : m_run[u];
-        a.L[(size_t)bh * a.Tq + myq] = ltot > 0.f ? mref * kLn2 + logf(ltot) : -INFINITY;
+        a.L[qrow0 + myq] = ltot > 0.f ? mref * kLn2 + logf(ltot) : -INFINITY;
       }
     }
   }
@@ -305,7 +314,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a, int nsplit) {
   constexpr int EPL = D / 16;
-  const long long rows = (long long)a.B * a.Hq * a.Tq;
+  const long long rows = a.cu_q ? (long long)a.Hq * a.total_q : (long long)a.B * a.Hq * a.Tq;
   const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int j = threadIdx.x & 15;
   if (row >= rows) return;
@@ -348,7 +357,8 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream, int nsplit) {
   hipError_t e = a.window > 0 ? launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, true>, blocks, nsplit, stream, a)
                               : launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, false>, blocks, nsplit, stream, a);
   if (e != hipSuccess || a.Opart == nullptr) return e;
-  const long long rows = (long long)a.B * a.Hq * a.Tq;
+  const long long rows = a.cu_q ? (long long)a.Hq * a.total_q : (long long)a.B * a.Hq * a.Tq;
+  if (rows == 0) return hipSuccess;
   return launch(fwd_merge_kernel<T, D>, (rows + 15) / 16, stream, a, nsplit);
 }
 

@@ -22,7 +22,51 @@ struct FwdArgs {
   // fp32, to Opart[s][row][d] and Lpart[s][row]; fwd_merge combines them.
   float* Opart;
   float* Lpart;
+  // Variable-length batch (cu_q != nullptr): sequence b has the rows
+  // cu_q[b] .. cu_q[b+1] - 1 of every query head and cu_k[b] .. cu_k[b+1] - 1
+  // of every K/V head, tensors packed head-major ([H][total][d], L [Hq][total_q]);
+  // Tq and Tk then hold the longest sequence (the grid's extent).
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
 };
+
+// One sequence of a batch: its lengths, and where its rows sit.  Row 0 of
+// query head hq is q_base + hq * q_hstride (fixed layout: b * Hq * Tq and Tq;
+// packed variable-length layout: the sequence's offset and total_q), and
+// likewise for keys; all computed once, so each use is one multiply-add.
+struct SeqView {
+  int Tq, Tk;
+  size_t q_base, q_hstride, k_base, k_hstride;
+  __device__ size_t q_row(int hq) const { return q_base + (size_t)hq * q_hstride; }
+  __device__ size_t k_row(int hk) const { return k_base + (size_t)hk * k_hstride; }
+};
+template <typename A>
+__device__ inline SeqView seq_view(const A& a, int b) {
+  SeqView v;
+  if (a.cu_q != nullptr) {
+    // Clamped so that even inconsistent offsets keep every access inside the
+    // packed tensors: 0 <= start, start + length <= total, length <= the
+    // longest sequence the grid was sized for.
+    const int q0 = __builtin_amdgcn_readfirstlane(a.cu_q[b]), q1 = __builtin_amdgcn_readfirstlane(a.cu_q[b + 1]);
+    const int k0 = __builtin_amdgcn_readfirstlane(a.cu_k[b]), k1 = __builtin_amdgcn_readfirstlane(a.cu_k[b + 1]);
+    const int qs = min(max(q0, 0), a.total_q), ks = min(max(k0, 0), a.total_k);
+    v.Tq = min(min(max(q1 - q0, 0), a.Tq), a.total_q - qs);
+    v.Tk = min(min(max(k1 - k0, 0), a.Tk), a.total_k - ks);
+    v.q_base = qs;
+    v.q_hstride = a.total_q;
+    v.k_base = ks;
+    v.k_hstride = a.total_k;
+  } else {
+    v.Tq = a.Tq;
+    v.Tk = a.Tk;
+    v.q_base = (size_t)b * a.Hq * a.Tq;
+    v.q_hstride = a.Tq;
+    v.k_base = (size_t)b * a.Hkv * a.Tk;
+    v.k_hstride = a.Tk;
+  }
+  return v;
+}
 
 struct BwdArgs {
   const void* Q;
@@ -39,6 +83,9 @@ struct BwdArgs {
   int B, Hq, Hkv, Tq, Tk;
   int Tqp;            // Tq rounded up to a multiple of 64
   int window;         // as FwdArgs::window
+  const int* cu_q;    // as FwdArgs (variable-length batch)
+  const int* cu_k;
+  int total_q, total_k;
   float scale;
   float scale_log2;
 };

@@ -186,6 +186,34 @@ int fa_fwd_splitk(const void* Q, const void* K, const void* V, void* O, float* L
                   size_t workspace_bytes, int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal,
                   int window, float scale, int dtype, int nsplit, void* stream);
 
+/*
+ * Variable-length batches: B sequences of different lengths packed together
+ * (the chunked-attention article's blocks of new positions each attend to a
+ * prefix of their own length, section "The Scene").  Sequence b owns the query
+ * rows cu_seqlens_q[b] .. cu_seqlens_q[b+1] - 1 and the key rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1] - 1 of every head; tensors are packed
+ * head-major: Q, O, dO, dQ [Hq][total_q][d], K, V, dK, dV [Hkv][total_k][d],
+ * L [Hq][total_q].  cu_seqlens_* are device arrays of B + 1 int32 offsets,
+ * non-decreasing from 0 to total_*, with no sequence longer than
+ * max_seqlen_*; the library does not read them on the host (they are device
+ * memory), and the kernels clamp every sequence into the packed tensors, so
+ * inconsistent offsets give meaningless rows but no out-of-bounds access.
+ * Causal alignment, window, GQA, empty rows and dtypes are per sequence as in
+ * fa_fwd_window / fa_bwd_window.  The backward workspace is
+ * fa_bwd_workspace_bytes(B, Hq, Hkv, max_seqlen_q, max_seqlen_k, d, dtype).
+ * Errors as fa_fwd / fa_bwd, plus FA_ERR_NULL_PTR for missing offsets,
+ * FA_ERR_ALIGNMENT for offsets not 4-byte aligned, FA_ERR_BAD_SHAPE for
+ * negative sizes or a max_seqlen above its total.
+ */
+int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L, const int* cu_seqlens_q,
+                  const int* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                  int max_seqlen_k, int d, int causal, int window, float scale, int dtype, void* stream);
+int fa_bwd_varlen(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                  const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                  const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv, int total_q,
+                  int total_k, int max_seqlen_q, int max_seqlen_k, int d, int causal, int window,
+                  float scale, int dtype, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* fa_status_string(int status);
 

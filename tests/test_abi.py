@@ -105,3 +105,29 @@ def test_bwd_stages_rejects_unknown_bits(lib):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         _binding.load_library(str(tmp_path / "nope.so"))
+
+
+def fwd_varlen(lib, cu_q=FAKE, cu_k=FAKE, B=2, Hq=2, Hkv=1, total_q=32, total_k=32, max_q=16, max_k=16,
+               d=64, Q=FAKE):
+    return lib.fa_fwd_varlen(Q, FAKE, FAKE, FAKE, FAKE, cu_q, cu_k, B, Hq, Hkv, total_q, total_k, max_q,
+                             max_k, d, 1, 0, 0.125, 1, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu_q=None), 1), (dict(cu_k=None), 1), (dict(cu_q=FAKE + 2), 8), (dict(total_q=-1), 2),
+    (dict(max_q=40), 2), (dict(max_k=-1), 2), (dict(Hq=3, Hkv=2), 3), (dict(d=80), 4), (dict(Q=None), 1),
+])
+def test_fwd_varlen_rejects_bad_arguments(lib, kw, status):
+    assert fwd_varlen(lib, **kw) == status
+
+
+def test_bwd_varlen_rejects_missing_workspace(lib):
+    args = (FAKE,) * 9 + (None, 0, FAKE, FAKE, 2, 2, 1, 32, 32, 16, 16, 64, 1, 0, 0.125, 1, None)
+    assert lib.fa_bwd_varlen(*args) == 7
+
+
+def test_splitk_rejects_too_many_slices(lib):
+    assert lib.fa_fwd_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 1, 2, 1, 16, 16, 64, 1, 0, 0.125, 1,
+                             5000, None) == 9
+    assert lib.fa_fwd_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 1, 2, 1, 16, 16, 64, 1, 0, 0.125, 1,
+                             4, None) == 7
