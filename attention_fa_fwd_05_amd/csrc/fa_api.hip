@@ -73,23 +73,30 @@ WsLayout ws_layout(int B, int Hq, int Tq, int d, int dtype) {
   return w;
 }
 
-// All Tq rows of a K/V group's G query heads fit one forward workgroup.
+// All Tq rows of a K/V group's G query heads fit one forward workgroup: in the
+// 4-wave decode shape (bf16; 2), else in the regular one (1); or not (0).
 int fwd_pack(int Hq, int Hkv, int Tq, int d, int dtype) {
-  const int nw = fa::fwd_waves(dtype == FA_DTYPE_BF16, d), G = Hq / Hkv;
+  const int G = Hq / Hkv;
+  const int nd = fa::fwd_decode_waves();
+  if (dtype == FA_DTYPE_BF16 && G <= nd && Tq <= 32 * (nd / G)) return 2;
+  const int nw = fa::fwd_waves(dtype == FA_DTYPE_BF16, d);
   return (G <= nw && Tq <= 32 * (nw / G)) ? 1 : 0;
 }
 
 // Key slices of a split forward: the requested count, or (nsplit <= 0) enough
-// slices for about two workgroups per compute unit, each of at least two key
-// tiles, at most 64.
+// slices for about one workgroup per compute unit (the decode shape fits two,
+// and the second slot absorbs uneven slices), each of at least eight key
+// tiles, at most 64.  Measured on the 32-query, 8032-key shape: 16 blocks x
+// 8 K/V heads run best at 2-4 slices, one block at 12-16.
 int fwd_splits(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int nsplit) {
   if (nsplit > 0) return nsplit;
-  const int nw = fa::fwd_waves(dtype == FA_DTYPE_BF16, d), bk = fa::fwd_block_keys(dtype == FA_DTYPE_BF16, d);
-  const long long items = fwd_pack(Hq, Hkv, Tq, d, dtype) ? (long long)B * Hkv
-                                                          : (long long)((Tq + 32 * nw - 1) / (32 * nw)) * B * Hq;
+  const int pack = fwd_pack(Hq, Hkv, Tq, d, dtype);
+  const int nw = fa::fwd_waves(dtype == FA_DTYPE_BF16, d);
+  const int bk = pack == 2 ? fa::fwd_decode_block_keys() : fa::fwd_block_keys(dtype == FA_DTYPE_BF16, d);
+  const long long items = pack ? (long long)B * Hkv : (long long)((Tq + 32 * nw - 1) / (32 * nw)) * B * Hq;
   const long long tiles = (Tk + bk - 1) / bk;
-  long long ns = items > 0 ? (512 + items - 1) / items : 1;
-  ns = ns < tiles / 2 ? ns : tiles / 2;
+  long long ns = items > 0 ? (256 + items - 1) / items : 1;
+  ns = ns < tiles / 8 ? ns : tiles / 8;
   ns = ns < 64 ? ns : 64;
   return ns < 1 ? 1 : (int)ns;
 }

@@ -37,18 +37,25 @@ constexpr float kTau = 8.0f;
 // its operands fit.
 // Keys per tile: 128, so a workgroup meets one barrier per 128 keys; fp32 with
 // d = 128 keeps 64 (two 128-key K / V buffers of it would exceed the LDS).
-template <typename T, int D> struct FwdShape {
+// Decode shape (DEC): a packed workgroup of 4 waves, one per query head of a
+// K/V group with up to 32 rows each, against 64-key tiles.  Its 64 KiB of LDS
+// and at most 256 registers per wave (two waves per SIMD, asked of the
+// compiler through the launch bounds) let two workgroups share a compute
+// unit, so twice the
+// K/V loads are in flight; few query rows make these loads, not the matrix
+// work, the bound.
+template <typename T, int D, bool DEC = false> struct FwdShape {
   static constexpr int QT = 1;
-  static constexpr int NW = (sizeof(T) == 4 && D == 128) ? 4 : 8;
+  static constexpr int NW = DEC ? 4 : (sizeof(T) == 4 && D == 128) ? 4 : 8;
   static constexpr int BQ = 32 * QT * NW;
-  static constexpr int BK = (sizeof(T) == 4 && D == 128) ? 64 : 128;
+  static constexpr int BK = DEC ? 64 : (sizeof(T) == 4 && D == 128) ? 64 : 128;
 };
 
-template <typename T, int D, bool CAUSAL, bool WIN>
-__global__ __launch_bounds__((64 * FwdShape<T, D>::NW)) void fwd_kernel(FwdArgs a) {
+template <typename T, int D, bool CAUSAL, bool WIN, bool DEC>
+__global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void fwd_kernel(FwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
-  using SH = FwdShape<T, D>;
+  using SH = FwdShape<T, D, DEC>;
   constexpr int QT = SH::QT, NW = SH::NW, NTHR = 64 * NW, BQ = SH::BQ, BK = SH::BK;
   constexpr int NKT = BK / 32;                      // 32-key sub-tiles per key tile
   constexpr int NE = 16 * NKT;                      // scores per lane per query tile
@@ -354,8 +361,19 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream, int nsplit) {
   const int nqb = (a.Tq + SH::BQ - 1) / SH::BQ;
   const long long blocks = a.pack ? (long long)a.B * a.Hkv : (long long)nqb * a.B * a.Hq;
   if (blocks == 0) return hipSuccess;
-  hipError_t e = a.window > 0 ? launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, true>, blocks, nsplit, stream, a)
-                              : launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, false>, blocks, nsplit, stream, a);
+  hipError_t e = hipSuccess;
+  bool launched = false;
+  if constexpr (sizeof(T) == 2) {
+    if (a.pack == 2) {
+      using SD = FwdShape<T, D, true>;
+      e = a.window > 0 ? launch2<64 * SD::NW>(fwd_kernel<T, D, CAUSAL, true, true>, blocks, nsplit, stream, a)
+                       : launch2<64 * SD::NW>(fwd_kernel<T, D, CAUSAL, false, true>, blocks, nsplit, stream, a);
+      launched = true;
+    }
+  }
+  if (!launched)
+    e = a.window > 0 ? launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, true, false>, blocks, nsplit, stream, a)
+                     : launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, false, false>, blocks, nsplit, stream, a);
   if (e != hipSuccess || a.Opart == nullptr) return e;
   const long long rows = a.cu_q ? (long long)a.Hq * a.total_q : (long long)a.B * a.Hq * a.Tq;
   if (rows == 0) return hipSuccess;
@@ -366,6 +384,8 @@ int fwd_waves(int dtype_bf16, int d) {
   return dtype_bf16 ? (d == 64 ? FwdShape<bf16, 64>::NW : FwdShape<bf16, 128>::NW)
                     : (d == 64 ? FwdShape<float, 64>::NW : FwdShape<float, 128>::NW);
 }
+int fwd_decode_waves() { return FwdShape<bf16, 128, true>::NW; }
+int fwd_decode_block_keys() { return FwdShape<bf16, 128, true>::BK; }
 int fwd_block_keys(int dtype_bf16, int d) {
   return dtype_bf16 ? (d == 64 ? FwdShape<bf16, 64>::BK : FwdShape<bf16, 128>::BK)
                     : (d == 64 ? FwdShape<float, 64>::BK : FwdShape<float, 128>::BK);

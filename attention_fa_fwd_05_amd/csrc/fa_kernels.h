@@ -16,7 +16,8 @@ struct FwdArgs {
   int B, Hq, Hkv, Tq, Tk;
   int window;         // > 0: query i sees keys j > i + Tk - Tq - window; else no window
   float scale_log2;   // scale * log2(e): scores are kept in the exp2 domain
-  int pack;           // 1: a workgroup holds all Tq rows of every query head of a K/V group
+  int pack;           // 1: a workgroup holds all Tq rows of every query head of a K/V group;
+                      // 2: the same in the 4-wave decode shape (bf16, G * 32-row blocks <= 4)
   // Split over keys (gridDim.y > 1 or Opart set): workgroup slice s = blockIdx.y
   // of the key tiles writes its normalised partial output and row logsumexp,
   // fp32, to Opart[s][row][d] and Lpart[s][row]; fwd_merge combines them.
@@ -114,6 +115,9 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipSt
 // Waves per forward workgroup for a dtype and head dim (pack needs G <= waves).
 int fwd_waves(int dtype_bf16, int d);
 int fwd_block_keys(int dtype_bf16, int d);
+// The decode-shape forward (bf16, FwdArgs::pack == 2): waves and keys per tile.
+int fwd_decode_waves();
+int fwd_decode_block_keys();
 // Backward stages (bit mask): preprocess, dK/dV kernel, dQ kernel.
 constexpr unsigned kStagePre = 1u, kStageDkDv = 2u, kStageDq = 4u;
 hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int d, int causal, unsigned stages,

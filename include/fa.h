@@ -174,7 +174,7 @@ int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, co
  * which is exactly the attention over the union of the slices (a row whose
  * keys all lie outside a slice has L_s = -inf there).  Results equal fa_fwd /
  * fa_fwd_window up to rounding.  nsplit <= 0 picks a count that fills the GPU
- * (about two workgroups per compute unit, at least two key tiles per slice,
+ * (about one workgroup per compute unit, at least eight key tiles per slice,
  * at most 64).  The workspace (device memory, 16-byte aligned, at least
  * fa_fwd_splitk_workspace_bytes for the same nsplit) holds nsplit * B * Hq *
  * Tq * (d + 1) floats; it carries nothing between calls.  Errors as fa_fwd,
