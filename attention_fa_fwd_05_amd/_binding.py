@@ -24,7 +24,8 @@ STATUS = {
     8: "FA_ERR_ALIGNMENT", 9: "FA_ERR_TOO_LARGE", 10: "FA_ERR_HIP", 11: "FA_ERR_STAGES",
 }
 STAGE_PRE, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
-EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_window", "fa_bwd_window", "fa_fwd_splitk",
+EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_window", "fa_bwd_window", "fa_fwd_dv", "fa_bwd_dv",
+           "fa_fwd_splitk",
            "fa_fwd_splitk_workspace_bytes", "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_workspace_bytes",
            "fa_status_string", "fa_hip_error_string", "fa_abi_version"]
 
@@ -72,6 +73,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_splitk.restype = i
     lib.fa_fwd_splitk_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
     lib.fa_fwd_splitk_workspace_bytes.restype = sz
+    lib.fa_fwd_dv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_dv.restype = i
+    lib.fa_bwd_dv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                              i, i, i, i, i, i, i, i, i, f, i, ctypes.c_uint, vp]
+    lib.fa_bwd_dv.restype = i
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_varlen.restype = i
     lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp,
@@ -113,11 +119,12 @@ def _stream(t) -> int:
 
 
 def _shapes(q, k, v):
+    """(B, Hq, Hkv, Tq, Tk, d) of q [B, Hq, Tq, d], k [B, Hkv, Tk, d], v [B, Hkv, Tk, dv]."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, T, d]")
     B, Hq, Tq, d = q.shape
     Bk, Hkv, Tk, dk = k.shape
-    if Bk != B or dk != d or tuple(v.shape) != (B, Hkv, Tk, d):
+    if Bk != B or dk != d or tuple(v.shape[:3]) != (B, Hkv, Tk):
         raise ValueError(f"inconsistent shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     for t in (q, k, v):
         if not t.is_contiguous():
@@ -133,13 +140,21 @@ def workspace_bytes(B, Hq, Hkv, Tq, Tk, d, dtype_code) -> int:
 
 def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
             window: int = 0):
-    """fa_fwd (fa_fwd_window when window > 0): returns (o, lse), o like q, lse float32 [B, Hq, Tq]."""
+    """fa_fwd (fa_fwd_window when window > 0, fa_fwd_dv when v's head dim differs from q's):
+    returns (o, lse), o [B, Hq, Tq, dv], lse float32 [B, Hq, Tq]."""
     import torch
     lib = load_library()
     B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
+    dv = v.shape[3]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o = torch.empty_like(q) if out is None else out
+    o = q.new_empty((B, Hq, Tq, dv)) if out is None else out
     L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if dv != d:
+        st = lib.fa_fwd_dv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), B, Hq, Hkv, Tq, Tk, d, dv,
+                           int(bool(causal)), int(window), scale, _dtype_code(q), _stream(q))
+        if st != 0:
+            raise FaError(st, "fa_fwd_dv")
+        return o, L
     if window > 0:
         st = lib.fa_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), B, Hq, Hkv, Tq, Tk, d,
                                int(bool(causal)), int(window), scale, _dtype_code(q), _stream(q))
@@ -239,9 +254,10 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
     import torch
     lib = load_library()
     B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
-    for t, shape in ((o, q.shape), (do, q.shape)):
-        if tuple(t.shape) != tuple(shape) or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError("o and do must match q")
+    oshape = tuple(q.shape[:3]) + (v.shape[3],)
+    for t in (o, do):
+        if tuple(t.shape) != oshape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("o and do must be [B, Hq, Tq, dv] like q")
     if tuple(lse.shape) != (B, Hq, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be float32 [B, Hq, Tq]")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -255,6 +271,12 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
     dv = torch.empty_like(v) if dv is None else dv
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
             _ptr(dv), ws.data_ptr(), ws.numel(), B, Hq, Hkv, Tq, Tk, d, int(bool(causal)))
+    if v.shape[3] != d:
+        st = lib.fa_bwd_dv(*args[:-1], v.shape[3], int(bool(causal)), int(window), scale, code, stages,
+                           _stream(q))
+        if st != 0:
+            raise FaError(st, "fa_bwd_dv")
+        return dq, dk, dv
     if window > 0:
         st = lib.fa_bwd_window(*args, int(window), scale, code, stages, _stream(q))
         if st != 0:

@@ -103,6 +103,14 @@ int fwd_splits(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int nsp
 
 constexpr int kMaxSplits = 1024;
 
+// Head dim of V (and O, dO, dV): equal to d, or, for bf16 only, 64 with d = 128
+// and 128 with d = 64.
+int check_dv(int d, int dv, int dtype) {
+  if (dv == d) return FA_OK;
+  if (dtype == FA_DTYPE_BF16 && ((d == 128 && dv == 64) || (d == 64 && dv == 128))) return FA_OK;
+  return FA_ERR_HEAD_DIM;
+}
+
 // Variable-length batch arguments: offsets present and 4-byte aligned, sizes
 // non-negative, the longest sequence within the totals.  The offsets
 // themselves live in device memory and are not read here; the kernels clamp
@@ -119,7 +127,7 @@ int check_varlen(const int* cu_q, const int* cu_k, int total_q, int total_k, int
 int bwd_core(const void* Q, const void* K, const void* V, const void* O, const float* L,
              const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
              const int* cu_q, const int* cu_k, int B, int Hq, int Hkv, int total_q, int total_k, int Tq,
-             int Tk, int d, int causal, int window, float scale, int dtype, unsigned stages, void* stream);
+             int Tk, int d, int dv, int causal, int window, float scale, int dtype, unsigned stages, void* stream);
 
 size_t splitk_ws_bytes(int B, int Hq, int Tq, int d, int ns) {
   const size_t rows = (size_t)B * Hq * Tq;
@@ -161,11 +169,18 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
 int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* L,
                   int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int window, float scale,
                   int dtype, void* stream) {
+  return fa_fwd_dv(Q, K, V, O, L, B, Hq, Hkv, Tq, Tk, d, d, causal, window, scale, dtype, stream);
+}
+
+int fa_fwd_dv(const void* Q, const void* K, const void* V, void* O, float* L, int B, int Hq, int Hkv, int Tq,
+              int Tk, int d, int dv, int causal, int window, float scale, int dtype, void* stream) {
   int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
   if (st != FA_OK) return st;
+  if ((st = check_dv(d, dv, dtype)) != FA_OK) return st;
   const long long nq = (long long)B * Hq * Tq * d, nkv = (long long)B * Hkv * Tk * d;
-  if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, nq)) || (st = check_ptr(K, nkv)) ||
-      (st = check_ptr(V, nkv)) || (st = check_ptr(L, (long long)B * Hq * Tq)))
+  const long long no = (long long)B * Hq * Tq * dv, nv = (long long)B * Hkv * Tk * dv;
+  if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, no)) || (st = check_ptr(K, nkv)) ||
+      (st = check_ptr(V, nv)) || (st = check_ptr(L, (long long)B * Hq * Tq)))
     return st;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if (Tq == 0) return FA_OK;
@@ -179,7 +194,7 @@ int fa_fwd_window(const void* Q, const void* K, const void* V, void* O, float* L
   a.Lpart = nullptr;
   a.cu_q = a.cu_k = nullptr;
   a.total_q = a.total_k = 0;
-  return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream));
+  return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream, 1, dv));
 }
 
 int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L, const int* cu_seqlens_q,
@@ -276,7 +291,15 @@ int fa_bwd_window(const void* Q, const void* K, const void* V, const void* O, co
                   int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, int window, float scale,
                   int dtype, unsigned stages, void* stream) {
   return bwd_core(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, nullptr, nullptr, B, Hq, Hkv,
-                  0, 0, Tq, Tk, d, causal, window, scale, dtype, stages, stream);
+                  0, 0, Tq, Tk, d, d, causal, window, scale, dtype, stages, stream);
+}
+
+int fa_bwd_dv(const void* Q, const void* K, const void* V, const void* O, const float* L, const void* dO,
+              void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+              int Tq, int Tk, int d, int dv, int causal, int window, float scale, int dtype, unsigned stages,
+              void* stream) {
+  return bwd_core(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, nullptr, nullptr, B, Hq, Hkv,
+                  0, 0, Tq, Tk, d, dv, causal, window, scale, dtype, stages, stream);
 }
 
 int fa_bwd_varlen(const void* Q, const void* K, const void* V, const void* O, const float* L,
@@ -287,7 +310,7 @@ int fa_bwd_varlen(const void* Q, const void* K, const void* V, const void* O, co
   int st = check_varlen(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max_seqlen_k);
   if (st != FA_OK) return st;
   return bwd_core(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, cu_seqlens_q, cu_seqlens_k, B,
-                  Hq, Hkv, total_q, total_k, max_seqlen_q, max_seqlen_k, d, causal, window, scale, dtype,
+                  Hq, Hkv, total_q, total_k, max_seqlen_q, max_seqlen_k, d, d, causal, window, scale, dtype,
                   FA_BWD_STAGE_ALL, stream);
 }
 
@@ -298,17 +321,18 @@ namespace {
 int bwd_core(const void* Q, const void* K, const void* V, const void* O, const float* L,
              const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
              const int* cu_q, const int* cu_k, int B, int Hq, int Hkv, int total_q, int total_k, int Tq,
-             int Tk, int d, int causal, int window, float scale, int dtype, unsigned stages, void* stream) {
+             int Tk, int d, int dv, int causal, int window, float scale, int dtype, unsigned stages, void* stream) {
   int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
   if (st != FA_OK) return st;
+  if ((st = check_dv(d, dv, dtype)) != FA_OK) return st;
   const bool varlen = cu_q != nullptr;
-  const long long nq = varlen ? (long long)Hq * total_q * d : (long long)B * Hq * Tq * d;
-  const long long nkv = varlen ? (long long)Hkv * total_k * d : (long long)B * Hkv * Tk * d;
-  if (nq > kMaxElems || nkv > kMaxElems) return FA_ERR_TOO_LARGE;
   const long long rows = varlen ? (long long)Hq * total_q : (long long)B * Hq * Tq;
-  if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, nq)) || (st = check_ptr(dO, nq)) ||
-      (st = check_ptr(dQ, nq)) || (st = check_ptr(K, nkv)) || (st = check_ptr(V, nkv)) ||
-      (st = check_ptr(dK, nkv)) || (st = check_ptr(dV, nkv)) || (st = check_ptr(L, rows)))
+  const long long krows = varlen ? (long long)Hkv * total_k : (long long)B * Hkv * Tk;
+  const long long nq = rows * d, no = rows * dv, nk = krows * d, nv = krows * dv;
+  if (nq > kMaxElems || no > kMaxElems || nk > kMaxElems || nv > kMaxElems) return FA_ERR_TOO_LARGE;
+  if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, no)) || (st = check_ptr(dO, no)) ||
+      (st = check_ptr(dQ, nq)) || (st = check_ptr(K, nk)) || (st = check_ptr(V, nv)) ||
+      (st = check_ptr(dK, nk)) || (st = check_ptr(dV, nv)) || (st = check_ptr(L, rows)))
     return st;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if (stages & ~(unsigned)FA_BWD_STAGE_ALL) return FA_ERR_STAGES;
@@ -334,7 +358,7 @@ int bwd_core(const void* Q, const void* K, const void* V, const void* O, const f
   a.total_k = total_k;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-  return hip_status(fa::launch_bwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, stages, (hipStream_t)stream));
+  return hip_status(fa::launch_bwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, stages, (hipStream_t)stream, dv));
 }
 
 }  // namespace

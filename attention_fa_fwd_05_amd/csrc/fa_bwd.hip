@@ -86,16 +86,20 @@ __host__ __device__ constexpr int interleave_rank(int m, int na, int nb) {
 __device__ inline void zero_elem(bf16x8& x, int e) { x[e] = (bf16)0.f; }
 __device__ inline void zero_elem(f32x4& x, int e) { x[e] = 0.f; }
 
-template <typename T, int D, bool CAUSAL, bool WIN>
+// D: head dim of Q, K, dK; DV: of V, dO, dV.
+template <typename T, int D, bool CAUSAL, bool WIN, int DV = D>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
   constexpr int BK = 128;                           // keys per workgroup, 32 per wave
   constexpr int BQ = 64;                            // queries per block: two 32-query tiles
   constexpr int KPER = M::KPER;
-  constexpr int NSD = (D / 2) / KPER;               // contraction steps over d
+  constexpr int NSD = (D / 2) / KPER;               // contraction steps over d (S = Q K^T)
+  constexpr int NSDV = (DV / 2) / KPER;             // ... over dv (dP = dO V^T)
   constexpr int NSQ = (BQ / 2) / KPER;              // contraction steps over a query block
-  constexpr int NDT = D / 32;
+  constexpr int NDT = D / 32;                       // 32-wide dK tiles
+  constexpr int NDTV = DV / 32;                     // 32-wide dV tiles
+  constexpr int NPS = NDT + NDTV;                   // dV and dK products per query step
   constexpr int NSH = NSQ / 2;                      // steps per 32-query tile
   // Three LDS buffers let block i+2 load while blocks i and i+1 are read;
   // fp32 with d = 128 fits two, and then loads without overlap.
@@ -115,19 +119,21 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   // issued.  Products and LDS reads go out in a fixed order with a fixed
   // number of operands in flight; the loop is unrolled over the buffers so
   // every LDS address is a lane offset plus a constant.
-  constexpr int NS1 = 2 * NSD;                      // S and dP products per tile
-  constexpr int NDQ = (NSH / 2) * 2 * NDT;          // dV/dK products per quarter of the steps
-  constexpr int NDH = NSH * 2 * NDT;                // ... per half
+  constexpr int NS1 = NSD + NSDV;                   // S and dP products per tile
+  constexpr int NDQ = (NSH / 2) * NPS;              // dV/dK products per quarter of the steps
+  constexpr int NDH = NSH * NPS;                    // ... per half
   constexpr int NPA = NS1 + NDQ;                    // products in phase 1a (and 1b)
-  constexpr int AHEAD = (sizeof(T) == 2 && NPA % 8 == 0) ? 8 : 4;   // operands in flight
+  // Operands in flight: a divisor of NPA, so the ring slots line up across phases.
+  constexpr int AHEAD = sizeof(T) != 2 ? 4 : NPA % 8 == 0 ? 8 : (D != DV && NPA % 6 == 0) ? 6 : 4;
   static_assert(NSH % 2 == 0, "quarters of the query steps");
   static_assert(NPA % AHEAD == 0, "operand ring slots line up across phases");
   static_assert(NPA >= 12 && NDH >= 8, "room for the vector stages");
-  static_assert(NB == 2 || 2 * (2 * DmaRows<T, D, BQ, 256>::PER + 1) <= NPA, "loads fit in phase 1b");
+  static_assert(NB == 2 || 2 * (DmaRows<T, D, BQ, 256>::PER + DmaRows<T, DV, BQ, 256>::PER + 1) <= NPA,
+                "loads fit in phase 1b");
   __shared__ __attribute__((aligned(16))) float sL[NB][64];
   __shared__ __attribute__((aligned(16))) float sD[NB][64];    // -D
   __shared__ __attribute__((aligned(16))) T sQ[NB][BQ * D];
-  __shared__ __attribute__((aligned(16))) T sdO[NB][BQ * D];
+  __shared__ __attribute__((aligned(16))) T sdO[NB][BQ * DV];
 
   // The wave index is uniform across a wave; readfirstlane tells the compiler,
   // so conditions built from it become scalar branches.
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   const bool ragged = k0 + BK > Tk;                 // uniform: this block holds the key end
 
   const T* Kp = reinterpret_cast<const T*>(a.K) + krow0 * D;
-  const T* Vp = reinterpret_cast<const T*>(a.V) + krow0 * D;
+  const T* Vp = reinterpret_cast<const T*>(a.V) + krow0 * DV;
 
   // Work list: every (query block that can see a key of this block, query
   // head of the group), query blocks from the last one down and heads
@@ -173,9 +179,9 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   auto issue = [&](int it, int buf) {
     const int bh = item_bh(it);
     const int q0 = item_q0(it);
-    const size_t qbase = item_qrow(it) * D;
+    const size_t qbase = item_qrow(it) * D, obase = item_qrow(it) * DV;
     dma_rows<T, D, BQ, 256>(sQ[buf], reinterpret_cast<const T*>(a.Q) + qbase, q0, Tq);
-    dma_rows<T, D, BQ, 256>(sdO[buf], reinterpret_cast<const T*>(a.dO) + qbase, q0, Tq);
+    dma_rows<T, DV, BQ, 256>(sdO[buf], reinterpret_cast<const T*>(a.dO) + obase, q0, Tq);
     if (w == 0) dma_floats64(sL[buf], a.Lg + (size_t)bh * a.Tqp + q0);
     if (w == 1) dma_floats64(sD[buf], a.Dvec + (size_t)bh * a.Tqp + q0);
   };
@@ -186,10 +192,13 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   // address unit is never backed up: NDMA pieces, Q rows, dO rows, then L2
   // and -D.
   using DR = DmaRows<T, D, BQ, 256>;
-  constexpr int NDMA = 2 * DR::PER + 1;
-  uint32_t src_off[DR::PER];                        // per-lane source byte offsets, one per instruction
+  using DRV = DmaRows<T, DV, BQ, 256>;
+  constexpr int NDMA = DR::PER + DRV::PER + 1;
+  uint32_t src_off[DR::PER], src_offv[DRV::PER];   // per-lane source byte offsets, one per instruction
 #pragma unroll
   for (int j = 0; j < DR::PER; ++j) src_off[j] = DR::src_off(j);
+#pragma unroll
+  for (int j = 0; j < DRV::PER; ++j) src_offv[j] = D == DV ? src_off[j % DR::PER] : DRV::src_off(j);
   // Uniform description of one block's loads (computed once per iteration).
   struct Src {
     const char* q;                                  // Q row q0 of the head
@@ -205,22 +214,27 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     r.q0 = item_q0(it);
     const size_t row = item_qrow(it) + r.q0;
     r.q = reinterpret_cast<const char*>(a.Q) + row * D * sizeof(T);
-    r.o = reinterpret_cast<const char*>(a.dO) + row * D * sizeof(T);
+    r.o = reinterpret_cast<const char*>(a.dO) + row * DV * sizeof(T);
     r.l = a.Lg + (size_t)bh * a.Tqp + r.q0;
     r.d = a.Dvec + (size_t)bh * a.Tqp + r.q0;
     r.whole = r.q0 + BQ <= Tq;
     return r;
   };
   auto dma_piece = [&](const Src& src, int buf, int j) {
-    if (j < 2 * DR::PER) {
-      const int i = j % DR::PER;
-      T* tile = j < DR::PER ? sQ[buf] : sdO[buf];
-      const char* base = j < DR::PER ? src.q : src.o;
+    if (j < DR::PER) {
       if (src.whole) {
-        dma16s(base, src_off[i], lds_addr(tile) + DR::lds_off(i));
+        dma16s(src.q, src_off[j], lds_addr(sQ[buf]) + DR::lds_off(j));
       } else {                                      // ragged end of the queries: clamped rows
-        const T* g = reinterpret_cast<const T*>(base) - (size_t)src.q0 * D;
-        DR::one(tile, g, src.q0, Tq, i);
+        const T* g = reinterpret_cast<const T*>(src.q) - (size_t)src.q0 * D;
+        DR::one(sQ[buf], g, src.q0, Tq, j);
+      }
+    } else if (j < DR::PER + DRV::PER) {
+      const int i = j - DR::PER;
+      if (src.whole) {
+        dma16s(src.o, src_offv[i], lds_addr(sdO[buf]) + DRV::lds_off(i));
+      } else {
+        const T* g = reinterpret_cast<const T*>(src.o) - (size_t)src.q0 * DV;
+        DRV::one(sdO[buf], g, src.q0, Tq, i);
       }
     } else {
       if (w == 0) dma_floats64(sL[buf], src.l);
@@ -228,29 +242,51 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     }
   };
 
-  Op kop[NSD], vop[NSD];
+  Op kop[NSD], vop[NSDV];
   {
     const size_t ro = (size_t)(key_ok ? mykey : 0) * D + h * (D / 2);
+    const size_t rov = (size_t)(key_ok ? mykey : 0) * DV + h * (DV / 2);
+    // K and V only feed matrix instructions: keep them in accumulation
+    // registers, leaving the vector registers to the softmax work.
 #pragma unroll
     for (int s = 0; s < NSD; ++s) {
       kop[s] = M::ld(Kp + ro + s * KPER);
-      vop[s] = M::ld(Vp + ro + s * KPER);
-      if (!key_ok) { kop[s] = Op{}; vop[s] = Op{}; }
-      // K and V only feed matrix instructions: keep them in accumulation
-      // registers, leaving the vector registers to the softmax work.
-      if constexpr (sizeof(T) == 2) {
-        asm volatile("" : "+a"(kop[s]));
-        asm volatile("" : "+a"(vop[s]));
-      }
+      if (!key_ok) kop[s] = Op{};
+      if constexpr (sizeof(T) == 2) asm volatile("" : "+a"(kop[s]));
+    }
+#pragma unroll
+    for (int s = 0; s < NSDV; ++s) {
+      vop[s] = M::ld(Vp + rov + s * KPER);
+      if (!key_ok) vop[s] = Op{};
+      if constexpr (sizeof(T) == 2) asm volatile("" : "+a"(vop[s]));
     }
   }
-  f32x16 dk[NDT], dv[NDT];
+  f32x16 dk[NDT], dv[NDTV];
 #pragma unroll
-  for (int t = 0; t < NDT; ++t) { dk[t] = f32x16{}; dv[t] = f32x16{}; }
+  for (int t = 0; t < NDT; ++t) dk[t] = f32x16{};
+#pragma unroll
+  for (int t = 0; t < NDTV; ++t) dv[t] = f32x16{};
+  // Natural and transposed operand fetchers of the Q tiles (width d) and the
+  // dO tiles (width dv).
   NatFetch<T, D> nat;
   nat.init(n, h);
   TrPermFetch<T, D> trp;
   trp.init(lane);
+  NatFetch<T, DV> natv;
+  TrPermFetch<T, DV> trpv;
+  if constexpr (DV != D) {
+    natv.init(n, h);
+    trpv.init(lane);
+  }
+  // dO natural / transposed operands through the fetcher of its width.
+  auto nat_o = [&](const T* tile, int t, int s) -> Op {
+    if constexpr (DV == D) return nat.ld(tile, t, s);
+    else return natv.ld(tile, t, s);
+  };
+  auto tr_o = [&](const T* tile, int t, int s) -> Op {
+    if constexpr (DV == D) return trp.ld(tile, t, s);
+    else return trpv.ld(tile, t, s);
+  };
 
   f32x16 sacc[2], dpacc[2];                         // S and dP - D of one block (lane = key)
   Op pop[NSQ], dsop[NSQ];                           // P, dS as operands, by query step
@@ -271,11 +307,13 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     if (m < NSD) sacc[t] = M::mma(x, kop[m], sacc[t]);
     else dpacc[t] = M::mma(x, vop[m - NSD], dpacc[t]);
   };
-  // dV / dK product m (0 .. NSQ * 2 * NDT): query step m / (2 NDT) outermost,
-  // then d tile, then dV (even) or dK (odd).
+  // dV / dK product m (0 .. NSQ * NPS): query step m / NPS outermost; within
+  // a step the NDTV dV and NDT dK products alternate as evenly as possible
+  // (strictly alternating, dV first, when d = dv).
   auto d_mma = [&](int m, const Op& x) {
-    const int s = m / (2 * NDT), t = (m >> 1) % NDT;
-    if (m & 1) dk[t] = M::mma(x, dsop[s], dk[t]);
+    const int s = m / NPS, r = m % NPS;
+    const int t = interleave_rank(r, NDTV, NDT);
+    if (interleave_is_b(r, NDTV, NDT)) dk[t] = M::mma(x, dsop[s], dk[t]);
     else dv[t] = M::mma(x, pop[s], dv[t]);
   };
   // L2 of one tile's queries in accumulator order.
@@ -353,7 +391,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       sacc[t] = f32x16{};
       seed_dp(sD[0], t);
 #pragma unroll
-      for (int m = 0; m < NS1; ++m) s_mma(t, m, nat.ld(m < NSD ? sQ[0] : sdO[0], t, m % NSD));
+      for (int m = 0; m < NS1; ++m) s_mma(t, m, m < NSD ? nat.ld(sQ[0], t, m) : nat_o(sdO[0], t, m - NSD));
     }
     load_l(sL[0], 0);
 #pragma unroll
@@ -379,10 +417,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 
     // S / dP operand of product m of tile t (block i+1), dV / dK operand of
     // product m (block i).
-    auto s_fetch = [&](int t, int m) -> Op { return nat.ld(m < NSD ? nQ : ndO, t, m % NSD); };
+    auto s_fetch = [&](int t, int m) -> Op { return m < NSD ? nat.ld(nQ, t, m) : nat_o(ndO, t, m - NSD); };
     auto d_fetch = [&](int m) -> Op {
-      const int s = m / (2 * NDT), t = (m >> 1) % NDT;
-      return trp.ld((m & 1) ? cQ : cdO, t, s);
+      const int s = m / NPS, r = m % NPS;
+      const int t = interleave_rank(r, NDTV, NDT);
+      return interleave_is_b(r, NDTV, NDT) ? trp.ld(cQ, t, s) : tr_o(cdO, t, s);
     };
     // Phases 1a and 1b: tile u of block i+1's S, dP interleaved with quarter u
     // of block i's dV, dK.
@@ -454,16 +493,17 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 
   if (key_ok) {
     T* dKr = reinterpret_cast<T*>(a.dK) + (krow0 + mykey) * D;
-    T* dVr = reinterpret_cast<T*>(a.dV) + (krow0 + mykey) * D;
+    T* dVr = reinterpret_cast<T*>(a.dV) + (krow0 + mykey) * DV;
     const float sc = a.scale;
 #pragma unroll
-    for (int t = 0; t < NDT; ++t) {
+    for (int t = 0; t < (NDT > NDTV ? NDT : NDTV); ++t) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = t * 32 + 8 * g + 4 * h;
-        store4(dKr + d0, dk[t][4 * g] * sc, dk[t][4 * g + 1] * sc, dk[t][4 * g + 2] * sc,
-               dk[t][4 * g + 3] * sc);
-        store4(dVr + d0, dv[t][4 * g], dv[t][4 * g + 1], dv[t][4 * g + 2], dv[t][4 * g + 3]);
+        if (t < NDT)
+          store4(dKr + d0, dk[t][4 * g] * sc, dk[t][4 * g + 1] * sc, dk[t][4 * g + 2] * sc,
+                 dk[t][4 * g + 3] * sc);
+        if (t < NDTV) store4(dVr + d0, dv[t][4 * g], dv[t][4 * g + 1], dv[t][4 * g + 2], dv[t][4 * g + 3]);
       }
     }
   }
@@ -474,13 +514,15 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 template <typename T, int D>
 constexpr int dq_waves() { return (sizeof(T) == 4 && D == 128) ? 4 : 8; }
 
-template <typename T, int D, bool CAUSAL, bool WIN>
+// D: head dim of Q, K, dQ; DV: of V and dO.
+template <typename T, int D, bool CAUSAL, bool WIN, int DV = D>
 __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
   constexpr int NW = dq_waves<T, D>(), NTHR = 64 * NW, BQ = 32 * NW, BK = 64;
   constexpr int KPER = M::KPER;
   constexpr int NSD = (D / 2) / KPER;
+  constexpr int NSDV = (DV / 2) / KPER;              // steps of dP^T = V dO^T
   constexpr int NSK = (BK / 2) / KPER;
   constexpr int NDT = D / 32;
   // Three K/V buffers: tile j+2 loads while tile j is read, so the wait at the
@@ -488,9 +530,10 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   // d = 128 fits two (its loads then wait within the tile).
   constexpr int NBUF = NW == 8 ? 3 : 2;
   constexpr int AHEAD = NBUF - 1;                   // tiles loaded beyond the current one
-  constexpr int TILE = BK * D;                      // elements of one K or V tile
-  // Buffer b: K tile, then V tile; 4096-byte alignment for XorFetch.
-  __shared__ __attribute__((aligned(4096))) T sKV[NBUF][2 * TILE];
+  constexpr int TILE = BK * D;                      // elements of one K tile (the V tile follows)
+  // Buffer b: K tile, then V tile; 4096-byte alignment for XorFetch (both
+  // tile sizes are multiples of 4096 bytes).
+  __shared__ __attribute__((aligned(4096))) T sKV[NBUF][BK * (D + DV)];
 
   // The wave index is uniform across a wave; readfirstlane tells the compiler,
   // so conditions built from it become scalar branches.
@@ -511,9 +554,9 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   const bool q_ok = myq < Tq;
 
   const T* Qp = reinterpret_cast<const T*>(a.Q) + qrow0 * D;
-  const T* dOp = reinterpret_cast<const T*>(a.dO) + qrow0 * D;
+  const T* dOp = reinterpret_cast<const T*>(a.dO) + qrow0 * DV;
   const T* Kp = reinterpret_cast<const T*>(a.K) + krow0 * D;
-  const T* Vp = reinterpret_cast<const T*>(a.V) + krow0 * D;
+  const T* Vp = reinterpret_cast<const T*>(a.V) + krow0 * DV;
 
   // Key tiles jt0 .. ntiles - 1 (before the window of the block's first
   // query, or after the causal bound of its last, nothing is visible).
@@ -527,39 +570,47 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   // tabulated once; in the tile holding the key end, rows past Tk are loaded
   // as copies of the last key (their scores are masked).
   using DR = DmaRows<T, D, BK, NTHR>;
-  uint32_t src_off[DR::PER];
+  using DRV = DmaRows<T, DV, BK, NTHR>;
+  uint32_t src_off[DR::PER], src_offv[DRV::PER];
 #pragma unroll
   for (int i = 0; i < DR::PER; ++i) src_off[i] = DR::src_off(i);
+#pragma unroll
+  for (int i = 0; i < DRV::PER; ++i) src_offv[i] = D == DV ? src_off[i % DR::PER] : DRV::src_off(i);
   auto issue = [&](int k0, int buf) {
     T* tk = sKV[buf];
     T* tv = sKV[buf] + TILE;
     if (k0 + BK <= Tk) {
       const T* kb = Kp + (size_t)k0 * D;
-      const T* vb = Vp + (size_t)k0 * D;
+      const T* vb = Vp + (size_t)k0 * DV;
 #pragma unroll
       for (int i = 0; i < DR::PER; ++i) dma16s(kb, src_off[i], lds_addr(tk) + DR::lds_off(i));
 #pragma unroll
-      for (int i = 0; i < DR::PER; ++i) dma16s(vb, src_off[i], lds_addr(tv) + DR::lds_off(i));
+      for (int i = 0; i < DRV::PER; ++i) dma16s(vb, src_offv[i], lds_addr(tv) + DRV::lds_off(i));
     } else {
       dma_rows<T, D, BK, NTHR>(tk, Kp, k0, Tk);
-      dma_rows<T, D, BK, NTHR>(tv, Vp, k0, Tk);
+      dma_rows<T, DV, BK, NTHR>(tv, Vp, k0, Tk);
     }
   };
   // Direct-load instructions per wave for one tile (K and V).
-  constexpr int NLD = 2 * DR::PER;
+  constexpr int NLD = DR::PER + DRV::PER;
 #pragma unroll
   for (int j = 0; j < AHEAD; ++j)
     if (jt0 + j < ntiles) issue((jt0 + j) * BK, j);
 
   // Q^T and dO^T operands for this lane's query, L2 and D of that row.
-  Op qop[NSD], gop[NSD];
+  Op qop[NSD], gop[NSDV];
   {
     const size_t ro = (size_t)(q_ok ? myq : 0) * D + h * (D / 2);
+    const size_t rov = (size_t)(q_ok ? myq : 0) * DV + h * (DV / 2);
 #pragma unroll
     for (int s = 0; s < NSD; ++s) {
       qop[s] = M::ld(Qp + ro + s * KPER);
-      gop[s] = M::ld(dOp + ro + s * KPER);
-      if (!q_ok) { qop[s] = Op{}; gop[s] = Op{}; }
+      if (!q_ok) qop[s] = Op{};
+    }
+#pragma unroll
+    for (int s = 0; s < NSDV; ++s) {
+      gop[s] = M::ld(dOp + rov + s * KPER);
+      if (!q_ok) gop[s] = Op{};
     }
   }
   const float l2 = q_ok ? a.Lg[(size_t)bh * a.Tqp + myq] : INFINITY;
@@ -567,21 +618,27 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   // Operand fetch: bf16 from one base register per tile (XorFetch); fp32
   // (test shapes only) from offset tables.
   XorFetch<D> xf;
+  XorFetch<DV> xfv;
   NatFetch<T, D> nat;
+  NatFetch<T, DV> natv;
   TrPermFetch<T, D> trp;
   if constexpr (sizeof(T) == 2) {
     xf.init(lane);
+    if constexpr (DV != D) xfv.init(lane);
   } else {
     nat.init(n, h);
+    natv.init(n, h);
     trp.init(lane);
   }
   // Natural K (kv = 0) or V (kv = 1) operand of key sub-tile t, step s, and
   // transposed K operand of d tile t, step s, from buffer buf.
   auto ld_nat = [&](int buf, int kv, int t, int s) -> Op {
     if constexpr (sizeof(T) == 2) {
-      return XorFetch<D>::nat(lds_addr(sKV[buf]) + xf.nat0 + kv * TILE * 2, t, s);
+      if (kv == 0) return XorFetch<D>::nat(lds_addr(sKV[buf]) + xf.nat0, t, s);
+      return XorFetch<DV>::nat(lds_addr(sKV[buf]) + (DV == D ? xf.nat0 : xfv.nat0) + TILE * 2, t, s);
     } else {
-      return nat.ld(sKV[buf] + kv * TILE, t, s);
+      if (kv == 0) return nat.ld(sKV[buf], t, s);
+      return natv.ld(sKV[buf] + TILE, t, s);
     }
   };
   auto ld_tr = [&](int buf, int t, int s) -> Op {
@@ -608,13 +665,17 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   auto s_phase = [&](int buf) {
     st0 = f32x16{}; st1 = f32x16{}; dp0 = f32x16{}; dp1 = f32x16{};
 #pragma unroll
-    for (int s = 0; s < NSD; ++s) {
-      st0 = M::mma(ld_nat(buf, 0, 0, s), qop[s], st0);
-      st1 = M::mma(ld_nat(buf, 0, 1, s), qop[s], st1);
-      dp0 = M::mma(ld_nat(buf, 1, 0, s), gop[s], dp0);
-      dp1 = M::mma(ld_nat(buf, 1, 1, s), gop[s], dp1);
+    for (int s = 0; s < (NSD > NSDV ? NSD : NSDV); ++s) {
+      if (s < NSD) {
+        st0 = M::mma(ld_nat(buf, 0, 0, s), qop[s], st0);
+        st1 = M::mma(ld_nat(buf, 0, 1, s), qop[s], st1);
+      }
+      if (s < NSDV) {
+        dp0 = M::mma(ld_nat(buf, 1, 0, s), gop[s], dp0);
+        dp1 = M::mma(ld_nat(buf, 1, 1, s), gop[s], dp1);
+      }
     }
-    sched_interleave<4 * NSD, 4>();
+    sched_interleave<2 * NSD + 2 * NSDV, 4>();
   };
   // dS^T from the tile's S^T, dP^T, then dQ^T += K^T dS^T (K^T through
   // transposed reads of the key tile).
@@ -681,31 +742,42 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   }
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, int DV = D>
 hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   const long long prows = (long long)a.B * a.Hq * a.Tqp;
   if ((stages & kStagePre) && prows > 0) {
-    hipError_t e = launch(bwd_pre_kernel<T, D>, (prows + 15) / 16, stream, a);
+    hipError_t e = launch(bwd_pre_kernel<T, DV>, (prows + 15) / 16, stream, a);
     if (e != hipSuccess) return e;
   }
   const long long kblocks = (long long)((a.Tk + 127) / 128) * a.B * a.Hkv;
   if ((stages & kStageDkDv) && kblocks > 0) {
-    hipError_t e = a.window > 0 ? launch(dkdv_kernel<T, D, CAUSAL, true>, kblocks, stream, a)
-                                : launch(dkdv_kernel<T, D, CAUSAL, false>, kblocks, stream, a);
+    hipError_t e = a.window > 0 ? launch(dkdv_kernel<T, D, CAUSAL, true, DV>, kblocks, stream, a)
+                                : launch(dkdv_kernel<T, D, CAUSAL, false, DV>, kblocks, stream, a);
     if (e != hipSuccess) return e;
   }
   constexpr int NW = dq_waves<T, D>();
   const long long qblocks = (long long)((a.Tq + 32 * NW - 1) / (32 * NW)) * a.B * a.Hq;
   if ((stages & kStageDq) && qblocks > 0) {
-    hipError_t e = a.window > 0 ? launch<64 * NW>(dq_kernel<T, D, CAUSAL, true>, qblocks, stream, a)
-                                : launch<64 * NW>(dq_kernel<T, D, CAUSAL, false>, qblocks, stream, a);
+    hipError_t e = a.window > 0 ? launch<64 * NW>(dq_kernel<T, D, CAUSAL, true, DV>, qblocks, stream, a)
+                                : launch<64 * NW>(dq_kernel<T, D, CAUSAL, false, DV>, qblocks, stream, a);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int d, int causal, unsigned stages,
-                      hipStream_t stream) {
+                      hipStream_t stream, int dv) {
+  if (dv < 0) dv = d;
+  if (dv != d) {                                     // bf16 only: d = 128 with dv = 64, and the reverse
+    if (!dtype_bf16) return hipErrorInvalidValue;
+    if (d == 128 && dv == 64)
+      return causal ? launch_bwd_t<bf16, 128, true, 64>(a, stages, stream)
+                    : launch_bwd_t<bf16, 128, false, 64>(a, stages, stream);
+    if (d == 64 && dv == 128)
+      return causal ? launch_bwd_t<bf16, 64, true, 128>(a, stages, stream)
+                    : launch_bwd_t<bf16, 64, false, 128>(a, stages, stream);
+    return hipErrorInvalidValue;
+  }
 #define FA_BWD_CASE(T, DD)                                                                         \
   if (d == DD)                                                                                     \
     return causal ? launch_bwd_t<T, DD, true>(a, stages, stream) : launch_bwd_t<T, DD, false>(a, stages, stream);

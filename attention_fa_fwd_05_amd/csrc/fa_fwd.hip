@@ -51,7 +51,8 @@ template <typename T, int D, bool DEC = false> struct FwdShape {
   static constexpr int BK = DEC ? 64 : (sizeof(T) == 4 && D == 128) ? 64 : 128;
 };
 
-template <typename T, int D, bool CAUSAL, bool WIN, bool DEC>
+// D: head dim of Q and K; DV: head dim of V and O.
+template <typename T, int D, bool CAUSAL, bool WIN, bool DEC, int DV = D>
 __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void fwd_kernel(FwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
@@ -62,11 +63,11 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
   constexpr int KPER = M::KPER;
   constexpr int NSD = (D / 2) / KPER;               // steps over the head dim
   constexpr int NSK = (BK / 2) / KPER;              // steps over a key tile
-  constexpr int NDT = D / 32;                       // 32-wide output tiles
+  constexpr int NDT = DV / 32;                      // 32-wide output tiles
   // K / V tiles, swizzled, double-buffered; the next tile is fetched by direct
   // global->LDS loads while the current one is used.
   __shared__ __attribute__((aligned(16))) T sK[2][BK * D];
-  __shared__ __attribute__((aligned(16))) T sV[2][BK * D];
+  __shared__ __attribute__((aligned(16))) T sV[2][BK * DV];
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, n = lane & 31;
@@ -112,7 +113,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
 
   const T* Qp = reinterpret_cast<const T*>(a.Q) + qrow0 * D;
   const T* Kp = reinterpret_cast<const T*>(a.K) + sq.k_row(hk) * D;
-  const T* Vp = reinterpret_cast<const T*>(a.V) + sq.k_row(hk) * D;
+  const T* Vp = reinterpret_cast<const T*>(a.V) + sq.k_row(hk) * DV;
 
   // Key tiles jt0 .. ntiles - 1: those before the sliding window of the
   // block's first query, and those after the causal bound of its last, are
@@ -132,20 +133,23 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
   // tabulated once; in the tile holding the key end, rows past Tk are loaded
   // as copies of the last key (their scores are masked).
   using DR = DmaRows<T, D, BK, NTHR>;
-  uint32_t src_off[DR::PER];
+  using DRV = DmaRows<T, DV, BK, NTHR>;
+  uint32_t src_off[DR::PER], src_offv[DRV::PER];
 #pragma unroll
   for (int i = 0; i < DR::PER; ++i) src_off[i] = DR::src_off(i);
+#pragma unroll
+  for (int i = 0; i < DRV::PER; ++i) src_offv[i] = D == DV ? src_off[i % DR::PER] : DRV::src_off(i);
   auto issue = [&](int k0, int buf) {
     if (k0 + BK <= Tk) {
       const T* kb = Kp + (size_t)k0 * D;
-      const T* vb = Vp + (size_t)k0 * D;
+      const T* vb = Vp + (size_t)k0 * DV;
 #pragma unroll
       for (int i = 0; i < DR::PER; ++i) dma16s(kb, src_off[i], lds_addr(sK[buf]) + DR::lds_off(i));
 #pragma unroll
-      for (int i = 0; i < DR::PER; ++i) dma16s(vb, src_off[i], lds_addr(sV[buf]) + DR::lds_off(i));
+      for (int i = 0; i < DRV::PER; ++i) dma16s(vb, src_offv[i], lds_addr(sV[buf]) + DRV::lds_off(i));
     } else {
       dma_rows<T, D, BK, NTHR>(sK[buf], Kp, k0, Tk);
-      dma_rows<T, D, BK, NTHR>(sV[buf], Vp, k0, Tk);
+      dma_rows<T, DV, BK, NTHR>(sV[buf], Vp, k0, Tk);
     }
   };
   if (jt0 < ntiles) issue(jt0 * BK, 0);
@@ -165,7 +169,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
   }
   NatFetch<T, D> nat;
   nat.init(n, h);
-  TrPermFetch<T, D> trp;
+  TrPermFetch<T, DV> trp;
   trp.init(lane);
   wait_vmcnt<0>();
   __syncthreads();
@@ -277,7 +281,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
         const size_t rows_all = (a.cu_q != nullptr) ? (size_t)a.Hq * a.total_q : (size_t)a.B * a.Hq * a.Tq;
         const size_t row = (size_t)blockIdx.y * rows_all + qrow0 + myq;
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        float* orow = a.Opart + row * D;
+        float* orow = a.Opart + row * DV;
 #pragma unroll
         for (int t = 0; t < NDT; ++t) {
 #pragma unroll
@@ -296,7 +300,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
     }
     if (active && myq < Tq) {
       const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-      T* orow = reinterpret_cast<T*>(a.O) + (qrow0 + myq) * D;
+      T* orow = reinterpret_cast<T*>(a.O) + (qrow0 + myq) * DV;
 #pragma unroll
       for (int t = 0; t < NDT; ++t) {
 #pragma unroll
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a, int nsplit) {
   if (j == 0) a.L[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, int DV = D>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream, int nsplit) {
   using SH = FwdShape<T, D>;
   const int nqb = (a.Tq + SH::BQ - 1) / SH::BQ;
@@ -366,18 +370,18 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream, int nsplit) {
   if constexpr (sizeof(T) == 2) {
     if (a.pack == 2) {
       using SD = FwdShape<T, D, true>;
-      e = a.window > 0 ? launch2<64 * SD::NW>(fwd_kernel<T, D, CAUSAL, true, true>, blocks, nsplit, stream, a)
-                       : launch2<64 * SD::NW>(fwd_kernel<T, D, CAUSAL, false, true>, blocks, nsplit, stream, a);
+      e = a.window > 0 ? launch2<64 * SD::NW>(fwd_kernel<T, D, CAUSAL, true, true, DV>, blocks, nsplit, stream, a)
+                       : launch2<64 * SD::NW>(fwd_kernel<T, D, CAUSAL, false, true, DV>, blocks, nsplit, stream, a);
       launched = true;
     }
   }
   if (!launched)
-    e = a.window > 0 ? launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, true, false>, blocks, nsplit, stream, a)
-                     : launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, false, false>, blocks, nsplit, stream, a);
+    e = a.window > 0 ? launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, true, false, DV>, blocks, nsplit, stream, a)
+                     : launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, false, false, DV>, blocks, nsplit, stream, a);
   if (e != hipSuccess || a.Opart == nullptr) return e;
   const long long rows = a.cu_q ? (long long)a.Hq * a.total_q : (long long)a.B * a.Hq * a.Tq;
   if (rows == 0) return hipSuccess;
-  return launch(fwd_merge_kernel<T, D>, (rows + 15) / 16, stream, a, nsplit);
+  return launch(fwd_merge_kernel<T, DV>, (rows + 15) / 16, stream, a, nsplit);
 }
 
 int fwd_waves(int dtype_bf16, int d) {
@@ -391,7 +395,19 @@ int fwd_block_keys(int dtype_bf16, int d) {
                     : (d == 64 ? FwdShape<float, 64>::BK : FwdShape<float, 128>::BK);
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream, int nsplit) {
+hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream, int nsplit,
+                      int dv) {
+  if (dv < 0) dv = d;
+  if (dv != d) {                                     // bf16 only: d = 128 with dv = 64, and the reverse
+    if (!dtype_bf16) return hipErrorInvalidValue;
+    if (d == 128 && dv == 64)
+      return causal ? launch_fwd_t<bf16, 128, true, 64>(a, stream, nsplit)
+                    : launch_fwd_t<bf16, 128, false, 64>(a, stream, nsplit);
+    if (d == 64 && dv == 128)
+      return causal ? launch_fwd_t<bf16, 64, true, 128>(a, stream, nsplit)
+                    : launch_fwd_t<bf16, 64, false, 128>(a, stream, nsplit);
+    return hipErrorInvalidValue;
+  }
 #define FA_FWD_CASE(T, DD)                                                              \
   if (d == DD)                                                                          \
     return causal ? launch_fwd_t<T, DD, true>(a, stream, nsplit) : launch_fwd_t<T, DD, false>(a, stream, nsplit);

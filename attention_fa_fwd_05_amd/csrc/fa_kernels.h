@@ -111,7 +111,10 @@ inline hipError_t launch2(void (*kernel)(Params...), long long blocks, int ny, h
 
 // Forward over nsplit key slices (nsplit >= 1; with Opart/Lpart set, the
 // slices' partials are merged into O and L by a second kernel).
-hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream, int nsplit = 1);
+// dv: head dim of V and O (d: of Q and K); dv != d only for bf16 with
+// (d, dv) = (128, 64) or (64, 128).
+hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream, int nsplit = 1,
+                      int dv = -1);
 // Waves per forward workgroup for a dtype and head dim (pack needs G <= waves).
 int fwd_waves(int dtype_bf16, int d);
 int fwd_block_keys(int dtype_bf16, int d);
@@ -121,6 +124,6 @@ int fwd_decode_block_keys();
 // Backward stages (bit mask): preprocess, dK/dV kernel, dQ kernel.
 constexpr unsigned kStagePre = 1u, kStageDkDv = 2u, kStageDq = 4u;
 hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int d, int causal, unsigned stages,
-                      hipStream_t stream);
+                      hipStream_t stream, int dv = -1);
 
 }  // namespace fa

@@ -7,7 +7,7 @@ bit-identical inputs.
 
 Recipe (for every workload): ``numpy.random.default_rng(seed)``, four
 ``standard_normal(..., dtype=float32)`` draws in the order Q [B,Hq,Tq,d],
-K [B,Hkv,Tk,d], V [B,Hkv,Tk,d], dO [B,Hq,Tq,d]; Q and K are then multiplied
+K [B,Hkv,Tk,d], V [B,Hkv,Tk,dv], dO [B,Hq,Tq,dv] (dv = d unless stated); Q and K are then multiplied
 by ``sigma_qk`` in float32 (1 unless stated); for bfloat16 workloads each
 value is rounded to bfloat16 with round-to-nearest-even on the float32 bits.
 """
@@ -33,6 +33,11 @@ class Workload:
     seed: int
     sigma_qk: float = 1.0
     window: int = 0      # > 0: sliding window of that many keys (query i sees j > i + Tk - Tq - window)
+    dv: int = 0          # head dim of V and O (and dO) when it differs from d; 0 means d
+
+    @property
+    def dvv(self) -> int:
+        return self.dv or self.d
 
     @property
     def G(self) -> int:
@@ -108,8 +113,8 @@ def make_inputs(w: Workload, seed: int | None = None) -> Inputs:
     rng = np.random.default_rng(w.seed if seed is None else seed)
     q = rng.standard_normal((w.B, w.Hq, w.Tq, w.d), dtype=np.float32)
     k = rng.standard_normal((w.B, w.Hkv, w.Tk, w.d), dtype=np.float32)
-    v = rng.standard_normal((w.B, w.Hkv, w.Tk, w.d), dtype=np.float32)
-    do = rng.standard_normal((w.B, w.Hq, w.Tq, w.d), dtype=np.float32)
+    v = rng.standard_normal((w.B, w.Hkv, w.Tk, w.dvv), dtype=np.float32)
+    do = rng.standard_normal((w.B, w.Hq, w.Tq, w.dvv), dtype=np.float32)
     if w.sigma_qk != 1.0:
         q *= np.float32(w.sigma_qk)
         k *= np.float32(w.sigma_qk)

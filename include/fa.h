@@ -214,6 +214,23 @@ int fa_bwd_varlen(const void* Q, const void* K, const void* V, const void* O, co
                   int total_k, int max_seqlen_q, int max_seqlen_k, int d, int causal, int window,
                   float scale, int dtype, void* stream);
 
+/*
+ * A value head dim dv different from the query/key head dim d ("What
+ * Ordinary Autograd Saves", section "The implementation under test": V is
+ * (Tk, dv)).  Layouts: Q, dQ [B][Hq][Tq][d]; K, dK [B][Hkv][Tk][d]; V, dV
+ * [B][Hkv][Tk][dv]; O, dO [B][Hq][Tq][dv]; L as usual.  Supported: dv == d
+ * (then identical to fa_fwd_window / fa_bwd_window), and for bf16 the pairs
+ * (d, dv) = (128, 64) and (64, 128); anything else is FA_ERR_HEAD_DIM.  All
+ * other arguments, ownership and errors are those of fa_fwd_window and
+ * fa_bwd_window (the backward workspace does not depend on d or dv).
+ */
+int fa_fwd_dv(const void* Q, const void* K, const void* V, void* O, float* L, int B, int Hq, int Hkv, int Tq,
+              int Tk, int d, int dv, int causal, int window, float scale, int dtype, void* stream);
+int fa_bwd_dv(const void* Q, const void* K, const void* V, const void* O, const float* L, const void* dO,
+              void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+              int Tq, int Tk, int d, int dv, int causal, int window, float scale, int dtype, unsigned stages,
+              void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* fa_status_string(int status);
 

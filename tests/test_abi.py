@@ -131,3 +131,9 @@ def test_splitk_rejects_too_many_slices(lib):
                              5000, None) == 9
     assert lib.fa_fwd_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 1, 2, 1, 16, 16, 64, 1, 0, 0.125, 1,
                              4, None) == 7
+
+
+@pytest.mark.parametrize("d,dv,dtype", [(128, 96, 1), (128, 256, 1), (128, 64, 0), (64, 128, 0), (96, 64, 1)])
+def test_dv_rejects_unsupported_pairs(lib, d, dv, dtype):
+    assert lib.fa_fwd_dv(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 16, 16, d, dv, 1, 0, 0.125, dtype, None) == 4
+    assert lib.fa_bwd_dv(*(FAKE,) * 10, 1 << 30, 1, 2, 1, 16, 16, d, dv, 1, 0, 0.125, dtype, 7, None) == 4
