@@ -26,7 +26,8 @@ STATUS = {
 STAGE_PRE, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
 EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_window", "fa_bwd_window", "fa_fwd_dv", "fa_bwd_dv",
            "fa_fwd_splitk",
-           "fa_fwd_splitk_workspace_bytes", "fa_fwd_varlen", "fa_bwd_varlen", "fa_bwd_workspace_bytes",
+           "fa_fwd_splitk_workspace_bytes", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fwd_paged",
+           "fa_fwd_paged_workspace_bytes", "fa_bwd_workspace_bytes",
            "fa_status_string", "fa_hip_error_string", "fa_abi_version"]
 
 _lib = None
@@ -78,6 +79,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_dv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                               i, i, i, i, i, i, i, i, i, f, i, ctypes.c_uint, vp]
     lib.fa_bwd_dv.restype = i
+    lib.fa_fwd_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, i, vp, sz, i, vp]
+    lib.fa_fwd_paged.restype = i
+    lib.fa_fwd_paged_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i]
+    lib.fa_fwd_paged_workspace_bytes.restype = sz
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_varlen.restype = i
     lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp,
@@ -245,6 +250,38 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     if st != 0:
         raise FaError(st, "fa_bwd_varlen")
     return dq, dk, dv
+
+
+def forward_paged(q, k_pages, v_pages, page_table, seqlens_k, causal: bool = False, scale: float | None = None,
+                  window: int = 0, nsplit: int = 0, workspace=None, out=None, lse=None):
+    """fa_fwd_paged: q [B, Hq, Tq, d]; k_pages, v_pages [num_pages, Hkv, page_size, d]; page_table
+    int32 [B, pages_per_seq]; seqlens_k int32 [B].  Returns (o like q, lse float32 [B, Hq, Tq])."""
+    import torch
+    lib = load_library()
+    if q.dim() != 4 or k_pages.dim() != 4 or tuple(v_pages.shape) != tuple(k_pages.shape):
+        raise ValueError("q [B, Hq, Tq, d], k_pages = v_pages shape [num_pages, Hkv, page_size, d]")
+    B, Hq, Tq, d = q.shape
+    num_pages, Hkv, page_size, dk = k_pages.shape
+    if dk != d or page_table.dim() != 2 or page_table.shape[0] != B or tuple(seqlens_k.shape) != (B,):
+        raise ValueError("inconsistent paged shapes")
+    for t in (q, k_pages, v_pages, page_table, seqlens_k):
+        if not t.is_contiguous() or t.device != q.device:
+            raise ValueError("tensors must be contiguous on q's device")
+    if page_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
+        raise ValueError("page_table and seqlens_k must be int32")
+    pps = page_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    need = int(lib.fa_fwd_paged_workspace_bytes(B, Hq, Hkv, Tq, pps, page_size, d, code, int(nsplit)))
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = lib.fa_fwd_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(o), _ptr(L), page_table.data_ptr(),
+                          seqlens_k.data_ptr(), B, Hq, Hkv, Tq, pps, page_size, num_pages, d, int(bool(causal)),
+                          int(window), scale, code, ws.data_ptr(), ws.numel(), int(nsplit), _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_fwd_paged")
+    return o, L
 
 
 def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,

@@ -265,6 +265,61 @@ int fa_fwd_splitk(const void* Q, const void* K, const void* V, void* O, float* L
   return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream, ns));
 }
 
+size_t fa_fwd_paged_workspace_bytes(int B, int Hq, int Hkv, int Tq, int pages_per_seq, int page_size, int d,
+                                    int dtype, int nsplit) {
+  if (pages_per_seq < 1 || page_size < 1) return 0;
+  const long long tk = (long long)pages_per_seq * page_size;
+  if (tk > kMaxSeq) return 0;
+  if (nsplit == 1) return 0;
+  return fa_fwd_splitk_workspace_bytes(B, Hq, Hkv, Tq, (int)tk, d, dtype, nsplit);
+}
+
+int fa_fwd_paged(const void* Q, const void* K_pages, const void* V_pages, void* O, float* L,
+                 const int* page_table, const int* seqlens_k, int B, int Hq, int Hkv, int Tq, int pages_per_seq,
+                 int page_size, int num_pages, int d, int causal, int window, float scale, int dtype,
+                 void* workspace, size_t workspace_bytes, int nsplit, void* stream) {
+  if (pages_per_seq < 1 || page_size < 1 || num_pages < 1) return FA_ERR_BAD_SHAPE;
+  if (page_size % 128 != 0) return FA_ERR_BAD_SHAPE;
+  const long long tk = (long long)pages_per_seq * page_size;
+  if (tk > kMaxSeq) return FA_ERR_TOO_LARGE;
+  int st = check_common(B, Hq, Hkv, Tq, (int)tk, d, dtype);
+  if (st != FA_OK) return st;
+  if (page_table == nullptr || seqlens_k == nullptr) return FA_ERR_NULL_PTR;
+  if ((reinterpret_cast<uintptr_t>(page_table) & 3u) || (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
+    return FA_ERR_ALIGNMENT;
+  const long long nq = (long long)B * Hq * Tq * d, npool = (long long)num_pages * Hkv * page_size * d;
+  if (npool > kMaxElems) return FA_ERR_TOO_LARGE;
+  if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, nq)) || (st = check_ptr(K_pages, npool)) ||
+      (st = check_ptr(V_pages, npool)) || (st = check_ptr(L, (long long)B * Hq * Tq)))
+    return st;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  const int ns = nsplit == 1 ? 1 : fwd_splits(B, Hq, Hkv, Tq, (int)tk, d, dtype, nsplit);
+  if (ns > kMaxSplits) return FA_ERR_TOO_LARGE;
+  const size_t need = ns == 1 ? 0 : splitk_ws_bytes(B, Hq, Tq, d, ns);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (misaligned(workspace)) return FA_ERR_ALIGNMENT;
+  }
+  if (Tq == 0) return FA_OK;
+  fa::FwdArgs a;
+  a.Q = Q; a.K = K_pages; a.V = V_pages; a.O = O; a.L = L;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = (int)tk;
+  a.window = window > 0 ? window : 0;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.pack = fwd_pack(Hq, Hkv, Tq, d, dtype);
+  a.cu_q = a.cu_k = nullptr;
+  a.total_q = a.total_k = 0;
+  a.pages = page_table;
+  a.seqlens_k = seqlens_k;
+  a.pages_per_seq = pages_per_seq;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
+  char* wsb = static_cast<char*>(workspace);
+  a.Opart = ns == 1 ? nullptr : reinterpret_cast<float*>(wsb);
+  a.Lpart = ns == 1 ? nullptr : reinterpret_cast<float*>(wsb + align_up((size_t)ns * B * Hq * Tq * d * 4));
+  return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream, ns));
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype) {
   if (check_common(B, Hq, Hkv, Tq, Tk, d, dtype) != FA_OK) return 0;
   return ws_layout(B, Hq, Tq, d, dtype).total;

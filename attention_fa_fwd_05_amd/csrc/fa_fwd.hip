@@ -139,8 +139,21 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
   for (int i = 0; i < DR::PER; ++i) src_off[i] = DR::src_off(i);
 #pragma unroll
   for (int i = 0; i < DRV::PER; ++i) src_offv[i] = D == DV ? src_off[i % DR::PER] : DRV::src_off(i);
+  // Paged keys: the tile's page from the sequence's page table (clamped into
+  // the pool); the whole page exists, so the tile loads without clamping rows
+  // (rows past the sequence's end are masked like any ragged tail).
   auto issue = [&](int k0, int buf) {
-    if (k0 + BK <= Tk) {
+    if (a.pages != nullptr) {
+      const int pg = min(max(__builtin_amdgcn_readfirstlane(a.pages[(size_t)b * a.pages_per_seq + k0 / a.page_size]),
+                             0), a.num_pages - 1);
+      const size_t row = ((size_t)pg * a.Hkv + hk) * a.page_size + k0 % a.page_size;
+      const T* kb = reinterpret_cast<const T*>(a.K) + row * D;
+      const T* vb = reinterpret_cast<const T*>(a.V) + row * DV;
+#pragma unroll
+      for (int i = 0; i < DR::PER; ++i) dma16s(kb, src_off[i], lds_addr(sK[buf]) + DR::lds_off(i));
+#pragma unroll
+      for (int i = 0; i < DRV::PER; ++i) dma16s(vb, src_offv[i], lds_addr(sV[buf]) + DRV::lds_off(i));
+    } else if (k0 + BK <= Tk) {
       const T* kb = Kp + (size_t)k0 * D;
       const T* vb = Vp + (size_t)k0 * DV;
 #pragma unroll

@@ -8,6 +8,7 @@
 namespace fa {
 
 struct FwdArgs {
+  static constexpr bool kPaged = true;   // may describe paged keys and values
   const void* Q;
   const void* K;
   const void* V;
@@ -30,6 +31,14 @@ struct FwdArgs {
   const int* cu_q;
   const int* cu_k;
   int total_q, total_k;
+  // Paged keys and values (pages != nullptr): K and V are pools of num_pages
+  // pages, [num_pages][Hkv][page_size][d] (V: [dv]); sequence b's key j is row
+  // j % page_size of page pages[b * pages_per_seq + j / page_size], and the
+  // sequence has seqlens_k[b] keys (Tk then holds pages_per_seq * page_size).
+  // page_size is a multiple of every key tile, so a tile lies in one page.
+  const int* pages = nullptr;
+  const int* seqlens_k = nullptr;
+  int pages_per_seq = 0, page_size = 0, num_pages = 0;
 };
 
 // One sequence of a batch: its lengths, and where its rows sit.  Row 0 of
@@ -61,6 +70,9 @@ __device__ inline SeqView seq_view(const A& a, int b) {
   } else {
     v.Tq = a.Tq;
     v.Tk = a.Tk;
+    if constexpr (A::kPaged) {
+      if (a.seqlens_k != nullptr) v.Tk = min(max(__builtin_amdgcn_readfirstlane(a.seqlens_k[b]), 0), a.Tk);
+    }
     v.q_base = (size_t)b * a.Hq * a.Tq;
     v.q_hstride = a.Tq;
     v.k_base = (size_t)b * a.Hkv * a.Tk;
@@ -70,6 +82,7 @@ __device__ inline SeqView seq_view(const A& a, int b) {
 }
 
 struct BwdArgs {
+  static constexpr bool kPaged = false;
   const void* Q;
   const void* K;
   const void* V;

@@ -231,6 +231,31 @@ int fa_bwd_dv(const void* Q, const void* K, const void* V, const void* O, const 
               int Tq, int Tk, int d, int dv, int causal, int window, float scale, int dtype, unsigned stages,
               void* stream);
 
+/*
+ * Forward over paged keys and values: a pool of fixed-size pages and a page
+ * table per sequence, the shape of the chunked-attention article's prefix
+ * cache, from which each block of new positions gathers its own prefix
+ * (section "The Scene").  K_pages and V_pages are [num_pages][Hkv][page_size][d];
+ * sequence b holds seqlens_k[b] keys (at most pages_per_seq * page_size), key
+ * j being row j % page_size of page page_table[b * pages_per_seq + j /
+ * page_size].  Q, O are [B][Hq][Tq][d] and L [B][Hq][Tq] as in fa_fwd; causal
+ * alignment and the window are per sequence (end-aligned on its own key
+ * count).  page_table and seqlens_k are device int32 arrays (B * pages_per_seq
+ * and B entries) that the host never reads; page indices are clamped into the
+ * pool and key counts into [0, pages_per_seq * page_size].  page_size must be a
+ * multiple of 128.  nsplit == 1 runs one pass with no workspace; otherwise the
+ * keys are split over slices and merged as in fa_fwd_splitk (nsplit <= 0:
+ * automatic), with a workspace of fa_fwd_paged_workspace_bytes bytes.  Errors
+ * as fa_fwd_splitk, plus FA_ERR_BAD_SHAPE for a page size that is not a
+ * positive multiple of 128 or an empty pool.
+ */
+size_t fa_fwd_paged_workspace_bytes(int B, int Hq, int Hkv, int Tq, int pages_per_seq, int page_size, int d,
+                                    int dtype, int nsplit);
+int fa_fwd_paged(const void* Q, const void* K_pages, const void* V_pages, void* O, float* L,
+                 const int* page_table, const int* seqlens_k, int B, int Hq, int Hkv, int Tq, int pages_per_seq,
+                 int page_size, int num_pages, int d, int causal, int window, float scale, int dtype,
+                 void* workspace, size_t workspace_bytes, int nsplit, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* fa_status_string(int status);
 

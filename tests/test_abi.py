@@ -137,3 +137,14 @@ def test_splitk_rejects_too_many_slices(lib):
 def test_dv_rejects_unsupported_pairs(lib, d, dv, dtype):
     assert lib.fa_fwd_dv(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 16, 16, d, dv, 1, 0, 0.125, dtype, None) == 4
     assert lib.fa_bwd_dv(*(FAKE,) * 10, 1 << 30, 1, 2, 1, 16, 16, d, dv, 1, 0, 0.125, dtype, 7, None) == 4
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=100), 2), (dict(P=0), 2), (dict(pps=0), 2), (dict(npages=0), 2), (dict(table=None), 1),
+    (dict(seqlens=None), 1), (dict(table=FAKE + 2), 8), (dict(d=80), 4),
+])
+def test_fwd_paged_rejects_bad_arguments(lib, kw, status):
+    a = dict(table=FAKE, seqlens=FAKE, pps=4, P=128, npages=8, d=64)
+    a.update(kw)
+    assert lib.fa_fwd_paged(FAKE, FAKE, FAKE, FAKE, FAKE, a["table"], a["seqlens"], 2, 2, 1, 16, a["pps"], a["P"],
+                            a["npages"], a["d"], 1, 0, 0.125, 1, None, 0, 1, None) == status

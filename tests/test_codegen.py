@@ -65,11 +65,11 @@ def test_m0_only_written_by_the_load_helpers(asm):
                     continue
                 assert not (in_idx and l.startswith("global_load_lds")), f"{src}:{name}: load inside an index bracket"
                 if re.search(r"\bm0\b", l):
-                    assert re.fullmatch(r"s_mov_b32 m0, s\d+", l), f"{src}:{name}: unexpected M0 use: {l}"
+                    assert re.fullmatch(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)", l), f"{src}:{name}: unexpected M0 use: {l}"
                     nxt = lines[i + 1]
                     assert nxt.startswith("global_load_lds_dword"), f"{src}:{name}: M0 write not followed by a load: {nxt}"
                 if l.startswith("global_load_lds_dword"):
-                    assert re.fullmatch(r"s_mov_b32 m0, s\d+", lines[i - 1]), f"{src}:{name}: load without M0 set: {l}"
+                    assert re.fullmatch(r"s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)", lines[i - 1]), f"{src}:{name}: load without M0 set: {l}"
 
 
 def test_bf16_kernels_use_no_scratch(asm):
