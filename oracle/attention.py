@@ -42,7 +42,13 @@ Readings where the pages are silent (each is listed in the design notes):
   span than the full-attention layer) lets query i see only keys
   j > i + (Tk - Tq) - window, i.e. at most ``window`` keys ending at its
   end-aligned diagonal position; it combines with the causal bound, and
-  window <= 0 means no window.
+  window <= 0 means no window;
+* a caller's boolean mask (the chunked-attention article, section "The GQA
+  Expansion Question": a boolean attention mask together with grouped-query
+  heads) is a [Tq, Tk] array, True where key j may be seen by query i, shared
+  by every head of a batch entry ([B, Tq, Tk] for one per entry, or [Tq, Tk]
+  for the whole batch); it narrows visibility further, after the causal
+  bound and the window.
 
 Layouts: Q, dO are [B, Hq, Tq, d]; K is [B, Hkv, Tk, d]; V is [B, Hkv, Tk, dv];
 O is [B, Hq, Tq, dv]; L is [B, Hq, Tq].  Query head h reads key/value head
@@ -66,11 +72,12 @@ def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
 
-def visible(Tq: int, Tk: int, causal: bool, window: int = 0) -> np.ndarray:
+def visible(Tq: int, Tk: int, causal: bool, window: int = 0, mask=None) -> np.ndarray:
     """Boolean [Tq, Tk] visibility of key j to query i.
 
     All True, narrowed by the end-aligned causal bound j <= i + Tk - Tq when
-    causal, and by the sliding window j > i + Tk - Tq - window when window > 0.
+    causal, by the sliding window j > i + Tk - Tq - window when window > 0,
+    and by a boolean [Tq, Tk] mask when one is given.
     """
     i = np.arange(Tq)[:, None]
     j = np.arange(Tk)[None, :]
@@ -79,6 +86,11 @@ def visible(Tq: int, Tk: int, causal: bool, window: int = 0) -> np.ndarray:
         vis &= j <= i + (Tk - Tq)
     if window > 0:
         vis &= j > i + (Tk - Tq) - window
+    if mask is not None:
+        mask = np.asarray(mask, dtype=bool)
+        if mask.shape != (Tq, Tk):
+            raise ValueError(f"mask must be [{Tq}, {Tk}], got {mask.shape}")
+        vis &= mask
     return vis
 
 
@@ -94,14 +106,15 @@ def _check_shapes(Q, K, V):
     return B, Hq, Hkv, Tq, Tk, d, V.shape[3]
 
 
-def head_forward(q, k, v, causal, scale, rows=None, Tq=None, window=0):
+def head_forward(q, k, v, causal, scale, rows=None, Tq=None, window=0, mask=None):
     """One query head against its key/value head, dense, fp64.
 
     Returns (O [Tq, dv], L [Tq], P [Tq, Tk]).  Steps as in standard attention:
     S = scale q k^T; masked scores do not exist (probability 0); per row
     m = max visible S, l = sum exp(S - m), L = m + ln l, P = exp(S - m) / l;
     O = P v.  With ``rows`` given, q holds only those query rows of a head
-    with ``Tq`` rows (the causal mask needs their positions).
+    with ``Tq`` rows (the causal mask needs their positions); ``mask`` is the
+    head's whole [Tq, Tk] boolean mask in either case.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -109,9 +122,9 @@ def head_forward(q, k, v, causal, scale, rows=None, Tq=None, window=0):
     Tk = k.shape[0]
     if rows is None:
         Tq = q.shape[0]
-        vis = visible(Tq, Tk, causal, window)
+        vis = visible(Tq, Tk, causal, window, mask)
     else:
-        vis = visible(Tq, Tk, causal, window)[np.asarray(rows)]
+        vis = visible(Tq, Tk, causal, window, mask)[np.asarray(rows)]
     S = (q @ k.T) * scale
     Sm = np.where(vis, S, -np.inf)
     m = Sm.max(axis=1) if Tk > 0 else np.full(q.shape[0], -np.inf)
@@ -145,18 +158,29 @@ def head_backward(q, k, v, dO, O, P, scale):
     return dq, dk, dv
 
 
-def attention_forward(Q, K, V, causal=False, scale=None, window=0):
-    """Dense exact attention with GQA: returns O [B,Hq,Tq,dv] and L [B,Hq,Tq] (fp64)."""
+def attention_forward(Q, K, V, causal=False, scale=None, window=0, mask=None):
+    """Dense exact attention with GQA: returns O [B,Hq,Tq,dv] and L [B,Hq,Tq] (fp64).
+
+    ``mask``: optional boolean [Tq, Tk] (every batch entry) or [B, Tq, Tk],
+    shared by all heads of an entry.
+    """
     B, Hq, Hkv, Tq, Tk, d, dv = _check_shapes(Q, K, V)
     if scale is None:
         scale = default_scale(d)
+    if mask is not None:
+        mask = np.asarray(mask, dtype=bool)
+        if mask.ndim == 2:
+            mask = np.broadcast_to(mask, (B,) + mask.shape)
+        if mask.shape != (B, Tq, Tk):
+            raise ValueError(f"mask must be [{Tq}, {Tk}] or [{B}, {Tq}, {Tk}], got {mask.shape}")
     G = Hq // Hkv
     O = np.zeros((B, Hq, Tq, dv))
     L = np.zeros((B, Hq, Tq))
     for b in range(B):
         for h in range(Hq):
             g = h // G
-            O[b, h], L[b, h], _ = head_forward(Q[b, h], K[b, g], V[b, g], causal, scale, window=window)
+            O[b, h], L[b, h], _ = head_forward(Q[b, h], K[b, g], V[b, g], causal, scale, window=window,
+                                               mask=None if mask is None else mask[b])
     return O, L
 
 
