@@ -28,6 +28,7 @@ EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_window", "fa_bwd_window"
            "fa_fwd_splitk",
            "fa_fwd_splitk_workspace_bytes", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fwd_paged",
            "fa_fwd_paged_workspace_bytes", "fa_bwd_workspace_bytes",
+           "fa_mask_row_words", "fa_mask_pack", "fa_fwd_mask",
            "fa_status_string", "fa_hip_error_string", "fa_abi_version"]
 
 _lib = None
@@ -88,6 +89,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp,
                                   i, i, i, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_bwd_varlen.restype = i
+    ll = ctypes.c_longlong
+    lib.fa_mask_row_words.argtypes = [i]
+    lib.fa_mask_row_words.restype = i
+    lib.fa_mask_pack.argtypes = [vp, vp, ll, i, vp]
+    lib.fa_mask_pack.restype = i
+    lib.fa_fwd_mask.argtypes = [vp, vp, vp, vp, vp, vp, ll, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_mask.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -281,6 +289,58 @@ def forward_paged(q, k_pages, v_pages, page_table, seqlens_k, causal: bool = Fal
                           int(window), scale, code, ws.data_ptr(), ws.numel(), int(nsplit), _stream(q))
     if st != 0:
         raise FaError(st, "fa_fwd_paged")
+    return o, L
+
+
+def pack_mask(mask, Tk: int | None = None):
+    """fa_mask_pack: a boolean (or uint8, nonzero = visible) mask [..., Tq, Tk] on the GPU to the
+    library's bit layout, int32 [..., Tq, fa_mask_row_words(Tk)] (the same leading dims)."""
+    import torch
+    lib = load_library()
+    if mask.dtype not in (torch.bool, torch.uint8) or not mask.is_contiguous() or mask.dim() < 2:
+        raise ValueError("mask must be a contiguous bool or uint8 tensor [..., Tq, Tk]")
+    Tk = mask.shape[-1] if Tk is None else Tk
+    if Tk != mask.shape[-1]:
+        raise ValueError("Tk does not match the mask")
+    rw = lib.fa_mask_row_words(Tk)
+    if rw < 0:
+        raise ValueError(f"Tk {Tk} out of range")
+    rows = mask.numel() // Tk if Tk > 0 else math.prod(mask.shape[:-1])
+    bits = torch.empty(tuple(mask.shape[:-1]) + (rw,), dtype=torch.int32, device=mask.device)
+    st = lib.fa_mask_pack(_ptr(mask), _ptr(bits), rows, Tk, _stream(mask))
+    if st != 0:
+        raise FaError(st, "fa_mask_pack")
+    return bits
+
+
+def forward_masked(q, k, v, mask, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """fa_fwd_mask: attention under a boolean mask shared by all heads of a batch entry.
+
+    ``mask``: bool/uint8 [Tq, Tk] (whole batch) or [B, Tq, Tk] (or [B, 1, Tq, Tk]), packed here
+    with fa_mask_pack; or an already packed int32 [..., Tq, fa_mask_row_words(Tk)].
+    Returns (o like q, lse float32 [B, Hq, Tq])."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
+    if mask.device != q.device:
+        raise ValueError("mask must be on q's device")
+    if mask.dim() == 4 and mask.shape[1] == 1:
+        mask = mask[:, 0]
+    bits = mask if mask.dtype == torch.int32 else pack_mask(mask.contiguous(), Tk)
+    rw = lib.fa_mask_row_words(Tk)
+    if not bits.is_contiguous() or tuple(bits.shape[-2:]) != (Tq, rw) or bits.dim() not in (2, 3):
+        raise ValueError(f"packed mask must be int32 [Tq, {rw}] or [B, Tq, {rw}]")
+    if bits.dim() == 3 and bits.shape[0] != B:
+        raise ValueError("per-entry mask needs B entries")
+    stride = Tq * rw if bits.dim() == 3 and B > 1 else 0
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    o = torch.empty_like(q) if out is None else out
+    L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = lib.fa_fwd_mask(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(bits), stride, B, Hq, Hkv, Tq, Tk, d,
+                         int(bool(causal)), scale, code, _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_fwd_mask")
     return o, L
 
 

@@ -138,7 +138,7 @@ size_t splitk_ws_bytes(int B, int Hq, int Tq, int d, int ns) {
 
 extern "C" {
 
-int fa_abi_version(void) { return (1 << 16) | 1; }
+int fa_abi_version(void) { return (1 << 16) | 2; }
 
 const char* fa_hip_error_string(void) { return t_hip_error; }
 
@@ -223,6 +223,54 @@ int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L
   a.cu_k = cu_seqlens_k;
   a.total_q = total_q;
   a.total_k = total_k;
+  return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream));
+}
+
+int fa_mask_row_words(int Tk) { return Tk < 0 || Tk > kMaxSeq ? -1 : 4 * ((Tk + 127) / 128); }
+
+int fa_mask_pack(const void* mask_bytes, uint32_t* mask_bits, long long rows, int Tk, void* stream) {
+  if (rows < 0 || Tk < 0) return FA_ERR_BAD_SHAPE;
+  if (Tk > kMaxSeq) return FA_ERR_TOO_LARGE;
+  const int rw = fa_mask_row_words(Tk);
+  if (rows > kMaxElems / (Tk > 0 ? Tk : 1) || rows * rw / 256 + 1 > kMaxGrid) return FA_ERR_TOO_LARGE;
+  if (rows * Tk > 0 && mask_bytes == nullptr) return FA_ERR_NULL_PTR;
+  int st;
+  if ((st = check_ptr(mask_bits, rows * rw))) return st;
+  return hip_status(fa::launch_mask_pack(static_cast<const uint8_t*>(mask_bytes), mask_bits, rows, Tk, rw,
+                                         (hipStream_t)stream));
+}
+
+int fa_fwd_mask(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
+                long long mask_batch_stride, int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal,
+                float scale, int dtype, void* stream) {
+  int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
+  if (st != FA_OK) return st;
+  const long long nq = (long long)B * Hq * Tq * d, nkv = (long long)B * Hkv * Tk * d;
+  if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, nq)) || (st = check_ptr(K, nkv)) ||
+      (st = check_ptr(V, nkv)) || (st = check_ptr(L, (long long)B * Hq * Tq)))
+    return st;
+  const long long rw = fa_mask_row_words(Tk), mwords = (long long)Tq * rw;
+  if (mask_batch_stride != 0 && mask_batch_stride < mwords) return FA_ERR_BAD_SHAPE;
+  if (mask_batch_stride < 0) return FA_ERR_BAD_SHAPE;
+  if (mask_batch_stride % 4 != 0) return FA_ERR_ALIGNMENT;     // every row stays 16-byte aligned
+  if (mask_batch_stride > kMaxElems / B) return FA_ERR_TOO_LARGE;
+  if ((st = check_ptr(mask_bits, mwords))) return st;
+  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (Tq == 0) return FA_OK;
+  fa::FwdArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
+  a.window = 0;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  const int G = Hq / Hkv, nw = fa::fwd_waves(dtype == FA_DTYPE_BF16, d);
+  a.pack = (G <= nw && Tq <= 32 * (nw / G)) ? 1 : 0;   // the plain shape's packing only
+  a.Opart = nullptr;
+  a.Lpart = nullptr;
+  a.cu_q = a.cu_k = nullptr;
+  a.total_q = a.total_k = 0;
+  a.mask = Tk > 0 ? mask_bits : nullptr;
+  a.mask_bstride = mask_batch_stride;
+  a.mask_row_words = (int)rw;
   return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream));
 }
 

@@ -51,8 +51,9 @@ template <typename T, int D, bool DEC = false> struct FwdShape {
   static constexpr int BK = DEC ? 64 : (sizeof(T) == 4 && D == 128) ? 64 : 128;
 };
 
-// D: head dim of Q and K; DV: head dim of V and O.
-template <typename T, int D, bool CAUSAL, bool WIN, bool DEC, int DV = D>
+// D: head dim of Q and K; DV: head dim of V and O.  MASK: scores are also
+// masked by a caller's boolean mask (FwdArgs::mask).
+template <typename T, int D, bool CAUSAL, bool WIN, bool DEC, int DV = D, bool MASK = false>
 __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void fwd_kernel(FwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
@@ -184,6 +185,17 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
   nat.init(n, h);
   TrPermFetch<T, DV> trp;
   trp.init(lane);
+  // Boolean mask: this lane's row of bits (query qw + n; rows past Tq read
+  // the last row and are never stored), one word per 32-key sub-tile, loaded
+  // a tile ahead into registers.
+  static_assert(!MASK || (QT == 1 && !WIN && !DEC), "the masked forward uses the plain shape");
+  typedef uint32_t MaskWords __attribute__((ext_vector_type(NKT)));
+  const uint32_t* mrow = nullptr;
+  MaskWords mcur{}, mnext{};
+  if constexpr (MASK) {
+    mrow = a.mask + (size_t)b * a.mask_bstride + (size_t)min(qw + n, Tq - 1) * a.mask_row_words;
+    if (jt0 < ntiles) mcur = *reinterpret_cast<const MaskWords*>(mrow + jt0 * NKT);
+  }
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -203,10 +215,18 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
     if (jt + 1 < ntiles) issue(k0 + BK, buf ^ 1);
     const T* cK = sK[buf];
     const T* cV = sV[buf];
+    bool any = true;
+    if constexpr (MASK) {
+      if (jt + 1 < ntiles) mnext = *reinterpret_cast<const MaskWords*>(mrow + (jt + 1) * NKT);
+      uint32_t orr = 0;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) orr |= mcur[kt];
+      any = __ballot(orr != 0) != 0;                 // the mask leaves some key of the tile to the wave
+    }
 
     // Some key of the tile is visible to this wave: not all after the causal
     // bound of its last row, nor all before the window of its first.
-    if (active && !(CAUSAL && k0 > qw + 32 * QT - 1 + off) && !(W > 0 && k0 + BK - 1 < qw + off - W + 1)) {
+    if (active && any && !(CAUSAL && k0 > qw + 32 * QT - 1 + off) && !(W > 0 && k0 + BK - 1 < qw + off - W + 1)) {
       // S^T = K Q^T: NKT key sub-tiles x QT query tiles; each K operand feeds QT products.
       f32x16 st[QT][NKT];
 #pragma unroll
@@ -224,7 +244,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
       }
       sched_interleave<NKT * NSD * QT, 4 * QT, 1, QT>();
 
-      const bool need_mask = (k0 + BK > Tk) || (CAUSAL && k0 + BK - 1 > qw + off) ||
+      const bool need_mask = MASK || (k0 + BK > Tk) || (CAUSAL && k0 + BK - 1 > qw + off) ||
                              (W > 0 && k0 < qw + 32 * QT - 1 + off - W + 1);
       Op pop[QT][NSK];
 #pragma unroll
@@ -240,6 +260,16 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
 #pragma unroll
           for (int r = 0; r < NE; ++r)
             if (perm_index(0, r) > lim || perm_index(0, r) < lo) x[r] = -INFINITY;
+          if constexpr (MASK) {
+            // Key k0 + perm_index(h, r) is bit perm_index(h, r) % 32 of word r / 16,
+            // i.e. bit perm_index(0, r) % 32 after shifting out this half's 4 h.
+#pragma unroll
+            for (int r = 0; r < NE; ++r) {
+              const uint32_t wsh = mcur[r >> 4] >> (4 * h);
+              const int keep = (int)(wsh << (31 - perm_index(0, r) % 32)) >> 31;   // 0 or all ones
+              x[r] = __int_as_float((__float_as_int(x[r]) & keep) | (int)(0xff800000u & ~(uint32_t)keep));
+            }
+          }
         }
         float mt = wave_xor32_max(max_tree<NE>(x)) * c;   // row max, exp2 units
         const bool need = mt > m_run[u] + kTau;
@@ -283,6 +313,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
     }
     wait_vmcnt<0>();                                 // this wave's loads of the next tile have landed
     __syncthreads();
+    if constexpr (MASK) mcur = mnext;
   }
 
 #pragma unroll
@@ -380,8 +411,16 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream, int nsplit) {
   if (blocks == 0) return hipSuccess;
   hipError_t e = hipSuccess;
   bool launched = false;
+  // A boolean mask: the plain shape (any packing fits it: packed rows of the
+  // decode shape fit its waves too); no window, split or paging.
+  if constexpr (DV == D) {
+    if (a.mask != nullptr) {
+      e = launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, false, false, D, true>, blocks, nsplit, stream, a);
+      launched = true;
+    }
+  }
   if constexpr (sizeof(T) == 2) {
-    if (a.pack == 2) {
+    if (!launched && a.pack == 2) {
       using SD = FwdShape<T, D, true>;
       e = a.window > 0 ? launch2<64 * SD::NW>(fwd_kernel<T, D, CAUSAL, true, true, DV>, blocks, nsplit, stream, a)
                        : launch2<64 * SD::NW>(fwd_kernel<T, D, CAUSAL, false, true, DV>, blocks, nsplit, stream, a);
@@ -395,6 +434,28 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream, int nsplit) {
   const long long rows = a.cu_q ? (long long)a.Hq * a.total_q : (long long)a.B * a.Hq * a.Tq;
   if (rows == 0) return hipSuccess;
   return launch(fwd_merge_kernel<T, DV>, (rows + 15) / 16, stream, a, nsplit);
+}
+
+// Boolean mask bytes [rows][Tk] (nonzero: visible) to the forward's bit
+// layout [rows][row_words]: one thread per 32-bit word, bit e of word w from
+// byte 32 w + e; bits past Tk are 0.
+__global__ __launch_bounds__(256) void mask_pack_kernel(const uint8_t* in, uint32_t* out, long long rows, int Tk,
+                                                         int row_words) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * row_words) return;
+  const long long r = i / row_words;
+  const int j0 = (int)(i % row_words) * 32;
+  const uint8_t* src = in + r * Tk;
+  uint32_t v = 0;
+  for (int e = 0; e < 32 && j0 + e < Tk; ++e) v |= (src[j0 + e] != 0 ? 1u : 0u) << e;
+  out[i] = v;
+}
+
+hipError_t launch_mask_pack(const uint8_t* in, uint32_t* out, long long rows, int Tk, int row_words,
+                            hipStream_t stream) {
+  const long long words = rows * row_words;
+  if (words == 0) return hipSuccess;
+  return launch(mask_pack_kernel, (words + 255) / 256, stream, in, out, rows, Tk, row_words);
 }
 
 int fwd_waves(int dtype_bf16, int d) {

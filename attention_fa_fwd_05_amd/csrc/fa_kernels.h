@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa {
 
@@ -39,6 +40,15 @@ struct FwdArgs {
   const int* pages = nullptr;
   const int* seqlens_k = nullptr;
   int pages_per_seq = 0, page_size = 0, num_pages = 0;
+  // Boolean mask (mask != nullptr): bit j % 32 of word mask[b * mask_bstride +
+  // i * mask_row_words + j / 32] set means key j is visible to query i (then
+  // also subject to the causal rule and j < Tk), for every head of batch
+  // entry b; mask_row_words = 4 * ceil(Tk / 128), so a 128-key tile's bits
+  // of a row are one aligned 16-byte word group; mask_bstride 0 shares one
+  // mask across the batch.
+  const uint32_t* mask = nullptr;
+  long long mask_bstride = 0;
+  int mask_row_words = 0;
 };
 
 // One sequence of a batch: its lengths, and where its rows sit.  Row 0 of
@@ -128,6 +138,9 @@ inline hipError_t launch2(void (*kernel)(Params...), long long blocks, int ny, h
 // (d, dv) = (128, 64) or (64, 128).
 hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream, int nsplit = 1,
                       int dv = -1);
+// Pack a boolean byte mask [rows][Tk] into FwdArgs::mask's bit layout.
+hipError_t launch_mask_pack(const uint8_t* in, uint32_t* out, long long rows, int Tk, int row_words,
+                            hipStream_t stream);
 // Waves per forward workgroup for a dtype and head dim (pack needs G <= waves).
 int fwd_waves(int dtype_bf16, int d);
 int fwd_block_keys(int dtype_bf16, int d);

@@ -53,6 +53,7 @@
 #define FA05_FA_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -255,6 +256,42 @@ int fa_fwd_paged(const void* Q, const void* K_pages, const void* V_pages, void* 
                  const int* page_table, const int* seqlens_k, int B, int Hq, int Hkv, int Tq, int pages_per_seq,
                  int page_size, int num_pages, int d, int causal, int window, float scale, int dtype,
                  void* workspace, size_t workspace_bytes, int nsplit, void* stream);
+
+/*
+ * Boolean attention mask with grouped-query heads ("The Autograd Memory Trap:
+ * Diagnosing a Backward-Pass OOM in Chunked Attention", section "The GQA
+ * Expansion Question": a caller's boolean mask together with query heads that
+ * share K/V heads, here without repeating K and V).  Forward only.
+ *
+ * Layout of the mask: 32-bit words, mask_bits[b * mask_batch_stride + i *
+ * fa_mask_row_words(Tk) + j / 32], bit j % 32 set meaning key j is visible to
+ * query i, for every query head of batch entry b.  Rows hold
+ * fa_mask_row_words(Tk) = 4 * ceil(Tk / 128) words (bits past Tk are ignored).
+ * mask_batch_stride (in words) is 0 for one mask shared by the whole batch,
+ * else at least Tq * fa_mask_row_words(Tk).  fa_mask_row_words returns -1 for
+ * Tk < 0 or Tk above the library's sequence limit.
+ *
+ * fa_mask_pack converts a byte mask, rows x Tk bytes, row-major, nonzero =
+ * visible (a torch.bool tensor's storage), to that layout: rows * row words,
+ * written in full (padding bits 0).  mask_bits must be 16-byte aligned;
+ * neither buffer is read by the host.  Errors: FA_ERR_BAD_SHAPE for negative
+ * sizes, FA_ERR_NULL_PTR / FA_ERR_ALIGNMENT for the buffers, FA_ERR_TOO_LARGE,
+ * FA_ERR_HIP.
+ *
+ * fa_fwd_mask computes fa_fwd's O and L where key j is visible to query i
+ * iff its mask bit is set, j < Tk and, if causal, j <= i + Tk - Tq.  Rows
+ * without a visible key get O = 0 and L = -inf.  d = dv in {64, 128}, both
+ * dtypes; no window.  The mask must be 16-byte aligned (it may be NULL only
+ * when Tq * fa_mask_row_words(Tk) == 0).  Errors as fa_fwd, plus
+ * FA_ERR_BAD_SHAPE for a mask_batch_stride that is negative or between 0 and
+ * Tq * fa_mask_row_words(Tk), FA_ERR_ALIGNMENT for one that is not a multiple
+ * of 4.  With a nonzero stride the mask holds B such entries.
+ */
+int fa_mask_row_words(int Tk);
+int fa_mask_pack(const void* mask_bytes, uint32_t* mask_bits, long long rows, int Tk, void* stream);
+int fa_fwd_mask(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
+                long long mask_batch_stride, int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal,
+                float scale, int dtype, void* stream);
 
 /* Static English text for a status code (never NULL). */
 const char* fa_status_string(int status);

@@ -148,3 +148,27 @@ def test_fwd_paged_rejects_bad_arguments(lib, kw, status):
     a.update(kw)
     assert lib.fa_fwd_paged(FAKE, FAKE, FAKE, FAKE, FAKE, a["table"], a["seqlens"], 2, 2, 1, 16, a["pps"], a["P"],
                             a["npages"], a["d"], 1, 0, 0.125, 1, None, 0, 1, None) == status
+
+
+def test_mask_row_words(lib):
+    assert [lib.fa_mask_row_words(t) for t in (0, 1, 127, 128, 129, 1000)] == [0, 4, 4, 4, 8, 32]
+    assert lib.fa_mask_row_words(-1) == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mask=None), 1), (dict(mask=FAKE + 4), 8), (dict(stride=-1), 2), (dict(stride=5), 2), (dict(stride=16 * 12 + 2), 8),
+    (dict(d=80), 4), (dict(Hkv=3), 3), (dict(scale=math.nan), 6),
+])
+def test_fwd_mask_rejects_bad_arguments(lib, kw, status):
+    a = dict(mask=FAKE, stride=0, d=64, Hkv=2, scale=0.125)
+    a.update(kw)
+    assert lib.fa_fwd_mask(FAKE, FAKE, FAKE, FAKE, FAKE, a["mask"], a["stride"], 2, 4, a["Hkv"], 16, 300, a["d"], 1,
+                           a["scale"], 1, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, FAKE, -1, 10), 2), ((FAKE, FAKE, 4, -1), 2), ((None, FAKE, 4, 10), 1), ((FAKE, None, 4, 10), 1),
+    ((FAKE, FAKE + 4, 4, 10), 8),
+])
+def test_mask_pack_rejects_bad_arguments(lib, args, status):
+    assert lib.fa_mask_pack(*args, None) == status

@@ -310,12 +310,12 @@ def _mutant_backward_sign(q, k, v, dO, O, P, scale):
     return scale * (dS @ k), scale * (dS.T @ q), P.T @ dO
 
 
-def _mutant_forward_log2(q, k, v, causal, scale, rows=None, Tq=None, window=0):
-    O, L, P = _ORIG_HEAD_FORWARD(q, k, v, causal, scale, rows, Tq, window=window)
+def _mutant_forward_log2(q, k, v, causal, scale, rows=None, Tq=None, window=0, mask=None):
+    O, L, P = _ORIG_HEAD_FORWARD(q, k, v, causal, scale, rows, Tq, window=window, mask=mask)
     return O, L / math.log(2.0), P                # L in log2
 
 
-def _mutant_visible_start_aligned(Tq, Tk, causal, window=0):
+def _mutant_visible_start_aligned(Tq, Tk, causal, window=0, mask=None):
     if not causal:
         return np.ones((Tq, Tk), dtype=bool)
     return np.arange(Tk)[None, :] <= np.arange(Tq)[:, None]
@@ -324,7 +324,7 @@ def _mutant_visible_start_aligned(Tq, Tk, causal, window=0):
 _ORIG_HEAD_FORWARD = oa.head_forward
 
 
-def _mutant_gqa_modulo(Q, K, V, causal=False, scale=None, window=0):
+def _mutant_gqa_modulo(Q, K, V, causal=False, scale=None, window=0, mask=None):
     B, Hq, Hkv, Tq, Tk, d, dv = oa._check_shapes(Q, K, V)
     scale = oa.default_scale(d) if scale is None else scale
     O = np.zeros((B, Hq, Tq, dv))

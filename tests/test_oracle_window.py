@@ -165,7 +165,7 @@ def test_window_tiled_recurrence_matches_dense(window, blocks):
 
 
 def test_planted_window_off_by_one_is_caught(monkeypatch):
-    def wrong(Tq, Tk, causal, window=0):
+    def wrong(Tq, Tk, causal, window=0, mask=None):
         i = np.arange(Tq)[:, None]
         j = np.arange(Tk)[None, :]
         vis = np.ones((Tq, Tk), dtype=bool)
