@@ -167,12 +167,7 @@ def attention_forward(Q, K, V, causal=False, scale=None, window=0, mask=None):
     B, Hq, Hkv, Tq, Tk, d, dv = _check_shapes(Q, K, V)
     if scale is None:
         scale = default_scale(d)
-    if mask is not None:
-        mask = np.asarray(mask, dtype=bool)
-        if mask.ndim == 2:
-            mask = np.broadcast_to(mask, (B,) + mask.shape)
-        if mask.shape != (B, Tq, Tk):
-            raise ValueError(f"mask must be [{Tq}, {Tk}] or [{B}, {Tq}, {Tk}], got {mask.shape}")
+    mask = _batch_masks(mask, B, Tq, Tk)
     G = Hq // Hkv
     O = np.zeros((B, Hq, Tq, dv))
     L = np.zeros((B, Hq, Tq))
@@ -184,17 +179,32 @@ def attention_forward(Q, K, V, causal=False, scale=None, window=0, mask=None):
     return O, L
 
 
-def group_forward_backward(Q, K, V, dO, b, g, causal=False, scale=None, window=0):
+def _batch_masks(mask, B, Tq, Tk):
+    """A [Tq, Tk] or [B, Tq, Tk] boolean mask as [B, Tq, Tk] (None stays None)."""
+    if mask is None:
+        return None
+    mask = np.asarray(mask, dtype=bool)
+    if mask.ndim == 2:
+        mask = np.broadcast_to(mask, (B,) + mask.shape)
+    if mask.shape != (B, Tq, Tk):
+        raise ValueError(f"mask must be [{Tq}, {Tk}] or [{B}, {Tq}, {Tk}], got {mask.shape}")
+    return mask
+
+
+def group_forward_backward(Q, K, V, dO, b, g, causal=False, scale=None, window=0, mask=None):
     """Everything for one (batch b, key/value head g): the G query heads of the group.
 
     Returns dict with O [G,Tq,dv], L [G,Tq], dQ [G,Tq,d], dK [Tk,d], dV [Tk,dv]
     (fp64).  dK and dV are summed over the group's query heads.  This is the
     unit the full functions loop over and the unit sampled at large sizes.
+    ``mask``: optional boolean [Tq, Tk] of batch entry b (or [B, Tq, Tk]).
     """
     B, Hq, Hkv, Tq, Tk, d, dv = _check_shapes(Q, K, V)
     if scale is None:
         scale = default_scale(d)
     G = Hq // Hkv
+    if mask is not None and np.ndim(mask) == 3:
+        mask = np.asarray(mask, dtype=bool)[b]
     kg = np.asarray(K[b, g], dtype=np.float64)
     vg = np.asarray(V[b, g], dtype=np.float64)
     out = {
@@ -207,7 +217,7 @@ def group_forward_backward(Q, K, V, dO, b, g, causal=False, scale=None, window=0
     for r in range(G):
         h = g * G + r
         q = np.asarray(Q[b, h], dtype=np.float64)
-        o, lse, p = head_forward(q, kg, vg, causal, scale, window=window)
+        o, lse, p = head_forward(q, kg, vg, causal, scale, window=window, mask=mask)
         dq, dk, dvv = head_backward(q, kg, vg, dO[b, h], o, p, scale)
         out["O"][r], out["L"][r], out["dQ"][r] = o, lse, dq
         out["dK"] += dk
@@ -215,11 +225,15 @@ def group_forward_backward(Q, K, V, dO, b, g, causal=False, scale=None, window=0
     return out
 
 
-def attention_forward_backward(Q, K, V, dO, causal=False, scale=None, window=0):
-    """Full dense forward and backward: (O, L, dQ, dK, dV), all fp64."""
+def attention_forward_backward(Q, K, V, dO, causal=False, scale=None, window=0, mask=None):
+    """Full dense forward and backward: (O, L, dQ, dK, dV), all fp64.
+
+    ``mask``: optional boolean [Tq, Tk] (every batch entry) or [B, Tq, Tk].
+    """
     B, Hq, Hkv, Tq, Tk, d, dv = _check_shapes(Q, K, V)
     if scale is None:
         scale = default_scale(d)
+    mask = _batch_masks(mask, B, Tq, Tk)
     G = Hq // Hkv
     O = np.zeros((B, Hq, Tq, dv))
     L = np.zeros((B, Hq, Tq))
@@ -228,7 +242,8 @@ def attention_forward_backward(Q, K, V, dO, causal=False, scale=None, window=0):
     dV = np.zeros((B, Hkv, Tk, dv))
     for b in range(B):
         for g in range(Hkv):
-            r = group_forward_backward(Q, K, V, dO, b, g, causal, scale, window)
+            r = group_forward_backward(Q, K, V, dO, b, g, causal, scale, window,
+                                       None if mask is None else mask[b])
             O[b, g * G:(g + 1) * G] = r["O"]
             L[b, g * G:(g + 1) * G] = r["L"]
             dQ[b, g * G:(g + 1) * G] = r["dQ"]

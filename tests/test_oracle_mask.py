@@ -14,7 +14,10 @@ code path:
   * exact invariants: an all-True mask is the unmasked call, the causal
     pattern as a mask is the causal call, a row with no True entry gives
     O = 0, L = -inf;
-  * a planted mistake (the mask read transposed) fails the SDPA pin.
+  * a planted mistake (the mask read transposed) fails the SDPA pin;
+  * gradients under the mask: torch autograd through the same float64 SDPA
+    call (a row without keys has no gradient), and central finite differences
+    of sum(O * dO).
 """
 
 import math
@@ -138,3 +141,65 @@ def test_mask_shape_is_checked():
     Q, K, V = inputs(Tq=5, Tk=6, seed=1)
     with pytest.raises(ValueError):
         oa.attention_forward(Q, K, V, False, 0.5, mask=np.ones((6, 5), dtype=bool))
+
+
+@pytest.mark.parametrize("per_entry", [False, True])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mask_gradients_match_torch_autograd(per_entry, causal):
+    """dQ, dK, dV under the mask: torch autograd through float64 SDPA with the same mask."""
+    import torch
+    import torch.nn.functional as F
+    Tq, Tk = 9, 12
+    Q, K, V = inputs(Tq=Tq, Tk=Tk, seed=21)
+    dO = rnd(Q.shape, 22)
+    mask = random_mask((2, Tq, Tk) if per_entry else (Tq, Tk), seed=23, density=0.5)
+    mask[..., 3, :] = False                                  # a row without keys: no gradient
+    m = torch.tensor(np.broadcast_to(mask, (2, Tq, Tk)).copy())
+    if causal:
+        m = m & (torch.arange(Tk)[None, :] <= torch.arange(Tq)[:, None] + Tk - Tq)[None]
+    rows = m.any(dim=-1)
+    q, k, v = (torch.tensor(x, requires_grad=True) for x in (Q, K, V))
+    out = F.scaled_dot_product_attention(q, k, v, attn_mask=m[:, None], scale=0.6, enable_gqa=True)
+    out = torch.where(rows[:, None, :, None], out, torch.zeros_like(out))
+    (out * torch.tensor(dO)).sum().backward()
+    O, L, dQ, dK, dV = oa.attention_forward_backward(Q, K, V, dO, causal, 0.6, mask=mask)
+    assert oa.relative_frobenius(O, out.detach().numpy()) < 1e-12
+    assert oa.relative_frobenius(dQ, np.nan_to_num(q.grad.numpy())) < 1e-12
+    assert oa.relative_frobenius(dK, np.nan_to_num(k.grad.numpy())) < 1e-12
+    assert oa.relative_frobenius(dV, np.nan_to_num(v.grad.numpy())) < 1e-12
+
+
+def test_mask_gradients_match_finite_differences():
+    Q, K, V = inputs(B=1, Hq=2, Hkv=1, Tq=5, Tk=7, d=3, seed=25)
+    dO = rnd(Q.shape, 26)
+    mask = random_mask((5, 7), seed=27, density=0.6)
+    scale, hstep = 0.7, 1e-6
+
+    def f(q, k, v):
+        O, _ = oa.attention_forward(q, k, v, False, scale, mask=mask)
+        return float((O * dO).sum())
+
+    _, _, dQ, dK, dV = oa.attention_forward_backward(Q, K, V, dO, False, scale, mask=mask)
+    for which, analytic in ((0, dQ), (1, dK), (2, dV)):
+        args = [Q.copy(), K.copy(), V.copy()]
+        fd = np.zeros_like(args[which])
+        for idx in np.ndindex(fd.shape):
+            base = args[which][idx]
+            args[which][idx] = base + hstep
+            fp = f(*args)
+            args[which][idx] = base - hstep
+            fm = f(*args)
+            args[which][idx] = base
+            fd[idx] = (fp - fm) / (2 * hstep)
+        assert np.abs(analytic - fd).max() / np.abs(fd).max() < 1e-7
+
+
+def test_group_unit_takes_the_entry_mask():
+    Q, K, V = inputs(Tq=8, Tk=10, seed=29)
+    dO = rnd(Q.shape, 30)
+    mask = random_mask((2, 8, 10), seed=31)
+    O, L, dQ, dK, dV = oa.attention_forward_backward(Q, K, V, dO, True, 0.5, mask=mask)
+    r = oa.group_forward_backward(Q, K, V, dO, 1, 1, True, 0.5, mask=mask)
+    assert np.array_equal(r["O"], O[1, 2:4]) and np.array_equal(r["dK"], dK[1, 1])
+    r2 = oa.group_forward_backward(Q, K, V, dO, 1, 1, True, 0.5, mask=mask[1])
+    assert np.array_equal(r2["dV"], dV[1, 1])
