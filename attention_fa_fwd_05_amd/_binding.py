@@ -28,7 +28,7 @@ EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_window", "fa_bwd_window"
            "fa_fwd_splitk",
            "fa_fwd_splitk_workspace_bytes", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fwd_paged",
            "fa_fwd_paged_workspace_bytes", "fa_bwd_workspace_bytes",
-           "fa_mask_row_words", "fa_mask_pack", "fa_fwd_mask",
+           "fa_mask_row_words", "fa_mask_pack", "fa_fwd_mask", "fa_bwd_mask", "fa_bwd_mask_workspace_bytes",
            "fa_status_string", "fa_hip_error_string", "fa_abi_version"]
 
 _lib = None
@@ -96,6 +96,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_mask_pack.restype = i
     lib.fa_fwd_mask.argtypes = [vp, vp, vp, vp, vp, vp, ll, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_mask.restype = i
+    lib.fa_bwd_mask.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ll, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_mask.restype = i
+    lib.fa_bwd_mask_workspace_bytes.argtypes = [i, i, i, i, i, i, i, ll]
+    lib.fa_bwd_mask_workspace_bytes.restype = sz
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -313,15 +317,9 @@ def pack_mask(mask, Tk: int | None = None):
     return bits
 
 
-def forward_masked(q, k, v, mask, causal: bool = False, scale: float | None = None, out=None, lse=None):
-    """fa_fwd_mask: attention under a boolean mask shared by all heads of a batch entry.
-
-    ``mask``: bool/uint8 [Tq, Tk] (whole batch) or [B, Tq, Tk] (or [B, 1, Tq, Tk]), packed here
-    with fa_mask_pack; or an already packed int32 [..., Tq, fa_mask_row_words(Tk)].
-    Returns (o like q, lse float32 [B, Hq, Tq])."""
+def _mask_bits(lib, mask, q, B, Tq, Tk):
+    """(packed int32 bits, batch stride in words) of a bool/uint8 or already packed mask."""
     import torch
-    lib = load_library()
-    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
     if mask.device != q.device:
         raise ValueError("mask must be on q's device")
     if mask.dim() == 4 and mask.shape[1] == 1:
@@ -332,7 +330,46 @@ def forward_masked(q, k, v, mask, causal: bool = False, scale: float | None = No
         raise ValueError(f"packed mask must be int32 [Tq, {rw}] or [B, Tq, {rw}]")
     if bits.dim() == 3 and bits.shape[0] != B:
         raise ValueError("per-entry mask needs B entries")
-    stride = Tq * rw if bits.dim() == 3 and B > 1 else 0
+    return bits, (Tq * rw if bits.dim() == 3 and B > 1 else 0)
+
+
+def backward_masked(q, k, v, o, lse, do, mask, causal: bool = False, scale: float | None = None,
+                    workspace=None, dq=None, dk=None, dv=None):
+    """fa_bwd_mask: gradients under the boolean mask of forward_masked; returns (dq, dk, dv)."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
+    for t in (o, do):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("o and do must be like q")
+    if tuple(lse.shape) != (B, Hq, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be float32 [B, Hq, Tq]")
+    bits, stride = _mask_bits(lib, mask, q, B, Tq, Tk)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    need = int(lib.fa_bwd_mask_workspace_bytes(B, Hq, Hkv, Tq, Tk, d, code, stride))
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    st = lib.fa_bwd_mask(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+                         ws.data_ptr(), ws.numel(), _ptr(bits), stride, B, Hq, Hkv, Tq, Tk, d, int(bool(causal)),
+                         scale, code, _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_bwd_mask")
+    return dq, dk, dv
+
+
+def forward_masked(q, k, v, mask, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """fa_fwd_mask: attention under a boolean mask shared by all heads of a batch entry.
+
+    ``mask``: bool/uint8 [Tq, Tk] (whole batch) or [B, Tq, Tk] (or [B, 1, Tq, Tk]), packed here
+    with fa_mask_pack; or an already packed int32 [..., Tq, fa_mask_row_words(Tk)].
+    Returns (o like q, lse float32 [B, Hq, Tq])."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
+    bits, stride = _mask_bits(lib, mask, q, B, Tq, Tk)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
     o = torch.empty_like(q) if out is None else out

@@ -127,7 +127,23 @@ int check_varlen(const int* cu_q, const int* cu_k, int total_q, int total_k, int
 int bwd_core(const void* Q, const void* K, const void* V, const void* O, const float* L,
              const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
              const int* cu_q, const int* cu_k, int B, int Hq, int Hkv, int total_q, int total_k, int Tq,
-             int Tk, int d, int dv, int causal, int window, float scale, int dtype, unsigned stages, void* stream);
+             int Tk, int d, int dv, int causal, int window, float scale, int dtype, unsigned stages, void* stream,
+             const uint32_t* mask = nullptr, long long mask_bstride = 0);
+// Boolean-mask arguments shared by the forward and the backward: the stride
+// is 0 (one mask for the batch) or a multiple of 4 words holding a whole
+// entry, and the mask has Tq rows of 4 * ceil(Tk / 128) words.
+int check_mask(const uint32_t* mask, long long stride, int B, int Tq, int Tk) {
+  const long long rw = 4LL * ((Tk + 127) / 128), mwords = (long long)Tq * rw;
+  if (stride < 0 || (stride != 0 && stride < mwords)) return FA_ERR_BAD_SHAPE;
+  if (stride % 4 != 0) return FA_ERR_ALIGNMENT;               // every row stays 16-byte aligned
+  if (stride > kMaxElems / B) return FA_ERR_TOO_LARGE;
+  return check_ptr(mask, mwords);
+}
+// Bytes of the backward's key-major mask copy (after the rest of its workspace).
+size_t mask_t_bytes(int B, int Tq, int Tk, long long stride) {
+  const long long entries = stride != 0 ? B : 1;
+  return align_up((size_t)entries * Tk * (4 * ((Tq + 127) / 128)) * 4);
+}
 
 size_t splitk_ws_bytes(int B, int Hq, int Tq, int d, int ns) {
   const size_t rows = (size_t)B * Hq * Tq;
@@ -249,12 +265,8 @@ int fa_fwd_mask(const void* Q, const void* K, const void* V, void* O, float* L, 
   if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, nq)) || (st = check_ptr(K, nkv)) ||
       (st = check_ptr(V, nkv)) || (st = check_ptr(L, (long long)B * Hq * Tq)))
     return st;
-  const long long rw = fa_mask_row_words(Tk), mwords = (long long)Tq * rw;
-  if (mask_batch_stride != 0 && mask_batch_stride < mwords) return FA_ERR_BAD_SHAPE;
-  if (mask_batch_stride < 0) return FA_ERR_BAD_SHAPE;
-  if (mask_batch_stride % 4 != 0) return FA_ERR_ALIGNMENT;     // every row stays 16-byte aligned
-  if (mask_batch_stride > kMaxElems / B) return FA_ERR_TOO_LARGE;
-  if ((st = check_ptr(mask_bits, mwords))) return st;
+  const long long rw = fa_mask_row_words(Tk);
+  if ((st = check_mask(mask_bits, mask_batch_stride, B, Tq, Tk))) return st;
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if (Tq == 0) return FA_OK;
   fa::FwdArgs a;
@@ -272,6 +284,23 @@ int fa_fwd_mask(const void* Q, const void* K, const void* V, void* O, float* L, 
   a.mask_bstride = mask_batch_stride;
   a.mask_row_words = (int)rw;
   return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream));
+}
+
+size_t fa_bwd_mask_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype,
+                                   long long mask_batch_stride) {
+  if (check_common(B, Hq, Hkv, Tq, Tk, d, dtype) != FA_OK || mask_batch_stride < 0) return 0;
+  return ws_layout(B, Hq, Tq, d, dtype).total + mask_t_bytes(B, Tq, Tk, mask_batch_stride);
+}
+
+int fa_bwd_mask(const void* Q, const void* K, const void* V, const void* O, const float* L, const void* dO,
+                void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, const uint32_t* mask_bits,
+                long long mask_batch_stride, int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal,
+                float scale, int dtype, void* stream) {
+  int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
+  if (st != FA_OK) return st;
+  if ((st = check_mask(mask_bits, mask_batch_stride, B, Tq, Tk))) return st;
+  return bwd_core(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, nullptr, nullptr, B, Hq, Hkv, 0, 0,
+                  Tq, Tk, d, d, causal, 0, scale, dtype, FA_BWD_STAGE_ALL, stream, mask_bits, mask_batch_stride);
 }
 
 size_t fa_fwd_splitk_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int nsplit) {
@@ -424,7 +453,8 @@ namespace {
 int bwd_core(const void* Q, const void* K, const void* V, const void* O, const float* L,
              const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
              const int* cu_q, const int* cu_k, int B, int Hq, int Hkv, int total_q, int total_k, int Tq,
-             int Tk, int d, int dv, int causal, int window, float scale, int dtype, unsigned stages, void* stream) {
+             int Tk, int d, int dv, int causal, int window, float scale, int dtype, unsigned stages, void* stream,
+             const uint32_t* mask, long long mask_bstride) {
   int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
   if (st != FA_OK) return st;
   if ((st = check_dv(d, dv, dtype)) != FA_OK) return st;
@@ -440,8 +470,10 @@ int bwd_core(const void* Q, const void* K, const void* V, const void* O, const f
   if (!isfinite(scale)) return FA_ERR_SCALE;
   if (stages & ~(unsigned)FA_BWD_STAGE_ALL) return FA_ERR_STAGES;
   const WsLayout ws = ws_layout(B, Hq, Tq, d, dtype);
-  if (ws.total > 0) {
-    if (workspace == nullptr || workspace_bytes < ws.total) return FA_ERR_WORKSPACE;
+  const bool masked = mask_bstride >= 0 && mask != nullptr && Tq > 0 && Tk > 0;
+  const size_t need = ws.total + (masked ? mask_t_bytes(B, Tq, Tk, mask_bstride) : 0);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (misaligned(workspace)) return FA_ERR_ALIGNMENT;
   }
   if (Tq == 0 && Tk == 0) return FA_OK;
@@ -461,6 +493,14 @@ int bwd_core(const void* Q, const void* K, const void* V, const void* O, const f
   a.total_k = total_k;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  if (masked) {
+    a.mask = mask;
+    a.mask_bstride = mask_bstride;
+    a.mask_row_words = 4 * ((Tk + 127) / 128);
+    a.mask_t = reinterpret_cast<uint32_t*>(wsb + ws.total);
+    a.mask_t_row_words = 4 * ((Tq + 127) / 128);
+    a.mask_t_bstride = mask_bstride != 0 ? (long long)Tk * a.mask_t_row_words : 0;
+  }
   return hip_status(fa::launch_bwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, stages, (hipStream_t)stream, dv));
 }
 

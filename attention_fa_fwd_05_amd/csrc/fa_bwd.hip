@@ -86,8 +86,35 @@ __host__ __device__ constexpr int interleave_rank(int m, int na, int nb) {
 __device__ inline void zero_elem(bf16x8& x, int e) { x[e] = (bf16)0.f; }
 __device__ inline void zero_elem(f32x4& x, int e) { x[e] = 0.f; }
 
+// LDS words of a boolean mask's bits for the tiles in flight: 64 per wave and
+// buffer, written by one 4-byte direct load per wave (lane l: word l % 2 of
+// row l / 2 of the wave's 32 rows) and read back as two words per lane.  Only
+// the kernels compiled with a mask instantiate it.
+template <int N>
+__device__ inline uint32_t* mask_lds() {
+  __shared__ __attribute__((aligned(16))) uint32_t m[N];
+  return m;
+}
+
+// Key-major copy of a query-major mask: word (b, w, j) of mask_t holds in bit
+// e the bit of (query 32 w + e, key j), 0 past Tq.  One thread per output
+// word, key fastest, so neighbouring threads read the same source words.
+__global__ __launch_bounds__(256) void mask_transpose_kernel(BwdArgs a, long long entries) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int rwq = a.mask_t_row_words;
+  const long long per = (long long)a.Tk * rwq;
+  if (i >= entries * per) return;
+  const long long b = i / per, r = i % per;
+  const int w = (int)(r / a.Tk), j = (int)(r % a.Tk);
+  const uint32_t* src = a.mask + b * a.mask_bstride + (j >> 5);
+  uint32_t v = 0;
+  for (int e = 0; e < 32 && 32 * w + e < a.Tq; ++e)
+    v |= ((src[(size_t)(32 * w + e) * a.mask_row_words] >> (j & 31)) & 1u) << e;
+  a.mask_t[b * a.mask_t_bstride + (size_t)j * rwq + w] = v;
+}
+
 // D: head dim of Q, K, dK; DV: of V, dO, dV.
-template <typename T, int D, bool CAUSAL, bool WIN, int DV = D>
+template <typename T, int D, bool CAUSAL, bool WIN, int DV = D, bool MASK = false>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
@@ -130,6 +157,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   static_assert(NPA >= 12 && NDH >= 8, "room for the vector stages");
   static_assert(NB == 2 || 2 * (DmaRows<T, D, BQ, 256>::PER + DmaRows<T, DV, BQ, 256>::PER + 1) <= NPA,
                 "loads fit in phase 1b");
+  static_assert(!MASK || (!WIN && D == DV), "the masked backward uses the plain shape");
   __shared__ __attribute__((aligned(16))) float sL[NB][64];
   __shared__ __attribute__((aligned(16))) float sD[NB][64];    // -D
   __shared__ __attribute__((aligned(16))) T sQ[NB][BQ * D];
@@ -176,6 +204,15 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   auto item_bh = [&](int it) { return wk.b * a.Hq + wk.hk * G + it % G; };   // workspace rows (padded)
   auto item_qrow = [&](int it) { return sq.q_row(wk.hk * G + it % G); };   // Q, dO rows
   // L2 and D rows are padded to 64 per head, so a 64-row window always loads.
+  // Boolean mask: this wave's keys' bits of a query block (key-major copy),
+  // two words per key; lane l loads word l % 2 of key kw + l / 2 (keys past Tk
+  // read the last key's row; their results are never stored).
+  uint32_t* sM = nullptr;
+  if constexpr (MASK) sM = mask_lds<NB * 256>();
+  auto mask_src = [&](int it) -> const uint32_t* {
+    return a.mask_t + (size_t)wk.b * a.mask_t_bstride +
+           (size_t)min(kw + (lane >> 1), Tk - 1) * a.mask_t_row_words + item_q0(it) / 32 + (lane & 1);
+  };
   auto issue = [&](int it, int buf) {
     const int bh = item_bh(it);
     const int q0 = item_q0(it);
@@ -184,6 +221,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     dma_rows<T, DV, BQ, 256>(sdO[buf], reinterpret_cast<const T*>(a.dO) + obase, q0, Tq);
     if (w == 0) dma_floats64(sL[buf], a.Lg + (size_t)bh * a.Tqp + q0);
     if (w == 1) dma_floats64(sD[buf], a.Dvec + (size_t)bh * a.Tqp + q0);
+    if constexpr (MASK) dma4(mask_src(it), lds_addr(sM + buf * 256 + w * 64));
   };
   if (total > 0) issue(0, 0);
   if (total > 1) issue(1, 1);
@@ -193,7 +231,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   // and -D.
   using DR = DmaRows<T, D, BQ, 256>;
   using DRV = DmaRows<T, DV, BQ, 256>;
-  constexpr int NDMA = DR::PER + DRV::PER + 1;
+  constexpr int NDMA = DR::PER + DRV::PER + 1 + (MASK ? 1 : 0);
+  static_assert(NB == 2 || 2 * NDMA <= NPA, "loads fit in phase 1b");
   uint32_t src_off[DR::PER], src_offv[DRV::PER];   // per-lane source byte offsets, one per instruction
 #pragma unroll
   for (int j = 0; j < DR::PER; ++j) src_off[j] = DR::src_off(j);
@@ -207,9 +246,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     const float* d;
     int q0;
     bool whole;                                     // all BQ rows exist: no clamping
+    const uint32_t* m;                              // this lane's mask word (MASK)
   };
   auto block_src = [&](int it) {
     Src r;
+    if constexpr (MASK) r.m = mask_src(it);
     const int bh = item_bh(it);
     r.q0 = item_q0(it);
     const size_t row = item_qrow(it) + r.q0;
@@ -236,9 +277,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
         const T* g = reinterpret_cast<const T*>(src.o) - (size_t)src.q0 * DV;
         DRV::one(sdO[buf], g, src.q0, Tq, i);
       }
-    } else {
+    } else if (!MASK || j == DR::PER + DRV::PER) {
       if (w == 0) dma_floats64(sL[buf], src.l);
       if (w == 1) dma_floats64(sD[buf], src.d);
+    } else {
+      dma4(src.m, lds_addr(sM + buf * 256 + w * 64));
     }
   };
 
@@ -368,13 +411,19 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   // P and dS of pairs the key may not see are cleared in the packed operands.
   // Register i of tile t holds query q0 + 32 t + 4 h + 8 (i / 4) + i % 4.
   // The sliding window clears pairs whose query is past the key's window.
-  auto mask_tile = [&](int q0, int t) {
-    if (ragged || (CAUSAL && k0 + BK - 1 > q0 + 32 * t + off) || (W > 0 && q0 + 32 * t + 31 > k0 - off + W - 1)) {
+  // A boolean mask clears the pairs whose bit is 0: word t of the block's two
+  // (buffer buf), bit 4 h + 8 (i / 4) + i % 4 for register i.
+  auto mask_tile = [&](int q0, int t, int buf) {
+    if (MASK || ragged || (CAUSAL && k0 + BK - 1 > q0 + 32 * t + off) ||
+        (W > 0 && q0 + 32 * t + 31 > k0 - off + W - 1)) {
       const int thr = !key_ok ? INT_MAX : (CAUSAL ? mykey - off - q0 - 32 * t - 4 * h : INT_MIN);
       const int thr_hi = W > 0 ? mykey - off + W - 1 - q0 - 32 * t - 4 * h : INT_MAX;
+      uint32_t mw = 0xffffffffu;
+      if constexpr (MASK) mw = sM[buf * 256 + w * 64 + 2 * n + t] >> (4 * h);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (8 * (i >> 2) + (i & 3) < thr || 8 * (i >> 2) + (i & 3) > thr_hi) {
+        if (8 * (i >> 2) + (i & 3) < thr || 8 * (i >> 2) + (i & 3) > thr_hi ||
+            (MASK && ((mw >> (8 * (i >> 2) + (i & 3))) & 1u) == 0)) {
           const int s = (16 * t + i) / KPER;
           zero_elem(pop[s], i % KPER);
           zero_elem(dsop[s], i % KPER);
@@ -396,7 +445,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     load_l(sL[0], 0);
 #pragma unroll
     for (int m = 0; m < 18; ++m) stages(0, m, 0, 16, 16);
-    mask_tile(item_q0(0), 0);
+    mask_tile(item_q0(0), 0, 0);
     load_l(sL[0], 1);
   }
 
@@ -460,7 +509,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       }
     };
     phase1(IC<0>{});
-    mask_tile(q0, 1);
+    mask_tile(q0, 1, cur);
     phase1(IC<1>{});
 
     // Phase 2: the second half of block i's dV, dK, with the second half of
@@ -473,7 +522,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       stages(0, m, 8, 16, SPAN2);
       __builtin_amdgcn_sched_barrier(0);
     }
-    mask_tile(nq0, 0);
+    mask_tile(nq0, 0, nxt);
     load_l(sL[nxt], 1);                            // for block i+1's tile-1 probabilities
     if (NB == 3) {
       wait_vmcnt<0>();                             // this wave's loads of block i+2 have landed
@@ -515,7 +564,7 @@ template <typename T, int D>
 constexpr int dq_waves() { return (sizeof(T) == 4 && D == 128) ? 4 : 8; }
 
 // D: head dim of Q, K, dQ; DV: of V and dO.
-template <typename T, int D, bool CAUSAL, bool WIN, int DV = D>
+template <typename T, int D, bool CAUSAL, bool WIN, int DV = D, bool MASK = false>
 __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
@@ -576,6 +625,12 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   for (int i = 0; i < DR::PER; ++i) src_off[i] = DR::src_off(i);
 #pragma unroll
   for (int i = 0; i < DRV::PER; ++i) src_offv[i] = D == DV ? src_off[i % DR::PER] : DRV::src_off(i);
+  // Boolean mask: this wave's rows' bits of a key tile (query-major), two
+  // words per row; lane l loads word l % 2 of row qw + l / 2 (rows past Tq
+  // read the last row; their results are never stored).
+  static_assert(!MASK || (!WIN && D == DV), "the masked backward uses the plain shape");
+  uint32_t* sM = nullptr;
+  if constexpr (MASK) sM = mask_lds<NBUF * NW * 64>();
   auto issue = [&](int k0, int buf) {
     T* tk = sKV[buf];
     T* tv = sKV[buf] + TILE;
@@ -590,9 +645,13 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
       dma_rows<T, D, BK, NTHR>(tk, Kp, k0, Tk);
       dma_rows<T, DV, BK, NTHR>(tv, Vp, k0, Tk);
     }
+    if constexpr (MASK)
+      dma4(a.mask + (size_t)wk.b * a.mask_bstride + (size_t)min(qw + (lane >> 1), Tq - 1) * a.mask_row_words +
+               k0 / 32 + (lane & 1),
+           lds_addr(sM + (buf * NW + w) * 64));
   };
-  // Direct-load instructions per wave for one tile (K and V).
-  constexpr int NLD = DR::PER + DRV::PER;
+  // Direct-load instructions per wave for one tile (K and V, and the mask).
+  constexpr int NLD = DR::PER + DRV::PER + (MASK ? 1 : 0);
 #pragma unroll
   for (int j = 0; j < AHEAD; ++j)
     if (jt0 + j < ntiles) issue((jt0 + j) * BK, j);
@@ -690,7 +749,7 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
     }
     // Only the diagonal tiles and the ragged key end (a uniform test) clear
     // dS of the keys this query may not see; every value above is finite.
-    if ((k0 + BK > Tk) || (CAUSAL && k0 + BK - 1 > qw + off) || (W > 0 && k0 < qw + 31 + off - W + 1)) {
+    if (MASK || (k0 + BK > Tk) || (CAUSAL && k0 + BK - 1 > qw + off) || (W > 0 && k0 < qw + 31 + off - W + 1)) {
       // First and last visible key offsets, less this lane half's 4 h,
       // against the compile-time part of perm_index (no per-lane table).
       const int lim = min(Tk - 1, CAUSAL ? myq + off : Tk - 1) - k0 - 4 * h;
@@ -698,6 +757,15 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
 #pragma unroll
       for (int r = 0; r < 32; ++r)
         if (perm_index(0, r) > lim || perm_index(0, r) < lo) ds[r] = 0.f;
+      if constexpr (MASK) {
+        // Key k0 + perm_index(h, r): bit perm_index(0, r) % 32 of word r / 16
+        // once this half's 4 h are shifted out.
+        const uint32_t m0 = sM[(buf * NW + w) * 64 + 2 * n] >> (4 * h);
+        const uint32_t m1 = sM[(buf * NW + w) * 64 + 2 * n + 1] >> (4 * h);
+#pragma unroll
+        for (int r = 0; r < 32; ++r)
+          if ((((r < 16 ? m0 : m1) >> (perm_index(0, r) % 32)) & 1u) == 0) ds[r] = 0.f;
+      }
     }
     Op dsop[NSK];
 #pragma unroll
@@ -714,7 +782,10 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   for (int jt = jt0; jt < ntiles; ++jt) {
     const bool issued = jt + AHEAD < ntiles;
     if (issued) issue((jt + AHEAD) * BK, buf + AHEAD >= NBUF ? buf + AHEAD - NBUF : buf + AHEAD);
-    if (visible(jt)) {
+    bool any = true;
+    if constexpr (MASK)                            // the mask leaves the wave some key of the tile
+      any = __ballot((sM[(buf * NW + w) * 64 + 2 * n] | sM[(buf * NW + w) * 64 + 2 * n + 1]) != 0) != 0;
+    if (visible(jt) && any) {
       s_phase(buf);
       dq_phase(jt, buf);
     }
@@ -750,13 +821,30 @@ hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const long long kblocks = (long long)((a.Tk + 127) / 128) * a.B * a.Hkv;
+  constexpr int NW = dq_waves<T, D>();
+  const long long qblocks = (long long)((a.Tq + 32 * NW - 1) / (32 * NW)) * a.B * a.Hq;
+  if constexpr (DV == D) {
+    // A boolean mask: its key-major copy, then the masked passes.
+    if (a.mask != nullptr) {
+      if ((stages & kStageDkDv) && kblocks > 0) {
+        const long long entries = a.mask_bstride != 0 ? a.B : 1;
+        const long long words = entries * a.Tk * a.mask_t_row_words;
+        hipError_t e = launch(mask_transpose_kernel, (words + 255) / 256, stream, a, entries);
+        if (e == hipSuccess) e = launch(dkdv_kernel<T, D, CAUSAL, false, D, true>, kblocks, stream, a);
+        if (e != hipSuccess) return e;
+      }
+      if ((stages & kStageDq) && qblocks > 0) {
+        hipError_t e = launch<64 * NW>(dq_kernel<T, D, CAUSAL, false, D, true>, qblocks, stream, a);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
+  }
   if ((stages & kStageDkDv) && kblocks > 0) {
     hipError_t e = a.window > 0 ? launch(dkdv_kernel<T, D, CAUSAL, true, DV>, kblocks, stream, a)
                                 : launch(dkdv_kernel<T, D, CAUSAL, false, DV>, kblocks, stream, a);
     if (e != hipSuccess) return e;
   }
-  constexpr int NW = dq_waves<T, D>();
-  const long long qblocks = (long long)((a.Tq + 32 * NW - 1) / (32 * NW)) * a.B * a.Hq;
   if ((stages & kStageDq) && qblocks > 0) {
     hipError_t e = a.window > 0 ? launch<64 * NW>(dq_kernel<T, D, CAUSAL, true, DV>, qblocks, stream, a)
                                 : launch<64 * NW>(dq_kernel<T, D, CAUSAL, false, DV>, qblocks, stream, a);

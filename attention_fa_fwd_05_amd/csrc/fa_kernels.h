@@ -112,6 +112,17 @@ struct BwdArgs {
   int total_q, total_k;
   float scale;
   float scale_log2;
+  // Boolean mask (mask != nullptr): the query-major bits of FwdArgs::mask
+  // (read by the dQ pass) and a key-major copy in the workspace (written by
+  // mask_transpose_kernel, read by the dK/dV pass): bit q % 32 of word
+  // mask_t[b * mask_t_bstride + j * mask_t_row_words + q / 32] is the bit of
+  // (query q, key j); mask_t_row_words = 4 * ceil(Tq / 128).
+  const uint32_t* mask = nullptr;
+  long long mask_bstride = 0;
+  int mask_row_words = 0;
+  uint32_t* mask_t = nullptr;
+  long long mask_t_bstride = 0;
+  int mask_t_row_words = 0;
 };
 
 // Launch a kernel of THREADS threads per workgroup on a 1-D grid and return

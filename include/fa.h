@@ -261,7 +261,8 @@ int fa_fwd_paged(const void* Q, const void* K_pages, const void* V_pages, void* 
  * Boolean attention mask with grouped-query heads ("The Autograd Memory Trap:
  * Diagnosing a Backward-Pass OOM in Chunked Attention", section "The GQA
  * Expansion Question": a caller's boolean mask together with query heads that
- * share K/V heads, here without repeating K and V).  Forward only.
+ * share K/V heads, here without repeating K and V).  The backward is
+ * fa_bwd_mask below.
  *
  * Layout of the mask: 32-bit words, mask_bits[b * mask_batch_stride + i *
  * fa_mask_row_words(Tk) + j / 32], bit j % 32 set meaning key j is visible to
@@ -290,6 +291,22 @@ int fa_fwd_paged(const void* Q, const void* K_pages, const void* V_pages, void* 
 int fa_mask_row_words(int Tk);
 int fa_mask_pack(const void* mask_bytes, uint32_t* mask_bits, long long rows, int Tk, void* stream);
 int fa_fwd_mask(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
+                long long mask_batch_stride, int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal,
+                float scale, int dtype, void* stream);
+
+/*
+ * The backward under the same mask (bits and stride as for fa_fwd_mask):
+ * fa_bwd's dQ, dK, dV where P is 0 on the pairs the mask hides.  O and L must
+ * come from fa_fwd_mask with the same mask.  The workspace is
+ * fa_bwd_mask_workspace_bytes: fa_bwd's plus a key-major copy of the mask
+ * (4 * ceil(Tq / 128) words per key and entry) that the call writes before
+ * its dK/dV pass.  Errors as fa_bwd, plus the mask errors of fa_fwd_mask.
+ * fa_bwd_mask_workspace_bytes returns 0 for invalid sizes.
+ */
+size_t fa_bwd_mask_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype,
+                                   long long mask_batch_stride);
+int fa_bwd_mask(const void* Q, const void* K, const void* V, const void* O, const float* L, const void* dO,
+                void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, const uint32_t* mask_bits,
                 long long mask_batch_stride, int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal,
                 float scale, int dtype, void* stream);
 

@@ -172,3 +172,24 @@ def test_fwd_mask_rejects_bad_arguments(lib, kw, status):
 ])
 def test_mask_pack_rejects_bad_arguments(lib, args, status):
     assert lib.fa_mask_pack(*args, None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mask=None), 1), (dict(stride=-4), 2), (dict(stride=6), 2), (dict(ws=None), 7), (dict(wsb=64), 7),
+    (dict(d=80), 4),
+])
+def test_bwd_mask_rejects_bad_arguments(lib, kw, status):
+    a = dict(mask=FAKE, stride=0, ws=FAKE, wsb=1 << 30, d=64)
+    a.update(kw)
+    assert lib.fa_bwd_mask(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["ws"], a["wsb"], a["mask"],
+                           a["stride"], 2, 4, 2, 16, 300, a["d"], 1, 0.125, 1, None) == status
+
+
+def test_bwd_mask_workspace_adds_the_key_major_copy(lib):
+    base = lib.fa_bwd_workspace_bytes(2, 4, 2, 200, 300, 64, 1)
+    shared = lib.fa_bwd_mask_workspace_bytes(2, 4, 2, 200, 300, 64, 1, 0)
+    per = lib.fa_bwd_mask_workspace_bytes(2, 4, 2, 200, 300, 64, 1, 200 * 12)
+    words = 300 * 4 * math.ceil(200 / 128)
+    assert shared - base == math.ceil(words * 4 / 256) * 256
+    assert per - base == math.ceil(2 * words * 4 / 256) * 256
+    assert lib.fa_bwd_mask_workspace_bytes(2, 4, 2, 200, 300, 64, 1, -1) == 0

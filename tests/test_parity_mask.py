@@ -1,8 +1,8 @@
-"""GPU parity of the boolean-mask forward (fa_mask_pack, fa_fwd_mask) against
-the fp64 oracle with the same mask.
+"""GPU parity of the boolean-mask forward and backward (fa_mask_pack,
+fa_fwd_mask, fa_bwd_mask) against the fp64 oracle with the same mask.
 
 The mask packer is integer work and is compared bit for bit with a packing
-written here in numpy.  The forward is compared with the oracle's O and L at
+written here in numpy.  O, L, dQ, dK and dV are compared with the oracle at
 the tolerance of the other parity tests: relative Frobenius error 1e-4 (fp32
 storage) and 2e-2 (bf16 storage); rows that the mask leaves without a key
 must have L = -inf and O = 0 exactly.
@@ -14,8 +14,8 @@ masked; a very sparse mask (most tiles skipped by whole waves); the
 prefix-plus-block layout of the chunked-attention article's drafter (32 new
 positions per entry, each seeing its own prefix length and its own block);
 no keys at all; and the headline shape (4096 x 4096, 32 query heads over 8
-K/V heads, causal) on sampled rows.  An all-True mask must reproduce fa_fwd
-bit for bit.
+K/V heads, causal) on one whole group and sampled rows.  An all-True mask must
+reproduce fa_fwd and fa_bwd bit for bit.
 """
 
 import numpy as np
@@ -64,12 +64,27 @@ def random_mask(shape, seed, density):
     return np.random.default_rng(seed).random(shape) < density
 
 
-def run(fa, w, mask_np, inp):
+def run(fa, w, mask_np, inp, backward=False):
     import torch
-    q, k, v, _ = wl.to_device(inp, w.dtype)
-    o, lse = fa.forward_masked(q, k, v, torch.from_numpy(mask_np).cuda(), w.causal, w.scale)
+    q, k, v, do = wl.to_device(inp, w.dtype)
+    m = torch.from_numpy(mask_np).cuda()
+    o, lse = fa.forward_masked(q, k, v, m, w.causal, w.scale)
+    out = {"O": o, "L": lse}
+    if backward:
+        out["dQ"], out["dK"], out["dV"] = fa.backward_masked(q, k, v, o, lse, do, m, w.causal, w.scale)
     torch.cuda.synchronize()
-    return o.float().cpu().numpy(), lse.cpu().numpy()
+    return {n: t.float().cpu().numpy() for n, t in out.items()}
+
+
+def check_all(name, dtype, got, ref):
+    errs = {n: oa.relative_frobenius(got[n], ref[n], finite_only=(n == "L")) for n in ref}
+    log(f"{name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    empty = np.isneginf(ref["L"])
+    assert np.all(got["O"][empty] == 0.0), f"{name}: rows without keys must give O = 0"
+    if "dQ" in ref:
+        assert np.all(got["dQ"][empty] == 0.0), f"{name}: rows without keys must give dQ = 0"
+    bad = {k: v for k, v in errs.items() if not v <= TOL[dtype]}
+    assert not bad, f"{name}: over tolerance {TOL[dtype]}: {bad}"
 
 
 def check(name, dtype, O, L, Oref, Lref):
@@ -127,9 +142,10 @@ def test_mask_parity_full(fa, name, shape, maker):
     w = wl.Workload(name, B, Hq, Hkv, Tq, Tk, d, dtype, causal, 31)
     inp = wl.make_inputs(w)
     mask = maker(B, Tq, Tk)
-    O, L = run(fa, w, mask, inp)
-    Oref, Lref = oa.attention_forward(inp.q, inp.k, inp.v, causal, w.scale, mask=mask)
-    check(name, dtype, O, L, Oref, Lref)
+    got = run(fa, w, mask, inp, backward=True)
+    ref = dict(zip(("O", "L", "dQ", "dK", "dV"),
+                   oa.attention_forward_backward(inp.q, inp.k, inp.v, inp.do, causal, w.scale, mask=mask)))
+    check_all(name, dtype, got, ref)
 
 
 def test_mask_without_keys(fa):
@@ -137,21 +153,28 @@ def test_mask_without_keys(fa):
     w = wl.Workload("gqa_bf16_T64_Tk0", 1, 4, 2, 64, 0, 128, "bf16", False, 3)
     inp = wl.make_inputs(w)
     q, k, v, _ = wl.to_device(inp, w.dtype)
-    o, lse = fa.forward_masked(q, k, v, torch.zeros(64, 0, dtype=torch.bool, device="cuda"))
+    m = torch.zeros(64, 0, dtype=torch.bool, device="cuda")
+    o, lse = fa.forward_masked(q, k, v, m)
+    dq, dk, dv = fa.backward_masked(q, k, v, o, lse, torch.ones_like(q), m)
     torch.cuda.synchronize()
-    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse)) and torch.all(dq == 0)
 
 
 @pytest.mark.parametrize("dtype,d,causal", [("bf16", 128, True), ("bf16", 64, False), ("fp32", 128, False)])
-def test_all_true_mask_is_the_plain_forward(fa, dtype, d, causal):
+def test_all_true_mask_is_the_plain_call(fa, dtype, d, causal):
     import torch
     w = wl.Workload("all_true", 2, 4, 2, 333, 333, d, dtype, causal, 12)
     inp = wl.make_inputs(w)
-    q, k, v, _ = wl.to_device(inp, w.dtype)
+    q, k, v, do = wl.to_device(inp, w.dtype)
+    ones = torch.ones(333, 333, dtype=torch.bool, device="cuda")
     o1, l1 = fa.forward(q, k, v, causal, w.scale)
-    o2, l2 = fa.forward_masked(q, k, v, torch.ones(333, 333, dtype=torch.bool, device="cuda"), causal, w.scale)
+    o2, l2 = fa.forward_masked(q, k, v, ones, causal, w.scale)
+    g1 = fa.backward(q, k, v, o1, l1, do, causal, w.scale)
+    g2 = fa.backward_masked(q, k, v, o1, l1, do, ones, causal, w.scale)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
 
 
 def test_mask_headline_shape_sampled(fa):
@@ -159,8 +182,9 @@ def test_mask_headline_shape_sampled(fa):
     log(f"case {w.name} B=1 with a random mask: generating inputs")
     inp = wl.make_inputs(w)
     mask = random_mask((w.Tq, w.Tk), 8, 0.5)
-    O, L = run(fa, w, mask, inp)
+    got = run(fa, w, mask, inp, backward=True)
     log("GPU done")
+    O, L = got["O"], got["L"]
     rng = np.random.default_rng(9)
     rows = np.unique(np.concatenate([[0, 1, 127, 128, 4095], rng.integers(0, w.Tq, 6)]))
     for h in (0, 13, 31):
@@ -168,3 +192,9 @@ def test_mask_headline_shape_sampled(fa):
         Oref, Lref, _ = oa.head_forward(inp.q[0, h, rows], inp.k[0, g], inp.v[0, g], True, w.scale, rows=rows,
                                         Tq=w.Tq, mask=mask)
         check(f"{w.name}[h={h}, {len(rows)} rows]", w.dtype, O[0, h, rows], L[0, h, rows], Oref, Lref)
+    g = 5
+    ref = oa.group_forward_backward(inp.q, inp.k, inp.v, inp.do, 0, g, True, w.scale, mask=mask)
+    sl = slice(g * w.G, (g + 1) * w.G)
+    check_all(f"{w.name}[b=0, g={g}]", w.dtype,
+              {"O": O[0, sl], "L": L[0, sl], "dQ": got["dQ"][0, sl], "dK": got["dK"][0, g], "dV": got["dV"][0, g]},
+              ref)
