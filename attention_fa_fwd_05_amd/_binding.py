@@ -433,18 +433,28 @@ def _autograd_function():
         """Autograd wrapper that saves exactly q, k, v, o and lse for the backward."""
 
         @staticmethod
-        def forward(ctx, q, k, v, causal, scale, window):
-            o, lse = forward(q, k, v, causal, scale, window=window)
+        def forward(ctx, q, k, v, causal, scale, window, mask):
+            if mask is None:
+                o, lse = forward(q, k, v, causal, scale, window=window)
+            else:
+                if window:
+                    raise ValueError("a boolean mask does not combine with a window")
+                if mask.dtype != torch.int32:
+                    mask = pack_mask(mask.contiguous(), k.shape[2])
+                o, lse = forward_masked(q, k, v, mask, causal, scale)
             ctx.save_for_backward(q, k, v, o, lse)
-            ctx.causal, ctx.scale, ctx.window = causal, scale, window
+            ctx.causal, ctx.scale, ctx.window, ctx.mask = causal, scale, window, mask
             return o
 
         @staticmethod
         def backward(ctx, do):
             q, k, v, o, lse = ctx.saved_tensors
-            dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), ctx.causal, ctx.scale,
-                                  window=ctx.window)
-            return dq, dk, dv, None, None, None
+            if ctx.mask is None:
+                dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), ctx.causal, ctx.scale,
+                                      window=ctx.window)
+            else:
+                dq, dk, dv = backward_masked(q, k, v, o, lse, do.contiguous(), ctx.mask, ctx.causal, ctx.scale)
+            return dq, dk, dv, None, None, None, None
 
     return FlashAttention
 
@@ -452,9 +462,10 @@ def _autograd_function():
 _FN = None
 
 
-def attention(q, k, v, causal: bool = False, scale: float | None = None, window: int = 0):
-    """Differentiable attention through the library (retains q, k, v, o, lse only)."""
+def attention(q, k, v, causal: bool = False, scale: float | None = None, window: int = 0, mask=None):
+    """Differentiable attention through the library (retains q, k, v, o, lse only, plus the
+    packed mask bits when a boolean ``mask`` [Tq, Tk] / [B, Tq, Tk] is given)."""
     global _FN
     if _FN is None:
         _FN = _autograd_function()
-    return _FN.apply(q, k, v, causal, scale, window)
+    return _FN.apply(q, k, v, causal, scale, window, mask)

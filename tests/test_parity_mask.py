@@ -15,7 +15,8 @@ prefix-plus-block layout of the chunked-attention article's drafter (32 new
 positions per entry, each seeing its own prefix length and its own block);
 no keys at all; and the headline shape (4096 x 4096, 32 query heads over 8
 K/V heads, causal) on one whole group and sampled rows.  An all-True mask must
-reproduce fa_fwd and fa_bwd bit for bit.
+reproduce fa_fwd and fa_bwd bit for bit, and the autograd wrapper with a mask
+the direct calls.
 """
 
 import numpy as np
@@ -198,3 +199,21 @@ def test_mask_headline_shape_sampled(fa):
     check_all(f"{w.name}[b=0, g={g}]", w.dtype,
               {"O": O[0, sl], "L": L[0, sl], "dQ": got["dQ"][0, sl], "dK": got["dK"][0, g], "dV": got["dV"][0, g]},
               ref)
+
+
+def test_autograd_wrapper_with_mask(fa):
+    """attention(..., mask=) runs fa_fwd_mask / fa_bwd_mask: the same values as the direct calls."""
+    import torch
+    w = wl.Workload("autograd_mask", 2, 4, 2, 200, 260, 64, "bf16", True, 41)
+    inp = wl.make_inputs(w)
+    q, k, v, do = wl.to_device(inp, w.dtype)
+    m = torch.from_numpy(random_mask((2, 200, 260), 42, 0.4)).cuda()
+    o_ref, l_ref = fa.forward_masked(q, k, v, m, True, w.scale)
+    g_ref = fa.backward_masked(q, k, v, o_ref, l_ref, do, m, True, w.scale)
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    o = fa.attention(qa, ka, va, True, w.scale, mask=m)
+    o.backward(do)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    for a, b in zip((qa.grad, ka.grad, va.grad), g_ref):
+        assert torch.equal(a, b)
