@@ -359,11 +359,25 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     if (interleave_is_b(r, NDTV, NDT)) dk[t] = M::mma(x, dsop[s], dk[t]);
     else dv[t] = M::mma(x, pop[s], dv[t]);
   };
-  // L2 of one tile's queries in accumulator order.
+  // L2 of one tile's queries in accumulator order (block in buffer buf).  A
+  // boolean mask enters here: a pair whose bit is 0 gets L2 = +inf, so its
+  // P = exp2(S c - L2) and dS are 0 through the ordinary stages (bit
+  // 4 h + 8 g + e of the tile's word for register 4 g + e).
   f32x4 lt[4];
-  auto load_l = [&](const float* lg, int t) {
+  auto load_l = [&](int buf, int t) {
+    const float* lg = sL[buf];
 #pragma unroll
     for (int g = 0; g < 4; ++g) lt[g] = *reinterpret_cast<const f32x4*>(lg + 32 * t + 8 * g + 4 * h);
+    if constexpr (MASK) {
+      const uint32_t mw = sM[buf * 256 + w * 64 + 2 * n + t] >> (4 * h);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int keep = (int)(mw << (31 - (8 * g + e))) >> 31;   // 0 or all ones
+          lt[g][e] = __int_as_float((__float_as_int(lt[g][e]) & keep) | (int)(0x7f800000u & ~(uint32_t)keep));
+        }
+    }
   };
   // The three vector stages of register e of tile t.
   float xa[16], pa[16];
@@ -411,19 +425,14 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   // P and dS of pairs the key may not see are cleared in the packed operands.
   // Register i of tile t holds query q0 + 32 t + 4 h + 8 (i / 4) + i % 4.
   // The sliding window clears pairs whose query is past the key's window.
-  // A boolean mask clears the pairs whose bit is 0: word t of the block's two
-  // (buffer buf), bit 4 h + 8 (i / 4) + i % 4 for register i.
-  auto mask_tile = [&](int q0, int t, int buf) {
-    if (MASK || ragged || (CAUSAL && k0 + BK - 1 > q0 + 32 * t + off) ||
-        (W > 0 && q0 + 32 * t + 31 > k0 - off + W - 1)) {
+  // (A boolean mask is applied through L2 in load_l.)
+  auto mask_tile = [&](int q0, int t) {
+    if (ragged || (CAUSAL && k0 + BK - 1 > q0 + 32 * t + off) || (W > 0 && q0 + 32 * t + 31 > k0 - off + W - 1)) {
       const int thr = !key_ok ? INT_MAX : (CAUSAL ? mykey - off - q0 - 32 * t - 4 * h : INT_MIN);
       const int thr_hi = W > 0 ? mykey - off + W - 1 - q0 - 32 * t - 4 * h : INT_MAX;
-      uint32_t mw = 0xffffffffu;
-      if constexpr (MASK) mw = sM[buf * 256 + w * 64 + 2 * n + t] >> (4 * h);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (8 * (i >> 2) + (i & 3) < thr || 8 * (i >> 2) + (i & 3) > thr_hi ||
-            (MASK && ((mw >> (8 * (i >> 2) + (i & 3))) & 1u) == 0)) {
+        if (8 * (i >> 2) + (i & 3) < thr || 8 * (i >> 2) + (i & 3) > thr_hi) {
           const int s = (16 * t + i) / KPER;
           zero_elem(pop[s], i % KPER);
           zero_elem(dsop[s], i % KPER);
@@ -442,11 +451,11 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int m = 0; m < NS1; ++m) s_mma(t, m, m < NSD ? nat.ld(sQ[0], t, m) : nat_o(sdO[0], t, m - NSD));
     }
-    load_l(sL[0], 0);
+    load_l(0, 0);
 #pragma unroll
     for (int m = 0; m < 18; ++m) stages(0, m, 0, 16, 16);
-    mask_tile(item_q0(0), 0, 0);
-    load_l(sL[0], 1);
+    mask_tile(item_q0(0), 0);
+    load_l(0, 1);
   }
 
   // One iteration with block i in buffer CUR, block i+1 in the next buffer.
@@ -497,7 +506,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
         if (NB == 3 && u == 1 && m % 2 == 1 && m / 2 < NDMA) dma_piece(dsrc, nn, m / 2);
         if (u == 0) {
           stages(1, m, 0, 16, SPAN1A);             // tile 1 of block i
-          if (m == LOADL0) load_l(sL[nxt], 0);     // L2 of block i+1's tile 0
+          if (m == LOADL0) load_l(nxt, 0);         // L2 of block i+1's tile 0
           if (m == NPA - 1) {                      // tile 1 of block i is done with S, dP
             sacc[1] = f32x16{};
             seed_dp(sD[nxt], 1);
@@ -509,7 +518,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       }
     };
     phase1(IC<0>{});
-    mask_tile(q0, 1, cur);
+    mask_tile(q0, 1);
     phase1(IC<1>{});
 
     // Phase 2: the second half of block i's dV, dK, with the second half of
@@ -522,8 +531,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       stages(0, m, 8, 16, SPAN2);
       __builtin_amdgcn_sched_barrier(0);
     }
-    mask_tile(nq0, 0, nxt);
-    load_l(sL[nxt], 1);                            // for block i+1's tile-1 probabilities
+    mask_tile(nq0, 0);
+    load_l(nxt, 1);                                // for block i+1's tile-1 probabilities
     if (NB == 3) {
       wait_vmcnt<0>();                             // this wave's loads of block i+2 have landed
       __syncthreads();

@@ -7,6 +7,8 @@ seeded synthetic tensors already resident in HBM; outputs and the workspace
 are allocated once, outside the timed region.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --decode        # key-split forward, 32 queries against 8032 keys
+    python bench.py --mask 0.5      # forward + backward under a random boolean mask
 
 Prints one JSON line: whole-step throughput in counted TFLOP/s (4*Tq*Tk*d
 forward + 10*Tq*Tk*d backward per query head, halved when causal), the
@@ -136,6 +138,81 @@ def decode_bench(args, fa, accounting, wl):
     return 0
 
 
+def mask_bench(args, fa, accounting, wl):
+    """Forward and backward under a boolean mask (fa_fwd_mask, fa_bwd_mask) on
+    the headline shape: each batch entry gets its own seeded random mask of the
+    given density, on top of the causal bound.  Counted work is 4d (forward)
+    and 10d (backward) per visible (query, key) pair, the pairs counted exactly
+    from the mask; the backward's roofline is its matrix work (14d per pair:
+    8d in the dK/dV pass, 6d in the dQ pass) over the whole fa_bwd_mask call."""
+    import numpy as np
+    import torch
+    w = wl.WORKLOADS[args.workload or wl.HEADLINE]
+    inp = wl.make_inputs(w)
+    q, k, v, do = wl.to_device(inp, w.dtype)
+    rng = np.random.default_rng(1000 + w.seed)
+    mask = rng.random((w.B, w.Tq, w.Tk), dtype=np.float32) < args.mask
+    if w.causal:
+        mask &= np.arange(w.Tk)[None, :] <= np.arange(w.Tq)[:, None] + (w.Tk - w.Tq)
+    pairs = int(mask.sum()) * w.Hq                   # visible pairs over all (entry, query head)
+    bits = fa.pack_mask(torch.from_numpy(mask).cuda())
+    del mask
+    code = fa.FA_DTYPE_BF16 if w.dtype == "bf16" else fa.FA_DTYPE_F32
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.Hq, w.Tq, dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stride = w.Tq * fa.load_library().fa_mask_row_words(w.Tk) if w.B > 1 else 0
+    ws = torch.empty(max(1, fa.load_library().fa_bwd_mask_workspace_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d,
+                                                                           code, stride)),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.forward_masked(q, k, v, bits, w.causal, w.scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        fa.backward_masked(q, k, v, o, lse, do, bits, w.causal, w.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_fwd = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    ms_bwd = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    f_fwd, f_bwd = 4.0 * w.d * pairs, 10.0 * w.d * pairs
+    ms_step = elapsed / args.steps * 1e3
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    peak = PEAK[w.dtype]
+    bwd_mm = 14.0 * w.d * pairs / (ms_bwd * 1e-3) / 1e12
+    out = {"metric": "attention fwd+bwd under a boolean mask: TFLOP/s on the exactly counted visible pairs",
+           "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+           "data": f"synthetic (seeded N(0,1) inputs and cotangent; seeded random mask, density {args.mask})",
+           "config": {"workload": f"{w.name}_mask{args.mask}", "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Tq": w.Tq,
+                      "Tk": w.Tk, "d": w.d, "causal": w.causal, "mask_density": args.mask,
+                      "visible_pairs": pairs, "parallelism": "single GPU"},
+           "pct_peak": round(100.0 * value / peak, 2),
+           "roofline": {"bound": "mfma", "kernel": "fa_bwd_mask (pre, transpose, dK/dV, dQ)",
+                        "achieved": round(bwd_mm, 2), "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(bwd_mm / peak, 4), "traffic": None,
+                        "flops_per_launch": 14.0 * w.d * pairs, "avg_launch_ms": round(ms_bwd, 4)},
+           "breakdown_ms": {"fwd_mask": round(ms_fwd, 4), "bwd_mask": round(ms_bwd, 4)},
+           "fwd_tflops": round(f_fwd / (ms_fwd * 1e-3) / 1e12, 2),
+           "bwd_tflops": round(f_bwd / (ms_bwd * 1e-3) / 1e12, 2),
+           "workspace_bytes": ws.numel()}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def copy_calibration(nbytes: int, reps: int):
     """A plain device copy of known size, for scaling rocprofv3 byte counters."""
     import torch
@@ -157,6 +234,8 @@ def main() -> int:
                     help="budget for the CPU oracle baseline (0 disables it)")
     ap.add_argument("--decode", action="store_true",
                     help="time the key-split forward on a decode-shaped workload instead")
+    ap.add_argument("--mask", type=float, default=0.0, metavar="DENSITY",
+                    help="time the boolean-mask forward and backward with a random mask of this density")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run only a device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -183,6 +262,8 @@ def main() -> int:
     fa.load_library()
     if args.decode:
         return decode_bench(args, fa, accounting, wl)
+    if args.mask > 0:
+        return mask_bench(args, fa, accounting, wl)
     w = wl.WORKLOADS[args.workload or wl.HEADLINE]
     inp = wl.make_inputs(w)
     q, k, v, do = wl.to_device(inp, w.dtype)
