@@ -750,15 +750,27 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   auto dq_phase = [&](int j, int buf) {
     const int k0 = j * BK;
     float ds[32];
+    // Boolean mask: key k0 + perm_index(h, r) is bit perm_index(0, r) % 32 of
+    // word r / 16 once this half's 4 h are shifted out; a hidden pair's score
+    // becomes -inf, so its P and dS are 0.
+    uint32_t m0 = 0, m1 = 0;
+    if constexpr (MASK) {
+      m0 = sM[(buf * NW + w) * 64 + 2 * n] >> (4 * h);
+      m1 = sM[(buf * NW + w) * 64 + 2 * n + 1] >> (4 * h);
+    }
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
-      const float sv = r < 16 ? st0[r] : st1[r - 16];
+      float sv = r < 16 ? st0[r] : st1[r - 16];
       const float dpv = r < 16 ? dp0[r] : dp1[r - 16];
+      if constexpr (MASK) {
+        const int keep = (int)((r < 16 ? m0 : m1) << (31 - perm_index(0, r) % 32)) >> 31;
+        sv = __int_as_float((__float_as_int(sv) & keep) | (int)(0xff800000u & ~(uint32_t)keep));
+      }
       ds[r] = fast_exp2(__builtin_fmaf(sv, c, -l2)) * (dpv + ndd);
     }
     // Only the diagonal tiles and the ragged key end (a uniform test) clear
     // dS of the keys this query may not see; every value above is finite.
-    if (MASK || (k0 + BK > Tk) || (CAUSAL && k0 + BK - 1 > qw + off) || (W > 0 && k0 < qw + 31 + off - W + 1)) {
+    if ((k0 + BK > Tk) || (CAUSAL && k0 + BK - 1 > qw + off) || (W > 0 && k0 < qw + 31 + off - W + 1)) {
       // First and last visible key offsets, less this lane half's 4 h,
       // against the compile-time part of perm_index (no per-lane table).
       const int lim = min(Tk - 1, CAUSAL ? myq + off : Tk - 1) - k0 - 4 * h;
@@ -766,15 +778,6 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
 #pragma unroll
       for (int r = 0; r < 32; ++r)
         if (perm_index(0, r) > lim || perm_index(0, r) < lo) ds[r] = 0.f;
-      if constexpr (MASK) {
-        // Key k0 + perm_index(h, r): bit perm_index(0, r) % 32 of word r / 16
-        // once this half's 4 h are shifted out.
-        const uint32_t m0 = sM[(buf * NW + w) * 64 + 2 * n] >> (4 * h);
-        const uint32_t m1 = sM[(buf * NW + w) * 64 + 2 * n + 1] >> (4 * h);
-#pragma unroll
-        for (int r = 0; r < 32; ++r)
-          if ((((r < 16 ? m0 : m1) >> (perm_index(0, r) % 32)) & 1u) == 0) ds[r] = 0.f;
-      }
     }
     Op dsop[NSK];
 #pragma unroll

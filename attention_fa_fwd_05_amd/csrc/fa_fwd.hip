@@ -244,7 +244,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
       }
       sched_interleave<NKT * NSD * QT, 4 * QT, 1, QT>();
 
-      const bool need_mask = MASK || (k0 + BK > Tk) || (CAUSAL && k0 + BK - 1 > qw + off) ||
+      const bool need_mask = (k0 + BK > Tk) || (CAUSAL && k0 + BK - 1 > qw + off) ||
                              (W > 0 && k0 < qw + 32 * QT - 1 + off - W + 1);
       Op pop[QT][NSK];
 #pragma unroll
@@ -260,15 +260,15 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
 #pragma unroll
           for (int r = 0; r < NE; ++r)
             if (perm_index(0, r) > lim || perm_index(0, r) < lo) x[r] = -INFINITY;
-          if constexpr (MASK) {
-            // Key k0 + perm_index(h, r) is bit perm_index(h, r) % 32 of word r / 16,
-            // i.e. bit perm_index(0, r) % 32 after shifting out this half's 4 h.
+        }
+        if constexpr (MASK) {
+          // Key k0 + perm_index(h, r) is bit perm_index(h, r) % 32 of word r / 16,
+          // i.e. bit perm_index(0, r) % 32 after shifting out this half's 4 h.
 #pragma unroll
-            for (int r = 0; r < NE; ++r) {
-              const uint32_t wsh = mcur[r >> 4] >> (4 * h);
-              const int keep = (int)(wsh << (31 - perm_index(0, r) % 32)) >> 31;   // 0 or all ones
-              x[r] = __int_as_float((__float_as_int(x[r]) & keep) | (int)(0xff800000u & ~(uint32_t)keep));
-            }
+          for (int r = 0; r < NE; ++r) {
+            const uint32_t wsh = mcur[r >> 4] >> (4 * h);
+            const int keep = (int)(wsh << (31 - perm_index(0, r) % 32)) >> 31;   // 0 or all ones
+            x[r] = __int_as_float((__float_as_int(x[r]) & keep) | (int)(0xff800000u & ~(uint32_t)keep));
           }
         }
         float mt = wave_xor32_max(max_tree<NE>(x)) * c;   // row max, exp2 units
