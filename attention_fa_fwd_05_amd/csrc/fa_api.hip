@@ -471,6 +471,10 @@ int bwd_core(const void* Q, const void* K, const void* V, const void* O, const f
   if (stages & ~(unsigned)FA_BWD_STAGE_ALL) return FA_ERR_STAGES;
   const WsLayout ws = ws_layout(B, Hq, Tq, d, dtype);
   const bool masked = mask_bstride >= 0 && mask != nullptr && Tq > 0 && Tk > 0;
+  if (masked) {                                      // one thread per word of the key-major copy
+    const long long words = (mask_bstride != 0 ? (long long)B : 1LL) * Tk * (4LL * ((Tq + 127) / 128));
+    if (words / 256 + 1 > kMaxGrid) return FA_ERR_TOO_LARGE;
+  }
   const size_t need = ws.total + (masked ? mask_t_bytes(B, Tq, Tk, mask_bstride) : 0);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
