@@ -732,6 +732,7 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   };
   auto s_phase = [&](int buf) {
     st0 = f32x16{}; st1 = f32x16{}; dp0 = f32x16{}; dp1 = f32x16{};
+    wave_prio<1>();
 #pragma unroll
     for (int s = 0; s < (NSD > NSDV ? NSD : NSDV); ++s) {
       if (s < NSD) {
@@ -744,6 +745,7 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
       }
     }
     sched_interleave<2 * NSD + 2 * NSDV, 4>();
+    wave_prio<0>();
   };
   // dS^T from the tile's S^T, dP^T, then dQ^T += K^T dS^T (K^T through
   // transposed reads of the key tile).
@@ -782,12 +784,14 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
     Op dsop[NSK];
 #pragma unroll
     for (int s = 0; s < NSK; ++s) dsop[s] = M::pack(ds + s * KPER);
+    wave_prio<1>();
 #pragma unroll
     for (int t = 0; t < NDT; ++t) {
 #pragma unroll
       for (int s = 0; s < NSK; ++s) acc[t] = M::mma(ld_tr(buf, t, s), dsop[s], acc[t]);
     }
     sched_interleave<NDT * NSK, 4, (sizeof(T) == 2 ? 2 : 1)>();
+    wave_prio<0>();
   };
 
   int buf = 0;                                      // buffer of tile jt

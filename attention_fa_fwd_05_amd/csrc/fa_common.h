@@ -330,6 +330,18 @@ __device__ inline void sched_interleave() {
   __builtin_amdgcn_sched_group_barrier(kMfma, AHEAD, 0);
 }
 
+// Issue priority of this wave (s_setprio), fenced so the scheduler keeps it
+// at this point of the instruction stream.  Kernels with two waves per SIMD
+// raise it around their matrix products: when the other wave is in its vector
+// phase, the arbiter then prefers the wave that feeds the matrix unit, and the
+// products of one wave overlap the vector work of the other more closely.
+template <int P>
+__device__ inline void wave_prio() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(P);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Work items in dispatch order.  Consecutive workgroup ids are spread over
 // the 8 XCDs round-robin; giving each XCD one contiguous range of the logical
 // order keeps the workgroups of a (batch, K/V head) group on one XCD, so the

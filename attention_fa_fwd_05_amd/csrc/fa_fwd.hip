@@ -233,6 +233,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
       for (int u = 0; u < QT; ++u)
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) st[u][kt] = f32x16{};
+      wave_prio<1>();
 #pragma unroll
       for (int s = 0; s < NSD; ++s) {
 #pragma unroll
@@ -243,6 +244,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
         }
       }
       sched_interleave<NKT * NSD * QT, 4 * QT, 1, QT>();
+      wave_prio<0>();
 
       const bool need_mask = (k0 + BK > Tk) || (CAUSAL && k0 + BK - 1 > qw + off) ||
                              (W > 0 && k0 < qw + 32 * QT - 1 + off - W + 1);
@@ -299,6 +301,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
         lsum[u] += (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
       }
 
+      wave_prio<1>();
       // O^T += V^T P^T; each V^T operand feeds QT products.
 #pragma unroll
       for (int t = 0; t < NDT; ++t) {
@@ -310,6 +313,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
         }
       }
       sched_interleave<NDT * NSK * QT, 4 * QT, (sizeof(T) == 2 ? 2 : 1), QT>();
+      wave_prio<0>();
     }
     wait_vmcnt<0>();                                 // this wave's loads of the next tile have landed
     __syncthreads();
