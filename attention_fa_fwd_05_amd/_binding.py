@@ -29,6 +29,7 @@ EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_window", "fa_bwd_window"
            "fa_fwd_splitk_workspace_bytes", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fwd_paged",
            "fa_fwd_paged_workspace_bytes", "fa_bwd_workspace_bytes",
            "fa_mask_row_words", "fa_mask_pack", "fa_fwd_mask", "fa_bwd_mask", "fa_bwd_mask_workspace_bytes",
+           "fa_fwd_mask_splitk", "fa_fwd_mask_splitk_workspace_bytes",
            "fa_status_string", "fa_hip_error_string", "fa_abi_version"]
 
 _lib = None
@@ -96,6 +97,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_mask_pack.restype = i
     lib.fa_fwd_mask.argtypes = [vp, vp, vp, vp, vp, vp, ll, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_mask.restype = i
+    lib.fa_fwd_mask_splitk.argtypes = [vp, vp, vp, vp, vp, vp, ll, vp, sz, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_mask_splitk.restype = i
+    lib.fa_fwd_mask_splitk_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+    lib.fa_fwd_mask_splitk_workspace_bytes.restype = sz
     lib.fa_bwd_mask.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ll, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_bwd_mask.restype = i
     lib.fa_bwd_mask_workspace_bytes.argtypes = [i, i, i, i, i, i, i, ll]
@@ -360,8 +365,10 @@ def backward_masked(q, k, v, o, lse, do, mask, causal: bool = False, scale: floa
     return dq, dk, dv
 
 
-def forward_masked(q, k, v, mask, causal: bool = False, scale: float | None = None, out=None, lse=None):
-    """fa_fwd_mask: attention under a boolean mask shared by all heads of a batch entry.
+def forward_masked(q, k, v, mask, causal: bool = False, scale: float | None = None, out=None, lse=None,
+                   nsplit: int = 1, workspace=None):
+    """fa_fwd_mask (nsplit == 1) or fa_fwd_mask_splitk: attention under a boolean mask shared by
+    all heads of a batch entry.
 
     ``mask``: bool/uint8 [Tq, Tk] (whole batch) or [B, Tq, Tk] (or [B, 1, Tq, Tk]), packed here
     with fa_mask_pack; or an already packed int32 [..., Tq, fa_mask_row_words(Tk)].
@@ -374,10 +381,19 @@ def forward_masked(q, k, v, mask, causal: bool = False, scale: float | None = No
     code = _dtype_code(q)
     o = torch.empty_like(q) if out is None else out
     L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
-    st = lib.fa_fwd_mask(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(bits), stride, B, Hq, Hkv, Tq, Tk, d,
-                         int(bool(causal)), scale, code, _stream(q))
+    if nsplit == 1:
+        st = lib.fa_fwd_mask(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(bits), stride, B, Hq, Hkv, Tq, Tk,
+                             d, int(bool(causal)), scale, code, _stream(q))
+        if st != 0:
+            raise FaError(st, "fa_fwd_mask")
+        return o, L
+    need = int(lib.fa_fwd_mask_splitk_workspace_bytes(B, Hq, Hkv, Tq, Tk, d, code, int(nsplit)))
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.fa_fwd_mask_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(bits), stride, ws.data_ptr(),
+                                ws.numel(), B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), scale, code, int(nsplit),
+                                _stream(q))
     if st != 0:
-        raise FaError(st, "fa_fwd_mask")
+        raise FaError(st, "fa_fwd_mask_splitk")
     return o, L
 
 

@@ -102,6 +102,22 @@ int fwd_splits(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int nsp
 }
 
 constexpr int kMaxSplits = 1024;
+// Key slices of the masked forward, which always runs the regular shape
+// (packed when a group's rows fit it): the requested count, or (nsplit <= 0)
+// enough for about one workgroup per compute unit, each of at least eight key
+// tiles, at most 64.
+int mask_splits(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int nsplit) {
+  if (nsplit > 0) return nsplit;
+  const int G = Hq / Hkv, nw = fa::fwd_waves(dtype == FA_DTYPE_BF16, d);
+  const bool pack = G <= nw && Tq <= 32 * (nw / G);
+  const long long items = pack ? (long long)B * Hkv : (long long)((Tq + 32 * nw - 1) / (32 * nw)) * B * Hq;
+  const long long tiles = (Tk + fa::fwd_block_keys(dtype == FA_DTYPE_BF16, d) - 1) /
+                          fa::fwd_block_keys(dtype == FA_DTYPE_BF16, d);
+  long long ns = items > 0 ? (256 + items - 1) / items : 1;
+  ns = ns < tiles / 8 ? ns : tiles / 8;
+  ns = ns < 64 ? ns : 64;
+  return ns < 1 ? 1 : (int)ns;
+}
 
 // Head dim of V (and O, dO, dV): equal to d, or, for bf16 only, 64 with d = 128
 // and 128 with d = 64.
@@ -259,6 +275,20 @@ int fa_mask_pack(const void* mask_bytes, uint32_t* mask_bits, long long rows, in
 int fa_fwd_mask(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
                 long long mask_batch_stride, int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal,
                 float scale, int dtype, void* stream) {
+  return fa_fwd_mask_splitk(Q, K, V, O, L, mask_bits, mask_batch_stride, nullptr, 0, B, Hq, Hkv, Tq, Tk, d, causal,
+                            scale, dtype, 1, stream);
+}
+
+size_t fa_fwd_mask_splitk_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int nsplit) {
+  if (check_common(B, Hq, Hkv, Tq, Tk, d, dtype) != FA_OK) return 0;
+  const int ns = mask_splits(B, Hq, Hkv, Tq, Tk, d, dtype, nsplit);
+  if (ns > kMaxSplits) return 0;
+  return ns == 1 ? 0 : splitk_ws_bytes(B, Hq, Tq, d, ns);
+}
+
+int fa_fwd_mask_splitk(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
+                       long long mask_batch_stride, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                       int Tq, int Tk, int d, int causal, float scale, int dtype, int nsplit, void* stream) {
   int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
   if (st != FA_OK) return st;
   const long long nq = (long long)B * Hq * Tq * d, nkv = (long long)B * Hkv * Tk * d;
@@ -268,6 +298,13 @@ int fa_fwd_mask(const void* Q, const void* K, const void* V, void* O, float* L, 
   const long long rw = fa_mask_row_words(Tk);
   if ((st = check_mask(mask_bits, mask_batch_stride, B, Tq, Tk))) return st;
   if (!isfinite(scale)) return FA_ERR_SCALE;
+  const int ns = mask_splits(B, Hq, Hkv, Tq, Tk, d, dtype, nsplit);
+  if (ns > kMaxSplits) return FA_ERR_TOO_LARGE;
+  const size_t need = ns == 1 ? 0 : splitk_ws_bytes(B, Hq, Tq, d, ns);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (misaligned(workspace)) return FA_ERR_ALIGNMENT;
+  }
   if (Tq == 0) return FA_OK;
   fa::FwdArgs a;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L;
@@ -283,7 +320,12 @@ int fa_fwd_mask(const void* Q, const void* K, const void* V, void* O, float* L, 
   a.mask = Tk > 0 ? mask_bits : nullptr;
   a.mask_bstride = mask_batch_stride;
   a.mask_row_words = (int)rw;
-  return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream));
+  if (ns > 1) {
+    char* wsb = static_cast<char*>(workspace);
+    a.Opart = reinterpret_cast<float*>(wsb);
+    a.Lpart = reinterpret_cast<float*>(wsb + align_up((size_t)ns * B * Hq * Tq * d * 4));
+  }
+  return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream, ns));
 }
 
 size_t fa_bwd_mask_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype,

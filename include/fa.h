@@ -295,6 +295,19 @@ int fa_fwd_mask(const void* Q, const void* K, const void* V, void* O, float* L, 
                 float scale, int dtype, void* stream);
 
 /*
+ * fa_fwd_mask with the keys split over slices and merged as in fa_fwd_splitk
+ * ("The Autograd Memory Trap...", section "The Scene": blocks of few new
+ * positions against a long prefix, here under a mask).  nsplit == 1 is
+ * fa_fwd_mask (no workspace); nsplit <= 0 picks the count; otherwise the
+ * workspace holds fa_fwd_mask_splitk_workspace_bytes bytes of fp32 partials.
+ * Errors as fa_fwd_mask and fa_fwd_splitk.
+ */
+size_t fa_fwd_mask_splitk_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int nsplit);
+int fa_fwd_mask_splitk(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
+                       long long mask_batch_stride, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                       int Tq, int Tk, int d, int causal, float scale, int dtype, int nsplit, void* stream);
+
+/*
  * The backward under the same mask (bits and stride as for fa_fwd_mask):
  * fa_bwd's dQ, dK, dV where P is 0 on the pairs the mask hides.  O and L must
  * come from fa_fwd_mask with the same mask.  The workspace is

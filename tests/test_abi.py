@@ -193,3 +193,17 @@ def test_bwd_mask_workspace_adds_the_key_major_copy(lib):
     assert shared - base == math.ceil(words * 4 / 256) * 256
     assert per - base == math.ceil(2 * words * 4 / 256) * 256
     assert lib.fa_bwd_mask_workspace_bytes(2, 4, 2, 200, 300, 64, 1, -1) == 0
+
+
+def test_mask_splitk_workspace_and_arguments(lib):
+    assert lib.fa_fwd_mask_splitk_workspace_bytes(4, 32, 8, 32, 1056, 128, 1, 1) == 0
+    n3 = lib.fa_fwd_mask_splitk_workspace_bytes(4, 32, 8, 32, 1056, 128, 1, 3)
+    rows = 4 * 32 * 32
+    assert n3 == math.ceil(3 * rows * 128 * 4 / 256) * 256 + math.ceil(3 * rows * 4 / 256) * 256
+    # a split call without its workspace, then with too small a one
+    assert lib.fa_fwd_mask_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, 0, 4, 32, 8, 32, 1056, 128, 0,
+                                  0.125, 1, 3, None) == 7
+    assert lib.fa_fwd_mask_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 64, 4, 32, 8, 32, 1056, 128, 0,
+                                  0.125, 1, 3, None) == 7
+    assert lib.fa_fwd_mask_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 30, 4, 32, 8, 32, 1056, 128, 0,
+                                  0.125, 1, 5000, None) == 9

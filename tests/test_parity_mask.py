@@ -217,3 +217,32 @@ def test_autograd_wrapper_with_mask(fa):
     assert torch.equal(o, o_ref)
     for a, b in zip((qa.grad, ka.grad, va.grad), g_ref):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("nsplit", [0, 3])
+def test_mask_split_forward_drafter_blocks(fa, nsplit):
+    """fa_fwd_mask_splitk on the drafter layout: 32 positions per entry against its own prefix."""
+    import torch
+    w = wl.Workload("gqa_bf16_B4_Tq32_Tk1056_d128_drafter_split", 4, 32, 8, 32, 1056, 128, "bf16", False, 43)
+    inp = wl.make_inputs(w)
+    q, k, v, _ = wl.to_device(inp, w.dtype)
+    mask = drafter_mask(4, 32, 1056, [1024, 700, 300, 0])
+    o, lse = fa.forward_masked(q, k, v, torch.from_numpy(mask).cuda(), False, w.scale, nsplit=nsplit)
+    torch.cuda.synchronize()
+    Oref, Lref = oa.attention_forward(inp.q, inp.k, inp.v, False, w.scale, mask=mask)
+    check(f"{w.name}[nsplit={nsplit}]", w.dtype, o.float().cpu().numpy(), lse.cpu().numpy(), Oref, Lref)
+
+
+def test_mask_split_forward_decode_shape(fa):
+    """The 16-block decode shape (32 positions against 8032 keys) under per-entry prefix masks,
+    automatic key split."""
+    import torch
+    w = wl.WORKLOADS["gqa_bf16_B16_Tq32_Tk8032_d128_causal"].with_(causal=False)
+    inp = wl.make_inputs(w)
+    q, k, v, _ = wl.to_device(inp, w.dtype)
+    prefixes = list(np.random.default_rng(44).integers(0, 8001, size=16))
+    mask = drafter_mask(16, 32, 8032, prefixes)
+    o, lse = fa.forward_masked(q, k, v, torch.from_numpy(mask).cuda(), False, w.scale, nsplit=0)
+    torch.cuda.synchronize()
+    Oref, Lref = oa.attention_forward(inp.q, inp.k, inp.v, False, w.scale, mask=mask)
+    check(f"{w.name} prefix masks, auto split", w.dtype, o.float().cpu().numpy(), lse.cpu().numpy(), Oref, Lref)
