@@ -333,9 +333,9 @@ def _mask_bits(lib, mask, q, B, Tq, Tk):
     rw = lib.fa_mask_row_words(Tk)
     if not bits.is_contiguous() or tuple(bits.shape[-2:]) != (Tq, rw) or bits.dim() not in (2, 3):
         raise ValueError(f"packed mask must be int32 [Tq, {rw}] or [B, Tq, {rw}]")
-    if bits.dim() == 3 and bits.shape[0] != B:
-        raise ValueError("per-entry mask needs B entries")
-    return bits, (Tq * rw if bits.dim() == 3 and B > 1 else 0)
+    if bits.dim() == 3 and bits.shape[0] not in (1, B):
+        raise ValueError("a per-entry mask needs B entries (or one, shared by the batch)")
+    return bits, (Tq * rw if bits.dim() == 3 and bits.shape[0] > 1 else 0)
 
 
 def backward_masked(q, k, v, o, lse, do, mask, causal: bool = False, scale: float | None = None,

@@ -246,3 +246,20 @@ def test_mask_split_forward_decode_shape(fa):
     torch.cuda.synchronize()
     Oref, Lref = oa.attention_forward(inp.q, inp.k, inp.v, False, w.scale, mask=mask)
     check(f"{w.name} prefix masks, auto split", w.dtype, o.float().cpu().numpy(), lse.cpu().numpy(), Oref, Lref)
+
+
+def test_mask_with_one_entry_is_shared(fa):
+    """A [1, Tq, Tk] mask serves every batch entry, as a [Tq, Tk] one does."""
+    import torch
+    w = wl.Workload("shared_entry", 3, 4, 2, 150, 270, 64, "bf16", True, 45)
+    inp = wl.make_inputs(w)
+    q, k, v, do = wl.to_device(inp, w.dtype)
+    m2 = torch.from_numpy(random_mask((150, 270), 46, 0.5)).cuda()
+    o1, l1 = fa.forward_masked(q, k, v, m2, True, w.scale)
+    o2, l2 = fa.forward_masked(q, k, v, m2[None], True, w.scale)
+    g1 = fa.backward_masked(q, k, v, o1, l1, do, m2, True, w.scale)
+    g2 = fa.backward_masked(q, k, v, o1, l1, do, m2[None], True, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
