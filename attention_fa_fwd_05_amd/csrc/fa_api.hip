@@ -33,7 +33,8 @@ int elem_bytes(int dtype) { return dtype == FA_DTYPE_BF16 ? 2 : 4; }
 int check_common(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 0 || Tk < 0) return FA_ERR_BAD_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_GQA_RATIO;
-  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  // 64 and 128; fp32 also 32 (the measured configuration of the tiling article)
+  if (d != 64 && d != 128 && !(d == 32 && dtype == FA_DTYPE_F32)) return FA_ERR_HEAD_DIM;
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (Tq > kMaxSeq || Tk > kMaxSeq) return FA_ERR_TOO_LARGE;
   const long long q = (long long)B * Hq * Tq * d, kv = (long long)B * Hkv * Tk * d;
@@ -180,7 +181,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_NULL_PTR: return "a required pointer is NULL";
     case FA_ERR_BAD_SHAPE: return "bad shape: B, Hq, Hkv must be >= 1 and Tq, Tk >= 0";
     case FA_ERR_GQA_RATIO: return "Hq must be a multiple of Hkv";
-    case FA_ERR_HEAD_DIM: return "unsupported head dimension (64 or 128)";
+    case FA_ERR_HEAD_DIM: return "unsupported head dimension (64 or 128; fp32 also 32)";
     case FA_ERR_DTYPE: return "unsupported dtype (FA_DTYPE_F32 or FA_DTYPE_BF16)";
     case FA_ERR_SCALE: return "scale must be finite";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_bwd_workspace_bytes";

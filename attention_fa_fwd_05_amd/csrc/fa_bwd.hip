@@ -889,6 +889,7 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int d, int causal, unsig
     FA_BWD_CASE(bf16, 64)
     FA_BWD_CASE(bf16, 128)
   } else {
+    FA_BWD_CASE(float, 32)
     FA_BWD_CASE(float, 64)
     FA_BWD_CASE(float, 128)
   }

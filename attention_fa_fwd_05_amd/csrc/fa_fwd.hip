@@ -390,20 +390,31 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdArgs a, int nsplit) {
       const float wt = __expf(ls - m);
       wsum += wt;
       const float* op = a.Opart + (s * rows + row) * D + j * EPL;
+      if constexpr (EPL % 4 == 0) {
 #pragma unroll
-      for (int e = 0; e < EPL; e += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(op + e);
-        acc[e] += wt * v[0];
-        acc[e + 1] += wt * v[1];
-        acc[e + 2] += wt * v[2];
-        acc[e + 3] += wt * v[3];
+        for (int e = 0; e < EPL; e += 4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(op + e);
+          acc[e] += wt * v[0];
+          acc[e + 1] += wt * v[1];
+          acc[e + 2] += wt * v[2];
+          acc[e + 3] += wt * v[3];
+        }
+      } else {                                      // d = 32: two elements per lane
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] += wt * op[e];
       }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   T* orow = reinterpret_cast<T*>(a.O) + row * D + j * EPL;
+  if constexpr (EPL % 4 == 0) {
 #pragma unroll
-  for (int e = 0; e < EPL; e += 4) store4(orow + e, acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+    for (int e = 0; e < EPL; e += 4)
+      store4(orow + e, acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) orow[e] = (T)(acc[e] * inv);
+  }
   if (j == 0) a.L[row] = wsum > 0.f ? m + logf(wsum) : -INFINITY;
 }
 
@@ -464,13 +475,15 @@ hipError_t launch_mask_pack(const uint8_t* in, uint32_t* out, long long rows, in
 
 int fwd_waves(int dtype_bf16, int d) {
   return dtype_bf16 ? (d == 64 ? FwdShape<bf16, 64>::NW : FwdShape<bf16, 128>::NW)
-                    : (d == 64 ? FwdShape<float, 64>::NW : FwdShape<float, 128>::NW);
+                    : (d == 32 ? FwdShape<float, 32>::NW
+                               : d == 64 ? FwdShape<float, 64>::NW : FwdShape<float, 128>::NW);
 }
 int fwd_decode_waves() { return FwdShape<bf16, 128, true>::NW; }
 int fwd_decode_block_keys() { return FwdShape<bf16, 128, true>::BK; }
 int fwd_block_keys(int dtype_bf16, int d) {
   return dtype_bf16 ? (d == 64 ? FwdShape<bf16, 64>::BK : FwdShape<bf16, 128>::BK)
-                    : (d == 64 ? FwdShape<float, 64>::BK : FwdShape<float, 128>::BK);
+                    : (d == 32 ? FwdShape<float, 32>::BK
+                               : d == 64 ? FwdShape<float, 64>::BK : FwdShape<float, 128>::BK);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream, int nsplit,
@@ -493,6 +506,7 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipSt
     FA_FWD_CASE(bf16, 64)
     FA_FWD_CASE(bf16, 128)
   } else {
+    FA_FWD_CASE(float, 32)
     FA_FWD_CASE(float, 64)
     FA_FWD_CASE(float, 128)
   }

@@ -207,3 +207,9 @@ def test_mask_splitk_workspace_and_arguments(lib):
                                   0.125, 1, 3, None) == 7
     assert lib.fa_fwd_mask_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 30, 4, 32, 8, 32, 1056, 128, 0,
                                   0.125, 1, 5000, None) == 9
+
+
+def test_head_dim_32_is_fp32_only(lib):
+    # d = 32 passes validation in fp32 (then fails on the NULL output) and is rejected in bf16
+    assert lib.fa_fwd(FAKE, FAKE, FAKE, None, FAKE, 1, 2, 1, 16, 16, 32, 0, 0.125, 0, None) == 1
+    assert lib.fa_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 16, 16, 32, 0, 0.125, 1, None) == 4
