@@ -140,20 +140,62 @@ def _stream(t) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _shapes(q, k, v):
-    """(B, Hq, Hkv, Tq, Tk, d) of q [B, Hq, Tq, d], k [B, Hkv, Tk, d], v [B, Hkv, Tk, dv]."""
+def _on_gpu(t, name):
+    """Every tensor handed to the library must live in device memory: a host pointer would be
+    dereferenced by a kernel."""
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+
+
+def _shapes(q, k, v, same_dv: bool = False):
+    """(B, Hq, Hkv, Tq, Tk, d) of q [B, Hq, Tq, d], k [B, Hkv, Tk, d], v [B, Hkv, Tk, dv].
+
+    ``same_dv``: the entry point has no dv argument (its kernels index V with stride d), so v's
+    head dim must equal q's."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, T, d]")
     B, Hq, Tq, d = q.shape
     Bk, Hkv, Tk, dk = k.shape
     if Bk != B or dk != d or tuple(v.shape[:3]) != (B, Hkv, Tk):
         raise ValueError(f"inconsistent shapes q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if same_dv and v.shape[3] != d:
+        raise ValueError(f"this entry point needs v's head dim ({v.shape[3]}) equal to q's ({d})")
     for t in (q, k, v):
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
         if t.dtype != q.dtype or t.device != q.device:
             raise ValueError("q, k, v must share dtype and device")
+    _on_gpu(q, "q")
     return B, Hq, Hkv, Tq, Tk, d
+
+
+def _out(t, name, shape, like, dtype=None):
+    """A caller-supplied output (or None, then allocated by the caller of this helper): it must
+    have the exact shape, the dtype (``like``'s unless given), ``like``'s device and be
+    contiguous, since the library writes every element of that extent."""
+    if t is None:
+        return None
+    dtype = like.dtype if dtype is None else dtype
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != like.device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {like.device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+    return t
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _ws(ws, need, like):
+    """The caller's workspace (a device tensor of at least ``need`` bytes) or a new one."""
+    import torch
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=like.device)
+    if ws.device != like.device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, {need} needed")
+    return ws
 
 
 def workspace_bytes(B, Hq, Hkv, Tq, Tk, d, dtype_code) -> int:
@@ -169,8 +211,10 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
     dv = v.shape[3]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o = q.new_empty((B, Hq, Tq, dv)) if out is None else out
-    L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = _out(out, "out", (B, Hq, Tq, dv), q)
+    o = q.new_empty((B, Hq, Tq, dv)) if o is None else o
+    L = _out(lse, "lse", (B, Hq, Tq), q, torch.float32)
+    L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if L is None else L
     if dv != d:
         st = lib.fa_fwd_dv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), B, Hq, Hkv, Tq, Tk, d, dv,
                            int(bool(causal)), int(window), scale, _dtype_code(q), _stream(q))
@@ -197,14 +241,16 @@ def forward_splitk(q, k, v, causal: bool = False, scale: float | None = None, wi
     """fa_fwd_splitk: the forward split over key slices and merged; returns (o, lse)."""
     import torch
     lib = load_library()
-    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
+    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v, same_dv=True)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
     need = splitk_workspace_bytes(B, Hq, Hkv, Tq, Tk, d, code, nsplit)
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q) if out is None else out
-    L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
-    st = lib.fa_fwd_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), ws.data_ptr(), ws.numel(),
+    ws = _ws(workspace, need, q)
+    o = _out(out, "out", q.shape, q)
+    o = torch.empty_like(q) if o is None else o
+    L = _out(lse, "lse", (B, Hq, Tq), q, torch.float32)
+    L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if L is None else L
+    st = lib.fa_fwd_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), ws.data_ptr(), _nbytes(ws),
                            B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), int(window), scale, code, int(nsplit),
                            _stream(q))
     if st != 0:
@@ -228,6 +274,7 @@ def _varlen_shapes(q, k, v, cu_q, cu_k):
             raise ValueError("cu_seqlens must be contiguous int32 [B + 1] on q's device")
     if cu_q.numel() != cu_k.numel() or cu_q.numel() < 2:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 >= 2 offsets")
+    _on_gpu(q, "q")
     return cu_q.numel() - 1, Hq, Hkv, total_q, total_k, d
 
 
@@ -239,8 +286,10 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
     lib = load_library()
     B, Hq, Hkv, total_q, total_k, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    o = torch.empty_like(q) if out is None else out
-    L = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = _out(out, "out", q.shape, q)
+    o = torch.empty_like(q) if o is None else o
+    L = _out(lse, "lse", (Hq, total_q), q, torch.float32)
+    L = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if L is None else L
     st = lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), cu_seqlens_q.data_ptr(),
                            cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q),
                            int(max_seqlen_k), d, int(bool(causal)), int(window), scale, _dtype_code(q), _stream(q))
@@ -255,13 +304,16 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     import torch
     lib = load_library()
     B, Hq, Hkv, total_q, total_k, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    _out(o, "o", q.shape, q)
+    _out(do, "do", q.shape, q)
+    _out(lse, "lse", (Hq, total_q), q, torch.float32)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
     need = workspace_bytes(B, Hq, Hkv, int(max_seqlen_q), int(max_seqlen_k), d, code)
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws = _ws(workspace, need, q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     st = lib.fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
-                           _ptr(dv), ws.data_ptr(), ws.numel(), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
+                           _ptr(dv), ws.data_ptr(), _nbytes(ws), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
                            B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), d,
                            int(bool(causal)), int(window), scale, code, _stream(q))
     if st != 0:
@@ -284,18 +336,23 @@ def forward_paged(q, k_pages, v_pages, page_table, seqlens_k, causal: bool = Fal
     for t in (q, k_pages, v_pages, page_table, seqlens_k):
         if not t.is_contiguous() or t.device != q.device:
             raise ValueError("tensors must be contiguous on q's device")
+    if k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise ValueError("q, k_pages, v_pages must share a dtype")
+    _on_gpu(q, "q")
     if page_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
         raise ValueError("page_table and seqlens_k must be int32")
     pps = page_table.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
     need = int(lib.fa_fwd_paged_workspace_bytes(B, Hq, Hkv, Tq, pps, page_size, d, code, int(nsplit)))
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q) if out is None else out
-    L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    ws = _ws(workspace, need, q)
+    o = _out(out, "out", q.shape, q)
+    o = torch.empty_like(q) if o is None else o
+    L = _out(lse, "lse", (B, Hq, Tq), q, torch.float32)
+    L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if L is None else L
     st = lib.fa_fwd_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(o), _ptr(L), page_table.data_ptr(),
                           seqlens_k.data_ptr(), B, Hq, Hkv, Tq, pps, page_size, num_pages, d, int(bool(causal)),
-                          int(window), scale, code, ws.data_ptr(), ws.numel(), int(nsplit), _stream(q))
+                          int(window), scale, code, ws.data_ptr(), _nbytes(ws), int(nsplit), _stream(q))
     if st != 0:
         raise FaError(st, "fa_fwd_paged")
     return o, L
@@ -308,6 +365,7 @@ def pack_mask(mask, Tk: int | None = None):
     lib = load_library()
     if mask.dtype not in (torch.bool, torch.uint8) or not mask.is_contiguous() or mask.dim() < 2:
         raise ValueError("mask must be a contiguous bool or uint8 tensor [..., Tq, Tk]")
+    _on_gpu(mask, "mask")
     Tk = mask.shape[-1] if Tk is None else Tk
     if Tk != mask.shape[-1]:
         raise ValueError("Tk does not match the mask")
@@ -343,22 +401,20 @@ def backward_masked(q, k, v, o, lse, do, mask, causal: bool = False, scale: floa
     """fa_bwd_mask: gradients under the boolean mask of forward_masked; returns (dq, dk, dv)."""
     import torch
     lib = load_library()
-    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
-    for t in (o, do):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError("o and do must be like q")
-    if tuple(lse.shape) != (B, Hq, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be float32 [B, Hq, Tq]")
+    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v, same_dv=True)
+    _out(o, "o", q.shape, q)
+    _out(do, "do", q.shape, q)
+    _out(lse, "lse", (B, Hq, Tq), q, torch.float32)
     bits, stride = _mask_bits(lib, mask, q, B, Tq, Tk)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
     need = int(lib.fa_bwd_mask_workspace_bytes(B, Hq, Hkv, Tq, Tk, d, code, stride))
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    ws = _ws(workspace, need, q)
+    dq = torch.empty_like(q) if _out(dq, "dq", q.shape, q) is None else dq
+    dk = torch.empty_like(k) if _out(dk, "dk", k.shape, q) is None else dk
+    dv = torch.empty_like(v) if _out(dv, "dv", v.shape, q) is None else dv
     st = lib.fa_bwd_mask(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
-                         ws.data_ptr(), ws.numel(), _ptr(bits), stride, B, Hq, Hkv, Tq, Tk, d, int(bool(causal)),
+                         ws.data_ptr(), _nbytes(ws), _ptr(bits), stride, B, Hq, Hkv, Tq, Tk, d, int(bool(causal)),
                          scale, code, _stream(q))
     if st != 0:
         raise FaError(st, "fa_bwd_mask")
@@ -375,12 +431,14 @@ def forward_masked(q, k, v, mask, causal: bool = False, scale: float | None = No
     Returns (o like q, lse float32 [B, Hq, Tq])."""
     import torch
     lib = load_library()
-    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
+    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v, same_dv=True)
     bits, stride = _mask_bits(lib, mask, q, B, Tq, Tk)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
-    o = torch.empty_like(q) if out is None else out
-    L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = _out(out, "out", q.shape, q)
+    o = torch.empty_like(q) if o is None else o
+    L = _out(lse, "lse", (B, Hq, Tq), q, torch.float32)
+    L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if L is None else L
     if nsplit == 1:
         st = lib.fa_fwd_mask(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(bits), stride, B, Hq, Hkv, Tq, Tk,
                              d, int(bool(causal)), scale, code, _stream(q))
@@ -388,7 +446,7 @@ def forward_masked(q, k, v, mask, causal: bool = False, scale: float | None = No
             raise FaError(st, "fa_fwd_mask")
         return o, L
     need = int(lib.fa_fwd_mask_splitk_workspace_bytes(B, Hq, Hkv, Tq, Tk, d, code, int(nsplit)))
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws = _ws(workspace, need, q)
     st = lib.fa_fwd_mask_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(bits), stride, ws.data_ptr(),
                                 ws.numel(), B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), scale, code, int(nsplit),
                                 _stream(q))
@@ -405,22 +463,18 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
     lib = load_library()
     B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
     oshape = tuple(q.shape[:3]) + (v.shape[3],)
-    for t in (o, do):
-        if tuple(t.shape) != oshape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError("o and do must be [B, Hq, Tq, dv] like q")
-    if tuple(lse.shape) != (B, Hq, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be float32 [B, Hq, Tq]")
+    _out(o, "o", oshape, q)
+    _out(do, "do", oshape, q)
+    _out(lse, "lse", (B, Hq, Tq), q, torch.float32)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
     need = workspace_bytes(B, Hq, Hkv, Tq, Tk, d, code)
-    ws = workspace
-    if ws is None:
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    ws = _ws(workspace, need, q)
+    dq = torch.empty_like(q) if _out(dq, "dq", q.shape, q) is None else dq
+    dk = torch.empty_like(k) if _out(dk, "dk", k.shape, q) is None else dk
+    dv = torch.empty_like(v) if _out(dv, "dv", v.shape, q) is None else dv
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
-            _ptr(dv), ws.data_ptr(), ws.numel(), B, Hq, Hkv, Tq, Tk, d, int(bool(causal)))
+            _ptr(dv), ws.data_ptr(), _nbytes(ws), B, Hq, Hkv, Tq, Tk, d, int(bool(causal)))
     if v.shape[3] != d:
         st = lib.fa_bwd_dv(*args[:-1], v.shape[3], int(bool(causal)), int(window), scale, code, stages,
                            _stream(q))
@@ -455,6 +509,8 @@ def _autograd_function():
             else:
                 if window:
                     raise ValueError("a boolean mask does not combine with a window")
+                if v.shape[-1] != q.shape[-1]:
+                    raise ValueError("a boolean mask needs v's head dim equal to q's")
                 if mask.dtype != torch.int32:
                     mask = pack_mask(mask.contiguous(), k.shape[2])
                 o, lse = forward_masked(q, k, v, mask, causal, scale)

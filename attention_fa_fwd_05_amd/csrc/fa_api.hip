@@ -3,6 +3,7 @@
 // library allocates nothing and keeps no state.
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "fa.h"
 #include "fa_kernels.h"
@@ -26,6 +27,19 @@ int hip_status(hipError_t e) {
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// The kernels mask invisible scores with -inf before multiplying by the scale
+// and take the row maximum of the unscaled scores, both of which hold only for
+// a positive scale (the pages' 1/sqrt(d)); zero, negative, NaN and infinite
+// scales are rejected.  The test reads the IEEE bits, since the library is
+// built without NaN semantics (-fno-honor-nans) and a floating-point compare
+// could be folded: positive finite values are exactly the bit patterns
+// 0x00000001 .. 0x7f7fffff.
+bool bad_scale(float scale) {
+  uint32_t bits;
+  memcpy(&bits, &scale, sizeof bits);
+  return bits - 1u >= 0x7f7fffffu;
+}
 
 int elem_bytes(int dtype) { return dtype == FA_DTYPE_BF16 ? 2 : 4; }
 
@@ -183,7 +197,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_GQA_RATIO: return "Hq must be a multiple of Hkv";
     case FA_ERR_HEAD_DIM: return "unsupported head dimension (64 or 128; fp32 also 32)";
     case FA_ERR_DTYPE: return "unsupported dtype (FA_DTYPE_F32 or FA_DTYPE_BF16)";
-    case FA_ERR_SCALE: return "scale must be finite";
+    case FA_ERR_SCALE: return "scale must be finite and positive";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_bwd_workspace_bytes";
     case FA_ERR_ALIGNMENT: return "pointers must be 16-byte aligned";
     case FA_ERR_TOO_LARGE: return "a size exceeds the library's index range";
@@ -215,7 +229,7 @@ int fa_fwd_dv(const void* Q, const void* K, const void* V, void* O, float* L, in
   if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, no)) || (st = check_ptr(K, nkv)) ||
       (st = check_ptr(V, nv)) || (st = check_ptr(L, (long long)B * Hq * Tq)))
     return st;
-  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (bad_scale(scale)) return FA_ERR_SCALE;
   if (Tq == 0) return FA_OK;
   fa::FwdArgs a;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L;
@@ -242,7 +256,7 @@ int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L
   if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, nq)) || (st = check_ptr(K, nkv)) ||
       (st = check_ptr(V, nkv)) || (st = check_ptr(L, (long long)Hq * total_q)))
     return st;
-  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (bad_scale(scale)) return FA_ERR_SCALE;
   if (max_seqlen_q == 0 || total_q == 0) return FA_OK;
   fa::FwdArgs a;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L;
@@ -298,7 +312,7 @@ int fa_fwd_mask_splitk(const void* Q, const void* K, const void* V, void* O, flo
     return st;
   const long long rw = fa_mask_row_words(Tk);
   if ((st = check_mask(mask_bits, mask_batch_stride, B, Tq, Tk))) return st;
-  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (bad_scale(scale)) return FA_ERR_SCALE;
   const int ns = mask_splits(B, Hq, Hkv, Tq, Tk, d, dtype, nsplit);
   if (ns > kMaxSplits) return FA_ERR_TOO_LARGE;
   const size_t need = ns == 1 ? 0 : splitk_ws_bytes(B, Hq, Tq, d, ns);
@@ -362,7 +376,7 @@ int fa_fwd_splitk(const void* Q, const void* K, const void* V, void* O, float* L
   if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, nq)) || (st = check_ptr(K, nkv)) ||
       (st = check_ptr(V, nkv)) || (st = check_ptr(L, (long long)B * Hq * Tq)))
     return st;
-  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (bad_scale(scale)) return FA_ERR_SCALE;
   const int ns = fwd_splits(B, Hq, Hkv, Tq, Tk, d, dtype, nsplit);
   if (ns > kMaxSplits) return FA_ERR_TOO_LARGE;
   const size_t need = splitk_ws_bytes(B, Hq, Tq, d, ns);
@@ -412,7 +426,7 @@ int fa_fwd_paged(const void* Q, const void* K_pages, const void* V_pages, void* 
   if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, nq)) || (st = check_ptr(K_pages, npool)) ||
       (st = check_ptr(V_pages, npool)) || (st = check_ptr(L, (long long)B * Hq * Tq)))
     return st;
-  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (bad_scale(scale)) return FA_ERR_SCALE;
   const int ns = nsplit == 1 ? 1 : fwd_splits(B, Hq, Hkv, Tq, (int)tk, d, dtype, nsplit);
   if (ns > kMaxSplits) return FA_ERR_TOO_LARGE;
   const size_t need = ns == 1 ? 0 : splitk_ws_bytes(B, Hq, Tq, d, ns);
@@ -510,7 +524,7 @@ int bwd_core(const void* Q, const void* K, const void* V, const void* O, const f
       (st = check_ptr(dQ, nq)) || (st = check_ptr(K, nk)) || (st = check_ptr(V, nv)) ||
       (st = check_ptr(dK, nk)) || (st = check_ptr(dV, nv)) || (st = check_ptr(L, rows)))
     return st;
-  if (!isfinite(scale)) return FA_ERR_SCALE;
+  if (bad_scale(scale)) return FA_ERR_SCALE;
   if (stages & ~(unsigned)FA_BWD_STAGE_ALL) return FA_ERR_STAGES;
   const WsLayout ws = ws_layout(B, Hq, Tq, d, dtype);
   const bool masked = mask_bstride >= 0 && mask != nullptr && Tq > 0 && Tk > 0;

@@ -61,11 +61,17 @@ def cpu_baseline(w, inp, budget_s: float):
     """Time the fp64 oracle on whole (batch, K/V head) groups until the budget is used."""
     import numpy as np
     import oracle.attention as oa
+    blas, threads = "unknown", None
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if pools:
+            threads = max(p.get("num_threads", 1) for p in pools)
+            blas = ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in pools}))
     except Exception:
-        cores = os.cpu_count() or 1
+        pass
+    host_cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cores = threads if threads else host_cores
     groups = [(b, g) for b in range(w.B) for g in range(w.Hkv)]
     rng = np.random.default_rng(0)
     rng.shuffle(groups)
@@ -83,7 +89,21 @@ def cpu_baseline(w, inp, budget_s: float):
         f = (4.0 + 10.0) * w.G * w.Tq * w.Tk * w.d * (0.5 if w.causal else 1.0) * done
     return {"value": f / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done} of {len(groups)} (batch, K/V head) groups ({done * w.G} query heads), "
-                      f"dense fp64 forward+backward, {elapsed:.1f} s"}
+                      f"dense fp64 forward+backward, {elapsed:.1f} s",
+            "host_cores": int(host_cores), "cpu_model": cpu_model(), "blas": blas}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def decode_bench(args, fa, accounting, wl):

@@ -36,7 +36,8 @@
  *    (aligned at the end; j <= i when Tq == Tk).  Keys beyond Tk do not exist.
  *  - A query row that sees no key (Tk == 0, or causal with i + Tk - Tq < 0)
  *    gets O = 0, L = -inf and dQ = 0, and adds nothing to dK or dV.
- *  - scale multiplies Q K^T; it must be finite (callers pass 1/sqrt(d)).
+ *  - scale multiplies Q K^T; it must be finite and positive (callers pass
+ *    1/sqrt(d), the value of the tiling article's implementation).
  *  - Pointers are device pointers (or host-coherent memory the GPU can reach),
  *    16-byte aligned, and must not alias one another.  A pointer may be NULL
  *    only when the tensor it names has no elements.
@@ -66,7 +67,7 @@ typedef enum {
   FA_ERR_GQA_RATIO = 3,  /* Hq is not a multiple of Hkv */
   FA_ERR_HEAD_DIM = 4,   /* d is not 64 or 128 (or 32 in fp32) */
   FA_ERR_DTYPE = 5,      /* dtype is not an fa_dtype value */
-  FA_ERR_SCALE = 6,      /* scale is NaN or infinite */
+  FA_ERR_SCALE = 6,      /* scale is NaN, infinite, zero or negative */
   FA_ERR_WORKSPACE = 7,  /* workspace missing or smaller than fa_bwd_workspace_bytes */
   FA_ERR_ALIGNMENT = 8,  /* a pointer is not 16-byte aligned */
   FA_ERR_TOO_LARGE = 9,  /* a size exceeds the library's index range */

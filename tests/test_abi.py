@@ -213,3 +213,78 @@ def test_head_dim_32_is_fp32_only(lib):
     # d = 32 passes validation in fp32 (then fails on the NULL output) and is rejected in bf16
     assert lib.fa_fwd(FAKE, FAKE, FAKE, None, FAKE, 1, 2, 1, 16, 16, 32, 0, 0.125, 0, None) == 1
     assert lib.fa_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 16, 16, 32, 0, 0.125, 1, None) == 4
+
+
+# Every entry point that takes a scale, called with arguments that pass every
+# other check (fake aligned pointers, room in the workspace), so that the scale
+# is what fails: zero and negative scales are rejected like NaN, because the
+# kernels mask scores with -inf before scaling and take the row maximum of the
+# unscaled scores, which hold only for a positive scale.
+def _scale_calls(lib, s):
+    W = 1 << 30
+    return {
+        "fa_fwd": lambda: lib.fa_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 16, 16, 64, 1, s, 1, None),
+        "fa_fwd_window": lambda: lib.fa_fwd_window(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 16, 16, 64, 1, 8, s, 1,
+                                                   None),
+        "fa_fwd_dv": lambda: lib.fa_fwd_dv(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 16, 16, 128, 64, 1, 0, s, 1, None),
+        "fa_fwd_splitk": lambda: lib.fa_fwd_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, W, 1, 2, 1, 16, 16, 64, 1, 0,
+                                                   s, 1, 2, None),
+        "fa_fwd_varlen": lambda: lib.fa_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 1, 32, 32, 16, 16,
+                                                   64, 1, 0, s, 1, None),
+        "fa_fwd_paged": lambda: lib.fa_fwd_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 1, 16, 4, 128, 8,
+                                                 64, 1, 0, s, 1, None, 0, 1, None),
+        "fa_fwd_mask": lambda: lib.fa_fwd_mask(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 4, 2, 16, 300, 64, 1, s, 1,
+                                               None),
+        "fa_fwd_mask_splitk": lambda: lib.fa_fwd_mask_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, W, 2, 4, 2,
+                                                             16, 300, 64, 1, s, 1, 2, None),
+        "fa_bwd": lambda: lib.fa_bwd(*(FAKE,) * 10, W, 1, 2, 1, 16, 16, 64, 1, s, 1, None),
+        "fa_bwd_stages": lambda: lib.fa_bwd_stages(*(FAKE,) * 10, W, 1, 2, 1, 16, 16, 64, 1, s, 1, 7, None),
+        "fa_bwd_window": lambda: lib.fa_bwd_window(*(FAKE,) * 10, W, 1, 2, 1, 16, 16, 64, 1, 8, s, 1, 7, None),
+        "fa_bwd_dv": lambda: lib.fa_bwd_dv(*(FAKE,) * 10, W, 1, 2, 1, 16, 16, 128, 64, 1, 0, s, 1, 7, None),
+        "fa_bwd_varlen": lambda: lib.fa_bwd_varlen(*(FAKE,) * 10, W, FAKE, FAKE, 2, 2, 1, 32, 32, 16, 16, 64, 1, 0,
+                                                   s, 1, None),
+        "fa_bwd_mask": lambda: lib.fa_bwd_mask(*(FAKE,) * 10, W, FAKE, 0, 2, 4, 2, 16, 300, 64, 1, s, 1, None),
+    }
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0, -0.1, -math.inf, math.inf, math.nan])
+def test_every_entry_point_rejects_a_non_positive_or_non_finite_scale(lib, scale):
+    calls = _scale_calls(lib, scale)
+    got = {name: call() for name, call in calls.items()}
+    assert got == {name: 6 for name in calls}
+
+
+def test_scale_table_covers_every_entry_point_that_takes_a_scale():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    with_scale = {m.group(1) for m in re.finditer(r"\b(fa_[a-z_0-9]+)\s*\(([^;]*?)\);", text, flags=re.S)
+                  if re.search(r"\bfloat\s+scale\b", m.group(2))}
+    assert with_scale == set(_scale_calls(None, 0.125))
+
+
+_NO_DEVICE_SCRIPT = r"""
+import ctypes, sys
+lib = ctypes.CDLL(sys.argv[1])
+vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+lib.fa_fwd.argtypes = [vp] * 5 + [i] * 7 + [f, i, vp]
+lib.fa_hip_error_string.restype = ctypes.c_char_p
+F = 1 << 20
+print(lib.fa_fwd(F, F, F, F, F, 1, 2, 1, 16, 16, 64, 0, 0.125, 1, None))
+print(lib.fa_hip_error_string().decode())
+"""
+
+
+def test_a_launch_without_a_device_returns_the_hip_status():
+    """With valid arguments and no HIP device the launch itself fails: the call returns
+    FA_ERR_HIP and the HIP text names the missing device.  The arguments are fake device
+    pointers, so this must never run where a GPU is visible (skipped there)."""
+    import subprocess
+    import sys
+    from conftest import gpu_available
+    if gpu_available() or os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU is visible: the fake pointers of this test must not reach it")
+    r = subprocess.run([sys.executable, "-c", _NO_DEVICE_SCRIPT, fa.LIB_PATH], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    status, text = r.stdout.strip().splitlines()[-2:]
+    assert int(status) == 10
+    assert "device" in text.lower()
