@@ -299,7 +299,8 @@ def forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_s
 
 
 def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
-                    causal: bool = False, scale: float | None = None, window: int = 0, workspace=None):
+                    causal: bool = False, scale: float | None = None, window: int = 0, workspace=None,
+                    dq=None, dk=None, dv=None):
     """fa_bwd_varlen: returns (dq, dk, dv) like q, k, v (packed head-major)."""
     import torch
     lib = load_library()
@@ -311,7 +312,9 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     code = _dtype_code(q)
     need = workspace_bytes(B, Hq, Hkv, int(max_seqlen_q), int(max_seqlen_k), d, code)
     ws = _ws(workspace, need, q)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq = torch.empty_like(q) if _out(dq, "dq", q.shape, q) is None else dq
+    dk = torch.empty_like(k) if _out(dk, "dk", k.shape, q) is None else dk
+    dv = torch.empty_like(v) if _out(dv, "dv", v.shape, q) is None else dv
     st = lib.fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
                            _ptr(dv), ws.data_ptr(), _nbytes(ws), cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(),
                            B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), d,
@@ -358,7 +361,7 @@ def forward_paged(q, k_pages, v_pages, page_table, seqlens_k, causal: bool = Fal
     return o, L
 
 
-def pack_mask(mask, Tk: int | None = None):
+def pack_mask(mask, Tk: int | None = None, out=None):
     """fa_mask_pack: a boolean (or uint8, nonzero = visible) mask [..., Tq, Tk] on the GPU to the
     library's bit layout, int32 [..., Tq, fa_mask_row_words(Tk)] (the same leading dims)."""
     import torch
@@ -373,7 +376,9 @@ def pack_mask(mask, Tk: int | None = None):
     if rw < 0:
         raise ValueError(f"Tk {Tk} out of range")
     rows = mask.numel() // Tk if Tk > 0 else math.prod(mask.shape[:-1])
-    bits = torch.empty(tuple(mask.shape[:-1]) + (rw,), dtype=torch.int32, device=mask.device)
+    shape = tuple(mask.shape[:-1]) + (rw,)
+    bits = _out(out, "out", shape, mask, torch.int32)
+    bits = torch.empty(shape, dtype=torch.int32, device=mask.device) if bits is None else bits
     st = lib.fa_mask_pack(_ptr(mask), _ptr(bits), rows, Tk, _stream(mask))
     if st != 0:
         raise FaError(st, "fa_mask_pack")

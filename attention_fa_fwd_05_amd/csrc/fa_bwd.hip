@@ -839,6 +839,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   const long long kblocks = (long long)((a.Tk + 127) / 128) * a.B * a.Hkv;
   constexpr int NW = dq_waves<T, D>();
   const long long qblocks = (long long)((a.Tq + 32 * NW - 1) / (32 * NW)) * a.B * a.Hq;
+  // bf16: the dK/dV pass on wave pairs (fa_dkdv.hip).
+  constexpr bool kPair = sizeof(T) == 2;
   if constexpr (DV == D) {
     // A boolean mask: its key-major copy, then the masked passes.
     if (a.mask != nullptr) {
@@ -846,7 +848,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t stream) {
         const long long entries = a.mask_bstride != 0 ? a.B : 1;
         const long long words = entries * a.Tk * a.mask_t_row_words;
         hipError_t e = launch(mask_transpose_kernel, (words + 255) / 256, stream, a, entries);
-        if (e == hipSuccess) e = launch(dkdv_kernel<T, D, CAUSAL, false, D, true>, kblocks, stream, a);
+        if (e == hipSuccess) {
+          if constexpr (kPair) e = launch_dkdv_pair(a, D, DV, CAUSAL, stream);
+          else e = launch(dkdv_kernel<T, D, CAUSAL, false, D, true>, kblocks, stream, a);
+        }
         if (e != hipSuccess) return e;
       }
       if ((stages & kStageDq) && qblocks > 0) {
@@ -857,8 +862,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t stream) {
     }
   }
   if ((stages & kStageDkDv) && kblocks > 0) {
-    hipError_t e = a.window > 0 ? launch(dkdv_kernel<T, D, CAUSAL, true, DV>, kblocks, stream, a)
-                                : launch(dkdv_kernel<T, D, CAUSAL, false, DV>, kblocks, stream, a);
+    hipError_t e;
+    if constexpr (kPair) e = launch_dkdv_pair(a, D, DV, CAUSAL, stream);
+    else e = a.window > 0 ? launch(dkdv_kernel<T, D, CAUSAL, true, DV>, kblocks, stream, a)
+                          : launch(dkdv_kernel<T, D, CAUSAL, false, DV>, kblocks, stream, a);
     if (e != hipSuccess) return e;
   }
   if ((stages & kStageDq) && qblocks > 0) {

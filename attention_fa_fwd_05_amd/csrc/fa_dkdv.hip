@@ -1,0 +1,336 @@
+// dK / dV pass of the backward for bf16, with the work of each key group split
+// between two waves that share a SIMD ("What Ordinary Autograd Saves",
+// section "Why this is FlashAttention's second idea": rebuild S and P from
+// Q, K, V, O and L instead of storing them; "Backward Pass Implementation",
+// section "The Recomputation Strategy").
+//
+// One workgroup per (128-key block, b, K/V head), 8 waves.  Waves w and w + 4
+// own the same 32 keys and run on the same SIMD:
+//  * the P-wave (w < 4) holds K and accumulates dV: per 64-query block it
+//    forms S = Q K^T, P = exp2(S c - L2) (0 where the pair is hidden), writes
+//    P (bf16) to LDS and adds dV^T += dO^T P;
+//  * the dS-wave (w >= 4) holds V and accumulates dK: per block it forms
+//    dP - D = dO V^T seeded with -D, and one block later, once the P-wave's
+//    P of that block is in LDS, dS = P (dP - D) and dK^T += Q^T dS.
+// Each wave then needs about half the registers of a wave doing all four
+// products, so two fit on a SIMD and one's vector work (exponentials, dS)
+// runs while the other keeps the matrix unit busy.  The dK and dV sums run
+// over every query block of every query head of the group (the GQA group
+// sum, "The Autograd Memory Trap", section "Tracing the Autograd Graph").
+//
+// Query blocks: from the last one down, heads innermost, so the key blocks of
+// a group (all on one XCD) step through the same Q / dO blocks together and
+// share them in L2.  Q / dO / L2 / -D blocks sit in three LDS buffers: block
+// i (read by both waves), block i - 1 (the dS-wave's Q^T for dK) and block
+// i + 1 (loading).  P goes through two LDS buffers.  One barrier per block.
+#include "fa_common.h"
+#include "fa_kernels.h"
+
+namespace fa {
+namespace {
+
+// Key-block work of the dK / dV pass: logical order = group, then key block
+// (heaviest first when causal: low key blocks see the most query blocks).
+struct KWork2 {
+  int b, hk, kb;
+};
+__device__ inline KWork2 kblock_work2(const BwdArgs& a, int nkb) {
+  const int logical = xcd_logical_block();
+  KWork2 w;
+  w.kb = logical % nkb;
+  const int grp = logical / nkb;
+  w.b = grp / a.Hkv;
+  w.hk = grp % a.Hkv;
+  return w;
+}
+
+}  // namespace
+
+// D: head dim of Q, K, dK; DV: of V, dO, dV.
+template <int D, int DV, bool CAUSAL, bool WIN, bool MASK>
+__global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
+  using T = bf16;
+  using M = MM<bf16>;
+  typedef bf16x8 Op;
+  constexpr int BK = 128;                           // keys per workgroup, 32 per wave pair
+  constexpr int BQ = 64;                            // queries per block: two 32-query tiles
+  constexpr int NTHR = 512;
+  constexpr int NSD = D / 16;                       // steps of S = Q K^T (contraction over d)
+  constexpr int NSDV = DV / 16;                     // steps of dP = dO V^T
+  constexpr int NSQ = BQ / 16;                      // steps over a query block (dV, dK)
+  constexpr int NDT = D / 32;                       // 32-wide dK tiles
+  constexpr int NDTV = DV / 32;                     // 32-wide dV tiles
+  constexpr int NB = 3;
+  static_assert(NSQ == 4, "P in LDS is 4 operands per lane");
+  // Tiles 4096-byte aligned (XorFetch): 64 rows of 64 or 128 bf16 are 8 or 16 KiB.
+  __shared__ __attribute__((aligned(4096))) T sQ[NB][BQ * D];
+  __shared__ __attribute__((aligned(4096))) T sdO[NB][BQ * DV];
+  __shared__ __attribute__((aligned(16))) bf16x8 sP[2][4][NSQ][64];   // [buffer][key group][step][lane]
+  __shared__ __attribute__((aligned(16))) float sL[NB][64];
+  __shared__ __attribute__((aligned(16))) float sD[NB][64];          // -D
+  __shared__ __attribute__((aligned(16))) uint32_t sM[MASK ? NB * 4 * 64 : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = w & 3;                             // key group: keys kw .. kw + 31
+  const bool pwave = w < 4;
+  const int h = lane >> 5, n = lane & 31;
+  const int nkb = (a.Tk + BK - 1) / BK;
+  const KWork2 wk = kblock_work2(a, nkb);
+  const int G = a.Hq / a.Hkv;
+  const int k0 = wk.kb * BK, kw = k0 + 32 * kg, mykey = kw + n;
+  const SeqView sq = seq_view(a, wk.b);
+  const int Tq = sq.Tq, Tk = sq.Tk;
+  if (k0 >= Tk) return;                             // uniform: before any barrier
+  const size_t krow0 = sq.k_row(wk.hk);
+  const int off = Tk - Tq;
+  const float c = a.scale_log2;
+  const bool key_ok = mykey < Tk;
+  const bool ragged = k0 + BK > Tk;
+
+  // Work list: (query block, head of the group) pairs, query blocks qb1 down
+  // to qb0 (those that see some key of this block), heads innermost.
+  const int nqb = (Tq + BQ - 1) / BQ;
+  const int W = WIN ? a.window : 0;
+  const int qb0 = CAUSAL ? min(nqb, max(0, k0 - off) / BQ) : 0;
+  const int qlast = W > 0 ? min(Tq - 1, k0 + BK - 1 - off + W - 1) : Tq - 1;
+  const int qb1 = qlast < 0 ? -1 : qlast / BQ;
+  const int total = G * max(0, qb1 - qb0 + 1);
+  auto item_q0 = [&](int it) { return (qb1 - it / G) * BQ; };
+  auto item_bh = [&](int it) { return wk.b * a.Hq + wk.hk * G + it % G; };
+  auto item_qrow = [&](int it) { return sq.q_row(wk.hk * G + it % G); };
+
+  // Loads of one block into buffer buf: Q and dO rows (clamped at Tq - 1; the
+  // padding rows have L2 = +inf and -D = 0, so they add nothing), L2 and -D
+  // (rows padded to 64 per head in the workspace), and for a boolean mask
+  // each P-wave's bits of its keys (key-major copy, two words per key).
+  auto issue = [&](int it, int buf) {
+    const int q0 = item_q0(it);
+    const size_t qr = item_qrow(it);
+    dma_rows<T, D, BQ, NTHR>(sQ[buf], reinterpret_cast<const T*>(a.Q) + qr * D, q0, Tq);
+    dma_rows<T, DV, BQ, NTHR>(sdO[buf], reinterpret_cast<const T*>(a.dO) + qr * DV, q0, Tq);
+    const size_t wrow = (size_t)item_bh(it) * a.Tqp + q0;
+    if (w == 0) dma_floats64(sL[buf], a.Lg + wrow);
+    if (w == 1) dma_floats64(sD[buf], a.Dvec + wrow);
+    if constexpr (MASK) {
+      if (pwave)
+        dma4(a.mask_t + (size_t)wk.b * a.mask_t_bstride +
+                 (size_t)min(kw + (lane >> 1), Tk - 1) * a.mask_t_row_words + q0 / 32 + (lane & 1),
+             lds_addr(sM + (buf * 4 + kg) * 64));
+    }
+  };
+
+  XorFetch<D> xf;
+  xf.init(lane);
+  XorFetch<DV> xfv;
+  xfv.init(lane);
+
+  if (total > 0) issue(0, 0);
+
+  if (pwave) {
+    // ------------------------------------------------------------ P-wave
+    Op kop[NSD];
+    {
+      const T* Kp = reinterpret_cast<const T*>(a.K) + (krow0 + (key_ok ? mykey : 0)) * D + h * (D / 2);
+#pragma unroll
+      for (int s = 0; s < NSD; ++s) {
+        kop[s] = M::ld(Kp + s * 8);
+        if (!key_ok) kop[s] = Op{};
+        asm volatile("" : "+a"(kop[s]));
+      }
+    }
+    f32x16 dv[NDTV];
+#pragma unroll
+    for (int t = 0; t < NDTV; ++t) dv[t] = f32x16{};
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int it = 0; it <= total; ++it) {
+      const int cur = it % NB;
+      if (it + 1 < total) issue(it + 1, (it + 1) % NB);
+      if (it < total) {
+        const int q0 = item_q0(it);
+        const uint32_t qb = lds_addr(sQ[cur]), ob = lds_addr(sdO[cur]);
+        // S = Q K^T for the two 32-query tiles (lane = key).
+        f32x16 sacc[2] = {f32x16{}, f32x16{}};
+        wave_prio<1>();
+#pragma unroll
+        for (int s = 0; s < NSD; ++s) {
+          sacc[0] = M::mma(XorFetch<D>::nat(qb + xf.nat0, 0, s), kop[s], sacc[0]);
+          sacc[1] = M::mma(XorFetch<D>::nat(qb + xf.nat0, 1, s), kop[s], sacc[1]);
+        }
+        sched_interleave<2 * NSD, 4>();
+        wave_prio<0>();
+        // P = exp2(S c - L2); register i of tile t holds query
+        // q0 + 32 t + 8 (i / 4) + 4 h + i % 4.  A boolean mask's hidden pairs
+        // get L2 = +inf (bit 4 h + 8 g + e of the tile's word for register
+        // 4 g + e).
+        Op pop[NSQ];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float p[16];
+          uint32_t mw = 0;
+          if constexpr (MASK) mw = sM[(cur * 4 + kg) * 64 + 2 * n + t] >> (4 * h);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[cur][32 * t + 8 * g + 4 * h]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float l = l4[e];
+              if constexpr (MASK) {
+                const int keep = (int)(mw << (31 - (8 * g + e))) >> 31;
+                l = __int_as_float((__float_as_int(l) & keep) | (int)(0x7f800000u & ~(uint32_t)keep));
+              }
+              p[4 * g + e] = fast_exp2(__builtin_fmaf(sacc[t][4 * g + e], c, -l));
+            }
+          }
+          // Causal diagonal, window edge and ragged key end: only on the
+          // blocks that have them (a uniform test), clear hidden pairs.
+          if (ragged || (CAUSAL && k0 + BK - 1 > q0 + 32 * t + off) ||
+              (W > 0 && q0 + 32 * t + 31 > k0 - off + W - 1)) {
+            const int thr = !key_ok ? INT_MAX : (CAUSAL ? mykey - off - q0 - 32 * t - 4 * h : INT_MIN);
+            const int thr_hi = W > 0 ? mykey - off + W - 1 - q0 - 32 * t - 4 * h : INT_MAX;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (8 * (i >> 2) + (i & 3) < thr || 8 * (i >> 2) + (i & 3) > thr_hi) p[i] = 0.f;
+          }
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            u32x4 wv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              wv[e] = __builtin_bit_cast(uint32_t, bf16x2{(bf16)p[8 * j + 2 * e], (bf16)p[8 * j + 2 * e + 1]});
+            pop[2 * t + j] = __builtin_bit_cast(bf16x8, wv);
+          }
+        }
+        // P to LDS for the dS-wave of this key group.
+#pragma unroll
+        for (int s = 0; s < NSQ; ++s) sP[it & 1][kg][s][lane] = pop[s];
+        // dV^T += dO^T P (dO^T by transposed reads of the dO tile).
+        wave_prio<1>();
+#pragma unroll
+        for (int t = 0; t < NDTV; ++t)
+#pragma unroll
+          for (int s = 0; s < NSQ; ++s) dv[t] = M::mma(XorFetch<DV>::tr(ob + xfv.tr0, t, s), pop[s], dv[t]);
+        sched_interleave<NDTV * NSQ, 4, 2>();
+        wave_prio<0>();
+      }
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+    if (key_ok) {
+      T* dVr = reinterpret_cast<T*>(a.dV) + (krow0 + mykey) * DV;
+#pragma unroll
+      for (int t = 0; t < NDTV; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store4(dVr + t * 32 + 8 * g + 4 * h, dv[t][4 * g], dv[t][4 * g + 1], dv[t][4 * g + 2], dv[t][4 * g + 3]);
+    }
+  } else {
+    // ------------------------------------------------------------ dS-wave
+    Op vop[NSDV];
+    {
+      const T* Vp = reinterpret_cast<const T*>(a.V) + (krow0 + (key_ok ? mykey : 0)) * DV + h * (DV / 2);
+#pragma unroll
+      for (int s = 0; s < NSDV; ++s) {
+        vop[s] = M::ld(Vp + s * 8);
+        if (!key_ok) vop[s] = Op{};
+        asm volatile("" : "+a"(vop[s]));
+      }
+    }
+    f32x16 dk[NDT];
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) dk[t] = f32x16{};
+    f32x16 dpacc[2];                                // dP - D of the previous block (lane = key)
+    wait_vmcnt<0>();
+    __syncthreads();
+    for (int it = 0; it <= total; ++it) {
+      const int cur = it % NB;
+      if (it + 1 < total) issue(it + 1, (it + 1) % NB);
+      if (it > 0) {
+        // dS = P (dP - D) of the previous block, then dK^T += Q^T dS.
+        const int prv = (it + NB - 1) % NB;
+        const uint32_t qb = lds_addr(sQ[prv]);
+        Op dsop[NSQ];
+#pragma unroll
+        for (int s = 0; s < NSQ; ++s) {
+          const u32x4 pw = __builtin_bit_cast(u32x4, sP[(it - 1) & 1][kg][s][lane]);
+          const f32x16& dp = dpacc[s >> 1];
+          u32x4 dw;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * (s & 1) + 2 * e;
+            const float p0 = __uint_as_float(pw[e] << 16), p1 = __uint_as_float(pw[e] & 0xffff0000u);
+            dw[e] = __builtin_bit_cast(uint32_t, bf16x2{(bf16)(p0 * dp[r]), (bf16)(p1 * dp[r + 1])});
+          }
+          dsop[s] = __builtin_bit_cast(bf16x8, dw);
+        }
+        wave_prio<1>();
+#pragma unroll
+        for (int t = 0; t < NDT; ++t)
+#pragma unroll
+          for (int s = 0; s < NSQ; ++s) dk[t] = M::mma(XorFetch<D>::tr(qb + xf.tr0, t, s), dsop[s], dk[t]);
+        sched_interleave<NDT * NSQ, 4, 2>();
+        wave_prio<0>();
+      }
+      if (it < total) {
+        // dP - D = dO V^T on a seed of -D (register i of tile t: query
+        // 32 t + 8 (i / 4) + 4 h + i % 4).
+        const uint32_t ob = lds_addr(sdO[cur]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&sD[cur][32 * t + 8 * g + 4 * h]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dpacc[t][4 * g + e] = v[e];
+          }
+        wave_prio<1>();
+#pragma unroll
+        for (int s = 0; s < NSDV; ++s) {
+          dpacc[0] = M::mma(XorFetch<DV>::nat(ob + xfv.nat0, 0, s), vop[s], dpacc[0]);
+          dpacc[1] = M::mma(XorFetch<DV>::nat(ob + xfv.nat0, 1, s), vop[s], dpacc[1]);
+        }
+        sched_interleave<2 * NSDV, 4>();
+        wave_prio<0>();
+      }
+      wait_vmcnt<0>();
+      __syncthreads();
+    }
+    if (key_ok) {
+      T* dKr = reinterpret_cast<T*>(a.dK) + (krow0 + mykey) * D;
+      const float sc = a.scale;
+#pragma unroll
+      for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          store4(dKr + t * 32 + 8 * g + 4 * h, dk[t][4 * g] * sc, dk[t][4 * g + 1] * sc, dk[t][4 * g + 2] * sc,
+                 dk[t][4 * g + 3] * sc);
+    }
+  }
+}
+
+template <int D, int DV, bool CAUSAL>
+hipError_t launch_dkdv_pair_t(const BwdArgs& a, long long blocks, hipStream_t stream) {
+  if (a.mask != nullptr) {
+    if constexpr (D == DV) return launch<512>(dkdv_pair_kernel<D, DV, CAUSAL, false, true>, blocks, stream, a);
+    return hipErrorInvalidValue;
+  }
+  if (a.window > 0) return launch<512>(dkdv_pair_kernel<D, DV, CAUSAL, true, false>, blocks, stream, a);
+  return launch<512>(dkdv_pair_kernel<D, DV, CAUSAL, false, false>, blocks, stream, a);
+}
+
+hipError_t launch_dkdv_pair(const BwdArgs& a, int d, int dv, int causal, hipStream_t stream) {
+  const long long blocks = (long long)((a.Tk + 127) / 128) * a.B * a.Hkv;
+  if (blocks <= 0) return hipSuccess;
+#define FA_DKDV_CASE(DD, DDV)                                                                        \
+  if (d == DD && dv == DDV)                                                                          \
+    return causal ? launch_dkdv_pair_t<DD, DDV, true>(a, blocks, stream)                             \
+                  : launch_dkdv_pair_t<DD, DDV, false>(a, blocks, stream);
+  FA_DKDV_CASE(128, 128)
+  FA_DKDV_CASE(64, 64)
+  FA_DKDV_CASE(128, 64)
+  FA_DKDV_CASE(64, 128)
+#undef FA_DKDV_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

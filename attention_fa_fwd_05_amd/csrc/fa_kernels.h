@@ -162,5 +162,8 @@ int fwd_decode_block_keys();
 constexpr unsigned kStagePre = 1u, kStageDkDv = 2u, kStageDq = 4u;
 hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int d, int causal, unsigned stages,
                       hipStream_t stream, int dv = -1);
+// The bf16 dK/dV pass on wave pairs (fa_dkdv.hip); a boolean mask needs its
+// key-major copy in BwdArgs::mask_t first.
+hipError_t launch_dkdv_pair(const BwdArgs& a, int d, int dv, int causal, hipStream_t stream);
 
 }  // namespace fa

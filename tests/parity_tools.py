@@ -10,9 +10,12 @@ Two measures per output tensor X against the oracle X*:
   (over a 131072-row group a completely wrong row moves the whole-tensor error
   by only about 0.004): for every row i (the last axis is the row's feature
   axis; L is one value per row) ||x_i - x*_i|| <= ROW_TOL * max(||x*_i||, f),
-  with the floor f = 0.1 * RMS_i ||x*_i|| so that rows whose exact value
-  nearly cancels are measured against the tensor's typical row size.  For L
-  the row error is |L_i - L*_i| against max(1, |L*_i|).
+  with the floor f = RMS_i ||x*_i||, so that rows whose exact value nearly
+  cancels are measured against the tensor's typical row size: a causal row
+  that sees one key has dQ = 0 exactly, while the bf16 path leaves a residue of
+  the order of the rounding of O (D is formed from the stored O).  A wrong row
+  of typical size still shows an error near 1.  For L the row error is
+  |L_i - L*_i| against max(1, |L*_i|).
 """
 
 import numpy as np
@@ -20,7 +23,10 @@ import numpy as np
 import oracle.attention as oa
 
 TOL = {"fp32": 1e-4, "bf16": 2e-2}
-ROW_TOL = {"fp32": 1e-3, "bf16": 5e-2}
+# A row may be off by 10% of the larger of its own size and the typical row size in bf16
+# (the worst bf16 rows are the early causal rows, whose exact dQ nearly cancels: about 0.06 at
+# T = 4096), 0.1% in fp32; a wrong row shows an error near 1.
+ROW_TOL = {"fp32": 1e-3, "bf16": 1e-1}
 
 
 def log(msg):
@@ -43,7 +49,7 @@ def row_error(x, ref, is_L=False):
     xr = x.reshape(-1, x.shape[-1])
     rr = ref.reshape(-1, ref.shape[-1])
     rn = np.linalg.norm(rr, axis=1)
-    floor = 0.1 * np.sqrt(np.mean(rn * rn))
+    floor = np.sqrt(np.mean(rn * rn))
     if floor == 0.0:
         return float(np.abs(xr).max()) if xr.size else 0.0
     return float((np.linalg.norm(xr - rr, axis=1) / np.maximum(rn, floor)).max())

@@ -249,7 +249,7 @@ def test_outputs_are_bitwise_reproducible(fa):
                            *fa.backward(q, k, v, *fa.forward(q, k, v, True, window=150), do, True, window=150)),
         "mask": lambda: (*fa.forward_masked(q, k, v, mask, True),
                          *fa.backward_masked(q, k, v, *fa.forward_masked(q, k, v, mask, True), do, mask, True)),
-        "split": lambda: fa.forward_splitk(q[:, :, :32], k, v, True, nsplit=4),
+        "split": lambda: fa.forward_splitk(q[:, :, :32].contiguous(), k, v, True, nsplit=4),
         "mask_split": lambda: fa.forward_masked(q, k, v, mask, True, nsplit=3),
     }
     for name, run in runs.items():
@@ -283,9 +283,14 @@ def test_workspace_too_small_is_rejected(fa):
     k = torch.randn(1, 2, 64, 128, device="cuda").to(torch.bfloat16)
     o, lse = fa.forward(q, k, k, False)
     ws = torch.empty(16, dtype=torch.uint8, device="cuda")
-    with pytest.raises(fa.FaError) as ei:
-        fa.backward(q, k, k, o, lse, torch.randn_like(q), False, workspace=ws)
-    assert ei.value.status == 7
+    do = torch.randn_like(q)
+    with pytest.raises(ValueError, match="needed"):          # the binding refuses first
+        fa.backward(q, k, k, o, lse, do, False, workspace=ws)
+    dq, dk = torch.empty_like(q), torch.empty_like(k)        # the library refuses on its own
+    st = fa.load_library().fa_bwd(q.data_ptr(), k.data_ptr(), k.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dk.data_ptr(), ws.data_ptr(), 16,
+                                  1, 2, 2, 64, 64, 128, 0, 128 ** -0.5, fa.FA_DTYPE_BF16, None)
+    assert st == 7
 
 
 def test_autograd_wrapper_retains_linear_state(fa):

@@ -86,6 +86,12 @@ def test_splitk_workspace_rules(fa):
     need = fa.splitk_workspace_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, fa.FA_DTYPE_BF16, 4)
     assert need >= 4 * w.B * w.Hq * w.Tq * (w.d + 1) * 4      # 4 slices of fp32 O and L
     small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
-    with pytest.raises(fa.FaError, match="WORKSPACE"):
+    with pytest.raises(ValueError, match="needed"):          # the binding refuses first
         fa.forward_splitk(q, k, v, True, w.scale, nsplit=4, workspace=small)
+    o = torch.empty_like(q)                                  # the library refuses on its own
+    lse = torch.empty(w.B, w.Hq, w.Tq, device="cuda")
+    st = fa.load_library().fa_fwd_splitk(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                         small.data_ptr(), need - 256, w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, 1, 0,
+                                         w.scale, fa.FA_DTYPE_BF16, 4, None)
+    assert st == 7
     assert fa.splitk_workspace_bytes(w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, fa.FA_DTYPE_BF16, 5000) == 0
