@@ -22,6 +22,7 @@ STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL_PTR", 2: "FA_ERR_BAD_SHAPE", 3: "FA_ERR_GQA_RATIO",
     4: "FA_ERR_HEAD_DIM", 5: "FA_ERR_DTYPE", 6: "FA_ERR_SCALE", 7: "FA_ERR_WORKSPACE",
     8: "FA_ERR_ALIGNMENT", 9: "FA_ERR_TOO_LARGE", 10: "FA_ERR_HIP", 11: "FA_ERR_STAGES",
+    12: "FA_ERR_SCRATCH",
 }
 STAGE_PRE, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
 EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_window", "fa_bwd_window", "fa_fwd_dv", "fa_bwd_dv",
@@ -30,6 +31,7 @@ EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_window", "fa_bwd_window"
            "fa_fwd_paged_workspace_bytes", "fa_bwd_workspace_bytes",
            "fa_mask_row_words", "fa_mask_pack", "fa_fwd_mask", "fa_bwd_mask", "fa_bwd_mask_workspace_bytes",
            "fa_fwd_mask_splitk", "fa_fwd_mask_splitk_workspace_bytes",
+           "fa_bwd_noalloc", "fa_bwd_noalloc_scratch_bytes",
            "fa_status_string", "fa_hip_error_string", "fa_abi_version"]
 
 _lib = None
@@ -105,6 +107,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_mask.restype = i
     lib.fa_bwd_mask_workspace_bytes.argtypes = [i, i, i, i, i, i, i, ll]
     lib.fa_bwd_mask_workspace_bytes.restype = sz
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_noalloc.restype = i
+    lib.fa_bwd_noalloc_scratch_bytes.argtypes = []
+    lib.fa_bwd_noalloc_scratch_bytes.restype = sz
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -498,6 +504,28 @@ def backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = No
         st = lib.fa_bwd_stages(*args, stages, _stream(q))
     if st != 0:
         raise FaError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None,
+                     dq=None, dk=None, dv=None):
+    """fa_bwd_noalloc: fa_bwd's gradients with the library's fixed per-device scratch instead of
+    a workspace (nothing is allocated by the library; dq, dk, dv may be passed in so that nothing
+    is allocated here either).  Returns (dq, dk, dv) like q, k, v."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v, same_dv=True)
+    _out(o, "o", q.shape, q)
+    _out(do, "do", q.shape, q)
+    _out(lse, "lse", (B, Hq, Tq), q, torch.float32)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if _out(dq, "dq", q.shape, q) is None else dq
+    dk = torch.empty_like(k) if _out(dk, "dk", k.shape, q) is None else dk
+    dv = torch.empty_like(v) if _out(dv, "dv", v.shape, q) is None else dv
+    st = lib.fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+                            B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), scale, _dtype_code(q), _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

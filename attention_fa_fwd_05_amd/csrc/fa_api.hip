@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_kernels.h"
 
@@ -159,7 +161,7 @@ int bwd_core(const void* Q, const void* K, const void* V, const void* O, const f
              const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
              const int* cu_q, const int* cu_k, int B, int Hq, int Hkv, int total_q, int total_k, int Tq,
              int Tk, int d, int dv, int causal, int window, float scale, int dtype, unsigned stages, void* stream,
-             const uint32_t* mask = nullptr, long long mask_bstride = 0);
+             const uint32_t* mask = nullptr, long long mask_bstride = 0, bool validate_only = false);
 // Boolean-mask arguments shared by the forward and the backward: the stride
 // is 0 (one mask for the batch) or a multiple of 4 words holding a whole
 // entry, and the mask has Tq rows of 4 * ceil(Tk / 128) words.
@@ -181,11 +183,70 @@ size_t splitk_ws_bytes(int B, int Hq, int Tq, int d, int ns) {
   return align_up((size_t)ns * rows * d * 4) + align_up((size_t)ns * rows * 4);
 }
 
+// Scratch of fa_bwd_noalloc: -D and the log2-domain L of every (padded)
+// query row, in the workspace layout of fa_bwd, for callers that cannot
+// allocate.  Each GPU the library runs on holds its own copy for the life of
+// the process.  Host code must never use this name as a device address (on
+// the host it is only a stand-in for the symbol): the per-device address
+// comes from hipGetSymbolAddress below.
+constexpr size_t kScratchBytes = 16u << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, looked up once per device
+// (with that device current) and kept.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) {
+    t_hip_error = "device ordinal beyond the library's per-device scratch table";
+    return FA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr) {
+      t_hip_error = "hipGetSymbolAddress returned no address for the scratch array";
+      return FA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int fa_abi_version(void) { return (1 << 16) | 2; }
+size_t fa_bwd_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                   const void* dO, void* dQ, void* dK, void* dV,
+                   int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
+                   int dtype, void* stream) {
+  // Every argument is validated (by the same checks as fa_bwd, with the
+  // scratch standing in for a workspace of exactly its size) before the
+  // scratch address is looked up, so a rejected call makes no HIP call.
+  int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
+  if (st != FA_OK) return st;
+  if (ws_layout(B, Hq, Tq, d, dtype).total > kScratchBytes) return FA_ERR_SCRATCH;
+  st = bwd_core(Q, K, V, O, L, dO, dQ, dK, dV, nullptr, kScratchBytes, nullptr, nullptr, B, Hq, Hkv, 0, 0, Tq,
+                Tk, d, d, causal, 0, scale, dtype, FA_BWD_STAGE_ALL, stream, nullptr, 0, /*validate_only=*/true);
+  if (st != FA_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != FA_OK) return st;
+  return bwd_core(Q, K, V, O, L, dO, dQ, dK, dV, ws, kScratchBytes, nullptr, nullptr, B, Hq, Hkv, 0, 0, Tq, Tk,
+                  d, d, causal, 0, scale, dtype, FA_BWD_STAGE_ALL, stream);
+}
+
+int fa_abi_version(void) { return (1 << 16) | 3; }
 
 const char* fa_hip_error_string(void) { return t_hip_error; }
 
@@ -203,6 +264,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_TOO_LARGE: return "a size exceeds the library's index range";
     case FA_ERR_HIP: return "HIP runtime error or kernel launch failure";
     case FA_ERR_STAGES: return "unknown backward stage bits";
+    case FA_ERR_SCRATCH: return "the call needs more than fa_bwd_noalloc's fixed scratch (fa_bwd_noalloc_scratch_bytes)";
     default: return "unknown status";
   }
 }
@@ -511,7 +573,7 @@ int bwd_core(const void* Q, const void* K, const void* V, const void* O, const f
              const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
              const int* cu_q, const int* cu_k, int B, int Hq, int Hkv, int total_q, int total_k, int Tq,
              int Tk, int d, int dv, int causal, int window, float scale, int dtype, unsigned stages, void* stream,
-             const uint32_t* mask, long long mask_bstride) {
+             const uint32_t* mask, long long mask_bstride, bool validate_only) {
   int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
   if (st != FA_OK) return st;
   if ((st = check_dv(d, dv, dtype)) != FA_OK) return st;
@@ -533,6 +595,7 @@ int bwd_core(const void* Q, const void* K, const void* V, const void* O, const f
     if (words / 256 + 1 > kMaxGrid) return FA_ERR_TOO_LARGE;
   }
   const size_t need = ws.total + (masked ? mask_t_bytes(B, Tq, Tk, mask_bstride) : 0);
+  if (validate_only) return need <= workspace_bytes ? FA_OK : FA_ERR_WORKSPACE;
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (misaligned(workspace)) return FA_ERR_ALIGNMENT;

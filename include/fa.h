@@ -44,7 +44,9 @@
  *  - stream is a hipStream_t (NULL = the null stream).  All work is enqueued
  *    on it; nothing synchronises the host, nothing prints, nothing allocates.
  *  - Ownership: the caller owns every buffer.  The library keeps no state
- *    between calls and may be called from several host threads at once.
+ *    between calls and may be called from several host threads at once
+ *    (fa_bwd_noalloc alone keeps a per-device scratch address and shares its
+ *    scratch between calls, see there).
  *  - Outputs are overwritten, never accumulated into.
  *  - Errors: arguments are validated before any HIP call and the first failing
  *    check is returned; a failed launch returns FA_ERR_HIP.  No C++ exception
@@ -72,7 +74,8 @@ typedef enum {
   FA_ERR_ALIGNMENT = 8,  /* a pointer is not 16-byte aligned */
   FA_ERR_TOO_LARGE = 9,  /* a size exceeds the library's index range */
   FA_ERR_HIP = 10,       /* a HIP runtime call or kernel launch failed */
-  FA_ERR_STAGES = 11     /* fa_bwd_stages: a bit outside FA_BWD_STAGE_ALL is set */
+  FA_ERR_STAGES = 11,    /* fa_bwd_stages: a bit outside FA_BWD_STAGE_ALL is set */
+  FA_ERR_SCRATCH = 12    /* fa_bwd_noalloc: the call needs more than its fixed scratch */
 } fa_status;
 
 typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1 } fa_dtype;
@@ -323,6 +326,31 @@ int fa_bwd_mask(const void* Q, const void* K, const void* V, const void* O, cons
                 void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, const uint32_t* mask_bits,
                 long long mask_batch_stride, int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal,
                 float scale, int dtype, void* stream);
+
+/*
+ * The backward pass of fa_bwd for callers that cannot allocate memory or pass
+ * a workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments and results as fa_bwd (bit for bit:
+ * the same kernels run), without the workspace: the per-row -D and log2-domain
+ * L live in a scratch array of fa_bwd_noalloc_scratch_bytes() bytes (16 MiB)
+ * that the library holds in device memory on every GPU it runs on, from load
+ * until the process ends.  A call needs 8 bytes per query row with rows padded
+ * to a multiple of 64 per head, B * Hq * ceil(Tq / 64) * 64 * 8 bytes, and
+ * returns FA_ERR_SCRATCH if that exceeds the scratch (up to 2,097,152 padded
+ * rows, e.g. B * Hq = 512 heads of 4096 rows).  Nothing is allocated; the
+ * first call on a device looks up that device's scratch address (a HIP symbol
+ * lookup, not an allocation) and keeps it.  The work runs on the current
+ * device, which must be the stream's.  All calls on one GPU share its scratch
+ * and every call rewrites the part it reads before reading it, so nothing has
+ * to be cleared between calls; calls that may overlap on one GPU (concurrent
+ * streams, host threads) race on it and must be serialised by the caller.
+ */
+int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                   const void* dO, void* dQ, void* dK, void* dV,
+                   int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
+                   int dtype, void* stream);
+/* Bytes of fa_bwd_noalloc's per-device scratch array. */
+size_t fa_bwd_noalloc_scratch_bytes(void);
 
 /* Static English text for a status code (never NULL). */
 const char* fa_status_string(int status);

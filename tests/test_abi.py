@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(12):
+    for code in range(13):
         s = fa.status_string(code)
         assert s and s != "unknown status"
     assert fa.status_string(99) == "unknown status"
@@ -244,6 +244,7 @@ def _scale_calls(lib, s):
         "fa_bwd_varlen": lambda: lib.fa_bwd_varlen(*(FAKE,) * 10, W, FAKE, FAKE, 2, 2, 1, 32, 32, 16, 16, 64, 1, 0,
                                                    s, 1, None),
         "fa_bwd_mask": lambda: lib.fa_bwd_mask(*(FAKE,) * 10, W, FAKE, 0, 2, 4, 2, 16, 300, 64, 1, s, 1, None),
+        "fa_bwd_noalloc": lambda: lib.fa_bwd_noalloc(*(FAKE,) * 9, 1, 2, 1, 16, 16, 64, 1, s, 1, None),
     }
 
 
@@ -288,3 +289,18 @@ def test_a_launch_without_a_device_returns_the_hip_status():
     status, text = r.stdout.strip().splitlines()[-2:]
     assert int(status) == 10
     assert "device" in text.lower()
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """fa_bwd_noalloc needs 8 bytes per padded query row; beyond its fixed scratch it returns
+    FA_ERR_SCRATCH before any HIP call (fake pointers: nothing is launched)."""
+    cap = lib.fa_bwd_noalloc_scratch_bytes()
+    assert cap == 16 << 20
+    rows_max = cap // 8                                    # 2,097,152 padded rows
+    ok_heads = rows_max // 4096
+    # one more head than fits: rejected; the other checks still come first
+    assert lib.fa_bwd_noalloc(*(FAKE,) * 9, 1, ok_heads + 1, 1, 4096, 64, 64, 1, 0.125, 1, None) == 12
+    assert lib.fa_bwd_noalloc(*(FAKE,) * 9, 1, 3, 2, 4096, 64, 64, 1, 0.125, 1, None) == 3
+    assert lib.fa_bwd_noalloc(*(FAKE,) * 8, None, 1, 2, 1, 16, 16, 64, 1, 0.125, 1, None) == 1
+    # padding counts: Tq = 4033 pads to 4096 rows per head
+    assert lib.fa_bwd_noalloc(*(FAKE,) * 9, 1, ok_heads + 1, 1, 4033, 64, 64, 1, 0.125, 1, None) == 12
