@@ -20,9 +20,10 @@
 //
 // Query blocks: from the last one down, heads innermost, so the key blocks of
 // a group (all on one XCD) step through the same Q / dO blocks together and
-// share them in L2.  Q / dO / L2 / -D blocks sit in three LDS buffers: block
-// i (read by both waves), block i - 1 (the dS-wave's Q^T for dK) and block
-// i + 1 (loading).  P goes through two LDS buffers.  One barrier per block.
+// share them in L2.  Blocks are loaded two ahead by direct global->LDS loads:
+// Q has four LDS slots (block i - 1 for the dS-wave's Q^T, block i for both
+// waves, blocks i + 1 and i + 2 in flight), dO, L2 and -D three (blocks i,
+// i + 1, i + 2).  P goes through two LDS buffers.  One barrier per block.
 #include "fa_common.h"
 #include "fa_kernels.h"
 
@@ -44,6 +45,27 @@ __device__ inline KWork2 kblock_work2(const BwdArgs& a, int nkb) {
   return w;
 }
 
+// Issue NP matrix products in a fixed order with AHEAD operands in flight:
+// fetch(m) reads product m's LDS operand, mma(m, x) issues product m, and
+// between(m) is the other work placed right after product m (vector work of
+// a later stage, single direct loads).  A scheduling fence after every step
+// keeps exactly this order, so operand reads stay AHEAD products ahead and
+// the vector work fills the time the products take.
+template <int NP, int AHEAD, typename Op, typename F, typename G, typename H>
+__device__ __forceinline__ void pipelined(F&& fetch, G&& mma, H&& between) {
+  Op ring[AHEAD];
+#pragma unroll
+  for (int m = 0; m < AHEAD; ++m) ring[m] = fetch(m);
+#pragma unroll
+  for (int m = 0; m < NP; ++m) {
+    const Op x = ring[m % AHEAD];
+    if (m + AHEAD < NP) ring[m % AHEAD] = fetch(m + AHEAD);
+    mma(m, x);
+    between(m);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 }  // namespace
 
 // D: head dim of Q, K, dK; DV: of V, dO, dV.
@@ -60,10 +82,10 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
   constexpr int NSQ = BQ / 16;                      // steps over a query block (dV, dK)
   constexpr int NDT = D / 32;                       // 32-wide dK tiles
   constexpr int NDTV = DV / 32;                     // 32-wide dV tiles
-  constexpr int NB = 3;
+  constexpr int NBQ = 4, NB = 3;                    // Q slots; dO, L2, -D (and mask) slots
   static_assert(NSQ == 4, "P in LDS is 4 operands per lane");
   // Tiles 4096-byte aligned (XorFetch): 64 rows of 64 or 128 bf16 are 8 or 16 KiB.
-  __shared__ __attribute__((aligned(4096))) T sQ[NB][BQ * D];
+  __shared__ __attribute__((aligned(4096))) T sQ[NBQ][BQ * D];
   __shared__ __attribute__((aligned(4096))) T sdO[NB][BQ * DV];
   __shared__ __attribute__((aligned(16))) bf16x8 sP[2][4][NSQ][64];   // [buffer][key group][step][lane]
   __shared__ __attribute__((aligned(16))) float sL[NB][64];
@@ -99,23 +121,79 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
   auto item_bh = [&](int it) { return wk.b * a.Hq + wk.hk * G + it % G; };
   auto item_qrow = [&](int it) { return sq.q_row(wk.hk * G + it % G); };
 
-  // Loads of one block into buffer buf: Q and dO rows (clamped at Tq - 1; the
-  // padding rows have L2 = +inf and -D = 0, so they add nothing), L2 and -D
-  // (rows padded to 64 per head in the workspace), and for a boolean mask
-  // each P-wave's bits of its keys (key-major copy, two words per key).
-  auto issue = [&](int it, int buf) {
-    const int q0 = item_q0(it);
-    const size_t qr = item_qrow(it);
-    dma_rows<T, D, BQ, NTHR>(sQ[buf], reinterpret_cast<const T*>(a.Q) + qr * D, q0, Tq);
-    dma_rows<T, DV, BQ, NTHR>(sdO[buf], reinterpret_cast<const T*>(a.dO) + qr * DV, q0, Tq);
-    const size_t wrow = (size_t)item_bh(it) * a.Tqp + q0;
-    if (w == 0) dma_floats64(sL[buf], a.Lg + wrow);
-    if (w == 1) dma_floats64(sD[buf], a.Dvec + wrow);
-    if constexpr (MASK) {
+  // Loads of block it: Q and dO rows (clamped at Tq - 1; the padding rows have
+  // L2 = +inf and -D = 0, so they add nothing), L2 and -D (rows padded to 64
+  // per head in the workspace), and for a boolean mask each P-wave's bits of
+  // its keys (key-major copy, two words per key).  A whole block is addressed
+  // from a wave-uniform row pointer plus per-lane byte offsets tabulated once;
+  // only the ragged last block clamps its rows.  The loads go out as single
+  // instructions ("pieces") spread over a phase of matrix products.
+  using DRQ = DmaRows<T, D, BQ, NTHR>;
+  using DRO = DmaRows<T, DV, BQ, NTHR>;
+  uint32_t qoff[DRQ::PER], ooff[DRO::PER];
+#pragma unroll
+  for (int j = 0; j < DRQ::PER; ++j) qoff[j] = DRQ::src_off(j);
+#pragma unroll
+  for (int j = 0; j < DRO::PER; ++j) ooff[j] = D == DV ? qoff[j % DRQ::PER] : DRO::src_off(j);
+  struct Src {
+    const T* q;                                     // Q row q0 of the block's head
+    const T* o;                                     // dO row q0
+    size_t wrow;                                    // workspace row of query q0
+    int q0, it;
+    bool whole;                                     // all BQ rows exist: no clamping
+  };
+  auto block_src = [&](int it) {
+    Src r;
+    r.it = it;
+    r.q0 = item_q0(it);
+    const size_t qr = item_qrow(it) + r.q0;
+    r.q = reinterpret_cast<const T*>(a.Q) + qr * D;
+    r.o = reinterpret_cast<const T*>(a.dO) + qr * DV;
+    r.wrow = (size_t)item_bh(it) * a.Tqp + r.q0;
+    r.whole = r.q0 + BQ <= Tq;
+    return r;
+  };
+  // Pieces 0 .. NPC - 1: Q, dO, then the L2 / -D row (waves 0 / 1) and the
+  // mask word (P-waves with a mask); a piece a wave has no share of is empty.
+  constexpr int NPC = DRQ::PER + DRO::PER + 1 + (MASK ? 1 : 0);
+  auto piece = [&](const Src& b, int j) {
+    const int buf = b.it % NB;
+    if (j < DRQ::PER) {
+      if (b.whole) dma16s(b.q, qoff[j], lds_addr(sQ[b.it % NBQ]) + DRQ::lds_off(j));
+      else DRQ::one(sQ[b.it % NBQ], b.q - (size_t)b.q0 * D, b.q0, Tq, j);
+    } else if (j < DRQ::PER + DRO::PER) {
+      const int i = j - DRQ::PER;
+      if (b.whole) dma16s(b.o, ooff[i], lds_addr(sdO[buf]) + DRO::lds_off(i));
+      else DRO::one(sdO[buf], b.o - (size_t)b.q0 * DV, b.q0, Tq, i);
+    } else if (j == DRQ::PER + DRO::PER) {
+      if (w == 0) dma_floats64(sL[buf], a.Lg + b.wrow);
+      if (w == 1) dma_floats64(sD[buf], a.Dvec + b.wrow);
+    } else if constexpr (MASK) {
       if (pwave)
         dma4(a.mask_t + (size_t)wk.b * a.mask_t_bstride +
-                 (size_t)min(kw + (lane >> 1), Tk - 1) * a.mask_t_row_words + q0 / 32 + (lane & 1),
+                 (size_t)min(kw + (lane >> 1), Tk - 1) * a.mask_t_row_words + b.q0 / 32 + (lane & 1),
              lds_addr(sM + (buf * 4 + kg) * 64));
+    }
+  };
+  auto issue = [&](int it) {
+    const Src b = block_src(it);
+#pragma unroll
+    for (int j = 0; j < NPC; ++j) piece(b, j);
+  };
+  static_assert(2 * NPC <= 2 * NSD && 2 * NPC <= 2 * NSDV, "pieces fit in a phase at every other product");
+
+  // Direct-load instructions this wave issues per block, so that the wait at
+  // the end of block i leaves block i + 2's loads in flight.
+  constexpr int NLD = DRQ::PER + DRO::PER;
+  auto wait_next = [&](bool two_in_flight) {
+    if (!two_in_flight) {
+      wait_vmcnt<0>();
+    } else if (w < 2) {                             // + the L2 or -D row
+      wait_vmcnt<NLD + 1 + (MASK ? 1 : 0)>();
+    } else if (pwave) {
+      wait_vmcnt<NLD + (MASK ? 1 : 0)>();
+    } else {
+      wait_vmcnt<NLD>();
     }
   };
 
@@ -124,7 +202,7 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
   XorFetch<DV> xfv;
   xfv.init(lane);
 
-  if (total > 0) issue(0, 0);
+  if (total > 0) issue(0);
 
   if (pwave) {
     // ------------------------------------------------------------ P-wave
@@ -135,85 +213,100 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
       for (int s = 0; s < NSD; ++s) {
         kop[s] = M::ld(Kp + s * 8);
         if (!key_ok) kop[s] = Op{};
-        asm volatile("" : "+a"(kop[s]));
       }
     }
     f32x16 dv[NDTV];
 #pragma unroll
     for (int t = 0; t < NDTV; ++t) dv[t] = f32x16{};
-    wait_vmcnt<0>();
+    if (total > 1) issue(1);
+    wait_next(total > 1);
     __syncthreads();
     for (int it = 0; it <= total; ++it) {
       const int cur = it % NB;
-      if (it + 1 < total) issue(it + 1, (it + 1) % NB);
+      const bool load = it + 2 < total;             // uniform
+      const Src nsrc = block_src(min(it + 2, total - 1));
       if (it < total) {
         const int q0 = item_q0(it);
-        const uint32_t qb = lds_addr(sQ[cur]), ob = lds_addr(sdO[cur]);
-        // S = Q K^T for the two 32-query tiles (lane = key).
-        f32x16 sacc[2] = {f32x16{}, f32x16{}};
-        wave_prio<1>();
-#pragma unroll
-        for (int s = 0; s < NSD; ++s) {
-          sacc[0] = M::mma(XorFetch<D>::nat(qb + xf.nat0, 0, s), kop[s], sacc[0]);
-          sacc[1] = M::mma(XorFetch<D>::nat(qb + xf.nat0, 1, s), kop[s], sacc[1]);
-        }
-        sched_interleave<2 * NSD, 4>();
-        wave_prio<0>();
+        const uint32_t qb = lds_addr(sQ[it % NBQ]), ob = lds_addr(sdO[cur]);
         // P = exp2(S c - L2); register i of tile t holds query
         // q0 + 32 t + 8 (i / 4) + 4 h + i % 4.  A boolean mask's hidden pairs
         // get L2 = +inf (bit 4 h + 8 g + e of the tile's word for register
-        // 4 g + e).
-        Op pop[NSQ];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float p[16];
-          uint32_t mw = 0;
-          if constexpr (MASK) mw = sM[(cur * 4 + kg) * 64 + 2 * n + t] >> (4 * h);
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[cur][32 * t + 8 * g + 4 * h]);
+        // 4 g + e).  Element i of tile t, in one of 4 pieces of 4 elements.
+        f32x16 sacc[2] = {f32x16{}, f32x16{}};
+        float p[2][16];
+        f32x4 lt[2][4];
+        uint32_t mw[2] = {0, 0};
+        auto exp_piece = [&](int t, int g) {
+          f32x4 l4 = lt[t][g];
+          if constexpr (MASK) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              float l = l4[e];
-              if constexpr (MASK) {
-                const int keep = (int)(mw << (31 - (8 * g + e))) >> 31;
-                l = __int_as_float((__float_as_int(l) & keep) | (int)(0x7f800000u & ~(uint32_t)keep));
-              }
-              p[4 * g + e] = fast_exp2(__builtin_fmaf(sacc[t][4 * g + e], c, -l));
+              const int keep = (int)(mw[t] << (31 - (8 * g + e))) >> 31;
+              l4[e] = __int_as_float((__float_as_int(l4[e]) & keep) | (int)(0x7f800000u & ~(uint32_t)keep));
             }
           }
-          // Causal diagonal, window edge and ragged key end: only on the
-          // blocks that have them (a uniform test), clear hidden pairs.
+#pragma unroll
+          for (int e = 0; e < 4; ++e) p[t][4 * g + e] = fast_exp2(__builtin_fmaf(sacc[t][4 * g + e], c, -l4[e]));
+        };
+        // Causal diagonal, window edge and ragged key end: only on the blocks
+        // that have them (a uniform test), clear hidden pairs; then pack the
+        // tile's two P operands and hand them to the dS-wave through LDS.
+        Op pop[NSQ];
+        auto finish_tile = [&](int t) {
           if (ragged || (CAUSAL && k0 + BK - 1 > q0 + 32 * t + off) ||
               (W > 0 && q0 + 32 * t + 31 > k0 - off + W - 1)) {
             const int thr = !key_ok ? INT_MAX : (CAUSAL ? mykey - off - q0 - 32 * t - 4 * h : INT_MIN);
             const int thr_hi = W > 0 ? mykey - off + W - 1 - q0 - 32 * t - 4 * h : INT_MAX;
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-              if (8 * (i >> 2) + (i & 3) < thr || 8 * (i >> 2) + (i & 3) > thr_hi) p[i] = 0.f;
+              if (8 * (i >> 2) + (i & 3) < thr || 8 * (i >> 2) + (i & 3) > thr_hi) p[t][i] = 0.f;
           }
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             u32x4 wv;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              wv[e] = __builtin_bit_cast(uint32_t, bf16x2{(bf16)p[8 * j + 2 * e], (bf16)p[8 * j + 2 * e + 1]});
+              wv[e] = __builtin_bit_cast(uint32_t, bf16x2{(bf16)p[t][8 * j + 2 * e], (bf16)p[t][8 * j + 2 * e + 1]});
             pop[2 * t + j] = __builtin_bit_cast(bf16x8, wv);
+            sP[it & 1][kg][2 * t + j][lane] = pop[2 * t + j];
           }
+        };
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) lt[t][g] = *reinterpret_cast<const f32x4*>(&sL[cur][32 * t + 8 * g + 4 * h]);
+          if constexpr (MASK) mw[t] = sM[(cur * 4 + kg) * 64 + 2 * n + t] >> (4 * h);
         }
-        // P to LDS for the dS-wave of this key group.
-#pragma unroll
-        for (int s = 0; s < NSQ; ++s) sP[it & 1][kg][s][lane] = pop[s];
-        // dV^T += dO^T P (dO^T by transposed reads of the dO tile).
+        // S = Q K^T, tile 0 then tile 1 (lane = key); tile 0's exponentials
+        // under the last products of tile 1; block it + 2's loads at every
+        // other product.
         wave_prio<1>();
-#pragma unroll
-        for (int t = 0; t < NDTV; ++t)
-#pragma unroll
-          for (int s = 0; s < NSQ; ++s) dv[t] = M::mma(XorFetch<DV>::tr(ob + xfv.tr0, t, s), pop[s], dv[t]);
-        sched_interleave<NDTV * NSQ, 4, 2>();
+        pipelined<2 * NSD, 4, Op>(
+            [&](int m) { return XorFetch<D>::nat(qb + xf.nat0, m / NSD, m % NSD); },
+            [&](int m, const Op& x) { sacc[m / NSD] = M::mma(x, kop[m % NSD], sacc[m / NSD]); },
+            [&](int m) {
+              if (m % 2 == 1 && m / 2 < NPC && load) piece(nsrc, m / 2);
+              const int k = m - (2 * NSD - 5);      // 4 pieces over the last 4 products
+              if (k >= 0 && k < 4) exp_piece(0, k);
+            });
+        finish_tile(0);
+        // dV^T += dO^T P (dO^T by transposed reads), query steps of tile 0
+        // first; tile 1's exponentials under those products.
+        pipelined<NSQ * NDTV, 4, Op>(
+            [&](int m) { return XorFetch<DV>::tr(ob + xfv.tr0, m % NDTV, m / NDTV); },
+            [&](int m, const Op& x) { dv[m % NDTV] = M::mma(x, pop[m / NDTV], dv[m % NDTV]); },
+            [&](int m) {
+              // 4 pieces from product E0 on; tile 1's operands (query steps 2
+              // and 3) are complete after product 2 NDTV - 1, before their use.
+              constexpr int E0 = 2 * NDTV >= 6 ? 1 : 0;
+              const int k = m - E0;
+              if (k >= 0 && k < 4) exp_piece(1, k);
+              if (m == 2 * NDTV - 1) finish_tile(1);
+            });
+        static_assert(2 * NDTV - 1 >= (2 * NDTV >= 6 ? 1 : 0) + 3, "tile 1's P is formed before its query steps");
         wave_prio<0>();
       }
-      wait_vmcnt<0>();
+      wait_next(load);
       __syncthreads();
     }
     if (key_ok) {
@@ -233,47 +326,51 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
       for (int s = 0; s < NSDV; ++s) {
         vop[s] = M::ld(Vp + s * 8);
         if (!key_ok) vop[s] = Op{};
-        asm volatile("" : "+a"(vop[s]));
       }
     }
     f32x16 dk[NDT];
 #pragma unroll
     for (int t = 0; t < NDT; ++t) dk[t] = f32x16{};
     f32x16 dpacc[2];                                // dP - D of the previous block (lane = key)
-    wait_vmcnt<0>();
+    if (total > 1) issue(1);
+    wait_next(total > 1);
     __syncthreads();
     for (int it = 0; it <= total; ++it) {
       const int cur = it % NB;
-      if (it + 1 < total) issue(it + 1, (it + 1) % NB);
+      const bool load = it + 2 < total;             // uniform
+      const Src nsrc = block_src(min(it + 2, total - 1));
+      wave_prio<1>();
       if (it > 0) {
-        // dS = P (dP - D) of the previous block, then dK^T += Q^T dS.
-        const int prv = (it + NB - 1) % NB;
-        const uint32_t qb = lds_addr(sQ[prv]);
-        Op dsop[NSQ];
+        // dS = P (dP - D) of the previous block and dK^T += Q^T dS: the dS
+        // operand of query step s + 1 is formed under the products of step s.
+        const uint32_t qb = lds_addr(sQ[(it + NBQ - 1) % NBQ]);
+        u32x4 pw[NSQ], dsw[NSQ];
 #pragma unroll
-        for (int s = 0; s < NSQ; ++s) {
-          const u32x4 pw = __builtin_bit_cast(u32x4, sP[(it - 1) & 1][kg][s][lane]);
+        for (int s = 0; s < NSQ; ++s) pw[s] = __builtin_bit_cast(u32x4, sP[(it - 1) & 1][kg][s][lane]);
+        auto ds_word = [&](int s, int e) {          // word e (elements 2e, 2e+1) of step s
           const f32x16& dp = dpacc[s >> 1];
-          u32x4 dw;
+          const int r = 8 * (s & 1) + 2 * e;
+          const float p0 = __uint_as_float(pw[s][e] << 16), p1 = __uint_as_float(pw[s][e] & 0xffff0000u);
+          dsw[s][e] = __builtin_bit_cast(uint32_t, bf16x2{(bf16)(p0 * dp[r]), (bf16)(p1 * dp[r + 1])});
+        };
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 8 * (s & 1) + 2 * e;
-            const float p0 = __uint_as_float(pw[e] << 16), p1 = __uint_as_float(pw[e] & 0xffff0000u);
-            dw[e] = __builtin_bit_cast(uint32_t, bf16x2{(bf16)(p0 * dp[r]), (bf16)(p1 * dp[r + 1])});
-          }
-          dsop[s] = __builtin_bit_cast(bf16x8, dw);
-        }
-        wave_prio<1>();
+        for (int e = 0; e < 4; ++e) ds_word(0, e);
+        pipelined<NSQ * NDT, 4, Op>(
+            [&](int m) { return XorFetch<D>::tr(qb + xf.tr0, m % NDT, m / NDT); },
+            [&](int m, const Op& x) {
+              dk[m % NDT] = M::mma(x, __builtin_bit_cast(bf16x8, dsw[m / NDT]), dk[m % NDT]);
+            },
+            [&](int m) {
+              const int s = m / NDT + 1, r = m % NDT;
+              if (s < NSQ)
 #pragma unroll
-        for (int t = 0; t < NDT; ++t)
-#pragma unroll
-          for (int s = 0; s < NSQ; ++s) dk[t] = M::mma(XorFetch<D>::tr(qb + xf.tr0, t, s), dsop[s], dk[t]);
-        sched_interleave<NDT * NSQ, 4, 2>();
-        wave_prio<0>();
+                for (int e = r * 4 / NDT; e < (r + 1) * 4 / NDT; ++e) ds_word(s, e);
+            });
       }
       if (it < total) {
         // dP - D = dO V^T on a seed of -D (register i of tile t: query
-        // 32 t + 8 (i / 4) + 4 h + i % 4).
+        // 32 t + 8 (i / 4) + 4 h + i % 4); block it + 2's loads at every other
+        // product.
         const uint32_t ob = lds_addr(sdO[cur]);
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -283,16 +380,15 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) dpacc[t][4 * g + e] = v[e];
           }
-        wave_prio<1>();
-#pragma unroll
-        for (int s = 0; s < NSDV; ++s) {
-          dpacc[0] = M::mma(XorFetch<DV>::nat(ob + xfv.nat0, 0, s), vop[s], dpacc[0]);
-          dpacc[1] = M::mma(XorFetch<DV>::nat(ob + xfv.nat0, 1, s), vop[s], dpacc[1]);
-        }
-        sched_interleave<2 * NSDV, 4>();
-        wave_prio<0>();
+        pipelined<2 * NSDV, 4, Op>(
+            [&](int m) { return XorFetch<DV>::nat(ob + xfv.nat0, m & 1, m >> 1); },
+            [&](int m, const Op& x) { dpacc[m & 1] = M::mma(x, vop[m >> 1], dpacc[m & 1]); },
+            [&](int m) {
+              if (m % 2 == 1 && m / 2 < NPC && load) piece(nsrc, m / 2);
+            });
       }
-      wait_vmcnt<0>();
+      wave_prio<0>();
+      wait_next(load);
       __syncthreads();
     }
     if (key_ok) {
