@@ -45,27 +45,6 @@ __device__ inline KWork2 kblock_work2(const BwdArgs& a, int nkb) {
   return w;
 }
 
-// Issue NP matrix products in a fixed order with AHEAD operands in flight:
-// fetch(m) reads product m's LDS operand, mma(m, x) issues product m, and
-// between(m) is the other work placed right after product m (vector work of
-// a later stage, single direct loads).  A scheduling fence after every step
-// keeps exactly this order, so operand reads stay AHEAD products ahead and
-// the vector work fills the time the products take.
-template <int NP, int AHEAD, typename Op, typename F, typename G, typename H>
-__device__ __forceinline__ void pipelined(F&& fetch, G&& mma, H&& between) {
-  Op ring[AHEAD];
-#pragma unroll
-  for (int m = 0; m < AHEAD; ++m) ring[m] = fetch(m);
-#pragma unroll
-  for (int m = 0; m < NP; ++m) {
-    const Op x = ring[m % AHEAD];
-    if (m + AHEAD < NP) ring[m % AHEAD] = fetch(m + AHEAD);
-    mma(m, x);
-    between(m);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
 }  // namespace
 
 // D: head dim of Q, K, dK; DV: of V, dO, dV.
