@@ -28,7 +28,7 @@ STAGE_PRE, STAGE_DKDV, STAGE_DQ, STAGE_ALL = 1, 2, 4, 7
 EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_window", "fa_bwd_window", "fa_fwd_dv", "fa_bwd_dv",
            "fa_fwd_splitk",
            "fa_fwd_splitk_workspace_bytes", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fwd_paged",
-           "fa_fwd_paged_workspace_bytes", "fa_bwd_workspace_bytes",
+           "fa_fwd_paged_workspace_bytes", "fa_bwd_paged", "fa_bwd_paged_workspace_bytes", "fa_bwd_workspace_bytes",
            "fa_mask_row_words", "fa_mask_pack", "fa_fwd_mask", "fa_bwd_mask", "fa_bwd_mask_workspace_bytes",
            "fa_fwd_mask_splitk", "fa_fwd_mask_splitk_workspace_bytes",
            "fa_bwd_noalloc", "fa_bwd_noalloc_scratch_bytes",
@@ -87,6 +87,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_paged.restype = i
     lib.fa_fwd_paged_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i]
     lib.fa_fwd_paged_workspace_bytes.restype = sz
+    lib.fa_bwd_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, i,
+                                 vp, sz, vp]
+    lib.fa_bwd_paged.restype = i
+    lib.fa_bwd_paged_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+    lib.fa_bwd_paged_workspace_bytes.restype = sz
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_varlen.restype = i
     lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp,
@@ -330,12 +335,8 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     return dq, dk, dv
 
 
-def forward_paged(q, k_pages, v_pages, page_table, seqlens_k, causal: bool = False, scale: float | None = None,
-                  window: int = 0, nsplit: int = 0, workspace=None, out=None, lse=None):
-    """fa_fwd_paged: q [B, Hq, Tq, d]; k_pages, v_pages [num_pages, Hkv, page_size, d]; page_table
-    int32 [B, pages_per_seq]; seqlens_k int32 [B].  Returns (o like q, lse float32 [B, Hq, Tq])."""
+def _paged_shapes(q, k_pages, v_pages, page_table, seqlens_k):
     import torch
-    lib = load_library()
     if q.dim() != 4 or k_pages.dim() != 4 or tuple(v_pages.shape) != tuple(k_pages.shape):
         raise ValueError("q [B, Hq, Tq, d], k_pages = v_pages shape [num_pages, Hkv, page_size, d]")
     B, Hq, Tq, d = q.shape
@@ -350,7 +351,16 @@ def forward_paged(q, k_pages, v_pages, page_table, seqlens_k, causal: bool = Fal
     _on_gpu(q, "q")
     if page_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
         raise ValueError("page_table and seqlens_k must be int32")
-    pps = page_table.shape[1]
+    return B, Hq, Tq, d, num_pages, Hkv, page_size, page_table.shape[1]
+
+
+def forward_paged(q, k_pages, v_pages, page_table, seqlens_k, causal: bool = False, scale: float | None = None,
+                  window: int = 0, nsplit: int = 0, workspace=None, out=None, lse=None):
+    """fa_fwd_paged: q [B, Hq, Tq, d]; k_pages, v_pages [num_pages, Hkv, page_size, d]; page_table
+    int32 [B, pages_per_seq]; seqlens_k int32 [B].  Returns (o like q, lse float32 [B, Hq, Tq])."""
+    import torch
+    lib = load_library()
+    B, Hq, Tq, d, num_pages, Hkv, page_size, pps = _paged_shapes(q, k_pages, v_pages, page_table, seqlens_k)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
     need = int(lib.fa_fwd_paged_workspace_bytes(B, Hq, Hkv, Tq, pps, page_size, d, code, int(nsplit)))
@@ -365,6 +375,35 @@ def forward_paged(q, k_pages, v_pages, page_table, seqlens_k, causal: bool = Fal
     if st != 0:
         raise FaError(st, "fa_fwd_paged")
     return o, L
+
+
+def backward_paged(q, k_pages, v_pages, o, lse, do, page_table, seqlens_k, causal: bool = False,
+                   scale: float | None = None, window: int = 0, workspace=None, dq=None, dk_pages=None,
+                   dv_pages=None):
+    """fa_bwd_paged: the backward of forward_paged.  Returns (dq like q, dk_pages like k_pages,
+    dv_pages like v_pages); a page no table entry references gets zeros."""
+    import torch
+    lib = load_library()
+    B, Hq, Tq, d, num_pages, Hkv, page_size, pps = _paged_shapes(q, k_pages, v_pages, page_table, seqlens_k)
+    _out(o, "o", q.shape, q)
+    _out(do, "do", q.shape, q)
+    _out(lse, "lse", (B, Hq, Tq), q, torch.float32)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    need = int(lib.fa_bwd_paged_workspace_bytes(B, Hq, Hkv, Tq, pps, page_size, d, code))
+    if need == 0:
+        raise ValueError("unsupported paged backward sizes")
+    ws = _ws(workspace, need, q)
+    dq = torch.empty_like(q) if _out(dq, "dq", q.shape, q) is None else dq
+    dk_pages = torch.empty_like(k_pages) if _out(dk_pages, "dk_pages", k_pages.shape, q) is None else dk_pages
+    dv_pages = torch.empty_like(v_pages) if _out(dv_pages, "dv_pages", v_pages.shape, q) is None else dv_pages
+    st = lib.fa_bwd_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                          _ptr(dk_pages), _ptr(dv_pages), page_table.data_ptr(), seqlens_k.data_ptr(), B, Hq, Hkv,
+                          Tq, pps, page_size, num_pages, d, int(bool(causal)), int(window), scale, code,
+                          ws.data_ptr(), _nbytes(ws), _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_bwd_paged")
+    return dq, dk_pages, dv_pages
 
 
 def pack_mask(mask, Tk: int | None = None, out=None):

@@ -22,7 +22,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa05.so")
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_dkdv.hip", "fa_api.hip"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_dkdv.hip", "fa_paged.hip", "fa_api.hip"]
 HEADERS = ["fa_common.h", "fa_kernels.h"]
 
 HIPCC_FLAGS = [

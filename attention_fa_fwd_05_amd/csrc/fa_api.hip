@@ -161,7 +161,8 @@ int bwd_core(const void* Q, const void* K, const void* V, const void* O, const f
              const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
              const int* cu_q, const int* cu_k, int B, int Hq, int Hkv, int total_q, int total_k, int Tq,
              int Tk, int d, int dv, int causal, int window, float scale, int dtype, unsigned stages, void* stream,
-             const uint32_t* mask = nullptr, long long mask_bstride = 0, bool validate_only = false);
+             const uint32_t* mask = nullptr, long long mask_bstride = 0, bool validate_only = false,
+             const int* seqlens_k = nullptr);
 // Boolean-mask arguments shared by the forward and the backward: the stride
 // is 0 (one mask for the batch) or a multiple of 4 words holding a whole
 // entry, and the mask has Tq rows of 4 * ceil(Tk / 128) words.
@@ -181,6 +182,23 @@ size_t mask_t_bytes(int B, int Tq, int Tk, long long stride) {
 size_t splitk_ws_bytes(int B, int Hq, int Tq, int d, int ns) {
   const size_t rows = (size_t)B * Hq * Tq;
   return align_up((size_t)ns * rows * d * 4) + align_up((size_t)ns * rows * 4);
+}
+
+// Workspace of the backward through a block table: the backward's own (-D,
+// L2 rows), then the gathered K and V and the per-sequence dK and dV, each
+// [B][Hkv][pages_per_seq * page_size][d] in the dtype.
+struct PagedWs {
+  size_t kg, vg, dkg, dvg, total;
+};
+PagedWs paged_ws(int B, int Hq, int Hkv, int Tq, long long tk_max, int d, int dtype) {
+  PagedWs w;
+  const size_t part = align_up((size_t)B * Hkv * tk_max * d * elem_bytes(dtype));
+  w.kg = ws_layout(B, Hq, Tq, d, dtype).total;
+  w.vg = w.kg + part;
+  w.dkg = w.vg + part;
+  w.dvg = w.dkg + part;
+  w.total = w.dvg + part;
+  return w;
 }
 
 // Scratch of fa_bwd_noalloc: -D and the log2-domain L of every (padded)
@@ -225,6 +243,58 @@ int scratch_address(void** out) {
 
 extern "C" {
 
+size_t fa_bwd_paged_workspace_bytes(int B, int Hq, int Hkv, int Tq, int pages_per_seq, int page_size, int d,
+                                    int dtype) {
+  if (pages_per_seq < 1 || page_size < 1 || page_size % 128 != 0) return 0;
+  const long long tk = (long long)pages_per_seq * page_size;
+  if (tk > kMaxSeq || check_common(B, Hq, Hkv, Tq, (int)tk, d, dtype) != FA_OK) return 0;
+  return paged_ws(B, Hq, Hkv, Tq, tk, d, dtype).total;
+}
+
+int fa_bwd_paged(const void* Q, const void* K_pages, const void* V_pages, const void* O, const float* L,
+                 const void* dO, void* dQ, void* dK_pages, void* dV_pages, const int* page_table,
+                 const int* seqlens_k, int B, int Hq, int Hkv, int Tq, int pages_per_seq, int page_size,
+                 int num_pages, int d, int causal, int window, float scale, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (pages_per_seq < 1 || page_size < 1 || num_pages < 1) return FA_ERR_BAD_SHAPE;
+  if (page_size % 128 != 0) return FA_ERR_BAD_SHAPE;
+  const long long tk = (long long)pages_per_seq * page_size;
+  if (tk > kMaxSeq) return FA_ERR_TOO_LARGE;
+  int st = check_common(B, Hq, Hkv, Tq, (int)tk, d, dtype);
+  if (st != FA_OK) return st;
+  if (page_table == nullptr || seqlens_k == nullptr) return FA_ERR_NULL_PTR;
+  if ((reinterpret_cast<uintptr_t>(page_table) & 3u) || (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
+    return FA_ERR_ALIGNMENT;
+  const long long nq = (long long)B * Hq * Tq * d, npool = (long long)num_pages * Hkv * page_size * d;
+  if (npool > kMaxElems) return FA_ERR_TOO_LARGE;
+  if ((long long)B * pages_per_seq > kMaxElems) return FA_ERR_TOO_LARGE;
+  if ((long long)num_pages * Hkv * (page_size / 128) > kMaxGrid) return FA_ERR_TOO_LARGE;
+  if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, nq)) || (st = check_ptr(dO, nq)) || (st = check_ptr(dQ, nq)) ||
+      (st = check_ptr(K_pages, npool)) || (st = check_ptr(V_pages, npool)) || (st = check_ptr(dK_pages, npool)) ||
+      (st = check_ptr(dV_pages, npool)) || (st = check_ptr(L, (long long)B * Hq * Tq)))
+    return st;
+  if (bad_scale(scale)) return FA_ERR_SCALE;
+  const PagedWs pw = paged_ws(B, Hq, Hkv, Tq, tk, d, dtype);
+  if (workspace == nullptr || workspace_bytes < pw.total) return FA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return FA_ERR_ALIGNMENT;
+  char* wsb = static_cast<char*>(workspace);
+  fa::PagedBwdArgs p;
+  p.K = K_pages; p.V = V_pages;
+  p.Kg = wsb + pw.kg; p.Vg = wsb + pw.vg;
+  p.dKg = wsb + pw.dkg; p.dVg = wsb + pw.dvg;
+  p.dK = dK_pages; p.dV = dV_pages;
+  p.table = page_table; p.seqlens = seqlens_k;
+  p.B = B; p.Hkv = Hkv; p.pps = pages_per_seq; p.page_size = page_size; p.num_pages = num_pages;
+  p.tk_max = (int)tk;
+  const bool bf = dtype == FA_DTYPE_BF16;
+  if ((st = hip_status(fa::launch_paged(p, bf, d, 0, (hipStream_t)stream))) != FA_OK) return st;
+  st = bwd_core(Q, wsb + pw.kg, wsb + pw.vg, O, L, dO, dQ, wsb + pw.dkg, wsb + pw.dvg, workspace, pw.kg, nullptr,
+                nullptr, B, Hq, Hkv, 0, 0, Tq, (int)tk, d, d, causal, window, scale, dtype, FA_BWD_STAGE_ALL, stream,
+                nullptr, 0, false, seqlens_k);
+  if (st != FA_OK) return st;
+  return hip_status(fa::launch_paged(p, bf, d, 1, (hipStream_t)stream));
+}
+
 size_t fa_bwd_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const float* L,
@@ -246,7 +316,7 @@ int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, c
                   d, d, causal, 0, scale, dtype, FA_BWD_STAGE_ALL, stream);
 }
 
-int fa_abi_version(void) { return (1 << 16) | 3; }
+int fa_abi_version(void) { return (1 << 16) | 4; }
 
 const char* fa_hip_error_string(void) { return t_hip_error; }
 
@@ -573,7 +643,7 @@ int bwd_core(const void* Q, const void* K, const void* V, const void* O, const f
              const void* dO, void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
              const int* cu_q, const int* cu_k, int B, int Hq, int Hkv, int total_q, int total_k, int Tq,
              int Tk, int d, int dv, int causal, int window, float scale, int dtype, unsigned stages, void* stream,
-             const uint32_t* mask, long long mask_bstride, bool validate_only) {
+             const uint32_t* mask, long long mask_bstride, bool validate_only, const int* seqlens_k) {
   int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
   if (st != FA_OK) return st;
   if ((st = check_dv(d, dv, dtype)) != FA_OK) return st;
@@ -617,6 +687,7 @@ int bwd_core(const void* Q, const void* K, const void* V, const void* O, const f
   a.total_k = total_k;
   a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.seqlens_k = seqlens_k;
   if (masked) {
     a.mask = mask;
     a.mask_bstride = mask_bstride;

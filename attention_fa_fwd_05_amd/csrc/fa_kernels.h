@@ -92,7 +92,7 @@ __device__ inline SeqView seq_view(const A& a, int b) {
 }
 
 struct BwdArgs {
-  static constexpr bool kPaged = false;
+  static constexpr bool kPaged = true;    // may give each sequence its own key count
   const void* Q;
   const void* K;
   const void* V;
@@ -123,7 +123,29 @@ struct BwdArgs {
   uint32_t* mask_t = nullptr;
   long long mask_t_bstride = 0;
   int mask_t_row_words = 0;
+  // Per-sequence key counts (seqlens_k != nullptr): sequence b has
+  // seqlens_k[b] keys of the fixed layout's Tk rows (the backward through a
+  // block table runs on gathered copies of the pages).
+  const int* seqlens_k = nullptr;
 };
+
+// Backward through a block table: gather of the pages into the fixed layout,
+// and the reduction of the per-sequence gradients into gradient pages.
+struct PagedBwdArgs {
+  const void* K;              // pools [num_pages][Hkv][page_size][d]
+  const void* V;
+  void* Kg;                   // gathered copies [B][Hkv][tk_max][d]
+  void* Vg;
+  const void* dKg;            // per-sequence gradients, gathered layout
+  const void* dVg;
+  void* dK;                   // gradient pools, the layout of K and V
+  void* dV;
+  const int* table;           // [B][pps] page indices (clamped into the pool)
+  const int* seqlens;         // [B] key counts (clamped into [0, tk_max])
+  int B, Hkv, pps, page_size, num_pages, tk_max;
+};
+// phase 0: gather K, V; phase 1: reduce dK, dV into the gradient pools.
+hipError_t launch_paged(const PagedBwdArgs& p, int dtype_bf16, int d, int phase, hipStream_t stream);
 
 // Launch a kernel of THREADS threads per workgroup on a 1-D grid and return
 // that launch's own status (the thread's sticky last-error state is neither

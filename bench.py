@@ -33,7 +33,7 @@ METRIC = "attention fwd+bwd TFLOP/s & % bf16 MFMA peak, d=128 T=4096 GQA causal"
 # MI355X dense matrix peaks (TFLOP/s): 256 CUs x 2.4 GHz x 4096 bf16 flop/clk/CU.
 PEAK = {"bf16": 2516.6, "fp32": 157.3}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["fa_common.h", "fa_kernels.h", "fa_fwd.hip", "fa_bwd.hip", "fa_dkdv.hip"]
+KERNEL_SOURCES = ["fa_common.h", "fa_kernels.h", "fa_fwd.hip", "fa_bwd.hip", "fa_dkdv.hip", "fa_paged.hip"]
 
 
 def kernel_source_hash() -> str:

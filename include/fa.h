@@ -262,6 +262,37 @@ int fa_fwd_paged(const void* Q, const void* K_pages, const void* V_pages, void* 
                  void* workspace, size_t workspace_bytes, int nsplit, void* stream);
 
 /*
+ * Backward of fa_fwd_paged ("The Autograd Memory Trap: Diagnosing a
+ * Backward-Pass OOM in Chunked Attention", sections "The Scene" and "The OOM:
+ * When Inference Lies": training differentiates through the gather of each
+ * block's prefix from the page pool).  The gradient of a page is the sum, over
+ * every table entry (b, slot) that points at it, of the gradients of the rows
+ * sequence b took from it: a page shared by several sequences collects all of
+ * them, the rows of a page past a sequence's key count contribute nothing, and
+ * pages no entry references come back as zeros.  dK_pages and dV_pages are
+ * written in full, with the layout of K_pages / V_pages; dQ is [B][Hq][Tq][d].
+ * O and L must come from fa_fwd_paged with the same table, key counts, causal
+ * flag, window and scale.  Sums run in fp32 in table order (b major, slot
+ * minor), so results are reproducible bit for bit.  Sizes, table, key counts
+ * and their clamping are those of fa_fwd_paged; d = dv in {64, 128} for bf16,
+ * {32, 64, 128} for fp32.
+ * Workspace: fa_bwd_paged_workspace_bytes bytes, 16-byte aligned, holding
+ * fa_bwd's workspace plus contiguous copies of each sequence's K, V, dK and dV
+ * ([B][Hkv][pages_per_seq * page_size][d] each, in the dtype); it returns 0 for
+ * invalid sizes.  The call reads K_pages and V_pages, writes dQ, dK_pages and
+ * dV_pages, and owns nothing after it returns.  Errors as fa_bwd and
+ * fa_fwd_paged (FA_ERR_BAD_SHAPE for a page size that is not a positive
+ * multiple of 128 or an empty pool).
+ */
+size_t fa_bwd_paged_workspace_bytes(int B, int Hq, int Hkv, int Tq, int pages_per_seq, int page_size, int d,
+                                    int dtype);
+int fa_bwd_paged(const void* Q, const void* K_pages, const void* V_pages, const void* O, const float* L,
+                 const void* dO, void* dQ, void* dK_pages, void* dV_pages, const int* page_table,
+                 const int* seqlens_k, int B, int Hq, int Hkv, int Tq, int pages_per_seq, int page_size,
+                 int num_pages, int d, int causal, int window, float scale, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/*
  * Boolean attention mask with grouped-query heads ("The Autograd Memory Trap:
  * Diagnosing a Backward-Pass OOM in Chunked Attention", section "The GQA
  * Expansion Question": a caller's boolean mask together with query heads that

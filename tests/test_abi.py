@@ -150,6 +150,30 @@ def test_fwd_paged_rejects_bad_arguments(lib, kw, status):
                             a["npages"], a["d"], 1, 0, 0.125, 1, None, 0, 1, None) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=100), 2), (dict(P=0), 2), (dict(pps=0), 2), (dict(npages=0), 2), (dict(table=None), 1),
+    (dict(seqlens=None), 1), (dict(table=FAKE + 2), 8), (dict(seqlens=FAKE + 1), 8), (dict(d=80), 4),
+    (dict(d=32), 4), (dict(ws=None), 7), (dict(wsb=4096), 7), (dict(ws=FAKE + 8), 8), (dict(Hkv=3), 3),
+])
+def test_bwd_paged_rejects_bad_arguments(lib, kw, status):
+    a = dict(table=FAKE, seqlens=FAKE, pps=4, P=128, npages=8, d=64, ws=FAKE, wsb=1 << 30, Hkv=1)
+    a.update(kw)
+    assert lib.fa_bwd_paged(*(FAKE,) * 9, a["table"], a["seqlens"], 2, 2, a["Hkv"], 16, a["pps"], a["P"],
+                            a["npages"], a["d"], 1, 0, 0.125, 1, a["ws"], a["wsb"], None) == status
+
+
+def test_bwd_paged_workspace_bytes(lib):
+    # fa_bwd's workspace, then gathered K, V and per-sequence dK, dV ([B][Hkv][pps * P][d] each)
+    B, Hq, Hkv, Tq, pps, P, d = 3, 8, 2, 33, 5, 128, 128
+    for code, esize in ((fa.FA_DTYPE_BF16, 2), (fa.FA_DTYPE_F32, 4)):
+        part = -(-B * Hkv * pps * P * d * esize // 256) * 256
+        base = lib.fa_bwd_workspace_bytes(B, Hq, Hkv, Tq, pps * P, d, code)
+        assert lib.fa_bwd_paged_workspace_bytes(B, Hq, Hkv, Tq, pps, P, d, code) == base + 4 * part
+    assert lib.fa_bwd_paged_workspace_bytes(B, Hq, Hkv, Tq, pps, 100, d, 1) == 0
+    assert lib.fa_bwd_paged_workspace_bytes(B, Hq, Hkv, Tq, 0, P, d, 1) == 0
+    assert lib.fa_bwd_paged_workspace_bytes(B, Hq, Hkv, Tq, pps, P, 80, 1) == 0
+
+
 def test_mask_row_words(lib):
     assert [lib.fa_mask_row_words(t) for t in (0, 1, 127, 128, 129, 1000)] == [0, 4, 4, 4, 8, 32]
     assert lib.fa_mask_row_words(-1) == -1
@@ -245,6 +269,8 @@ def _scale_calls(lib, s):
                                                    s, 1, None),
         "fa_bwd_mask": lambda: lib.fa_bwd_mask(*(FAKE,) * 10, W, FAKE, 0, 2, 4, 2, 16, 300, 64, 1, s, 1, None),
         "fa_bwd_noalloc": lambda: lib.fa_bwd_noalloc(*(FAKE,) * 9, 1, 2, 1, 16, 16, 64, 1, s, 1, None),
+        "fa_bwd_paged": lambda: lib.fa_bwd_paged(*(FAKE,) * 11, 2, 2, 1, 16, 4, 128, 8, 64, 1, 0, s, 1, FAKE, W,
+                                                 None),
     }
 
 

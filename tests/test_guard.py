@@ -8,7 +8,7 @@ words past the last row) would otherwise go unseen.  Shapes have ragged tails
 in both lengths so that the last row of every output sits in a partial tile.
 Covered: forward (plain, window, dv != d, fp32 d = 32), backward (same), the
 key-split forward and its merge (bf16, fp32 d = 64 and d = 32), variable-length
-forward and backward, paged forward (one pass and split), mask packing, masked
+forward and backward, paged forward (one pass and split) and backward, mask packing, masked
 forward (one pass and split) and masked backward (whose workspace holds the
 key-major mask copy).
 """
@@ -169,6 +169,31 @@ def test_paged_stays_in_bounds(fa, nsplit):
     o, lse = g.tensor("O", q.shape, torch.bfloat16), g.tensor("L", (B, Hq, Tq), torch.float32)
     fa.forward_paged(q, kp, vp, table, seqlens, True, nsplit=nsplit, workspace=ws, out=o, lse=lse)
     g.check(f"paged nsplit={nsplit}")
+
+
+@pytest.mark.parametrize("dtn,d", [("bf16", 128), ("fp32", 32)])
+def test_paged_backward_stays_in_bounds(fa, dtn, d):
+    import torch
+    t = torch.bfloat16 if dtn == "bf16" else torch.float32
+    code = fa.FA_DTYPE_BF16 if dtn == "bf16" else fa.FA_DTYPE_F32
+    B, Hq, Hkv, Tq, P = 3, 4, 2, 33, 128
+    lens = [0, 300, 513]
+    pps = max((n + P - 1) // P for n in lens)
+    num_pages = 3 * pps + 1
+    q, do = rnd((B, Hq, Tq, d), t, 15), rnd((B, Hq, Tq, d), t, 16)
+    kp, vp = rnd((num_pages, Hkv, P, d), t, 17), rnd((num_pages, Hkv, P, d), t, 18)
+    table = torch.tensor(np.random.default_rng(4).permutation(num_pages)[:B * pps].reshape(B, pps)
+                         .astype(np.int32)).cuda()
+    seqlens = torch.tensor(np.array(lens, dtype=np.int32)).cuda()
+    o, lse = fa.forward_paged(q, kp, vp, table, seqlens, True)
+    need = int(fa.load_library().fa_bwd_paged_workspace_bytes(B, Hq, Hkv, Tq, pps, P, d, code))
+    g = Guarded()
+    ws = g.workspace("paged backward workspace", need)
+    dq = g.tensor("dQ", q.shape, t)
+    dkp, dvp = g.tensor("dK pages", kp.shape, t), g.tensor("dV pages", vp.shape, t)
+    fa.backward_paged(q, kp, vp, o, lse, do, table, seqlens, True, workspace=ws, dq=dq, dk_pages=dkp,
+                      dv_pages=dvp)
+    g.check(f"paged backward {dtn} d={d}")
 
 
 @pytest.mark.parametrize("Tq,Tk", [(1, 1), (77, 129), (200, 333), (64, 128)])
