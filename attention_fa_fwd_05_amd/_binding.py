@@ -30,7 +30,7 @@ EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_window", "fa_bwd_window"
            "fa_fwd_splitk_workspace_bytes", "fa_fwd_varlen", "fa_bwd_varlen", "fa_fwd_paged",
            "fa_fwd_paged_workspace_bytes", "fa_bwd_paged", "fa_bwd_paged_workspace_bytes", "fa_bwd_workspace_bytes",
            "fa_mask_row_words", "fa_mask_pack", "fa_fwd_mask", "fa_bwd_mask", "fa_bwd_mask_workspace_bytes",
-           "fa_fwd_mask_splitk", "fa_fwd_mask_splitk_workspace_bytes",
+           "fa_fwd_mask_splitk", "fa_fwd_mask_splitk_workspace_bytes", "fa_fwd_varlen_mask", "fa_bwd_varlen_mask",
            "fa_bwd_noalloc", "fa_bwd_noalloc_scratch_bytes",
            "fa_status_string", "fa_hip_error_string", "fa_abi_version"]
 
@@ -102,14 +102,21 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_mask_row_words.restype = i
     lib.fa_mask_pack.argtypes = [vp, vp, ll, i, vp]
     lib.fa_mask_pack.restype = i
-    lib.fa_fwd_mask.argtypes = [vp, vp, vp, vp, vp, vp, ll, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_mask.argtypes = [vp, vp, vp, vp, vp, vp, ll, i, i, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_mask.restype = i
-    lib.fa_fwd_mask_splitk.argtypes = [vp, vp, vp, vp, vp, vp, ll, vp, sz, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_mask_splitk.argtypes = [vp, vp, vp, vp, vp, vp, ll, vp, sz, i, i, i, i, i, i, i, i, i, f, i, i,
+                                       vp]
     lib.fa_fwd_mask_splitk.restype = i
-    lib.fa_fwd_mask_splitk_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+    lib.fa_fwd_mask_splitk_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i]
     lib.fa_fwd_mask_splitk_workspace_bytes.restype = sz
-    lib.fa_bwd_mask.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ll, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_mask.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ll, i, i, i, i, i, i, i, i, i, f, i,
+                                vp]
     lib.fa_bwd_mask.restype = i
+    lib.fa_fwd_varlen_mask.argtypes = [vp, vp, vp, vp, vp, vp, ll, vp, vp, i, i, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_varlen_mask.restype = i
+    lib.fa_bwd_varlen_mask.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ll, vp, vp,
+                                       i, i, i, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_bwd_varlen_mask.restype = i
     lib.fa_bwd_mask_workspace_bytes.argtypes = [i, i, i, i, i, i, i, ll]
     lib.fa_bwd_mask_workspace_bytes.restype = sz
     lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
@@ -335,6 +342,61 @@ def backward_varlen(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     return dq, dk, dv
 
 
+def _varlen_mask_bits(lib, mask, q, B, max_q, max_k):
+    """(packed int32 bits, per-sequence stride in words) of a varlen mask: bool/uint8 or packed
+    int32, [max_q, max_k] (shared) or [B, max_q, max_k]."""
+    return _mask_bits(lib, mask, q, B, max_q, max_k)
+
+
+def forward_varlen_masked(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, mask,
+                          causal: bool = False, scale: float | None = None, window: int = 0, out=None,
+                          lse=None):
+    """fa_fwd_varlen_mask: forward_varlen under a boolean mask per sequence (``mask`` [max_q, max_k]
+    for every sequence or [B, max_q, max_k], indexed by each sequence's own positions)."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, total_q, total_k, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    bits, stride = _varlen_mask_bits(lib, mask, q, B, int(max_seqlen_q), int(max_seqlen_k))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if _out(out, "out", q.shape, q) is None else out
+    L = _out(lse, "lse", (Hq, total_q), q, torch.float32)
+    L = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if L is None else L
+    st = lib.fa_fwd_varlen_mask(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(bits), stride,
+                                cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q, total_k,
+                                int(max_seqlen_q), int(max_seqlen_k), d, int(bool(causal)), int(window), scale,
+                                _dtype_code(q), _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_fwd_varlen_mask")
+    return o, L
+
+
+def backward_varlen_masked(q, k, v, o, lse, do, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                           mask, causal: bool = False, scale: float | None = None, window: int = 0,
+                           workspace=None, dq=None, dk=None, dv=None):
+    """fa_bwd_varlen_mask: the backward of forward_varlen_masked; returns (dq, dk, dv)."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, total_q, total_k, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    _out(o, "o", q.shape, q)
+    _out(do, "do", q.shape, q)
+    _out(lse, "lse", (Hq, total_q), q, torch.float32)
+    bits, stride = _varlen_mask_bits(lib, mask, q, B, int(max_seqlen_q), int(max_seqlen_k))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    need = int(lib.fa_bwd_mask_workspace_bytes(B, Hq, Hkv, int(max_seqlen_q), int(max_seqlen_k), d, code, stride))
+    ws = _ws(workspace, need, q)
+    dq = torch.empty_like(q) if _out(dq, "dq", q.shape, q) is None else dq
+    dk = torch.empty_like(k) if _out(dk, "dk", k.shape, q) is None else dk
+    dv = torch.empty_like(v) if _out(dv, "dv", v.shape, q) is None else dv
+    st = lib.fa_bwd_varlen_mask(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                _ptr(dv), ws.data_ptr(), _nbytes(ws), _ptr(bits), stride, cu_seqlens_q.data_ptr(),
+                                cu_seqlens_k.data_ptr(), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q),
+                                int(max_seqlen_k), d, int(bool(causal)), int(window), scale, code, _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_bwd_varlen_mask")
+    return dq, dk, dv
+
+
 def _paged_shapes(q, k_pages, v_pages, page_table, seqlens_k):
     import torch
     if q.dim() != 4 or k_pages.dim() != 4 or tuple(v_pages.shape) != tuple(k_pages.shape):
@@ -447,13 +509,15 @@ def _mask_bits(lib, mask, q, B, Tq, Tk):
 
 
 def backward_masked(q, k, v, o, lse, do, mask, causal: bool = False, scale: float | None = None,
-                    workspace=None, dq=None, dk=None, dv=None):
-    """fa_bwd_mask: gradients under the boolean mask of forward_masked; returns (dq, dk, dv)."""
+                    workspace=None, dq=None, dk=None, dv=None, window: int = 0):
+    """fa_bwd_mask: gradients under the boolean mask (and window) of forward_masked; returns
+    (dq, dk, dv)."""
     import torch
     lib = load_library()
-    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v, same_dv=True)
-    _out(o, "o", q.shape, q)
-    _out(do, "do", q.shape, q)
+    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
+    dvh = v.shape[3]
+    _out(o, "o", (B, Hq, Tq, dvh), q)
+    _out(do, "do", (B, Hq, Tq, dvh), q)
     _out(lse, "lse", (B, Hq, Tq), q, torch.float32)
     bits, stride = _mask_bits(lib, mask, q, B, Tq, Tk)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -464,42 +528,43 @@ def backward_masked(q, k, v, o, lse, do, mask, causal: bool = False, scale: floa
     dk = torch.empty_like(k) if _out(dk, "dk", k.shape, q) is None else dk
     dv = torch.empty_like(v) if _out(dv, "dv", v.shape, q) is None else dv
     st = lib.fa_bwd_mask(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
-                         ws.data_ptr(), _nbytes(ws), _ptr(bits), stride, B, Hq, Hkv, Tq, Tk, d, int(bool(causal)),
-                         scale, code, _stream(q))
+                         ws.data_ptr(), _nbytes(ws), _ptr(bits), stride, B, Hq, Hkv, Tq, Tk, d, dvh,
+                         int(bool(causal)), int(window), scale, code, _stream(q))
     if st != 0:
         raise FaError(st, "fa_bwd_mask")
     return dq, dk, dv
 
 
 def forward_masked(q, k, v, mask, causal: bool = False, scale: float | None = None, out=None, lse=None,
-                   nsplit: int = 1, workspace=None):
+                   nsplit: int = 1, workspace=None, window: int = 0):
     """fa_fwd_mask (nsplit == 1) or fa_fwd_mask_splitk: attention under a boolean mask shared by
-    all heads of a batch entry.
+    all heads of a batch entry (with the causal bound and a sliding window if given).
 
     ``mask``: bool/uint8 [Tq, Tk] (whole batch) or [B, Tq, Tk] (or [B, 1, Tq, Tk]), packed here
     with fa_mask_pack; or an already packed int32 [..., Tq, fa_mask_row_words(Tk)].
-    Returns (o like q, lse float32 [B, Hq, Tq])."""
+    Returns (o [B, Hq, Tq, dv], lse float32 [B, Hq, Tq])."""
     import torch
     lib = load_library()
-    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v, same_dv=True)
+    B, Hq, Hkv, Tq, Tk, d = _shapes(q, k, v)
+    dvh = v.shape[3]
     bits, stride = _mask_bits(lib, mask, q, B, Tq, Tk)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
-    o = _out(out, "out", q.shape, q)
-    o = torch.empty_like(q) if o is None else o
+    o = _out(out, "out", (B, Hq, Tq, dvh), q)
+    o = torch.empty((B, Hq, Tq, dvh), dtype=q.dtype, device=q.device) if o is None else o
     L = _out(lse, "lse", (B, Hq, Tq), q, torch.float32)
     L = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if L is None else L
     if nsplit == 1:
         st = lib.fa_fwd_mask(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(bits), stride, B, Hq, Hkv, Tq, Tk,
-                             d, int(bool(causal)), scale, code, _stream(q))
+                             d, dvh, int(bool(causal)), int(window), scale, code, _stream(q))
         if st != 0:
             raise FaError(st, "fa_fwd_mask")
         return o, L
-    need = int(lib.fa_fwd_mask_splitk_workspace_bytes(B, Hq, Hkv, Tq, Tk, d, code, int(nsplit)))
+    need = int(lib.fa_fwd_mask_splitk_workspace_bytes(B, Hq, Hkv, Tq, Tk, d, dvh, code, int(nsplit)))
     ws = _ws(workspace, need, q)
     st = lib.fa_fwd_mask_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), _ptr(bits), stride, ws.data_ptr(),
-                                ws.numel(), B, Hq, Hkv, Tq, Tk, d, int(bool(causal)), scale, code, int(nsplit),
-                                _stream(q))
+                                _nbytes(ws), B, Hq, Hkv, Tq, Tk, d, dvh, int(bool(causal)), int(window), scale,
+                                code, int(nsplit), _stream(q))
     if st != 0:
         raise FaError(st, "fa_fwd_mask_splitk")
     return o, L
@@ -579,13 +644,9 @@ def _autograd_function():
             if mask is None:
                 o, lse = forward(q, k, v, causal, scale, window=window)
             else:
-                if window:
-                    raise ValueError("a boolean mask does not combine with a window")
-                if v.shape[-1] != q.shape[-1]:
-                    raise ValueError("a boolean mask needs v's head dim equal to q's")
                 if mask.dtype != torch.int32:
                     mask = pack_mask(mask.contiguous(), k.shape[2])
-                o, lse = forward_masked(q, k, v, mask, causal, scale)
+                o, lse = forward_masked(q, k, v, mask, causal, scale, window=window)
             ctx.save_for_backward(q, k, v, o, lse)
             ctx.causal, ctx.scale, ctx.window, ctx.mask = causal, scale, window, mask
             return o
@@ -597,7 +658,8 @@ def _autograd_function():
                 dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), ctx.causal, ctx.scale,
                                       window=ctx.window)
             else:
-                dq, dk, dv = backward_masked(q, k, v, o, lse, do.contiguous(), ctx.mask, ctx.causal, ctx.scale)
+                dq, dk, dv = backward_masked(q, k, v, o, lse, do.contiguous(), ctx.mask, ctx.causal, ctx.scale,
+                                             window=ctx.window)
             return dq, dk, dv, None, None, None, None
 
     return FlashAttention

@@ -316,7 +316,7 @@ int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, c
                   d, d, causal, 0, scale, dtype, FA_BWD_STAGE_ALL, stream);
 }
 
-int fa_abi_version(void) { return (1 << 16) | 4; }
+int fa_abi_version(void) { return (2 << 16) | 0; }
 
 const char* fa_hip_error_string(void) { return t_hip_error; }
 
@@ -420,59 +420,96 @@ int fa_mask_pack(const void* mask_bytes, uint32_t* mask_bits, long long rows, in
 }
 
 int fa_fwd_mask(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
-                long long mask_batch_stride, int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal,
-                float scale, int dtype, void* stream) {
-  return fa_fwd_mask_splitk(Q, K, V, O, L, mask_bits, mask_batch_stride, nullptr, 0, B, Hq, Hkv, Tq, Tk, d, causal,
-                            scale, dtype, 1, stream);
+                long long mask_batch_stride, int B, int Hq, int Hkv, int Tq, int Tk, int d, int dv, int causal,
+                int window, float scale, int dtype, void* stream) {
+  return fa_fwd_mask_splitk(Q, K, V, O, L, mask_bits, mask_batch_stride, nullptr, 0, B, Hq, Hkv, Tq, Tk, d, dv,
+                            causal, window, scale, dtype, 1, stream);
 }
 
-size_t fa_fwd_mask_splitk_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int nsplit) {
-  if (check_common(B, Hq, Hkv, Tq, Tk, d, dtype) != FA_OK) return 0;
+size_t fa_fwd_mask_splitk_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dv, int dtype,
+                                          int nsplit) {
+  if (check_common(B, Hq, Hkv, Tq, Tk, d, dtype) != FA_OK || check_dv(d, dv, dtype) != FA_OK) return 0;
   const int ns = mask_splits(B, Hq, Hkv, Tq, Tk, d, dtype, nsplit);
   if (ns > kMaxSplits) return 0;
-  return ns == 1 ? 0 : splitk_ws_bytes(B, Hq, Tq, d, ns);
+  return ns == 1 ? 0 : splitk_ws_bytes(B, Hq, Tq, dv, ns);
 }
 
-int fa_fwd_mask_splitk(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
-                       long long mask_batch_stride, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
-                       int Tq, int Tk, int d, int causal, float scale, int dtype, int nsplit, void* stream) {
+namespace {
+
+// The masked forward for the fixed layout (cu_q == nullptr; Tq, Tk) or a
+// variable-length batch (offsets; Tq, Tk the longest sequences).  Runs the
+// plain shape (its packing only), split over ns key slices when ns > 1.
+int fwd_mask_core(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
+                  long long mask_batch_stride, const int* cu_q, const int* cu_k, int B, int Hq, int Hkv,
+                  int total_q, int total_k, int Tq, int Tk, int d, int dv, int causal, int window, float scale,
+                  int dtype, void* workspace, size_t workspace_bytes, int nsplit, void* stream) {
   int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
   if (st != FA_OK) return st;
-  const long long nq = (long long)B * Hq * Tq * d, nkv = (long long)B * Hkv * Tk * d;
-  if ((st = check_ptr(Q, nq)) || (st = check_ptr(O, nq)) || (st = check_ptr(K, nkv)) ||
-      (st = check_ptr(V, nkv)) || (st = check_ptr(L, (long long)B * Hq * Tq)))
+  if ((st = check_dv(d, dv, dtype)) != FA_OK) return st;
+  const bool varlen = cu_q != nullptr;
+  const long long rows = varlen ? (long long)Hq * total_q : (long long)B * Hq * Tq;
+  const long long krows = varlen ? (long long)Hkv * total_k : (long long)B * Hkv * Tk;
+  if (rows * d > kMaxElems || rows * dv > kMaxElems || krows * d > kMaxElems || krows * dv > kMaxElems)
+    return FA_ERR_TOO_LARGE;
+  if ((st = check_ptr(Q, rows * d)) || (st = check_ptr(O, rows * dv)) || (st = check_ptr(K, krows * d)) ||
+      (st = check_ptr(V, krows * dv)) || (st = check_ptr(L, rows)))
     return st;
   const long long rw = fa_mask_row_words(Tk);
   if ((st = check_mask(mask_bits, mask_batch_stride, B, Tq, Tk))) return st;
   if (bad_scale(scale)) return FA_ERR_SCALE;
-  const int ns = mask_splits(B, Hq, Hkv, Tq, Tk, d, dtype, nsplit);
+  const int ns = varlen ? 1 : mask_splits(B, Hq, Hkv, Tq, Tk, d, dtype, nsplit);
   if (ns > kMaxSplits) return FA_ERR_TOO_LARGE;
-  const size_t need = ns == 1 ? 0 : splitk_ws_bytes(B, Hq, Tq, d, ns);
+  const size_t need = ns == 1 ? 0 : splitk_ws_bytes(B, Hq, Tq, dv, ns);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (misaligned(workspace)) return FA_ERR_ALIGNMENT;
   }
-  if (Tq == 0) return FA_OK;
+  if (Tq == 0 || rows == 0) return FA_OK;
   fa::FwdArgs a;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Tq = Tq; a.Tk = Tk;
-  a.window = 0;
+  a.window = window > 0 ? window : 0;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   const int G = Hq / Hkv, nw = fa::fwd_waves(dtype == FA_DTYPE_BF16, d);
   a.pack = (G <= nw && Tq <= 32 * (nw / G)) ? 1 : 0;   // the plain shape's packing only
   a.Opart = nullptr;
   a.Lpart = nullptr;
-  a.cu_q = a.cu_k = nullptr;
-  a.total_q = a.total_k = 0;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.total_q = varlen ? total_q : 0;
+  a.total_k = varlen ? total_k : 0;
   a.mask = Tk > 0 ? mask_bits : nullptr;
   a.mask_bstride = mask_batch_stride;
   a.mask_row_words = (int)rw;
   if (ns > 1) {
     char* wsb = static_cast<char*>(workspace);
     a.Opart = reinterpret_cast<float*>(wsb);
-    a.Lpart = reinterpret_cast<float*>(wsb + align_up((size_t)ns * B * Hq * Tq * d * 4));
+    a.Lpart = reinterpret_cast<float*>(wsb + align_up((size_t)ns * B * Hq * Tq * dv * 4));
   }
-  return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream, ns));
+  return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream, ns, dv));
+}
+
+}  // namespace
+
+int fa_fwd_mask_splitk(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
+                       long long mask_batch_stride, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                       int Tq, int Tk, int d, int dv, int causal, int window, float scale, int dtype, int nsplit,
+                       void* stream) {
+  return fwd_mask_core(Q, K, V, O, L, mask_bits, mask_batch_stride, nullptr, nullptr, B, Hq, Hkv, 0, 0, Tq, Tk, d,
+                       dv, causal, window, scale, dtype, workspace, workspace_bytes, nsplit, stream);
+}
+
+int fa_fwd_varlen_mask(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
+                       long long mask_seq_stride, const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq,
+                       int Hkv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d, int causal,
+                       int window, float scale, int dtype, void* stream) {
+  int st = check_common(B, Hq, Hkv, max_seqlen_q, max_seqlen_k, d, dtype);
+  if (st != FA_OK) return st;
+  if ((st = check_varlen(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max_seqlen_k)) != FA_OK)
+    return st;
+  return fwd_mask_core(Q, K, V, O, L, mask_bits, mask_seq_stride, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q,
+                       total_k, max_seqlen_q, max_seqlen_k, d, d, causal, window, scale, dtype, nullptr, 0, 1,
+                       stream);
 }
 
 size_t fa_bwd_mask_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype,
@@ -483,13 +520,30 @@ size_t fa_bwd_mask_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d
 
 int fa_bwd_mask(const void* Q, const void* K, const void* V, const void* O, const float* L, const void* dO,
                 void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, const uint32_t* mask_bits,
-                long long mask_batch_stride, int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal,
-                float scale, int dtype, void* stream) {
+                long long mask_batch_stride, int B, int Hq, int Hkv, int Tq, int Tk, int d, int dv, int causal,
+                int window, float scale, int dtype, void* stream) {
   int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
   if (st != FA_OK) return st;
+  if ((st = check_dv(d, dv, dtype)) != FA_OK) return st;
   if ((st = check_mask(mask_bits, mask_batch_stride, B, Tq, Tk))) return st;
   return bwd_core(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, nullptr, nullptr, B, Hq, Hkv, 0, 0,
-                  Tq, Tk, d, d, causal, 0, scale, dtype, FA_BWD_STAGE_ALL, stream, mask_bits, mask_batch_stride);
+                  Tq, Tk, d, dv, causal, window, scale, dtype, FA_BWD_STAGE_ALL, stream, mask_bits,
+                  mask_batch_stride);
+}
+
+int fa_bwd_varlen_mask(const void* Q, const void* K, const void* V, const void* O, const float* L, const void* dO,
+                       void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                       const uint32_t* mask_bits, long long mask_seq_stride, const int* cu_seqlens_q,
+                       const int* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                       int max_seqlen_k, int d, int causal, int window, float scale, int dtype, void* stream) {
+  int st = check_common(B, Hq, Hkv, max_seqlen_q, max_seqlen_k, d, dtype);
+  if (st != FA_OK) return st;
+  if ((st = check_varlen(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max_seqlen_k)) != FA_OK)
+    return st;
+  if ((st = check_mask(mask_bits, mask_seq_stride, B, max_seqlen_q, max_seqlen_k))) return st;
+  return bwd_core(Q, K, V, O, L, dO, dQ, dK, dV, workspace, workspace_bytes, cu_seqlens_q, cu_seqlens_k, B, Hq,
+                  Hkv, total_q, total_k, max_seqlen_q, max_seqlen_k, d, d, causal, window, scale, dtype,
+                  FA_BWD_STAGE_ALL, stream, mask_bits, mask_seq_stride);
 }
 
 size_t fa_fwd_splitk_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int nsplit) {

@@ -157,7 +157,6 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   static_assert(NPA >= 12 && NDH >= 8, "room for the vector stages");
   static_assert(NB == 2 || 2 * (DmaRows<T, D, BQ, 256>::PER + DmaRows<T, DV, BQ, 256>::PER + 1) <= NPA,
                 "loads fit in phase 1b");
-  static_assert(!MASK || (!WIN && D == DV), "the masked backward uses the plain shape");
   __shared__ __attribute__((aligned(16))) float sL[NB][64];
   __shared__ __attribute__((aligned(16))) float sD[NB][64];    // -D
   __shared__ __attribute__((aligned(16))) T sQ[NB][BQ * D];
@@ -637,7 +636,6 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   // Boolean mask: this wave's rows' bits of a key tile (query-major), two
   // words per row; lane l loads word l % 2 of row qw + l / 2 (rows past Tq
   // read the last row; their results are never stored).
-  static_assert(!MASK || (!WIN && D == DV), "the masked backward uses the plain shape");
   uint32_t* sM = nullptr;
   if constexpr (MASK) sM = mask_lds<NBUF * NW * 64>();
   auto issue = [&](int k0, int buf) {
@@ -841,25 +839,26 @@ hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   const long long qblocks = (long long)((a.Tq + 32 * NW - 1) / (32 * NW)) * a.B * a.Hq;
   // bf16: the dK/dV pass on wave pairs (fa_dkdv.hip).
   constexpr bool kPair = sizeof(T) == 2;
-  if constexpr (DV == D) {
-    // A boolean mask: its key-major copy, then the masked passes.
-    if (a.mask != nullptr) {
-      if ((stages & kStageDkDv) && kblocks > 0) {
-        const long long entries = a.mask_bstride != 0 ? a.B : 1;
-        const long long words = entries * a.Tk * a.mask_t_row_words;
-        hipError_t e = launch(mask_transpose_kernel, (words + 255) / 256, stream, a, entries);
-        if (e == hipSuccess) {
-          if constexpr (kPair) e = launch_dkdv_pair(a, D, DV, CAUSAL, stream);
-          else e = launch(dkdv_kernel<T, D, CAUSAL, false, D, true>, kblocks, stream, a);
-        }
-        if (e != hipSuccess) return e;
+  // A boolean mask: its key-major copy, then the masked passes (with or
+  // without a window).
+  if (a.mask != nullptr) {
+    if ((stages & kStageDkDv) && kblocks > 0) {
+      const long long entries = a.mask_bstride != 0 ? a.B : 1;
+      const long long words = entries * a.Tk * a.mask_t_row_words;
+      hipError_t e = launch(mask_transpose_kernel, (words + 255) / 256, stream, a, entries);
+      if (e == hipSuccess) {
+        if constexpr (kPair) e = launch_dkdv_pair(a, D, DV, CAUSAL, stream);
+        else e = a.window > 0 ? launch(dkdv_kernel<T, D, CAUSAL, true, DV, true>, kblocks, stream, a)
+                              : launch(dkdv_kernel<T, D, CAUSAL, false, DV, true>, kblocks, stream, a);
       }
-      if ((stages & kStageDq) && qblocks > 0) {
-        hipError_t e = launch<64 * NW>(dq_kernel<T, D, CAUSAL, false, D, true>, qblocks, stream, a);
-        if (e != hipSuccess) return e;
-      }
-      return hipSuccess;
+      if (e != hipSuccess) return e;
     }
+    if ((stages & kStageDq) && qblocks > 0) {
+      hipError_t e = a.window > 0 ? launch<64 * NW>(dq_kernel<T, D, CAUSAL, true, DV, true>, qblocks, stream, a)
+                                  : launch<64 * NW>(dq_kernel<T, D, CAUSAL, false, DV, true>, qblocks, stream, a);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   if ((stages & kStageDkDv) && kblocks > 0) {
     hipError_t e;

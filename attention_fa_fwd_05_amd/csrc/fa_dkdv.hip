@@ -159,7 +159,11 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < NPC; ++j) piece(b, j);
   };
-  static_assert(2 * NPC <= 2 * NSD && 2 * NPC <= 2 * NSDV, "pieces fit in a phase at every other product");
+  // Pieces go out at every other product of a phase when they fit, else at
+  // every product (a mask word with d != dv).
+  static_assert(NPC <= 2 * NSD && NPC <= 2 * NSDV, "pieces fit in a phase");
+  constexpr int SPS = 2 * NPC <= 2 * NSD ? 2 : 1;   // spacing in the S phase (2 NSD products)
+  constexpr int SPP = 2 * NPC <= 2 * NSDV ? 2 : 1;  // ... in the dP phase (2 NSDV products)
 
   // Direct-load instructions this wave issues per block, so that the wait at
   // the end of block i leaves block i + 2's loads in flight.
@@ -264,7 +268,7 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
             [&](int m) { return XorFetch<D>::nat(qb + xf.nat0, m / NSD, m % NSD); },
             [&](int m, const Op& x) { sacc[m / NSD] = M::mma(x, kop[m % NSD], sacc[m / NSD]); },
             [&](int m) {
-              if (m % 2 == 1 && m / 2 < NPC && load) piece(nsrc, m / 2);
+              if (m % SPS == SPS - 1 && m / SPS < NPC && load) piece(nsrc, m / SPS);
               const int k = m - (2 * NSD - 5);      // 4 pieces over the last 4 products
               if (k >= 0 && k < 4) exp_piece(0, k);
             });
@@ -363,7 +367,7 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
             [&](int m) { return XorFetch<DV>::nat(ob + xfv.nat0, m & 1, m >> 1); },
             [&](int m, const Op& x) { dpacc[m & 1] = M::mma(x, vop[m >> 1], dpacc[m & 1]); },
             [&](int m) {
-              if (m % 2 == 1 && m / 2 < NPC && load) piece(nsrc, m / 2);
+              if (m % SPP == SPP - 1 && m / SPP < NPC && load) piece(nsrc, m / SPP);
             });
       }
       wave_prio<0>();
@@ -385,10 +389,9 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
 
 template <int D, int DV, bool CAUSAL>
 hipError_t launch_dkdv_pair_t(const BwdArgs& a, long long blocks, hipStream_t stream) {
-  if (a.mask != nullptr) {
-    if constexpr (D == DV) return launch<512>(dkdv_pair_kernel<D, DV, CAUSAL, false, true>, blocks, stream, a);
-    return hipErrorInvalidValue;
-  }
+  if (a.mask != nullptr)
+    return a.window > 0 ? launch<512>(dkdv_pair_kernel<D, DV, CAUSAL, true, true>, blocks, stream, a)
+                        : launch<512>(dkdv_pair_kernel<D, DV, CAUSAL, false, true>, blocks, stream, a);
   if (a.window > 0) return launch<512>(dkdv_pair_kernel<D, DV, CAUSAL, true, false>, blocks, stream, a);
   return launch<512>(dkdv_pair_kernel<D, DV, CAUSAL, false, false>, blocks, stream, a);
 }

@@ -188,7 +188,7 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
   // Boolean mask: this lane's row of bits (query qw + n; rows past Tq read
   // the last row and are never stored), one word per 32-key sub-tile, loaded
   // a tile ahead into registers.
-  static_assert(!MASK || (QT == 1 && !WIN && !DEC), "the masked forward uses the plain shape");
+  static_assert(!MASK || (QT == 1 && !DEC), "the masked forward uses the plain shape");
   typedef uint32_t MaskWords __attribute__((ext_vector_type(NKT)));
   const uint32_t* mrow = nullptr;
   MaskWords mcur{}, mnext{};
@@ -426,13 +426,13 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream, int nsplit) {
   if (blocks == 0) return hipSuccess;
   hipError_t e = hipSuccess;
   bool launched = false;
-  // A boolean mask: the plain shape (any packing fits it: packed rows of the
-  // decode shape fit its waves too); no window, split or paging.
-  if constexpr (DV == D) {
-    if (a.mask != nullptr) {
-      e = launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, false, false, D, true>, blocks, nsplit, stream, a);
-      launched = true;
-    }
+  // A boolean mask: the plain shape (its packing only), with or without a
+  // window, split or not; no paging.
+  if (a.mask != nullptr) {
+    e = a.window > 0
+            ? launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, true, false, DV, true>, blocks, nsplit, stream, a)
+            : launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, false, false, DV, true>, blocks, nsplit, stream, a);
+    launched = true;
   }
   if constexpr (sizeof(T) == 2) {
     if (!launched && a.pack == 2) {

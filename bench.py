@@ -329,8 +329,10 @@ def main() -> int:
     peak = PEAK[w.dtype]
     # Each kernel's own matrix work per visible (query, key) pair: forward 4d
     # (S, PV), dK/dV pass 8d (S, dP, dV, dK), dQ pass 6d (S, dP, dQ).
+    # bf16 runs the dK/dV pass on wave pairs (dkdv_pair_kernel), fp32 on dkdv_kernel.
     kf = accounting.kernel_flops(w.B, w.Hq, w.Tq, w.Tk, w.d, w.causal, w.window)
-    kernels = {"fwd_kernel": (kf["fwd_kernel"], ms_fwd), "dkdv_kernel": (kf["dkdv_kernel"], ms_dkdv),
+    dkdv_name = "dkdv_pair_kernel" if w.dtype == "bf16" else "dkdv_kernel"
+    kernels = {"fwd_kernel": (kf["fwd_kernel"], ms_fwd), dkdv_name: (kf["dkdv_kernel"], ms_dkdv),
                "dq_kernel": (kf["dq_kernel"], ms_dq)}
     dom = max(kernels, key=lambda n: kernels[n][1])
     dom_flops, dom_ms = kernels[dom]
@@ -360,9 +362,11 @@ def main() -> int:
                      "traffic": stored_traffic(w.name, dom),
                      "flops_per_launch": dom_flops, "avg_launch_ms": round(dom_ms, 4)},
         "breakdown_ms": {"fwd_kernel": round(ms_fwd, 4), "bwd_pre_kernel": round(ms_pre, 4),
-                         "dkdv_kernel": round(ms_dkdv, 4), "dq_kernel": round(ms_dq, 4)},
+                         dkdv_name: round(ms_dkdv, 4), "dq_kernel": round(ms_dq, 4)},
         "fwd_tflops": round(f_fwd / (ms_fwd * 1e-3) / 1e12, 2),
         "bwd_tflops": round(f_bwd / ((ms_pre + ms_dkdv + ms_dq) * 1e-3) / 1e12, 2),
+        "fwd_pct_peak": round(100.0 * f_fwd / (ms_fwd * 1e-3) / 1e12 / peak, 2),
+        "bwd_pct_peak": round(100.0 * f_bwd / ((ms_pre + ms_dkdv + ms_dq) * 1e-3) / 1e12 / peak, 2),
         "retained_bytes": {"recompute_qkvoL": ret, "dense_qkv_plus_P": dense,
                            "ratio": round(dense / ret, 2)},
         "workspace_bytes": ws.numel(),

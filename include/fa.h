@@ -314,11 +314,17 @@ int fa_bwd_paged(const void* Q, const void* K_pages, const void* V_pages, const 
  * sizes, FA_ERR_NULL_PTR / FA_ERR_ALIGNMENT for the buffers, FA_ERR_TOO_LARGE,
  * FA_ERR_HIP.
  *
- * fa_fwd_mask computes fa_fwd's O and L where key j is visible to query i
- * iff its mask bit is set, j < Tk and, if causal, j <= i + Tk - Tq.  Rows
- * without a visible key get O = 0 and L = -inf.  d = dv in {64, 128}, both
- * dtypes; no window.  The mask must be 16-byte aligned (it may be NULL only
- * when Tq * fa_mask_row_words(Tk) == 0).  Errors as fa_fwd, plus
+ * fa_fwd_mask computes fa_fwd_dv's O and L where key j is visible to query i
+ * iff its mask bit is set, j < Tk, if causal j <= i + Tk - Tq, and with a
+ * window (window > 0) j > i + Tk - Tq - window: the mask narrows the causal
+ * bound and the sliding window of fa_fwd_window (the drafter of "The Autograd
+ * Memory Trap...", sections "The GQA Expansion Question" and "Assumptions and
+ * Uncertainties", has full layers under a block mask and sliding-window
+ * layers).  Rows without a
+ * visible key get O = 0 and L = -inf.  Head dims as fa_fwd_dv: d = dv in
+ * {64, 128} (fp32 also 32), and for bf16 (d, dv) = (128, 64) or (64, 128);
+ * V and O are dv wide.  The mask must be 16-byte aligned (it may be NULL only
+ * when Tq * fa_mask_row_words(Tk) == 0).  Errors as fa_fwd_dv, plus
  * FA_ERR_BAD_SHAPE for a mask_batch_stride that is negative or between 0 and
  * Tq * fa_mask_row_words(Tk), FA_ERR_ALIGNMENT for one that is not a multiple
  * of 4.  With a nonzero stride the mask holds B such entries.
@@ -326,37 +332,68 @@ int fa_bwd_paged(const void* Q, const void* K_pages, const void* V_pages, const 
 int fa_mask_row_words(int Tk);
 int fa_mask_pack(const void* mask_bytes, uint32_t* mask_bits, long long rows, int Tk, void* stream);
 int fa_fwd_mask(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
-                long long mask_batch_stride, int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal,
-                float scale, int dtype, void* stream);
+                long long mask_batch_stride, int B, int Hq, int Hkv, int Tq, int Tk, int d, int dv, int causal,
+                int window, float scale, int dtype, void* stream);
 
 /*
  * fa_fwd_mask with the keys split over slices and merged as in fa_fwd_splitk
  * ("The Autograd Memory Trap...", section "The Scene": blocks of few new
  * positions against a long prefix, here under a mask).  nsplit == 1 is
  * fa_fwd_mask (no workspace); nsplit <= 0 picks the count; otherwise the
- * workspace holds fa_fwd_mask_splitk_workspace_bytes bytes of fp32 partials.
- * Errors as fa_fwd_mask and fa_fwd_splitk.
+ * workspace holds fa_fwd_mask_splitk_workspace_bytes bytes of fp32 partials
+ * (dv wide).  Errors as fa_fwd_mask and fa_fwd_splitk; the workspace size
+ * function returns 0 for invalid sizes.
  */
-size_t fa_fwd_mask_splitk_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int nsplit);
+size_t fa_fwd_mask_splitk_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dv, int dtype,
+                                          int nsplit);
 int fa_fwd_mask_splitk(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
                        long long mask_batch_stride, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
-                       int Tq, int Tk, int d, int causal, float scale, int dtype, int nsplit, void* stream);
+                       int Tq, int Tk, int d, int dv, int causal, int window, float scale, int dtype, int nsplit,
+                       void* stream);
 
 /*
  * The backward under the same mask (bits and stride as for fa_fwd_mask):
- * fa_bwd's dQ, dK, dV where P is 0 on the pairs the mask hides.  O and L must
- * come from fa_fwd_mask with the same mask.  The workspace is
+ * fa_bwd_dv's dQ, dK, dV where P is 0 on the pairs the mask, the causal bound
+ * and the window hide.  O and L must come from fa_fwd_mask with the same
+ * mask, causal flag and window.  Head dims as fa_fwd_mask.  The workspace is
  * fa_bwd_mask_workspace_bytes: fa_bwd's plus a key-major copy of the mask
  * (4 * ceil(Tq / 128) words per key and entry) that the call writes before
- * its dK/dV pass.  Errors as fa_bwd, plus the mask errors of fa_fwd_mask.
+ * its dK/dV pass.  Errors as fa_bwd_dv, plus the mask errors of fa_fwd_mask.
  * fa_bwd_mask_workspace_bytes returns 0 for invalid sizes.
  */
 size_t fa_bwd_mask_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype,
                                    long long mask_batch_stride);
 int fa_bwd_mask(const void* Q, const void* K, const void* V, const void* O, const float* L, const void* dO,
                 void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes, const uint32_t* mask_bits,
-                long long mask_batch_stride, int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal,
-                float scale, int dtype, void* stream);
+                long long mask_batch_stride, int B, int Hq, int Hkv, int Tq, int Tk, int d, int dv, int causal,
+                int window, float scale, int dtype, void* stream);
+
+/*
+ * A boolean mask over a variable-length batch ("The Autograd Memory Trap...",
+ * sections "The Scene" and "The GQA Expansion Question": blocks of new
+ * positions with prefixes of their own lengths, under a caller's mask).
+ * Layout and offsets as fa_fwd_varlen / fa_bwd_varlen (packed head-major, d =
+ * dv, causal alignment and window per sequence).  The mask of sequence b is a
+ * [max_seqlen_q][fa_mask_row_words(max_seqlen_k)] array of words at
+ * mask_bits + b * mask_seq_stride, indexed by the sequence's own query and key
+ * positions (bit j % 32 of word i * row_words + j / 32 for query i, key j of
+ * the sequence); rows and bits past the sequence's lengths are ignored.
+ * mask_seq_stride is 0 (one mask for every sequence) or at least
+ * max_seqlen_q * fa_mask_row_words(max_seqlen_k) and a multiple of 4.  The
+ * backward's workspace is fa_bwd_mask_workspace_bytes(B, Hq, Hkv,
+ * max_seqlen_q, max_seqlen_k, d, dtype, mask_seq_stride).  No key split.
+ * Errors as fa_fwd_varlen / fa_bwd_varlen plus the mask errors of fa_fwd_mask
+ * (with max_seqlen_q, max_seqlen_k in place of Tq, Tk).
+ */
+int fa_fwd_varlen_mask(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
+                       long long mask_seq_stride, const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq,
+                       int Hkv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d, int causal,
+                       int window, float scale, int dtype, void* stream);
+int fa_bwd_varlen_mask(const void* Q, const void* K, const void* V, const void* O, const float* L, const void* dO,
+                       void* dQ, void* dK, void* dV, void* workspace, size_t workspace_bytes,
+                       const uint32_t* mask_bits, long long mask_seq_stride, const int* cu_seqlens_q,
+                       const int* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                       int max_seqlen_k, int d, int causal, int window, float scale, int dtype, void* stream);
 
 /*
  * The backward pass of fa_bwd for callers that cannot allocate memory or pass

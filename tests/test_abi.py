@@ -44,7 +44,7 @@ def test_status_strings(lib):
         s = fa.status_string(code)
         assert s and s != "unknown status"
     assert fa.status_string(99) == "unknown status"
-    assert lib.fa_abi_version() >> 16 == 1
+    assert lib.fa_abi_version() >> 16 == 2
 
 
 def test_workspace_bytes(lib):
@@ -181,13 +181,14 @@ def test_mask_row_words(lib):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(mask=None), 1), (dict(mask=FAKE + 4), 8), (dict(stride=-1), 2), (dict(stride=5), 2), (dict(stride=16 * 12 + 2), 8),
-    (dict(d=80), 4), (dict(Hkv=3), 3), (dict(scale=math.nan), 6),
+    (dict(d=80, dv=80), 4), (dict(Hkv=3), 3), (dict(scale=math.nan), 6), (dict(dv=96), 4),
+    (dict(d=128, dv=64, dtype=0), 4), (dict(d=64, dv=128, dtype=0), 4),
 ])
 def test_fwd_mask_rejects_bad_arguments(lib, kw, status):
-    a = dict(mask=FAKE, stride=0, d=64, Hkv=2, scale=0.125)
+    a = dict(mask=FAKE, stride=0, d=64, dv=64, Hkv=2, scale=0.125, dtype=1)
     a.update(kw)
-    assert lib.fa_fwd_mask(FAKE, FAKE, FAKE, FAKE, FAKE, a["mask"], a["stride"], 2, 4, a["Hkv"], 16, 300, a["d"], 1,
-                           a["scale"], 1, None) == status
+    assert lib.fa_fwd_mask(FAKE, FAKE, FAKE, FAKE, FAKE, a["mask"], a["stride"], 2, 4, a["Hkv"], 16, 300, a["d"],
+                           a["dv"], 1, 50, a["scale"], a["dtype"], None) == status
 
 
 @pytest.mark.parametrize("args,status", [
@@ -200,13 +201,29 @@ def test_mask_pack_rejects_bad_arguments(lib, args, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(mask=None), 1), (dict(stride=-4), 2), (dict(stride=6), 2), (dict(ws=None), 7), (dict(wsb=64), 7),
-    (dict(d=80), 4),
+    (dict(d=80, dv=80), 4), (dict(dv=96), 4), (dict(d=128, dv=64, dtype=0), 4),
 ])
 def test_bwd_mask_rejects_bad_arguments(lib, kw, status):
-    a = dict(mask=FAKE, stride=0, ws=FAKE, wsb=1 << 30, d=64)
+    a = dict(mask=FAKE, stride=0, ws=FAKE, wsb=1 << 30, d=64, dv=64, dtype=1)
     a.update(kw)
     assert lib.fa_bwd_mask(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["ws"], a["wsb"], a["mask"],
-                           a["stride"], 2, 4, 2, 16, 300, a["d"], 1, 0.125, 1, None) == status
+                           a["stride"], 2, 4, 2, 16, 300, a["d"], a["dv"], 1, 50, 0.125, a["dtype"], None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mask=None), 1), (dict(stride=-4), 2), (dict(stride=6), 2), (dict(cu_q=None), 1), (dict(cu_k=FAKE + 2), 8),
+    (dict(max_q=40), 2), (dict(d=80), 4), (dict(scale=0.0), 6),
+])
+def test_varlen_mask_rejects_bad_arguments(lib, kw, status):
+    a = dict(mask=FAKE, stride=0, cu_q=FAKE, cu_k=FAKE, max_q=16, d=64, scale=0.125)
+    a.update(kw)
+    # B = 2 sequences, Hq = 4, Hkv = 2, total_q = 32, total_k = 300, longest 16 and 200
+    assert lib.fa_fwd_varlen_mask(*(FAKE,) * 5, a["mask"], a["stride"], a["cu_q"], a["cu_k"], 2, 4, 2, 32, 300,
+                                  a["max_q"], 200, a["d"], 1, 0, a["scale"], 1, None) == status
+    assert lib.fa_bwd_varlen_mask(*(FAKE,) * 9, FAKE, 1 << 30, a["mask"], a["stride"], a["cu_q"], a["cu_k"], 2, 4, 2,
+                                  32, 300, a["max_q"], 200, a["d"], 1, 0, a["scale"], 1, None) == status
+    assert lib.fa_bwd_varlen_mask(*(FAKE,) * 9, None, 0, FAKE, 0, FAKE, FAKE, 2, 4, 2, 32, 300, 16, 200, 64, 1, 0,
+                                  0.125, 1, None) == 7
 
 
 def test_bwd_mask_workspace_adds_the_key_major_copy(lib):
@@ -220,17 +237,21 @@ def test_bwd_mask_workspace_adds_the_key_major_copy(lib):
 
 
 def test_mask_splitk_workspace_and_arguments(lib):
-    assert lib.fa_fwd_mask_splitk_workspace_bytes(4, 32, 8, 32, 1056, 128, 1, 1) == 0
-    n3 = lib.fa_fwd_mask_splitk_workspace_bytes(4, 32, 8, 32, 1056, 128, 1, 3)
+    assert lib.fa_fwd_mask_splitk_workspace_bytes(4, 32, 8, 32, 1056, 128, 128, 1, 1) == 0
+    n3 = lib.fa_fwd_mask_splitk_workspace_bytes(4, 32, 8, 32, 1056, 128, 128, 1, 3)
     rows = 4 * 32 * 32
     assert n3 == math.ceil(3 * rows * 128 * 4 / 256) * 256 + math.ceil(3 * rows * 4 / 256) * 256
+    # fp32 partials dv wide
+    n3v = lib.fa_fwd_mask_splitk_workspace_bytes(4, 32, 8, 32, 1056, 128, 64, 1, 3)
+    assert n3v == math.ceil(3 * rows * 64 * 4 / 256) * 256 + math.ceil(3 * rows * 4 / 256) * 256
+    assert lib.fa_fwd_mask_splitk_workspace_bytes(4, 32, 8, 32, 1056, 128, 96, 1, 3) == 0
     # a split call without its workspace, then with too small a one
-    assert lib.fa_fwd_mask_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, 0, 4, 32, 8, 32, 1056, 128, 0,
-                                  0.125, 1, 3, None) == 7
-    assert lib.fa_fwd_mask_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 64, 4, 32, 8, 32, 1056, 128, 0,
-                                  0.125, 1, 3, None) == 7
-    assert lib.fa_fwd_mask_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 30, 4, 32, 8, 32, 1056, 128, 0,
-                                  0.125, 1, 5000, None) == 9
+    assert lib.fa_fwd_mask_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, 0, 4, 32, 8, 32, 1056, 128, 128, 0,
+                                  0, 0.125, 1, 3, None) == 7
+    assert lib.fa_fwd_mask_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 64, 4, 32, 8, 32, 1056, 128, 128, 0,
+                                  0, 0.125, 1, 3, None) == 7
+    assert lib.fa_fwd_mask_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 1 << 30, 4, 32, 8, 32, 1056, 128, 128,
+                                  0, 0, 0.125, 1, 5000, None) == 9
 
 
 def test_head_dim_32_is_fp32_only(lib):
@@ -257,17 +278,21 @@ def _scale_calls(lib, s):
                                                    64, 1, 0, s, 1, None),
         "fa_fwd_paged": lambda: lib.fa_fwd_paged(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 1, 16, 4, 128, 8,
                                                  64, 1, 0, s, 1, None, 0, 1, None),
-        "fa_fwd_mask": lambda: lib.fa_fwd_mask(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 4, 2, 16, 300, 64, 1, s, 1,
-                                               None),
+        "fa_fwd_mask": lambda: lib.fa_fwd_mask(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 4, 2, 16, 300, 64, 64, 1, 0,
+                                               s, 1, None),
         "fa_fwd_mask_splitk": lambda: lib.fa_fwd_mask_splitk(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, W, 2, 4, 2,
-                                                             16, 300, 64, 1, s, 1, 2, None),
+                                                             16, 300, 64, 64, 1, 0, s, 1, 2, None),
+        "fa_fwd_varlen_mask": lambda: lib.fa_fwd_varlen_mask(*(FAKE,) * 6, 0, FAKE, FAKE, 2, 4, 2, 32, 300, 16, 200, 64,
+                                                             1, 0, s, 1, None),
+        "fa_bwd_varlen_mask": lambda: lib.fa_bwd_varlen_mask(*(FAKE,) * 10, W, FAKE, 0, FAKE, FAKE, 2, 4, 2, 32, 300,
+                                                             16, 200, 64, 1, 0, s, 1, None),
         "fa_bwd": lambda: lib.fa_bwd(*(FAKE,) * 10, W, 1, 2, 1, 16, 16, 64, 1, s, 1, None),
         "fa_bwd_stages": lambda: lib.fa_bwd_stages(*(FAKE,) * 10, W, 1, 2, 1, 16, 16, 64, 1, s, 1, 7, None),
         "fa_bwd_window": lambda: lib.fa_bwd_window(*(FAKE,) * 10, W, 1, 2, 1, 16, 16, 64, 1, 8, s, 1, 7, None),
         "fa_bwd_dv": lambda: lib.fa_bwd_dv(*(FAKE,) * 10, W, 1, 2, 1, 16, 16, 128, 64, 1, 0, s, 1, 7, None),
         "fa_bwd_varlen": lambda: lib.fa_bwd_varlen(*(FAKE,) * 10, W, FAKE, FAKE, 2, 2, 1, 32, 32, 16, 16, 64, 1, 0,
                                                    s, 1, None),
-        "fa_bwd_mask": lambda: lib.fa_bwd_mask(*(FAKE,) * 10, W, FAKE, 0, 2, 4, 2, 16, 300, 64, 1, s, 1, None),
+        "fa_bwd_mask": lambda: lib.fa_bwd_mask(*(FAKE,) * 10, W, FAKE, 0, 2, 4, 2, 16, 300, 64, 64, 1, 0, s, 1, None),
         "fa_bwd_noalloc": lambda: lib.fa_bwd_noalloc(*(FAKE,) * 9, 1, 2, 1, 16, 16, 64, 1, s, 1, None),
         "fa_bwd_paged": lambda: lib.fa_bwd_paged(*(FAKE,) * 11, 2, 2, 1, 16, 4, 128, 8, 64, 1, 0, s, 1, FAKE, W,
                                                  None),

@@ -1,9 +1,9 @@
 """Argument checks of the Python binding that need no GPU: every one raises before the
 library is called, so these run on host tensors.
 
-The masked and split entry points have no dv argument (their kernels index V and dV with
-stride d), so a v whose head dim differs from q's must be refused by the binding, or the
-forward would read past V's end and the masked backward write past dV's."""
+The key-split forward has no dv argument (its kernels index V with stride d), so a v whose
+head dim differs from q's must be refused by the binding, or the forward would read past V's
+end."""
 
 import math
 
@@ -21,36 +21,10 @@ def qkv(d=128, dv=64, B=1, Hq=2, Hkv=1, Tq=8, Tk=8, dtype=torch.bfloat16):
     return q, k, v
 
 
-def test_forward_masked_refuses_dv_not_d():
-    q, k, v = qkv()
-    with pytest.raises(ValueError, match="head dim"):
-        _binding.forward_masked(q, k, v, torch.ones(8, 8, dtype=torch.bool))
-
-
-def test_forward_masked_split_refuses_dv_not_d():
-    q, k, v = qkv()
-    with pytest.raises(ValueError, match="head dim"):
-        _binding.forward_masked(q, k, v, torch.ones(8, 8, dtype=torch.bool), nsplit=2)
-
-
-def test_backward_masked_refuses_dv_not_d():
-    q, k, v = qkv()
-    o = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
-    lse = torch.zeros(1, 2, 8)
-    with pytest.raises(ValueError, match="head dim"):
-        _binding.backward_masked(q, k, v, o, lse, o, torch.ones(8, 8, dtype=torch.bool))
-
-
 def test_forward_splitk_refuses_dv_not_d():
     q, k, v = qkv()
     with pytest.raises(ValueError, match="head dim"):
         _binding.forward_splitk(q, k, v)
-
-
-def test_attention_with_mask_refuses_dv_not_d():
-    q, k, v = qkv()
-    with pytest.raises(ValueError, match="head dim"):
-        fa.attention(q, k, v, mask=torch.ones(8, 8, dtype=torch.bool))
 
 
 def test_host_tensors_are_refused():

@@ -10,7 +10,8 @@ Covered: forward (plain, window, dv != d, fp32 d = 32), backward (same), the
 key-split forward and its merge (bf16, fp32 d = 64 and d = 32), variable-length
 forward and backward, paged forward (one pass and split) and backward, mask packing, masked
 forward (one pass and split) and masked backward (whose workspace holds the
-key-major mask copy).
+key-major mask copy), also with a window and dv != d, and the masked varlen
+forward and backward.
 """
 
 import math
@@ -207,27 +208,52 @@ def test_mask_pack_stays_in_bounds(fa, Tq, Tk):
     g.check(f"pack {Tq}x{Tk}")
 
 
-@pytest.mark.parametrize("dtn,d", [("bf16", 128), ("fp32", 64), ("fp32", 32)])
-def test_masked_paths_stay_in_bounds(fa, dtn, d):
+@pytest.mark.parametrize("dtn,d,dvh,window", [("bf16", 128, 128, 0), ("fp32", 64, 64, 0), ("fp32", 32, 32, 0),
+                                              ("bf16", 128, 64, 70), ("bf16", 64, 128, 0), ("fp32", 32, 32, 45)])
+def test_masked_paths_stay_in_bounds(fa, dtn, d, dvh, window):
     import torch
     t = dt(dtn)
     B, Hq, Hkv, Tq, Tk = 2, 4, 2, 200, 333
-    q, k, v = rnd((B, Hq, Tq, d), t, 15), rnd((B, Hkv, Tk, d), t, 16), rnd((B, Hkv, Tk, d), t, 17)
-    do = rnd((B, Hq, Tq, d), t, 18)
+    q, k, v = rnd((B, Hq, Tq, d), t, 15), rnd((B, Hkv, Tk, d), t, 16), rnd((B, Hkv, Tk, dvh), t, 17)
+    do = rnd((B, Hq, Tq, dvh), t, 18)
     mask = torch.from_numpy(np.random.default_rng(9).random((B, Tq, Tk)) < 0.5).cuda()
     bits = fa.pack_mask(mask)
     lib = fa.load_library()
     code = fa.FA_DTYPE_BF16 if dtn == "bf16" else fa.FA_DTYPE_F32
     stride = Tq * lib.fa_mask_row_words(Tk)
     g = Guarded()
-    o, lse = g.tensor("O", q.shape, t), g.tensor("L", (B, Hq, Tq), torch.float32)
-    fa.forward_masked(q, k, v, bits, True, out=o, lse=lse)
-    ws = g.workspace("mask split workspace", int(lib.fa_fwd_mask_splitk_workspace_bytes(B, Hq, Hkv, Tq, Tk, d,
+    o, lse = g.tensor("O", (B, Hq, Tq, dvh), t), g.tensor("L", (B, Hq, Tq), torch.float32)
+    fa.forward_masked(q, k, v, bits, True, out=o, lse=lse, window=window)
+    ws = g.workspace("mask split workspace", int(lib.fa_fwd_mask_splitk_workspace_bytes(B, Hq, Hkv, Tq, Tk, d, dvh,
                                                                                         code, 3)))
-    o2, lse2 = g.tensor("O (split)", q.shape, t), g.tensor("L (split)", (B, Hq, Tq), torch.float32)
-    fa.forward_masked(q, k, v, bits, True, out=o2, lse=lse2, nsplit=3, workspace=ws)
+    o2, lse2 = g.tensor("O (split)", (B, Hq, Tq, dvh), t), g.tensor("L (split)", (B, Hq, Tq), torch.float32)
+    fa.forward_masked(q, k, v, bits, True, out=o2, lse=lse2, nsplit=3, workspace=ws, window=window)
     wsb = g.workspace("mask backward workspace", int(lib.fa_bwd_mask_workspace_bytes(B, Hq, Hkv, Tq, Tk, d, code,
                                                                                       stride)))
     dq, dk, dvv = g.tensor("dQ", q.shape, t), g.tensor("dK", k.shape, t), g.tensor("dV", v.shape, t)
-    fa.backward_masked(q, k, v, o, lse, do, bits, True, workspace=wsb, dq=dq, dk=dk, dv=dvv)
-    g.check(f"masked {dtn} d={d}")
+    fa.backward_masked(q, k, v, o, lse, do, bits, True, workspace=wsb, dq=dq, dk=dk, dv=dvv, window=window)
+    g.check(f"masked {dtn} d={d} dv={dvh} window={window}")
+
+
+def test_varlen_masked_paths_stay_in_bounds(fa):
+    import torch
+    lens = [(1, 1), (120, 333), (0, 40), (77, 0), (200, 150)]
+    B, Hq, Hkv, d = len(lens), 4, 2, 128
+    mq, mk = max(a for a, _ in lens), max(b for _, b in lens)
+    tq, tk = sum(a for a, _ in lens), sum(b for _, b in lens)
+    t = torch.bfloat16
+    q, k, v, do = rnd((Hq, tq, d), t, 19), rnd((Hkv, tk, d), t, 20), rnd((Hkv, tk, d), t, 21), rnd((Hq, tq, d), t, 22)
+    cu_q = torch.tensor(np.concatenate([[0], np.cumsum([a for a, _ in lens])]).astype(np.int32)).cuda()
+    cu_k = torch.tensor(np.concatenate([[0], np.cumsum([b for _, b in lens])]).astype(np.int32)).cuda()
+    mask = torch.from_numpy(np.random.default_rng(10).random((B, mq, mk)) < 0.5).cuda()
+    lib = fa.load_library()
+    stride = mq * lib.fa_mask_row_words(mk)
+    g = Guarded()
+    o, lse = g.tensor("O", q.shape, t), g.tensor("L", (Hq, tq), torch.float32)
+    fa.forward_varlen_masked(q, k, v, cu_q, cu_k, mq, mk, mask, True, window=60, out=o, lse=lse)
+    ws = g.workspace("varlen mask workspace", int(lib.fa_bwd_mask_workspace_bytes(B, Hq, Hkv, mq, mk, d,
+                                                                                   fa.FA_DTYPE_BF16, stride)))
+    dq, dk, dvv = g.tensor("dQ", q.shape, t), g.tensor("dK", k.shape, t), g.tensor("dV", v.shape, t)
+    fa.backward_varlen_masked(q, k, v, o, lse, do, cu_q, cu_k, mq, mk, mask, True, window=60, workspace=ws,
+                              dq=dq, dk=dk, dv=dvv)
+    g.check("varlen masked")
