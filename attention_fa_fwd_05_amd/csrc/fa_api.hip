@@ -49,8 +49,8 @@ int elem_bytes(int dtype) { return dtype == FA_DTYPE_BF16 ? 2 : 4; }
 int check_common(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 0 || Tk < 0) return FA_ERR_BAD_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_GQA_RATIO;
-  // 64 and 128; fp32 also 32 (the measured configuration of the tiling article)
-  if (d != 64 && d != 128 && !(d == 32 && dtype == FA_DTYPE_F32)) return FA_ERR_HEAD_DIM;
+  // 32 (the measured configuration of the tiling article), 64 and 128
+  if (d != 32 && d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (Tq > kMaxSeq || Tk > kMaxSeq) return FA_ERR_TOO_LARGE;
   const long long q = (long long)B * Hq * Tq * d, kv = (long long)B * Hkv * Tk * d;
@@ -136,11 +136,12 @@ int mask_splits(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int ns
   return ns < 1 ? 1 : (int)ns;
 }
 
-// Head dim of V (and O, dO, dV): equal to d, or, for bf16 only, 64 with d = 128
-// and 128 with d = 64.
+// Head dim of V (and O, dO, dV): equal to d, or 64 with d = 128 and 128 with
+// d = 64 (both dtypes).
 int check_dv(int d, int dv, int dtype) {
+  (void)dtype;
   if (dv == d) return FA_OK;
-  if (dtype == FA_DTYPE_BF16 && ((d == 128 && dv == 64) || (d == 64 && dv == 128))) return FA_OK;
+  if ((d == 128 && dv == 64) || (d == 64 && dv == 128)) return FA_OK;
   return FA_ERR_HEAD_DIM;
 }
 
@@ -326,7 +327,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_NULL_PTR: return "a required pointer is NULL";
     case FA_ERR_BAD_SHAPE: return "bad shape: B, Hq, Hkv must be >= 1 and Tq, Tk >= 0";
     case FA_ERR_GQA_RATIO: return "Hq must be a multiple of Hkv";
-    case FA_ERR_HEAD_DIM: return "unsupported head dimension (64 or 128; fp32 also 32)";
+    case FA_ERR_HEAD_DIM: return "unsupported head dimension (32, 64 or 128; dv != d as (128, 64) or (64, 128))";
     case FA_ERR_DTYPE: return "unsupported dtype (FA_DTYPE_F32 or FA_DTYPE_BF16)";
     case FA_ERR_SCALE: return "scale must be finite and positive";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_bwd_workspace_bytes";

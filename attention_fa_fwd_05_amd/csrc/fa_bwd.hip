@@ -569,7 +569,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 // Waves per dQ workgroup: 8 (256 query rows), or 4 where fp32 d = 128
 // operands would not fit in 256 registers.
 template <typename T, int D>
-constexpr int dq_waves() { return (sizeof(T) == 4 && D == 128) ? 4 : 8; }
+constexpr int dq_waves() { return sizeof(T) == 4 || D == 32 ? 4 : 8; }
 
 // D: head dim of Q, K, dQ; DV: of V and dO.
 template <typename T, int D, bool CAUSAL, bool WIN, int DV = D, bool MASK = false>
@@ -878,20 +878,27 @@ hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t stream) {
 hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int d, int causal, unsigned stages,
                       hipStream_t stream, int dv) {
   if (dv < 0) dv = d;
-  if (dv != d) {                                     // bf16 only: d = 128 with dv = 64, and the reverse
-    if (!dtype_bf16) return hipErrorInvalidValue;
-    if (d == 128 && dv == 64)
-      return causal ? launch_bwd_t<bf16, 128, true, 64>(a, stages, stream)
-                    : launch_bwd_t<bf16, 128, false, 64>(a, stages, stream);
-    if (d == 64 && dv == 128)
-      return causal ? launch_bwd_t<bf16, 64, true, 128>(a, stages, stream)
-                    : launch_bwd_t<bf16, 64, false, 128>(a, stages, stream);
+  if (dv != d) {                                     // d = 128 with dv = 64, and the reverse
+#define FA_BWD_DV_CASE(T)                                                                        \
+  if (d == 128 && dv == 64)                                                                      \
+    return causal ? launch_bwd_t<T, 128, true, 64>(a, stages, stream)                            \
+                  : launch_bwd_t<T, 128, false, 64>(a, stages, stream);                          \
+  if (d == 64 && dv == 128)                                                                      \
+    return causal ? launch_bwd_t<T, 64, true, 128>(a, stages, stream)                            \
+                  : launch_bwd_t<T, 64, false, 128>(a, stages, stream);
+    if (dtype_bf16) {
+      FA_BWD_DV_CASE(bf16)
+    } else {
+      FA_BWD_DV_CASE(float)
+    }
+#undef FA_BWD_DV_CASE
     return hipErrorInvalidValue;
   }
 #define FA_BWD_CASE(T, DD)                                                                         \
   if (d == DD)                                                                                     \
     return causal ? launch_bwd_t<T, DD, true>(a, stages, stream) : launch_bwd_t<T, DD, false>(a, stages, stream);
   if (dtype_bf16) {
+    FA_BWD_CASE(bf16, 32)
     FA_BWD_CASE(bf16, 64)
     FA_BWD_CASE(bf16, 128)
   } else {

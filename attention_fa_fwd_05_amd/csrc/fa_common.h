@@ -88,17 +88,22 @@ template <> struct MM<float> {
 //    run {c .. c+3} (c a multiple of 4) that 32 lanes of a transposed read take
 //    from each of the 4 rows lands on 16 distinct slots.
 // For 128-byte rows (two rows per bank sweep) the same holds with
-// fsw(r) = 4 ((r >> 1) & 1) + ((r >> 2) & 3).  fsw depends on r & 15 only, so
-// per-lane offsets can be tabulated over a 16-row period.  The layout can be
+// fsw(r) = 4 ((r >> 1) & 1) + ((r >> 2) & 3), and for 64-byte rows (four rows
+// per sweep, 4 chunks each) with fsw(r) = (r >> 2) & 3: the 16 rows of a
+// natural read fall in 4 row classes (r & 3, which picks the sweep quarter)
+// times 4 swizzles, and a transposed read takes all 4 chunks of 4 rows of
+// distinct r & 3.  fsw depends on r & 15 only, so per-lane offsets can be
+// tabulated over a 16-row period.  The layout can be
 // filled by direct global->LDS loads, which write 64 consecutive 16-byte slots
 // per wave instruction.
 template <typename T, int D>
 struct SwzTile {
   static constexpr int EPC = 16 / (int)sizeof(T);   // elements per chunk
   static constexpr int NCH = D / EPC;               // chunks per row
-  static_assert(NCH == 8 || NCH == 16 || NCH == 32, "row must be 8, 16 or 32 chunks");
+  static_assert(NCH == 4 || NCH == 8 || NCH == 16 || NCH == 32, "row must be 4, 8, 16 or 32 chunks");
   __device__ static inline int fsw(int r) {
-    return NCH >= 16 ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
+    return NCH >= 16 ? (4 * (r & 3) + ((r >> 2) & 3))
+                     : NCH == 8 ? (4 * ((r >> 1) & 1) + ((r >> 2) & 3)) : ((r >> 2) & 3);
   }
   // element index of (row, col)
   __device__ static inline int elem(int r, int col) {
@@ -140,16 +145,26 @@ __device__ inline void dma4(const void* gsrc, uint32_t lds_base) {
 }
 
 // Issue direct loads of global rows [g0, g0 + ROWS) (each clamped to
-// nrows - 1, which must be >= 0) into a swizzled tile.  NTHR threads take
-// part; each wave issues ROWS * NCH / NTHR instructions.
-template <typename T, int D, int ROWS, int NTHR>
+// nrows - 1, which must be >= 0) into a swizzled tile.  Waves W0 .. W0 + NWS
+// - 1 of a workgroup of NTHR threads take part (all of them by default; a
+// tile smaller than one 16-byte slot per thread goes to a subset), each
+// issuing ROWS * NCH / (64 NWS) instructions; other waves issue none.
+template <typename T, int D, int ROWS, int NTHR, int W0 = 0, int NWS = NTHR / 64>
 struct DmaRows {
   using TL = SwzTile<T, D>;
-  static constexpr int SLOTS = ROWS * TL::NCH, NWV = NTHR / 64, PER = SLOTS / NTHR;
-  static_assert(PER * NTHR == SLOTS, "tile must split evenly over the threads");
+  static constexpr int SLOTS = ROWS * TL::NCH, NWV = NWS, PER = SLOTS / (64 * NWS);
+  static_assert(PER >= 1 && PER * 64 * NWS == SLOTS, "tile must split evenly over the waves");
+  static_assert(W0 >= 0 && W0 + NWS <= NTHR / 64, "waves within the workgroup");
+  // This wave takes part (uniform).
+  __device__ static inline bool mine() {
+    if constexpr (W0 == 0 && NWS == NTHR / 64) return true;
+    const int wave = threadIdx.x >> 6;
+    return wave >= W0 && wave < W0 + NWS;
+  }
   // Instruction i (0 <= i < PER) of this wave.
   __device__ static inline void one(T* tile, const T* g, int g0, int nrows, int i) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (!mine()) return;
+    const int wave = (threadIdx.x >> 6) - W0, lane = threadIdx.x & 63;
     const int blk = i * NWV + wave;                 // 64-slot block of this wave instruction
     const int pos = blk * 64 + lane;
     const int r = pos / TL::NCH, x = pos % TL::NCH;
@@ -159,12 +174,14 @@ struct DmaRows {
   // Byte offset from row 0 of the tile's source rows for instruction i of this
   // lane (rows not clamped), and the LDS byte offset of its 64-slot block.
   __device__ static inline uint32_t src_off(int i) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = (threadIdx.x >> 6) - W0, lane = threadIdx.x & 63;
     const int pos = (i * NWV + wave) * 64 + lane;
     const int r = pos / TL::NCH, x = pos % TL::NCH;
     return (uint32_t)((r * D + (x ^ TL::fsw(r)) * TL::EPC) * (int)sizeof(T));
   }
-  __device__ static inline uint32_t lds_off(int i) { return (uint32_t)((i * NWV + (threadIdx.x >> 6)) * 1024); }
+  __device__ static inline uint32_t lds_off(int i) {
+    return (uint32_t)((i * NWV + (threadIdx.x >> 6) - W0) * 1024);
+  }
 };
 template <typename T, int D, int ROWS, int NTHR>
 __device__ inline void dma_rows(T* tile, const T* g, int g0, int nrows) {

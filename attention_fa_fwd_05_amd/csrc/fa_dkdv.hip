@@ -63,7 +63,7 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
   constexpr int NDTV = DV / 32;                     // 32-wide dV tiles
   constexpr int NBQ = 4, NB = 3;                    // Q slots; dO, L2, -D (and mask) slots
   static_assert(NSQ == 4, "P in LDS is 4 operands per lane");
-  // Tiles 4096-byte aligned (XorFetch): 64 rows of 64 or 128 bf16 are 8 or 16 KiB.
+  // Tiles 4096-byte aligned (XorFetch): 64 rows of 32, 64 or 128 bf16 are 4, 8 or 16 KiB.
   __shared__ __attribute__((aligned(4096))) T sQ[NBQ][BQ * D];
   __shared__ __attribute__((aligned(4096))) T sdO[NB][BQ * DV];
   __shared__ __attribute__((aligned(16))) bf16x8 sP[2][4][NSQ][64];   // [buffer][key group][step][lane]
@@ -106,14 +106,18 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
   // its keys (key-major copy, two words per key).  A whole block is addressed
   // from a wave-uniform row pointer plus per-lane byte offsets tabulated once;
   // only the ragged last block clamps its rows.  The loads go out as single
-  // instructions ("pieces") spread over a phase of matrix products.
-  using DRQ = DmaRows<T, D, BQ, NTHR>;
-  using DRO = DmaRows<T, DV, BQ, NTHR>;
+  // instructions ("pieces") spread over a phase of matrix products.  A block
+  // of 32-wide rows (4 KiB) is half a slot per thread: the P-waves then load
+  // Q and the dS-waves dO, one instruction each.
+  constexpr bool SPLIT = BQ * D * 2 / 16 < NTHR;
+  static_assert(!SPLIT || D == DV, "split loads for d = dv = 32");
+  using DRQ = DmaRows<T, D, BQ, NTHR, 0, SPLIT ? 4 : NTHR / 64>;
+  using DRO = DmaRows<T, DV, BQ, NTHR, SPLIT ? 4 : 0, SPLIT ? 4 : NTHR / 64>;
   uint32_t qoff[DRQ::PER], ooff[DRO::PER];
 #pragma unroll
   for (int j = 0; j < DRQ::PER; ++j) qoff[j] = DRQ::src_off(j);
 #pragma unroll
-  for (int j = 0; j < DRO::PER; ++j) ooff[j] = D == DV ? qoff[j % DRQ::PER] : DRO::src_off(j);
+  for (int j = 0; j < DRO::PER; ++j) ooff[j] = D == DV && !SPLIT ? qoff[j % DRQ::PER] : DRO::src_off(j);
   struct Src {
     const T* q;                                     // Q row q0 of the block's head
     const T* o;                                     // dO row q0
@@ -138,10 +142,12 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
   auto piece = [&](const Src& b, int j) {
     const int buf = b.it % NB;
     if (j < DRQ::PER) {
+      if (!DRQ::mine()) return;
       if (b.whole) dma16s(b.q, qoff[j], lds_addr(sQ[b.it % NBQ]) + DRQ::lds_off(j));
       else DRQ::one(sQ[b.it % NBQ], b.q - (size_t)b.q0 * D, b.q0, Tq, j);
     } else if (j < DRQ::PER + DRO::PER) {
       const int i = j - DRQ::PER;
+      if (!DRO::mine()) return;
       if (b.whole) dma16s(b.o, ooff[i], lds_addr(sdO[buf]) + DRO::lds_off(i));
       else DRO::one(sdO[buf], b.o - (size_t)b.q0 * DV, b.q0, Tq, i);
     } else if (j == DRQ::PER + DRO::PER) {
@@ -165,18 +171,20 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
   constexpr int SPS = 2 * NPC <= 2 * NSD ? 2 : 1;   // spacing in the S phase (2 NSD products)
   constexpr int SPP = 2 * NPC <= 2 * NSDV ? 2 : 1;  // ... in the dP phase (2 NSDV products)
 
-  // Direct-load instructions this wave issues per block, so that the wait at
-  // the end of block i leaves block i + 2's loads in flight.
-  constexpr int NLD = DRQ::PER + DRO::PER;
+  // Direct-load instructions this wave issues per block (Q and dO rows: P-
+  // and dS-waves differ when the loads are split), so that the wait at the
+  // end of block i leaves block i + 2's loads in flight.
+  constexpr int NLDP = SPLIT ? DRQ::PER : DRQ::PER + DRO::PER;
+  constexpr int NLDS = SPLIT ? DRO::PER : DRQ::PER + DRO::PER;
   auto wait_next = [&](bool two_in_flight) {
     if (!two_in_flight) {
       wait_vmcnt<0>();
     } else if (w < 2) {                             // + the L2 or -D row
-      wait_vmcnt<NLD + 1 + (MASK ? 1 : 0)>();
+      wait_vmcnt<NLDP + 1 + (MASK ? 1 : 0)>();
     } else if (pwave) {
-      wait_vmcnt<NLD + (MASK ? 1 : 0)>();
+      wait_vmcnt<NLDP + (MASK ? 1 : 0)>();
     } else {
-      wait_vmcnt<NLD>();
+      wait_vmcnt<NLDS>();
     }
   };
 
@@ -269,24 +277,39 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
             [&](int m, const Op& x) { sacc[m / NSD] = M::mma(x, kop[m % NSD], sacc[m / NSD]); },
             [&](int m) {
               if (m % SPS == SPS - 1 && m / SPS < NPC && load) piece(nsrc, m / SPS);
-              const int k = m - (2 * NSD - 5);      // 4 pieces over the last 4 products
-              if (k >= 0 && k < 4) exp_piece(0, k);
+              if constexpr (2 * NSD >= 5) {
+                const int k = m - (2 * NSD - 5);    // 4 pieces over the last 4 products
+                if (k >= 0 && k < 4) exp_piece(0, k);
+              }
             });
+        if constexpr (2 * NSD < 5) {                // d = 32: too few products to hide them
+#pragma unroll
+          for (int k = 0; k < 4; ++k) exp_piece(0, k);
+        }
         finish_tile(0);
         // dV^T += dO^T P (dO^T by transposed reads), query steps of tile 0
-        // first; tile 1's exponentials under those products.
+        // first; tile 1's exponentials under those products (d = 32: before
+        // them, as tile 0's steps are two products only).
+        if constexpr (NDTV == 1) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) exp_piece(1, k);
+          finish_tile(1);
+        }
         pipelined<NSQ * NDTV, 4, Op>(
             [&](int m) { return XorFetch<DV>::tr(ob + xfv.tr0, m % NDTV, m / NDTV); },
             [&](int m, const Op& x) { dv[m % NDTV] = M::mma(x, pop[m / NDTV], dv[m % NDTV]); },
             [&](int m) {
               // 4 pieces from product E0 on; tile 1's operands (query steps 2
               // and 3) are complete after product 2 NDTV - 1, before their use.
-              constexpr int E0 = 2 * NDTV >= 6 ? 1 : 0;
-              const int k = m - E0;
-              if (k >= 0 && k < 4) exp_piece(1, k);
-              if (m == 2 * NDTV - 1) finish_tile(1);
+              if constexpr (NDTV > 1) {
+                constexpr int E0 = 2 * NDTV >= 6 ? 1 : 0;
+                const int k = m - E0;
+                if (k >= 0 && k < 4) exp_piece(1, k);
+                if (m == 2 * NDTV - 1) finish_tile(1);
+              }
             });
-        static_assert(2 * NDTV - 1 >= (2 * NDTV >= 6 ? 1 : 0) + 3, "tile 1's P is formed before its query steps");
+        static_assert(NDTV == 1 || 2 * NDTV - 1 >= (2 * NDTV >= 6 ? 1 : 0) + 3,
+                      "tile 1's P is formed before its query steps");
         wave_prio<0>();
       }
       wait_next(load);
@@ -405,6 +428,7 @@ hipError_t launch_dkdv_pair(const BwdArgs& a, int d, int dv, int causal, hipStre
                   : launch_dkdv_pair_t<DD, DDV, false>(a, blocks, stream);
   FA_DKDV_CASE(128, 128)
   FA_DKDV_CASE(64, 64)
+  FA_DKDV_CASE(32, 32)
   FA_DKDV_CASE(128, 64)
   FA_DKDV_CASE(64, 128)
 #undef FA_DKDV_CASE

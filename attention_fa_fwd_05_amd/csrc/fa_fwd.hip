@@ -33,10 +33,15 @@ constexpr float kTau = 8.0f;
 // K / V operand read from LDS feeds two matrix instructions, but a wave then
 // needs the whole register file (one wave per SIMD) and its softmax no longer
 // overlaps another wave's matrix work, which costs more than the LDS saving:
-// QT = 1 with 8 waves (two per SIMD) is faster.  fp32 d = 128 uses 4 waves so
-// its operands fit.
-// Keys per tile: 128, so a workgroup meets one barrier per 128 keys; fp32 with
-// d = 128 keeps 64 (two 128-key K / V buffers of it would exceed the LDS).
+// QT = 1 with 8 waves (two per SIMD) is faster.
+// Keys per tile: 128, so a workgroup meets one barrier per 128 keys.
+// fp32: 4 waves (128 query rows) against 64-key tiles.  Its matrix rate is an
+// eighth of bf16's, so each tile is long enough that one wave per SIMD keeps
+// the unit busy; 128-row blocks give twice the workgroups of 256-row ones
+// (the fp32 shapes are small: 32 heads of 1000 rows make 256 workgroups, one
+// per compute unit, instead of 128), and 64-key tiles keep a workgroup's LDS
+// at 64 KiB (d = dv = 64) so two fit a compute unit, or within the LDS at all
+// when d or dv is 128.
 // Decode shape (DEC): a packed workgroup of 4 waves, one per query head of a
 // K/V group with up to 32 rows each, against 64-key tiles.  Its 64 KiB of LDS
 // and at most 256 registers per wave (two waves per SIMD, asked of the
@@ -46,9 +51,9 @@ constexpr float kTau = 8.0f;
 // work, the bound.
 template <typename T, int D, bool DEC = false> struct FwdShape {
   static constexpr int QT = 1;
-  static constexpr int NW = DEC ? 4 : (sizeof(T) == 4 && D == 128) ? 4 : 8;
+  static constexpr int NW = DEC ? 4 : sizeof(T) == 4 ? 4 : 8;
   static constexpr int BQ = 32 * QT * NW;
-  static constexpr int BK = DEC ? 64 : (sizeof(T) == 4 && D == 128) ? 64 : 128;
+  static constexpr int BK = DEC ? 64 : sizeof(T) == 4 ? 64 : 128;
 };
 
 // D: head dim of Q and K; DV: head dim of V and O.  MASK: scores are also
@@ -474,14 +479,14 @@ hipError_t launch_mask_pack(const uint8_t* in, uint32_t* out, long long rows, in
 }
 
 int fwd_waves(int dtype_bf16, int d) {
-  return dtype_bf16 ? (d == 64 ? FwdShape<bf16, 64>::NW : FwdShape<bf16, 128>::NW)
+  return dtype_bf16 ? (d == 32 ? FwdShape<bf16, 32>::NW : d == 64 ? FwdShape<bf16, 64>::NW : FwdShape<bf16, 128>::NW)
                     : (d == 32 ? FwdShape<float, 32>::NW
                                : d == 64 ? FwdShape<float, 64>::NW : FwdShape<float, 128>::NW);
 }
 int fwd_decode_waves() { return FwdShape<bf16, 128, true>::NW; }
 int fwd_decode_block_keys() { return FwdShape<bf16, 128, true>::BK; }
 int fwd_block_keys(int dtype_bf16, int d) {
-  return dtype_bf16 ? (d == 64 ? FwdShape<bf16, 64>::BK : FwdShape<bf16, 128>::BK)
+  return dtype_bf16 ? (d == 32 ? FwdShape<bf16, 32>::BK : d == 64 ? FwdShape<bf16, 64>::BK : FwdShape<bf16, 128>::BK)
                     : (d == 32 ? FwdShape<float, 32>::BK
                                : d == 64 ? FwdShape<float, 64>::BK : FwdShape<float, 128>::BK);
 }
@@ -489,20 +494,27 @@ int fwd_block_keys(int dtype_bf16, int d) {
 hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream, int nsplit,
                       int dv) {
   if (dv < 0) dv = d;
-  if (dv != d) {                                     // bf16 only: d = 128 with dv = 64, and the reverse
-    if (!dtype_bf16) return hipErrorInvalidValue;
-    if (d == 128 && dv == 64)
-      return causal ? launch_fwd_t<bf16, 128, true, 64>(a, stream, nsplit)
-                    : launch_fwd_t<bf16, 128, false, 64>(a, stream, nsplit);
-    if (d == 64 && dv == 128)
-      return causal ? launch_fwd_t<bf16, 64, true, 128>(a, stream, nsplit)
-                    : launch_fwd_t<bf16, 64, false, 128>(a, stream, nsplit);
+  if (dv != d) {                                     // d = 128 with dv = 64, and the reverse
+#define FA_FWD_DV_CASE(T)                                                                        \
+  if (d == 128 && dv == 64)                                                                      \
+    return causal ? launch_fwd_t<T, 128, true, 64>(a, stream, nsplit)                            \
+                  : launch_fwd_t<T, 128, false, 64>(a, stream, nsplit);                          \
+  if (d == 64 && dv == 128)                                                                      \
+    return causal ? launch_fwd_t<T, 64, true, 128>(a, stream, nsplit)                            \
+                  : launch_fwd_t<T, 64, false, 128>(a, stream, nsplit);
+    if (dtype_bf16) {
+      FA_FWD_DV_CASE(bf16)
+    } else {
+      FA_FWD_DV_CASE(float)
+    }
+#undef FA_FWD_DV_CASE
     return hipErrorInvalidValue;
   }
 #define FA_FWD_CASE(T, DD)                                                              \
   if (d == DD)                                                                          \
     return causal ? launch_fwd_t<T, DD, true>(a, stream, nsplit) : launch_fwd_t<T, DD, false>(a, stream, nsplit);
   if (dtype_bf16) {
+    FA_FWD_CASE(bf16, 32)
     FA_FWD_CASE(bf16, 64)
     FA_FWD_CASE(bf16, 128)
   } else {

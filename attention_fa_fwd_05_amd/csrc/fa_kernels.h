@@ -167,7 +167,7 @@ inline hipError_t launch2(void (*kernel)(Params...), long long blocks, int ny, h
 
 // Forward over nsplit key slices (nsplit >= 1; with Opart/Lpart set, the
 // slices' partials are merged into O and L by a second kernel).
-// dv: head dim of V and O (d: of Q and K); dv != d only for bf16 with
+// dv: head dim of V and O (d: of Q and K); dv != d only as
 // (d, dv) = (128, 64) or (64, 128).
 hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipStream_t stream, int nsplit = 1,
                       int dv = -1);

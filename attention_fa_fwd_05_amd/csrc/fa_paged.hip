@@ -130,6 +130,7 @@ hipError_t launch_paged_t(const PagedBwdArgs& p, int phase, hipStream_t stream) 
 
 hipError_t launch_paged(const PagedBwdArgs& p, int dtype_bf16, int d, int phase, hipStream_t stream) {
   if (dtype_bf16) {
+    if (d == 32) return launch_paged_t<bf16, 32>(p, phase, stream);
     if (d == 64) return launch_paged_t<bf16, 64>(p, phase, stream);
     if (d == 128) return launch_paged_t<bf16, 128>(p, phase, stream);
   } else {

@@ -29,7 +29,7 @@
  *  - dtype: FA_DTYPE_F32 (float) or FA_DTYPE_BF16 (bfloat16 storage, float32
  *    accumulation, outputs rounded to nearest even).  It applies to Q, K, V,
  *    O, dO, dQ, dK, dV.
- *  - d (head dimension, equal for Q/K and V): 64 or 128; in fp32 also 32.
+ *  - d (head dimension, equal for Q/K and V): 32, 64 or 128.
  *  - GQA: Hq must be a multiple of Hkv; query head h reads K/V head
  *    h / (Hq / Hkv).  dK and dV are summed over the query heads of a group.
  *  - causal != 0: key j is visible to query i iff j <= i + (Tk - Tq)
@@ -67,7 +67,7 @@ typedef enum {
   FA_ERR_NULL_PTR = 1,   /* a required pointer is NULL */
   FA_ERR_BAD_SHAPE = 2,  /* B, Hq or Hkv < 1, Tq or Tk < 0 */
   FA_ERR_GQA_RATIO = 3,  /* Hq is not a multiple of Hkv */
-  FA_ERR_HEAD_DIM = 4,   /* d is not 64 or 128 (or 32 in fp32) */
+  FA_ERR_HEAD_DIM = 4,   /* d is not 32, 64 or 128 (or an unsupported (d, dv) pair) */
   FA_ERR_DTYPE = 5,      /* dtype is not an fa_dtype value */
   FA_ERR_SCALE = 6,      /* scale is NaN, infinite, zero or negative */
   FA_ERR_WORKSPACE = 7,  /* workspace missing or smaller than fa_bwd_workspace_bytes */
@@ -224,8 +224,8 @@ int fa_bwd_varlen(const void* Q, const void* K, const void* V, const void* O, co
  * Ordinary Autograd Saves", section "The implementation under test": V is
  * (Tk, dv)).  Layouts: Q, dQ [B][Hq][Tq][d]; K, dK [B][Hkv][Tk][d]; V, dV
  * [B][Hkv][Tk][dv]; O, dO [B][Hq][Tq][dv]; L as usual.  Supported: dv == d
- * (then identical to fa_fwd_window / fa_bwd_window), and for bf16 the pairs
- * (d, dv) = (128, 64) and (64, 128); anything else is FA_ERR_HEAD_DIM.  All
+ * (then identical to fa_fwd_window / fa_bwd_window), and in both dtypes the
+ * pairs (d, dv) = (128, 64) and (64, 128); anything else is FA_ERR_HEAD_DIM.  All
  * other arguments, ownership and errors are those of fa_fwd_window and
  * fa_bwd_window (the backward workspace does not depend on d or dv).
  */
@@ -322,7 +322,7 @@ int fa_bwd_paged(const void* Q, const void* K_pages, const void* V_pages, const 
  * Uncertainties", has full layers under a block mask and sliding-window
  * layers).  Rows without a
  * visible key get O = 0 and L = -inf.  Head dims as fa_fwd_dv: d = dv in
- * {64, 128} (fp32 also 32), and for bf16 (d, dv) = (128, 64) or (64, 128);
+ * {32, 64, 128}, and (d, dv) = (128, 64) or (64, 128);
  * V and O are dv wide.  The mask must be 16-byte aligned (it may be NULL only
  * when Tq * fa_mask_row_words(Tk) == 0).  Errors as fa_fwd_dv, plus
  * FA_ERR_BAD_SHAPE for a mask_batch_stride that is negative or between 0 and

@@ -133,7 +133,7 @@ def test_splitk_rejects_too_many_slices(lib):
                              4, None) == 7
 
 
-@pytest.mark.parametrize("d,dv,dtype", [(128, 96, 1), (128, 256, 1), (128, 64, 0), (64, 128, 0), (96, 64, 1)])
+@pytest.mark.parametrize("d,dv,dtype", [(128, 96, 1), (128, 256, 1), (32, 64, 0), (64, 32, 0), (96, 64, 1)])
 def test_dv_rejects_unsupported_pairs(lib, d, dv, dtype):
     assert lib.fa_fwd_dv(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 16, 16, d, dv, 1, 0, 0.125, dtype, None) == 4
     assert lib.fa_bwd_dv(*(FAKE,) * 10, 1 << 30, 1, 2, 1, 16, 16, d, dv, 1, 0, 0.125, dtype, 7, None) == 4
@@ -153,7 +153,7 @@ def test_fwd_paged_rejects_bad_arguments(lib, kw, status):
 @pytest.mark.parametrize("kw,status", [
     (dict(P=100), 2), (dict(P=0), 2), (dict(pps=0), 2), (dict(npages=0), 2), (dict(table=None), 1),
     (dict(seqlens=None), 1), (dict(table=FAKE + 2), 8), (dict(seqlens=FAKE + 1), 8), (dict(d=80), 4),
-    (dict(d=32), 4), (dict(ws=None), 7), (dict(wsb=4096), 7), (dict(ws=FAKE + 8), 8), (dict(Hkv=3), 3),
+    (dict(d=96), 4), (dict(ws=None), 7), (dict(wsb=4096), 7), (dict(ws=FAKE + 8), 8), (dict(Hkv=3), 3),
 ])
 def test_bwd_paged_rejects_bad_arguments(lib, kw, status):
     a = dict(table=FAKE, seqlens=FAKE, pps=4, P=128, npages=8, d=64, ws=FAKE, wsb=1 << 30, Hkv=1)
@@ -182,7 +182,7 @@ def test_mask_row_words(lib):
 @pytest.mark.parametrize("kw,status", [
     (dict(mask=None), 1), (dict(mask=FAKE + 4), 8), (dict(stride=-1), 2), (dict(stride=5), 2), (dict(stride=16 * 12 + 2), 8),
     (dict(d=80, dv=80), 4), (dict(Hkv=3), 3), (dict(scale=math.nan), 6), (dict(dv=96), 4),
-    (dict(d=128, dv=64, dtype=0), 4), (dict(d=64, dv=128, dtype=0), 4),
+    (dict(d=32, dv=64, dtype=0), 4), (dict(d=128, dv=32, dtype=0), 4),
 ])
 def test_fwd_mask_rejects_bad_arguments(lib, kw, status):
     a = dict(mask=FAKE, stride=0, d=64, dv=64, Hkv=2, scale=0.125, dtype=1)
@@ -201,7 +201,7 @@ def test_mask_pack_rejects_bad_arguments(lib, args, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(mask=None), 1), (dict(stride=-4), 2), (dict(stride=6), 2), (dict(ws=None), 7), (dict(wsb=64), 7),
-    (dict(d=80, dv=80), 4), (dict(dv=96), 4), (dict(d=128, dv=64, dtype=0), 4),
+    (dict(d=80, dv=80), 4), (dict(dv=96), 4), (dict(d=32, dv=64, dtype=0), 4),
 ])
 def test_bwd_mask_rejects_bad_arguments(lib, kw, status):
     a = dict(mask=FAKE, stride=0, ws=FAKE, wsb=1 << 30, d=64, dv=64, dtype=1)
@@ -254,10 +254,11 @@ def test_mask_splitk_workspace_and_arguments(lib):
                                   0, 0, 0.125, 1, 5000, None) == 9
 
 
-def test_head_dim_32_is_fp32_only(lib):
-    # d = 32 passes validation in fp32 (then fails on the NULL output) and is rejected in bf16
-    assert lib.fa_fwd(FAKE, FAKE, FAKE, None, FAKE, 1, 2, 1, 16, 16, 32, 0, 0.125, 0, None) == 1
-    assert lib.fa_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 1, 16, 16, 32, 0, 0.125, 1, None) == 4
+@pytest.mark.parametrize("d,status", [(32, 1), (64, 1), (128, 1), (16, 4), (96, 4), (256, 4)])
+def test_head_dims(lib, d, status):
+    # supported head dims pass validation in both dtypes (then fail on the NULL output)
+    for dtype in (0, 1):
+        assert lib.fa_fwd(FAKE, FAKE, FAKE, None, FAKE, 1, 2, 1, 16, 16, d, 0, 0.125, dtype, None) == status
 
 
 # Every entry point that takes a scale, called with arguments that pass every

@@ -79,6 +79,8 @@ DENSE = [
     ("bf16_d128_dv64", "bf16", 1, 4, 2, 131, 257, 128, 64, False, 0),
     ("bf16_d64_dv128", "bf16", 1, 2, 1, 131, 257, 64, 128, True, 0),
     ("fp32_d64", "fp32", 1, 2, 2, 130, 77, 64, 64, False, 0),
+    ("bf16_d32_causal", "bf16", 2, 4, 2, 200, 333, 32, 32, True, 0),
+    ("fp32_d128_dv64", "fp32", 1, 2, 1, 131, 257, 128, 64, True, 0),
     ("fp32_d32_causal", "fp32", 2, 4, 2, 201, 201, 32, 32, True, 0),
     ("fp32_d128", "fp32", 1, 2, 1, 70, 150, 128, 128, True, 0),
 ]

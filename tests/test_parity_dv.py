@@ -1,8 +1,8 @@
 """GPU parity of a value head dim different from the query/key head dim
-(fa_fwd_dv, fa_bwd_dv): bf16 with (d, dv) = (128, 64) and (64, 128), causal
-and not, GQA, ragged tails, a window, against the fp64 oracle (which takes
-V of width dv).  Tolerance 2e-2 relative Frobenius error over O, L, dQ, dK,
-dV; -inf rows of L must match.  Unsupported pairs are rejected.
+(fa_fwd_dv, fa_bwd_dv): (d, dv) = (128, 64) and (64, 128) in bf16 and fp32,
+causal and not, GQA, ragged tails, a window, against the fp64 oracle (which
+takes V of width dv).  Tolerance 2e-2 (bf16) / 1e-4 (fp32) relative Frobenius
+error over O, L, dQ, dK, dV; -inf rows of L must match.
 """
 
 import numpy as np
@@ -21,8 +21,11 @@ def fa(require_gpu):
     return fa_mod
 
 
-def case(name, B, Hq, Hkv, Tq, Tk, d, dv, causal, window=0, seed=41):
-    return wl.Workload(name, B, Hq, Hkv, Tq, Tk, d, "bf16", causal, seed, window=window, dv=dv)
+def case(name, B, Hq, Hkv, Tq, Tk, d, dv, causal, window=0, seed=41, dtype="bf16"):
+    return wl.Workload(name, B, Hq, Hkv, Tq, Tk, d, dtype, causal, seed, window=window, dv=dv)
+
+
+TOL = {"bf16": 2e-2, "fp32": 1e-4}
 
 
 CASES = [
@@ -34,6 +37,10 @@ CASES = [
     case("gqa_bf16_Tq333_Tk200_d64_dv128_causal", 1, 4, 2, 333, 200, 64, 128, True),
     case("gqa_bf16_T600_d128_dv64_causal_w100", 1, 8, 2, 600, 600, 128, 64, True, 100),
     case("gqa_bf16_T1024_d64_dv128_causal", 2, 8, 2, 1024, 1024, 64, 128, True),
+    case("gqa_fp32_T300_d128_dv64_causal", 2, 4, 2, 300, 300, 128, 64, True, dtype="fp32"),
+    case("gqa_fp32_T257_d64_dv128", 1, 4, 1, 257, 257, 64, 128, False, dtype="fp32"),
+    case("gqa_fp32_Tq200_Tk333_d64_dv128_causal_w70", 1, 4, 2, 200, 333, 64, 128, True, 70, dtype="fp32"),
+    case("gqa_fp32_Tq333_Tk200_d128_dv64", 1, 2, 1, 333, 200, 128, 64, False, dtype="fp32"),
 ]
 
 
@@ -56,13 +63,13 @@ def test_dv_parity(fa, w):
             "dK": oa.relative_frobenius(got["dK"], dK),
             "dV": oa.relative_frobenius(got["dV"], dV)}
     print(f"{w.name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
-    assert all(e <= 2e-2 for e in errs.values()), errs
+    assert all(e <= TOL[w.dtype] for e in errs.values()), errs
 
 
 def test_dv_unsupported_pairs_are_rejected(fa):
     import torch
     q = torch.zeros(1, 2, 8, 128, dtype=torch.float32, device="cuda")
     k = torch.zeros(1, 2, 8, 128, dtype=torch.float32, device="cuda")
-    v = torch.zeros(1, 2, 8, 64, dtype=torch.float32, device="cuda")
+    v = torch.zeros(1, 2, 8, 32, dtype=torch.float32, device="cuda")
     with pytest.raises(fa.FaError, match="HEAD_DIM"):
-        fa.forward(q, k, v)                        # dv != d is bf16-only
+        fa.forward(q, k, v)                        # (128, 32) is not a supported pair

@@ -43,6 +43,7 @@ CASES = [
     ("bf16_decode32_window", "bf16", 8, 2, 128, 32, [1000, 2100], 128, True, 300, 0),
     ("fp32_decode16_noncausal", "fp32", 4, 2, 64, 16, [77, 640], 128, False, 0, 1),
     ("fp32_d32_decode32_split", "fp32", 4, 2, 32, 32, [32, 300, 900], 128, True, 0, 0),
+    ("bf16_d32_decode32_split3", "bf16", 4, 2, 32, 32, [32, 300, 900], 128, True, 0, 3),
 ]
 
 

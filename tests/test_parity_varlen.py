@@ -40,6 +40,7 @@ CASES = [
     ("bf16_d128_decode_blocks", 8, 2, 128, "bf16", True, 0, [(32, 32), (32, 100), (32, 1000), (32, 2080), (32, 4000)]),
     ("fp32_d128_causal_mix", 2, 1, 128, "fp32", True, 0, [(100, 100), (200, 200), (33, 33)]),
     ("fp32_d32_causal_mix", 2, 1, 32, "fp32", True, 0, [(5, 5), (130, 130), (300, 300), (0, 0), (77, 200)]),
+    ("bf16_d32_causal_mix", 4, 2, 32, "bf16", True, 0, [(5, 5), (130, 130), (300, 300), (0, 0), (77, 200)]),
 ]
 
 
