@@ -41,7 +41,9 @@ constexpr float kTau = 8.0f;
 // (the fp32 shapes are small: 32 heads of 1000 rows make 256 workgroups, one
 // per compute unit, instead of 128), and 64-key tiles keep a workgroup's LDS
 // at 64 KiB (d = dv = 64) so two fit a compute unit, or within the LDS at all
-// when d or dv is 128.
+// when d or dv is 128.  bf16 d = 256 takes the same shape: its 256-wide output
+// accumulator (128 registers per wave) and Q operands need the register file
+// of one wave per SIMD, and 64-key tiles of 512-byte rows fill 128 KiB.
 // Decode shape (DEC): a packed workgroup of 4 waves, one per query head of a
 // K/V group with up to 32 rows each, against 64-key tiles.  Its 64 KiB of LDS
 // and at most 256 registers per wave (two waves per SIMD, asked of the
@@ -51,9 +53,9 @@ constexpr float kTau = 8.0f;
 // work, the bound.
 template <typename T, int D, bool DEC = false> struct FwdShape {
   static constexpr int QT = 1;
-  static constexpr int NW = DEC ? 4 : sizeof(T) == 4 ? 4 : 8;
+  static constexpr int NW = DEC ? 4 : (sizeof(T) == 4 || D == 256) ? 4 : 8;
   static constexpr int BQ = 32 * QT * NW;
-  static constexpr int BK = DEC ? 64 : sizeof(T) == 4 ? 64 : 128;
+  static constexpr int BK = DEC ? 64 : (sizeof(T) == 4 || D == 256) ? 64 : 128;
 };
 
 // D: head dim of Q and K; DV: head dim of V and O.  MASK: scores are also
@@ -439,7 +441,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream, int nsplit) {
             : launch2<64 * SH::NW>(fwd_kernel<T, D, CAUSAL, false, false, DV, true>, blocks, nsplit, stream, a);
     launched = true;
   }
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (sizeof(T) == 2 && D <= 128) {
     if (!launched && a.pack == 2) {
       using SD = FwdShape<T, D, true>;
       e = a.window > 0 ? launch2<64 * SD::NW>(fwd_kernel<T, D, CAUSAL, true, true, DV>, blocks, nsplit, stream, a)
@@ -479,14 +481,20 @@ hipError_t launch_mask_pack(const uint8_t* in, uint32_t* out, long long rows, in
 }
 
 int fwd_waves(int dtype_bf16, int d) {
-  return dtype_bf16 ? (d == 32 ? FwdShape<bf16, 32>::NW : d == 64 ? FwdShape<bf16, 64>::NW : FwdShape<bf16, 128>::NW)
+  return dtype_bf16 ? (d == 32    ? FwdShape<bf16, 32>::NW
+                       : d == 64  ? FwdShape<bf16, 64>::NW
+                       : d == 256 ? FwdShape<bf16, 256>::NW
+                                  : FwdShape<bf16, 128>::NW)
                     : (d == 32 ? FwdShape<float, 32>::NW
                                : d == 64 ? FwdShape<float, 64>::NW : FwdShape<float, 128>::NW);
 }
 int fwd_decode_waves() { return FwdShape<bf16, 128, true>::NW; }
 int fwd_decode_block_keys() { return FwdShape<bf16, 128, true>::BK; }
 int fwd_block_keys(int dtype_bf16, int d) {
-  return dtype_bf16 ? (d == 32 ? FwdShape<bf16, 32>::BK : d == 64 ? FwdShape<bf16, 64>::BK : FwdShape<bf16, 128>::BK)
+  return dtype_bf16 ? (d == 32    ? FwdShape<bf16, 32>::BK
+                       : d == 64  ? FwdShape<bf16, 64>::BK
+                       : d == 256 ? FwdShape<bf16, 256>::BK
+                                  : FwdShape<bf16, 128>::BK)
                     : (d == 32 ? FwdShape<float, 32>::BK
                                : d == 64 ? FwdShape<float, 64>::BK : FwdShape<float, 128>::BK);
 }
@@ -517,6 +525,7 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype_bf16, int d, int causal, hipSt
     FA_FWD_CASE(bf16, 32)
     FA_FWD_CASE(bf16, 64)
     FA_FWD_CASE(bf16, 128)
+    FA_FWD_CASE(bf16, 256)
   } else {
     FA_FWD_CASE(float, 32)
     FA_FWD_CASE(float, 64)

@@ -75,7 +75,7 @@ def bwd(lib, ws=FAKE, ws_bytes=1 << 30, Q=FAKE, dQ=FAKE, B=1, Hq=2, Hkv=1, Tq=16
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2), (dict(Tq=-1), 2), (dict(Tk=-5), 2),
-    (dict(Hq=3, Hkv=2), 3), (dict(d=96), 4), (dict(d=256), 4), (dict(dtype=7), 5),
+    (dict(Hq=3, Hkv=2), 3), (dict(d=96), 4), (dict(d=256, dtype=0), 4), (dict(dtype=7), 5),
     (dict(scale=math.inf), 6), (dict(scale=math.nan), 6),
     (dict(Q=None), 1), (dict(L=None), 1), (dict(V=FAKE + 4), 8), (dict(Tq=1 << 25), 9),
 ])
@@ -254,11 +254,26 @@ def test_mask_splitk_workspace_and_arguments(lib):
                                   0, 0, 0.125, 1, 5000, None) == 9
 
 
-@pytest.mark.parametrize("d,status", [(32, 1), (64, 1), (128, 1), (16, 4), (96, 4), (256, 4)])
-def test_head_dims(lib, d, status):
-    # supported head dims pass validation in both dtypes (then fail on the NULL output)
-    for dtype in (0, 1):
+@pytest.mark.parametrize("d,fp32,bf16", [(32, 1, 1), (64, 1, 1), (128, 1, 1), (16, 4, 4), (96, 4, 4), (256, 4, 1)])
+def test_head_dims(lib, d, fp32, bf16):
+    # supported head dims pass validation (then fail on the NULL output); 256 is bf16 only
+    for dtype, status in ((0, fp32), (1, bf16)):
         assert lib.fa_fwd(FAKE, FAKE, FAKE, None, FAKE, 1, 2, 1, 16, 16, d, 0, 0.125, dtype, None) == status
+
+
+def test_head_dim_256_is_forward_only(lib):
+    W = 1 << 30
+    assert lib.fa_bwd(*(FAKE,) * 10, W, 1, 2, 1, 16, 16, 256, 1, 0.125, 1, None) == 4
+    assert lib.fa_bwd_mask(*(FAKE,) * 10, W, FAKE, 0, 1, 2, 1, 16, 16, 256, 256, 1, 0, 0.125, 1, None) == 4
+    assert lib.fa_bwd_paged(*(FAKE,) * 11, 2, 2, 1, 16, 4, 128, 8, 256, 1, 0, 0.125, 1, FAKE, W, None) == 4
+    assert lib.fa_bwd_noalloc(*(FAKE,) * 9, 1, 2, 1, 16, 16, 256, 1, 0.125, 1, None) == 4
+    for f in (lambda: lib.fa_bwd_workspace_bytes(1, 2, 1, 16, 16, 256, 1),
+              lambda: lib.fa_bwd_mask_workspace_bytes(1, 2, 1, 16, 16, 256, 1, 0),
+              lambda: lib.fa_bwd_paged_workspace_bytes(2, 2, 1, 16, 4, 128, 256, 1)):
+        assert f() == 0
+    # the forward entry points take it
+    assert lib.fa_fwd_mask(FAKE, FAKE, FAKE, None, FAKE, FAKE, 0, 2, 4, 2, 16, 300, 256, 256, 1, 0, 0.125, 1,
+                           None) == 1
 
 
 # Every entry point that takes a scale, called with arguments that pass every
