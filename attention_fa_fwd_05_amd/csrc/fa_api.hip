@@ -50,7 +50,7 @@ int check_common(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Tq < 0 || Tk < 0) return FA_ERR_BAD_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_GQA_RATIO;
   // 32 (the measured configuration of the tiling article), 64 and 128; bf16
-  // also 256, forward only (the backward entry points refuse it)
+  // also 256
   if (d != 32 && d != 64 && d != 128 && !(d == 256 && dtype == FA_DTYPE_BF16)) return FA_ERR_HEAD_DIM;
   if (dtype != FA_DTYPE_F32 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
   if (Tq > kMaxSeq || Tk > kMaxSeq) return FA_ERR_TOO_LARGE;
@@ -136,9 +136,6 @@ int mask_splits(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype, int ns
   ns = ns < 64 ? ns : 64;
   return ns < 1 ? 1 : (int)ns;
 }
-
-// Head dims the backward kernels are built for: all of check_common's but 256.
-int check_bwd_dim(int d) { return d == 256 ? FA_ERR_HEAD_DIM : FA_OK; }
 
 // Head dim of V (and O, dO, dV): equal to d, or 64 with d = 128 and 128 with
 // d = 64 (both dtypes).
@@ -252,8 +249,7 @@ size_t fa_bwd_paged_workspace_bytes(int B, int Hq, int Hkv, int Tq, int pages_pe
                                     int dtype) {
   if (pages_per_seq < 1 || page_size < 1 || page_size % 128 != 0) return 0;
   const long long tk = (long long)pages_per_seq * page_size;
-  if (tk > kMaxSeq || check_common(B, Hq, Hkv, Tq, (int)tk, d, dtype) != FA_OK || check_bwd_dim(d) != FA_OK)
-    return 0;
+  if (tk > kMaxSeq || check_common(B, Hq, Hkv, Tq, (int)tk, d, dtype) != FA_OK) return 0;
   return paged_ws(B, Hq, Hkv, Tq, tk, d, dtype).total;
 }
 
@@ -268,7 +264,6 @@ int fa_bwd_paged(const void* Q, const void* K_pages, const void* V_pages, const 
   if (tk > kMaxSeq) return FA_ERR_TOO_LARGE;
   int st = check_common(B, Hq, Hkv, Tq, (int)tk, d, dtype);
   if (st != FA_OK) return st;
-  if ((st = check_bwd_dim(d)) != FA_OK) return st;
   if (page_table == nullptr || seqlens_k == nullptr) return FA_ERR_NULL_PTR;
   if ((reinterpret_cast<uintptr_t>(page_table) & 3u) || (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
     return FA_ERR_ALIGNMENT;
@@ -521,8 +516,7 @@ int fa_fwd_varlen_mask(const void* Q, const void* K, const void* V, void* O, flo
 
 size_t fa_bwd_mask_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype,
                                    long long mask_batch_stride) {
-  if (check_common(B, Hq, Hkv, Tq, Tk, d, dtype) != FA_OK || check_bwd_dim(d) != FA_OK || mask_batch_stride < 0)
-    return 0;
+  if (check_common(B, Hq, Hkv, Tq, Tk, d, dtype) != FA_OK || mask_batch_stride < 0) return 0;
   return ws_layout(B, Hq, Tq, d, dtype).total + mask_t_bytes(B, Tq, Tk, mask_batch_stride);
 }
 
@@ -649,7 +643,7 @@ int fa_fwd_paged(const void* Q, const void* K_pages, const void* V_pages, void* 
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype) {
-  if (check_common(B, Hq, Hkv, Tq, Tk, d, dtype) != FA_OK || check_bwd_dim(d) != FA_OK) return 0;
+  if (check_common(B, Hq, Hkv, Tq, Tk, d, dtype) != FA_OK) return 0;
   return ws_layout(B, Hq, Tq, d, dtype).total;
 }
 
@@ -708,7 +702,6 @@ int bwd_core(const void* Q, const void* K, const void* V, const void* O, const f
              const uint32_t* mask, long long mask_bstride, bool validate_only, const int* seqlens_k) {
   int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
   if (st != FA_OK) return st;
-  if ((st = check_bwd_dim(d)) != FA_OK) return st;
   if ((st = check_dv(d, dv, dtype)) != FA_OK) return st;
   const bool varlen = cu_q != nullptr;
   const long long rows = varlen ? (long long)Hq * total_q : (long long)B * Hq * Tq;

@@ -113,8 +113,10 @@ __global__ __launch_bounds__(256) void mask_transpose_kernel(BwdArgs a, long lon
   a.mask_t[b * a.mask_t_bstride + (size_t)j * rwq + w] = v;
 }
 
-// D: head dim of Q, K, dK; DV: of V, dO, dV.
-template <typename T, int D, bool CAUSAL, bool WIN, int DV = D, bool MASK = false>
+// D: head dim of Q, K, dK; DV: of V, dO, dV.  HSPLIT: each workgroup forms
+// one half of the columns of dK and dV (blockIdx.y; S and dP still contract
+// over the whole head dim), so that a 256-wide head's accumulators fit.
+template <typename T, int D, bool CAUSAL, bool WIN, int DV = D, bool MASK = false, bool HSPLIT = false>
 __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   using M = MM<T>;
   typedef typename M::Op Op;
@@ -124,13 +126,13 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   constexpr int NSD = (D / 2) / KPER;               // contraction steps over d (S = Q K^T)
   constexpr int NSDV = (DV / 2) / KPER;             // ... over dv (dP = dO V^T)
   constexpr int NSQ = (BQ / 2) / KPER;              // contraction steps over a query block
-  constexpr int NDT = D / 32;                       // 32-wide dK tiles
-  constexpr int NDTV = DV / 32;                     // 32-wide dV tiles
+  constexpr int NDT = D / (HSPLIT ? 64 : 32);       // 32-wide dK tiles (of this workgroup's half)
+  constexpr int NDTV = DV / (HSPLIT ? 64 : 32);     // 32-wide dV tiles
   constexpr int NPS = NDT + NDTV;                   // dV and dK products per query step
   constexpr int NSH = NSQ / 2;                      // steps per 32-query tile
   // Three LDS buffers let block i+2 load while blocks i and i+1 are read;
   // fp32 with d = 128 fits two, and then loads without overlap.
-  constexpr int NB = (sizeof(T) == 4 && D == 128) ? 2 : 3;
+  constexpr int NB = ((sizeof(T) == 4 && D == 128) || D == 256) ? 2 : 3;
   // Software pipeline over the query blocks of the work list, iteration i:
   //   phase 1a: S, dP of block i+1 tile 0  |  dV, dK of block i, first quarter
   //             of its query steps  |  P, dS of block i tile 1;
@@ -170,6 +172,8 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
   const KWork wk = kblock_work(a, nkb);
   const int G = a.Hq / a.Hkv;
   const int k0 = wk.kb * BK, kw = k0 + 32 * w, mykey = kw + n;
+  const int T0 = HSPLIT ? (int)blockIdx.y * NDT : 0;      // first dK tile (and dV tile) of the half
+  const int T0V = HSPLIT ? (int)blockIdx.y * NDTV : 0;
   // This workgroup's sequence (a variable-length batch has its own lengths
   // and rows; the grid covers the longest).  No key of it here: leave before
   // any barrier (uniform).
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
     auto d_fetch = [&](int m) -> Op {
       const int s = m / NPS, r = m % NPS;
       const int t = interleave_rank(r, NDTV, NDT);
-      return interleave_is_b(r, NDTV, NDT) ? trp.ld(cQ, t, s) : tr_o(cdO, t, s);
+      return interleave_is_b(r, NDTV, NDT) ? trp.ld(cQ, T0 + t, s) : tr_o(cdO, T0V + t, s);
     };
     // Phases 1a and 1b: tile u of block i+1's S, dP interleaved with quarter u
     // of block i's dV, dK.
@@ -558,9 +562,10 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int d0 = t * 32 + 8 * g + 4 * h;
         if (t < NDT)
-          store4(dKr + d0, dk[t][4 * g] * sc, dk[t][4 * g + 1] * sc, dk[t][4 * g + 2] * sc,
+          store4(dKr + T0 * 32 + d0, dk[t][4 * g] * sc, dk[t][4 * g + 1] * sc, dk[t][4 * g + 2] * sc,
                  dk[t][4 * g + 3] * sc);
-        if (t < NDTV) store4(dVr + d0, dv[t][4 * g], dv[t][4 * g + 1], dv[t][4 * g + 2], dv[t][4 * g + 3]);
+        if (t < NDTV)
+          store4(dVr + T0V * 32 + d0, dv[t][4 * g], dv[t][4 * g + 1], dv[t][4 * g + 2], dv[t][4 * g + 3]);
       }
     }
   }
@@ -569,7 +574,7 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdArgs a) {
 // Waves per dQ workgroup: 8 (256 query rows), or 4 where fp32 d = 128
 // operands would not fit in 256 registers.
 template <typename T, int D>
-constexpr int dq_waves() { return sizeof(T) == 4 || D == 32 ? 4 : 8; }
+constexpr int dq_waves() { return sizeof(T) == 4 || D == 32 || D == 256 ? 4 : 8; }
 
 // D: head dim of Q, K, dQ; DV: of V and dO.
 template <typename T, int D, bool CAUSAL, bool WIN, int DV = D, bool MASK = false>
@@ -837,8 +842,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   const long long kblocks = (long long)((a.Tk + 127) / 128) * a.B * a.Hkv;
   constexpr int NW = dq_waves<T, D>();
   const long long qblocks = (long long)((a.Tq + 32 * NW - 1) / (32 * NW)) * a.B * a.Hq;
-  // bf16: the dK/dV pass on wave pairs (fa_dkdv.hip).
-  constexpr bool kPair = sizeof(T) == 2;
+  // bf16: the dK/dV pass on wave pairs (fa_dkdv.hip); d = 256 on the 4-wave
+  // kernel, each workgroup forming half the columns of dK and dV (grid y).
+  constexpr bool kPair = sizeof(T) == 2 && D <= 128;
+  constexpr bool kHalf = D == 256;
+  constexpr int kNy = kHalf ? 2 : 1;
   // A boolean mask: its key-major copy, then the masked passes (with or
   // without a window).
   if (a.mask != nullptr) {
@@ -848,8 +856,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t stream) {
       hipError_t e = launch(mask_transpose_kernel, (words + 255) / 256, stream, a, entries);
       if (e == hipSuccess) {
         if constexpr (kPair) e = launch_dkdv_pair(a, D, DV, CAUSAL, stream);
-        else e = a.window > 0 ? launch(dkdv_kernel<T, D, CAUSAL, true, DV, true>, kblocks, stream, a)
-                              : launch(dkdv_kernel<T, D, CAUSAL, false, DV, true>, kblocks, stream, a);
+        else e = a.window > 0 ? launch2(dkdv_kernel<T, D, CAUSAL, true, DV, true, kHalf>, kblocks, kNy, stream, a)
+                              : launch2(dkdv_kernel<T, D, CAUSAL, false, DV, true, kHalf>, kblocks, kNy, stream, a);
       }
       if (e != hipSuccess) return e;
     }
@@ -863,8 +871,8 @@ hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t stream) {
   if ((stages & kStageDkDv) && kblocks > 0) {
     hipError_t e;
     if constexpr (kPair) e = launch_dkdv_pair(a, D, DV, CAUSAL, stream);
-    else e = a.window > 0 ? launch(dkdv_kernel<T, D, CAUSAL, true, DV>, kblocks, stream, a)
-                          : launch(dkdv_kernel<T, D, CAUSAL, false, DV>, kblocks, stream, a);
+    else e = a.window > 0 ? launch2(dkdv_kernel<T, D, CAUSAL, true, DV, false, kHalf>, kblocks, kNy, stream, a)
+                          : launch2(dkdv_kernel<T, D, CAUSAL, false, DV, false, kHalf>, kblocks, kNy, stream, a);
     if (e != hipSuccess) return e;
   }
   if ((stages & kStageDq) && qblocks > 0) {
@@ -901,6 +909,7 @@ hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int d, int causal, unsig
     FA_BWD_CASE(bf16, 32)
     FA_BWD_CASE(bf16, 64)
     FA_BWD_CASE(bf16, 128)
+    FA_BWD_CASE(bf16, 256)
   } else {
     FA_BWD_CASE(float, 32)
     FA_BWD_CASE(float, 64)

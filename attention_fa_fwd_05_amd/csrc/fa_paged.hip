@@ -133,6 +133,7 @@ hipError_t launch_paged(const PagedBwdArgs& p, int dtype_bf16, int d, int phase,
     if (d == 32) return launch_paged_t<bf16, 32>(p, phase, stream);
     if (d == 64) return launch_paged_t<bf16, 64>(p, phase, stream);
     if (d == 128) return launch_paged_t<bf16, 128>(p, phase, stream);
+    if (d == 256) return launch_paged_t<bf16, 256>(p, phase, stream);
   } else {
     if (d == 32) return launch_paged_t<float, 32>(p, phase, stream);
     if (d == 64) return launch_paged_t<float, 64>(p, phase, stream);

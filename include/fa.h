@@ -29,9 +29,7 @@
  *  - dtype: FA_DTYPE_F32 (float) or FA_DTYPE_BF16 (bfloat16 storage, float32
  *    accumulation, outputs rounded to nearest even).  It applies to Q, K, V,
  *    O, dO, dQ, dK, dV.
- *  - d (head dimension, equal for Q/K and V): 32, 64 or 128; bf16 also 256 in
- *    the forward entry points (every backward entry point returns
- *    FA_ERR_HEAD_DIM for 256, and the backward workspace functions 0).
+ *  - d (head dimension, equal for Q/K and V): 32, 64 or 128; bf16 also 256.
  *  - GQA: Hq must be a multiple of Hkv; query head h reads K/V head
  *    h / (Hq / Hkv).  dK and dV are summed over the query heads of a group.
  *  - causal != 0: key j is visible to query i iff j <= i + (Tk - Tq)
@@ -69,7 +67,7 @@ typedef enum {
   FA_ERR_NULL_PTR = 1,   /* a required pointer is NULL */
   FA_ERR_BAD_SHAPE = 2,  /* B, Hq or Hkv < 1, Tq or Tk < 0 */
   FA_ERR_GQA_RATIO = 3,  /* Hq is not a multiple of Hkv */
-  FA_ERR_HEAD_DIM = 4,   /* d is not 32, 64, 128 (bf16 forward: or 256), or an unsupported (d, dv) pair */
+  FA_ERR_HEAD_DIM = 4,   /* d is not 32, 64, 128 (bf16: or 256), or an unsupported (d, dv) pair */
   FA_ERR_DTYPE = 5,      /* dtype is not an fa_dtype value */
   FA_ERR_SCALE = 6,      /* scale is NaN, infinite, zero or negative */
   FA_ERR_WORKSPACE = 7,  /* workspace missing or smaller than fa_bwd_workspace_bytes */

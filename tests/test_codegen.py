@@ -9,7 +9,7 @@ is one of those helper sequences, that no other instruction that reads M0
 appears, and that register-indexing brackets (s_set_gpr_idx_on .. _off, which
 keep their index in M0; the compiler emits them only in the fp32 d = 128
 test-path kernel) contain no direct load.  It also checks that the bf16 kernels keep everything in registers
-(no scratch), which the schedules assume.
+(no scratch), which the schedules assume (head dim 256's backward excepted).
 """
 
 import os
@@ -76,7 +76,11 @@ def test_bf16_kernels_use_no_scratch(asm):
     for src, text in asm.items():
         for m in re.finditer(r"\.amdhsa_kernel (_ZN2fa\w+)(.*?)\.end_amdhsa_kernel", text, flags=re.S):
             name, desc = m.group(1), m.group(2)
-            if "DF16b" not in name:
+            if "DF16b" not in name and "dkdv_pair_kernel" not in name:
+                continue
+            # head dim 256's backward (a 256-wide dQ accumulator, or half of dK and dV beside the
+            # whole of K and V) fills the register file of one wave per SIMD; it may spill.
+            if ("dkdv_kernel" in name or "dq_kernel" in name) and "Li256E" in name:
                 continue
             size = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", desc).group(1))
             assert size == 0, f"{src}:{name} uses {size} bytes of scratch per lane"

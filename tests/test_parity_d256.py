@@ -1,15 +1,16 @@
-"""GPU parity of head dim 256 (bf16, forward only) against the fp64 oracle.
+"""GPU parity of head dim 256 (bf16) against the fp64 oracle.
 
 The forward runs 4-wave, 128-row workgroups against 64-key tiles of 512-byte
-rows (one wave per SIMD holds the 256-wide output accumulator).  The backward
-kernels are not built for d = 256: every backward entry point refuses it with
-FA_ERR_HEAD_DIM, and the backward workspace functions return 0.
+rows (one wave per SIMD holds the 256-wide output accumulator); the dQ pass
+4-wave workgroups; the dK/dV pass the 4-wave kernel with each workgroup
+forming one half of the columns of dK and dV.
 
 Cases: causal and not, GQA, ragged lengths, Tq != Tk both ways, a sliding
-window, the key-split forward (automatic and 3 slices, 32 queries against
-1000 keys), a boolean mask, variable-length and paged batches.  O and L at
-relative Frobenius error 2e-2 and the per-row bound of parity_tools; rows
-without keys give O = 0, L = -inf.
+window (forward and backward); the key-split forward (automatic and 3 slices,
+32 queries against 1000 keys); a boolean mask (forward and backward);
+variable-length and paged batches (forward).  O, L, dQ, dK, dV at relative
+Frobenius error 2e-2 and the per-row bound of parity_tools; rows without keys
+give O = 0, L = -inf.
 """
 
 import numpy as np
@@ -52,14 +53,19 @@ def got_of(o, lse):
 
 
 @pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
-def test_d256_forward_parity(fa, w):
+def test_d256_parity(fa, w):
     import torch
     print(f"case {w.name}", flush=True)
     inp = wl.make_inputs(w)
-    q, k, v, _ = wl.to_device(inp, w.dtype)
+    q, k, v, do = wl.to_device(inp, w.dtype)
     o, lse = fa.forward(q, k, v, w.causal, w.scale, window=w.window)
+    dq, dk, dv = fa.backward(q, k, v, o, lse, do, w.causal, w.scale, window=w.window)
     torch.cuda.synchronize()
-    check(w.name, "bf16", errors(got_of(o, lse), ref_fwd(inp, w)))
+    got = got_of(o, lse)
+    got.update({n: t.float().cpu().numpy() for n, t in (("dQ", dq), ("dK", dk), ("dV", dv))})
+    ref = dict(zip(("O", "L", "dQ", "dK", "dV"),
+                   oa.attention_forward_backward(inp.q, inp.k, inp.v, inp.do, w.causal, w.scale, window=w.window)))
+    check(w.name, "bf16", errors(got, ref))
 
 
 def test_d256_split_and_mask(fa):
@@ -73,9 +79,16 @@ def test_d256_split_and_mask(fa):
         torch.cuda.synchronize()
         check(f"{w.name} nsplit={ns}", "bf16", errors(got_of(o, lse), ref))
     mask = np.random.default_rng(73).random((w.B, w.Tq, w.Tk)) < 0.5
-    o, lse = fa.forward_masked(q, k, v, torch.from_numpy(mask).cuda(), True, w.scale)
+    m = torch.from_numpy(mask).cuda()
+    do = wl.to_device(inp, w.dtype)[3]
+    o, lse = fa.forward_masked(q, k, v, m, True, w.scale)
+    dq, dk, dv = fa.backward_masked(q, k, v, o, lse, do, m, True, w.scale)
     torch.cuda.synchronize()
-    check(f"{w.name} mask", "bf16", errors(got_of(o, lse), ref_fwd(inp, w, mask)))
+    got = got_of(o, lse)
+    got.update({n: t.float().cpu().numpy() for n, t in (("dQ", dq), ("dK", dk), ("dV", dv))})
+    ref = dict(zip(("O", "L", "dQ", "dK", "dV"),
+                   oa.attention_forward_backward(inp.q, inp.k, inp.v, inp.do, True, w.scale, mask=mask)))
+    check(f"{w.name} mask", "bf16", errors(got, ref))
 
 
 def test_d256_varlen_and_paged(fa):
@@ -125,13 +138,3 @@ def test_d256_varlen_and_paged(fa):
                                       True, wq.scale)
         O[b], L[b] = Ob[0], Lb[0]
     check("d256 paged", "bf16", errors(got_of(o, lse), {"O": O, "L": L}))
-
-
-def test_d256_backward_is_refused(fa):
-    import torch
-    q = torch.zeros(1, 2, 64, 256, dtype=torch.bfloat16, device="cuda")
-    o, lse = fa.forward(q, q, q)
-    with pytest.raises((fa.FaError, ValueError)):
-        fa.backward(q, q, q, o, lse, o)
-    lib = fa.load_library()
-    assert lib.fa_bwd_workspace_bytes(1, 2, 2, 64, 64, 256, fa.FA_DTYPE_BF16) == 0

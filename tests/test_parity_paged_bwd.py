@@ -7,7 +7,7 @@ two slots of one sequence to the same page, and one sequence has no keys.
 Covered: decode-like blocks (16, 32 and 64 new queries) and 300-query blocks
 against key counts from 0 to 2100 (tails that end inside a page, rows with no
 visible key under end-aligned causal), page sizes 128 and 256, a window, GQA,
-bf16 d = 32, 64 and 128, fp32 d = 32, 64 and 128.  Checked: dQ and the gradient
+bf16 d = 32, 64, 128 and 256, fp32 d = 32, 64 and 128.  Checked: dQ and the gradient
 pools, whole-tensor relative Frobenius error 1e-4 (fp32) / 2e-2 (bf16) and the
 per-row bound of parity_tools; pages no entry references and pool rows no
 sequence reads are exactly zero; two calls agree bit for bit.
@@ -45,6 +45,7 @@ CASES = [
     ("fp32_d64_decode16_noncausal", "fp32", 4, 2, 64, 16, [77, 640], 128, False, 0, False),
     ("fp32_d128_q40_empty_seq", "fp32", 2, 1, 128, 40, [0, 129, 257], 128, True, 0, False),
     ("bf16_d32_decode32_p128", "bf16", 4, 2, 32, 32, [32, 300, 900], 128, True, 0, True),
+    ("bf16_d256_decode32_p128", "bf16", 4, 2, 256, 32, [32, 300, 600], 128, True, 0, False),
 ]
 
 

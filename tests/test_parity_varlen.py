@@ -41,6 +41,7 @@ CASES = [
     ("fp32_d128_causal_mix", 2, 1, 128, "fp32", True, 0, [(100, 100), (200, 200), (33, 33)]),
     ("fp32_d32_causal_mix", 2, 1, 32, "fp32", True, 0, [(5, 5), (130, 130), (300, 300), (0, 0), (77, 200)]),
     ("bf16_d32_causal_mix", 4, 2, 32, "bf16", True, 0, [(5, 5), (130, 130), (300, 300), (0, 0), (77, 200)]),
+    ("bf16_d256_causal_mix", 2, 1, 256, "bf16", True, 0, [(5, 5), (130, 130), (300, 300), (0, 0), (77, 200)]),
 ]
 
 
