@@ -3,11 +3,15 @@
 // FlashAttention's second idea": keep O and the row statistic L, rebuild the
 // rest; "Backward Pass Implementation", section "The Recomputation Strategy").
 //
-// Three launches on one stream:
+// Two launches on one stream (dQ pass first), or three when the caller runs
+// the preprocessing on its own:
 //  1. bwd_pre_kernel: -D_i = -rowsum(dO_i * O_i) and L_i in log2 units (+inf
 //     for rows without keys, so their probabilities vanish).  Rows are padded
 //     to a multiple of 64 per head (padding: -D = 0, L2 = +inf).  The negated
-//     D seeds the dP accumulators, which then hold dP - D directly.
+//     D seeds the dP accumulators, which then hold dP - D directly.  When the
+//     dQ pass runs in the same call it forms these rows itself (each lane has
+//     its query's dO in registers and reads O alongside) and writes them for
+//     the dK/dV pass, which then follows it; this kernel is skipped.
 //  2. dkdv_kernel: one workgroup per (128-key block, b, K/V head); each of the
 //     4 waves owns 32 keys, whose K and V rows sit in registers, and dK, dV
 //     accumulate in registers across every query block of every query head of
@@ -684,8 +688,32 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
       if (!q_ok) gop[s] = Op{};
     }
   }
-  const float l2 = q_ok ? a.Lg[(size_t)bh * a.Tqp + myq] : INFINITY;
-  const float ndd = q_ok ? a.Dvec[(size_t)bh * a.Tqp + myq] : 0.f;   // -D of this lane's query
+  // L2 and -D of this lane's query: read from the workspace, or formed here
+  // (-D = -rowsum(dO * O): this lane's half of the row against its dO
+  // operands, then the other half's from lane n + 32 h') and written there
+  // for the dK/dV pass, padding rows (+inf, 0) included.
+  float l2, ndd;
+  if (a.fuse_pre) {
+    const T* Orow = reinterpret_cast<const T*>(a.O) + (qrow0 + (q_ok ? myq : 0)) * DV + h * (DV / 2);
+    float acc = 0.f;
+#pragma unroll
+    for (int s = 0; s < NSDV; ++s) {
+      const Op o = M::ld(Orow + s * KPER);
+#pragma unroll
+      for (int e = 0; e < KPER; ++e) acc += (float)o[e] * (float)gop[s][e];
+    }
+    acc += __shfl_xor(acc, 32, 64);
+    const float l = q_ok ? a.L[qrow0 + myq] : -INFINITY;
+    l2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    ndd = q_ok ? -acc : 0.f;
+    if (h == 0 && myq < a.Tqp) {
+      a.Lg[(size_t)bh * a.Tqp + myq] = l2;
+      a.Dvec[(size_t)bh * a.Tqp + myq] = ndd;
+    }
+  } else {
+    l2 = q_ok ? a.Lg[(size_t)bh * a.Tqp + myq] : INFINITY;
+    ndd = q_ok ? a.Dvec[(size_t)bh * a.Tqp + myq] : 0.f;
+  }
   // Operand fetch: bf16 from one base register per tile (XorFetch); fp32
   // (test shapes only) from offset tables.
   XorFetch<D> xf;
@@ -833,54 +861,54 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
 }
 
 template <typename T, int D, bool CAUSAL, int DV = D>
-hipError_t launch_bwd_t(const BwdArgs& a, unsigned stages, hipStream_t stream) {
-  const long long prows = (long long)a.B * a.Hq * a.Tqp;
-  if ((stages & kStagePre) && prows > 0) {
-    hipError_t e = launch(bwd_pre_kernel<T, DV>, (prows + 15) / 16, stream, a);
-    if (e != hipSuccess) return e;
-  }
-  const long long kblocks = (long long)((a.Tk + 127) / 128) * a.B * a.Hkv;
+hipError_t launch_bwd_t(const BwdArgs& args, unsigned stages, hipStream_t stream) {
+  const long long prows = (long long)args.B * args.Hq * args.Tqp;
+  const long long kblocks = (long long)((args.Tk + 127) / 128) * args.B * args.Hkv;
   constexpr int NW = dq_waves<T, D>();
-  const long long qblocks = (long long)((a.Tq + 32 * NW - 1) / (32 * NW)) * a.B * a.Hq;
+  const long long qblocks = (long long)((args.Tq + 32 * NW - 1) / (32 * NW)) * args.B * args.Hq;
   // bf16: the dK/dV pass on wave pairs (fa_dkdv.hip); d = 256 on the 4-wave
   // kernel, each workgroup forming half the columns of dK and dV (grid y).
   constexpr bool kPair = sizeof(T) == 2 && D <= 128;
   constexpr bool kHalf = D == 256;
   constexpr int kNy = kHalf ? 2 : 1;
-  // A boolean mask: its key-major copy, then the masked passes (with or
-  // without a window).
+  // Order: the dQ pass first, forming every row's -D and L2 itself and
+  // writing them for the dK/dV pass (no separate preprocessing pass over O
+  // and dO); without the dQ pass, bwd_pre_kernel writes them.
+  BwdArgs a = args;
+  a.fuse_pre = (stages & kStageDq) && qblocks > 0;
+  hipError_t e = hipSuccess;
+  if (!a.fuse_pre && (stages & kStagePre) && prows > 0) {
+    if ((e = launch(bwd_pre_kernel<T, DV>, (prows + 15) / 16, stream, a)) != hipSuccess) return e;
+  }
+  if (a.fuse_pre) {
+    if (a.mask != nullptr)
+      e = a.window > 0 ? launch<64 * NW>(dq_kernel<T, D, CAUSAL, true, DV, true>, qblocks, stream, a)
+                       : launch<64 * NW>(dq_kernel<T, D, CAUSAL, false, DV, true>, qblocks, stream, a);
+    else
+      e = a.window > 0 ? launch<64 * NW>(dq_kernel<T, D, CAUSAL, true, DV>, qblocks, stream, a)
+                       : launch<64 * NW>(dq_kernel<T, D, CAUSAL, false, DV>, qblocks, stream, a);
+    if (e != hipSuccess) return e;
+  }
+  if (!(stages & kStageDkDv) || kblocks <= 0) return hipSuccess;
+  // A boolean mask: its key-major copy, then the masked pass (with or without
+  // a window).
   if (a.mask != nullptr) {
-    if ((stages & kStageDkDv) && kblocks > 0) {
-      const long long entries = a.mask_bstride != 0 ? a.B : 1;
-      const long long words = entries * a.Tk * a.mask_t_row_words;
-      hipError_t e = launch(mask_transpose_kernel, (words + 255) / 256, stream, a, entries);
-      if (e == hipSuccess) {
-        if constexpr (kPair) e = launch_dkdv_pair(a, D, DV, CAUSAL, stream);
-        else e = a.window > 0 ? launch2(dkdv_kernel<T, D, CAUSAL, true, DV, true, kHalf>, kblocks, kNy, stream, a)
-                              : launch2(dkdv_kernel<T, D, CAUSAL, false, DV, true, kHalf>, kblocks, kNy, stream, a);
-      }
-      if (e != hipSuccess) return e;
+    const long long entries = a.mask_bstride != 0 ? a.B : 1;
+    const long long words = entries * a.Tk * a.mask_t_row_words;
+    if ((e = launch(mask_transpose_kernel, (words + 255) / 256, stream, a, entries)) != hipSuccess) return e;
+    if constexpr (kPair) {
+      return launch_dkdv_pair(a, D, DV, CAUSAL, stream);
+    } else {
+      return a.window > 0 ? launch2(dkdv_kernel<T, D, CAUSAL, true, DV, true, kHalf>, kblocks, kNy, stream, a)
+                          : launch2(dkdv_kernel<T, D, CAUSAL, false, DV, true, kHalf>, kblocks, kNy, stream, a);
     }
-    if ((stages & kStageDq) && qblocks > 0) {
-      hipError_t e = a.window > 0 ? launch<64 * NW>(dq_kernel<T, D, CAUSAL, true, DV, true>, qblocks, stream, a)
-                                  : launch<64 * NW>(dq_kernel<T, D, CAUSAL, false, DV, true>, qblocks, stream, a);
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
   }
-  if ((stages & kStageDkDv) && kblocks > 0) {
-    hipError_t e;
-    if constexpr (kPair) e = launch_dkdv_pair(a, D, DV, CAUSAL, stream);
-    else e = a.window > 0 ? launch2(dkdv_kernel<T, D, CAUSAL, true, DV, false, kHalf>, kblocks, kNy, stream, a)
-                          : launch2(dkdv_kernel<T, D, CAUSAL, false, DV, false, kHalf>, kblocks, kNy, stream, a);
-    if (e != hipSuccess) return e;
+  if constexpr (kPair) {
+    return launch_dkdv_pair(a, D, DV, CAUSAL, stream);
+  } else {
+    return a.window > 0 ? launch2(dkdv_kernel<T, D, CAUSAL, true, DV, false, kHalf>, kblocks, kNy, stream, a)
+                        : launch2(dkdv_kernel<T, D, CAUSAL, false, DV, false, kHalf>, kblocks, kNy, stream, a);
   }
-  if ((stages & kStageDq) && qblocks > 0) {
-    hipError_t e = a.window > 0 ? launch<64 * NW>(dq_kernel<T, D, CAUSAL, true, DV>, qblocks, stream, a)
-                                : launch<64 * NW>(dq_kernel<T, D, CAUSAL, false, DV>, qblocks, stream, a);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, int dtype_bf16, int d, int causal, unsigned stages,

@@ -102,8 +102,12 @@ struct BwdArgs {
   void* dQ;
   void* dK;
   void* dV;
-  float* Dvec;        // [B*Hq][Tqp] rowsum(dO * O); 0 in padding rows
+  float* Dvec;        // [B*Hq][Tqp] -rowsum(dO * O); 0 in padding rows
   float* Lg;          // [B*Hq][Tqp] L * log2(e); +inf for rows without keys and padding
+  // The dQ pass forms its rows' -D and L2 itself (from O, dO and L) and
+  // writes them to Dvec and Lg for the dK/dV pass that follows it, instead of
+  // reading what bwd_pre_kernel wrote.
+  bool fuse_pre = false;
   int B, Hq, Hkv, Tq, Tk;
   int Tqp;            // Tq rounded up to a multiple of 64
   int window;         // as FwdArgs::window

@@ -124,14 +124,18 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const flo
            int dtype, void* stream);
 
 /*
- * The backward pass in three stages, for callers that time or schedule them
+ * The backward pass in stages, for callers that time or schedule them
  * separately.  Same arguments and semantics as fa_bwd, plus a bit mask:
- *   FA_BWD_STAGE_PRE   D = rowsum(dO * O) and log2-domain L into the workspace;
+ *   FA_BWD_STAGE_PRE   -D = -rowsum(dO * O) and log2-domain L of every query
+ *                      row into the workspace, as a pass of its own;
  *   FA_BWD_STAGE_DKDV  rebuild S and P per key block; write dK and dV;
- *   FA_BWD_STAGE_DQ    rebuild S and P per query block; write dQ.
- * DKDV and DQ read what PRE left in the workspace (and nothing else of each
- * other), so PRE must run first on the same stream with identical arguments;
- * fa_bwd runs all three.
+ *   FA_BWD_STAGE_DQ    rebuild S and P per query block; write dQ.  This pass
+ *                      forms the rows of PRE itself and writes them to the
+ *                      workspace too, so with DQ set PRE does nothing.
+ * Within one call the order is PRE (if it runs), DQ, then DKDV.  DKDV reads
+ * the rows from the workspace: they must come from PRE or DQ in this call or
+ * an earlier call on the same stream with identical arguments.  fa_bwd runs
+ * DQ then DKDV.
  */
 #define FA_BWD_STAGE_PRE 1u
 #define FA_BWD_STAGE_DKDV 2u
