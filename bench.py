@@ -221,7 +221,7 @@ def mask_bench(args, fa, accounting, wl):
                       "Tk": w.Tk, "d": w.d, "causal": w.causal, "mask_density": args.mask,
                       "visible_pairs": pairs, "parallelism": "single GPU"},
            "pct_peak": round(100.0 * value / peak, 2),
-           "roofline": {"bound": "mfma", "kernel": "fa_bwd_mask (pre, transpose, dK/dV, dQ)",
+           "roofline": {"bound": "mfma", "kernel": "fa_bwd_mask (dQ with the -D, L2 rows; mask transpose; dK/dV)",
                         "achieved": round(bwd_mm, 2), "peak": peak, "unit": "TFLOP/s",
                         "frac": round(bwd_mm / peak, 4), "traffic": None,
                         "flops_per_launch": 14.0 * w.d * pairs, "avg_launch_ms": round(ms_bwd, 4)},
