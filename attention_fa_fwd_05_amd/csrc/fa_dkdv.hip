@@ -96,9 +96,20 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
   const int qlast = W > 0 ? min(Tq - 1, k0 + BK - 1 - off + W - 1) : Tq - 1;
   const int qb1 = qlast < 0 ? -1 : qlast / BQ;
   const int total = G * max(0, qb1 - qb0 + 1);
-  auto item_q0 = [&](int it) { return (qb1 - it / G) * BQ; };
-  auto item_bh = [&](int it) { return wk.b * a.Hq + wk.hk * G + it % G; };
-  auto item_qrow = [&](int it) { return sq.q_row(wk.hk * G + it % G); };
+  // A position in the work list: its query block, head within the group and
+  // LDS slot of dO, L2, -D (mod NB).  The loops step cursors forward by one
+  // item per block instead of dividing by G.
+  struct Cursor {
+    int qb, g, buf;
+  };
+  auto cursor_at = [&](int it) { return Cursor{qb1 - it / G, it % G, it % NB}; };
+  auto step = [&](Cursor& c) {
+    if (++c.g == G) {
+      c.g = 0;
+      --c.qb;
+    }
+    c.buf = c.buf == NB - 1 ? 0 : c.buf + 1;
+  };
 
   // Loads of block it: Q and dO rows (clamped at Tq - 1; the padding rows have
   // L2 = +inf and -D = 0, so they add nothing), L2 and -D (rows padded to 64
@@ -122,29 +133,32 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
     const T* q;                                     // Q row q0 of the block's head
     const T* o;                                     // dO row q0
     size_t wrow;                                    // workspace row of query q0
-    int q0, it;
+    int q0, qs, buf;                                // Q slot (it mod NBQ), dO / L2 / -D slot
     bool whole;                                     // all BQ rows exist: no clamping
   };
-  auto block_src = [&](int it) {
+  auto block_src = [&](const Cursor& c, int it) {
     Src r;
-    r.it = it;
-    r.q0 = item_q0(it);
-    const size_t qr = item_qrow(it) + r.q0;
+    r.q0 = c.qb * BQ;
+    r.qs = it & (NBQ - 1);
+    r.buf = c.buf;
+    const int hq = wk.hk * G + c.g;
+    const size_t qr = sq.q_row(hq) + r.q0;
     r.q = reinterpret_cast<const T*>(a.Q) + qr * D;
     r.o = reinterpret_cast<const T*>(a.dO) + qr * DV;
-    r.wrow = (size_t)item_bh(it) * a.Tqp + r.q0;
+    r.wrow = (size_t)(wk.b * a.Hq + hq) * a.Tqp + r.q0;
     r.whole = r.q0 + BQ <= Tq;
     return r;
   };
+  static_assert((NBQ & (NBQ - 1)) == 0, "Q slots by mask");
   // Pieces 0 .. NPC - 1: Q, dO, then the L2 / -D row (waves 0 / 1) and the
   // mask word (P-waves with a mask); a piece a wave has no share of is empty.
   constexpr int NPC = DRQ::PER + DRO::PER + 1 + (MASK ? 1 : 0);
   auto piece = [&](const Src& b, int j) {
-    const int buf = b.it % NB;
+    const int buf = b.buf;
     if (j < DRQ::PER) {
       if (!DRQ::mine()) return;
-      if (b.whole) dma16s(b.q, qoff[j], lds_addr(sQ[b.it % NBQ]) + DRQ::lds_off(j));
-      else DRQ::one(sQ[b.it % NBQ], b.q - (size_t)b.q0 * D, b.q0, Tq, j);
+      if (b.whole) dma16s(b.q, qoff[j], lds_addr(sQ[b.qs]) + DRQ::lds_off(j));
+      else DRQ::one(sQ[b.qs], b.q - (size_t)b.q0 * D, b.q0, Tq, j);
     } else if (j < DRQ::PER + DRO::PER) {
       const int i = j - DRQ::PER;
       if (!DRO::mine()) return;
@@ -161,7 +175,7 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
     }
   };
   auto issue = [&](int it) {
-    const Src b = block_src(it);
+    const Src b = block_src(cursor_at(it), it);
 #pragma unroll
     for (int j = 0; j < NPC; ++j) piece(b, j);
   };
@@ -212,12 +226,13 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
     if (total > 1) issue(1);
     wait_next(total > 1);
     __syncthreads();
-    for (int it = 0; it <= total; ++it) {
-      const int cur = it % NB;
+    Cursor ccur = cursor_at(0), ncur = cursor_at(2);   // the block worked on, the block loaded
+    for (int it = 0; it <= total; ++it, step(ccur), step(ncur)) {
+      const int cur = ccur.buf;
       const bool load = it + 2 < total;             // uniform
-      const Src nsrc = block_src(min(it + 2, total - 1));
+      const Src nsrc = block_src(ncur, it + 2);     // used only when load
       if (it < total) {
-        const int q0 = item_q0(it);
+        const int q0 = ccur.qb * BQ;
         const uint32_t qb = lds_addr(sQ[it % NBQ]), ob = lds_addr(sdO[cur]);
         // P = exp2(S c - L2); register i of tile t holds query
         // q0 + 32 t + 8 (i / 4) + 4 h + i % 4.  A boolean mask's hidden pairs
@@ -341,10 +356,11 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
     if (total > 1) issue(1);
     wait_next(total > 1);
     __syncthreads();
-    for (int it = 0; it <= total; ++it) {
-      const int cur = it % NB;
+    Cursor ccur = cursor_at(0), ncur = cursor_at(2);   // the block worked on, the block loaded
+    for (int it = 0; it <= total; ++it, step(ccur), step(ncur)) {
+      const int cur = ccur.buf;
       const bool load = it + 2 < total;             // uniform
-      const Src nsrc = block_src(min(it + 2, total - 1));
+      const Src nsrc = block_src(ncur, it + 2);     // used only when load
       wave_prio<1>();
       if (it > 0) {
         // dS = P (dP - D) of the previous block and dK^T += Q^T dS: the dS
