@@ -702,7 +702,7 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
 #pragma unroll
       for (int e = 0; e < KPER; ++e) acc += (float)o[e] * (float)gop[s][e];
     }
-    acc += __shfl_xor(acc, 32, 64);
+    acc = wave_xor32_sum(acc);
     const float l = q_ok ? a.L[qrow0 + myq] : -INFINITY;
     l2 = l == -INFINITY ? INFINITY : l * kLog2e;
     ndd = q_ok ? -acc : 0.f;

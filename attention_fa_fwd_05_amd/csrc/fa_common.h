@@ -442,7 +442,19 @@ __device__ __forceinline__ void pipelined(F&& fetch, G&& mma, H&& between) {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ inline float wave_xor32_max(float v) { return fmaxf(v, __shfl_xor(v, 32, 64)); }
+// Lane l and lane l ^ 32 combined, on the vector ALU: v_permlane32_swap hands
+// every lane the values of lanes l % 32 and l % 32 + 32 (in that order, so
+// both halves get bit-identical results) without a round trip through LDS.
+__device__ inline void lane_halves(float v, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ inline float wave_xor32_max(float v) {
+  float lo, hi;
+  lane_halves(v, lo, hi);
+  return fmaxf(lo, hi);
+}
 
 // Maximum of N values as a tree of three-input maxima (v_max3_f32 once NaNs
 // need not be propagated, which the library's build assumes).
@@ -468,7 +480,11 @@ __device__ inline void sum_bf16x8(const bf16x8& p, float* acc4) {
   acc4[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), one, acc4[2], false);
   acc4[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), one, acc4[3], false);
 }
-__device__ inline float wave_xor32_sum(float v) { return v + __shfl_xor(v, 32, 64); }
+__device__ inline float wave_xor32_sum(float v) {
+  float lo, hi;
+  lane_halves(v, lo, hi);
+  return lo + hi;
+}
 
 // 16-byte global <-> LDS copy helpers.
 __device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
