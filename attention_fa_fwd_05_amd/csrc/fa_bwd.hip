@@ -755,14 +755,20 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
 #pragma unroll
   for (int t = 0; t < NDT; ++t) acc[t] = f32x16{};
   // S^T = K Q^T and dP^T = V dO^T of one tile: 64 keys x 32 queries each.
+  // The dP^T products start from -D (this lane's row), read from a register
+  // tile that stays fixed over the loop, so they form dP - D without a
+  // per-element add or per-tile copies.
   f32x16 st0, st1, dp0, dp1;
+  f32x16 dseed;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dseed[r] = ndd;
 
   // Some key of tile j is visible to this wave's queries.
   auto visible = [&](int j) {
     return !(CAUSAL && j * BK > qw + 31 + off) && !(W > 0 && j * BK + BK - 1 < qw + off - W + 1);
   };
   auto s_phase = [&](int buf) {
-    st0 = f32x16{}; st1 = f32x16{}; dp0 = f32x16{}; dp1 = f32x16{};
+    st0 = f32x16{}; st1 = f32x16{}; dp0 = dseed; dp1 = dseed;
     wave_prio<1>();
 #pragma unroll
     for (int s = 0; s < (NSD > NSDV ? NSD : NSDV); ++s) {
@@ -799,7 +805,7 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
         const int keep = (int)((r < 16 ? m0 : m1) << (31 - perm_index(0, r) % 32)) >> 31;
         sv = __int_as_float((__float_as_int(sv) & keep) | (int)(0xff800000u & ~(uint32_t)keep));
       }
-      ds[r] = fast_exp2(__builtin_fmaf(sv, c, -l2)) * (dpv + ndd);
+      ds[r] = fast_exp2(__builtin_fmaf(sv, c, -l2)) * dpv;
     }
     // Only the diagonal tiles and the ragged key end (a uniform test) clear
     // dS of the keys this query may not see; every value above is finite.
