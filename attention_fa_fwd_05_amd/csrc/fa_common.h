@@ -457,7 +457,9 @@ __device__ inline float wave_xor32_max(float v) {
 }
 
 // Maximum of N values as a tree of three-input maxima (v_max3_f32 once NaNs
-// need not be propagated, which the library's build assumes).
+// need not be propagated, which the library's build assumes): each level
+// takes the values in groups of three, so N values cost about N / 2
+// instructions.
 template <int N>
 __device__ inline float max_tree(const float* v) {
   if constexpr (N == 1) {
@@ -465,8 +467,13 @@ __device__ inline float max_tree(const float* v) {
   } else if constexpr (N == 2) {
     return fmaxf(v[0], v[1]);
   } else {
-    constexpr int A = N / 3, B = (N - A) / 2, C = N - A - B;
-    return fmaxf(fmaxf(max_tree<A>(v), max_tree<B>(v + A)), max_tree<C>(v + A + B));
+    constexpr int G = N / 3, R = N % 3, M = G + (R ? 1 : 0);
+    float t[M];
+#pragma unroll
+    for (int g = 0; g < G; ++g) t[g] = fmaxf(fmaxf(v[3 * g], v[3 * g + 1]), v[3 * g + 2]);
+    if constexpr (R == 1) t[G] = v[3 * G];
+    if constexpr (R == 2) t[G] = fmaxf(v[3 * G], v[3 * G + 1]);
+    return max_tree<M>(t);
   }
 }
 
