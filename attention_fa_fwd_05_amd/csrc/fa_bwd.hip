@@ -591,11 +591,15 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   constexpr int NSDV = (DV / 2) / KPER;              // steps of dP^T = V dO^T
   constexpr int NSK = (BK / 2) / KPER;
   constexpr int NDT = D / 32;
-  // Three K/V buffers: tile j+2 loads while tile j is read, so the wait at the
-  // end of a tile only covers loads issued a whole tile earlier.  fp32 with
-  // d = 128 fits two (its loads then wait within the tile).
-  constexpr int NBUF = NW == 8 ? 3 : 2;
-  constexpr int AHEAD = NBUF - 1;                   // tiles loaded beyond the current one
+  // K/V buffers.  8 waves (bf16, d <= 128): four, taken two tiles per
+  // barrier: tiles j+2 and j+3 load while tiles j and j+1 are read, so the
+  // workgroup meets one barrier per 128 keys, and the wave that finishes
+  // tile j first goes on to tile j+1 instead of waiting for the others.
+  // 4 waves: two (fp32 with d = 128 fits no more; its loads then wait within
+  // the tile), one tile per barrier.
+  constexpr bool STEP2 = NW == 8;
+  constexpr int NBUF = STEP2 ? 4 : 2;
+  constexpr int AHEAD = STEP2 ? 2 : 1;             // tiles loaded before the first barrier
   constexpr int TILE = BK * D;                      // elements of one K tile (the V tile follows)
   // Buffer b: K tile, then V tile; 4096-byte alignment for XorFetch (both
   // tile sizes are multiples of 4096 bytes).
@@ -666,8 +670,6 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
                k0 / 32 + (lane & 1),
            lds_addr(sM + (buf * NW + w) * 64));
   };
-  // Direct-load instructions per wave for one tile (K and V, and the mask).
-  constexpr int NLD = DR::PER + DRV::PER + (MASK ? 1 : 0);
 #pragma unroll
   for (int j = 0; j < AHEAD; ++j)
     if (jt0 + j < ntiles) issue((jt0 + j) * BK, j);
@@ -832,23 +834,46 @@ __global__ __launch_bounds__((64 * dq_waves<T, D>())) void dq_kernel(BwdArgs a) 
   };
 
   int buf = 0;                                      // buffer of tile jt
-  for (int jt = jt0; jt < ntiles; ++jt) {
-    const bool issued = jt + AHEAD < ntiles;
-    if (issued) issue((jt + AHEAD) * BK, buf + AHEAD >= NBUF ? buf + AHEAD - NBUF : buf + AHEAD);
-    bool any = true;
-    if constexpr (MASK)                            // the mask leaves the wave some key of the tile
-      any = __ballot((sM[(buf * NW + w) * 64 + 2 * n] | sM[(buf * NW + w) * 64 + 2 * n + 1]) != 0) != 0;
-    if (visible(jt) && any) {
-      s_phase(buf);
-      dq_phase(jt, buf);
+  if constexpr (STEP2) {
+    // Tiles jt and jt + 1 (buffers buf, buf + 1) between two barriers; the
+    // loads of jt + 2 and jt + 3 go to the buffers of jt - 2 and jt - 1,
+    // which every wave finished before the last barrier.
+    for (int jt = jt0; jt < ntiles; jt += 2) {
+      if (jt + 2 < ntiles) issue((jt + 2) * BK, (buf + 2) & 3);
+      if (jt + 3 < ntiles) issue((jt + 3) * BK, (buf + 3) & 3);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = jt + u, b = (buf + u) & 3;
+        bool any = j < ntiles;
+        if constexpr (MASK)                        // the mask leaves the wave some key of the tile
+          any = any && __ballot((sM[(b * NW + w) * 64 + 2 * n] | sM[(b * NW + w) * 64 + 2 * n + 1]) != 0) != 0;
+        if (any && visible(j)) {
+          s_phase(b);
+          dq_phase(j, b);
+        }
+      }
+      // This wave's loads of tiles jt + 2 and jt + 3 have landed; the barrier
+      // makes every wave's share visible and frees buffers buf, buf + 1.
+      wait_vmcnt<0>();
+      __syncthreads();
+      buf = (buf + 2) & 3;
     }
-    // This wave's loads of tile jt+1 have landed (those of tile jt+2, issued
-    // just now, may still be in flight); the barrier makes every wave's share
-    // visible and frees buffer buf for the loads issued next.
-    if (AHEAD == 2 && issued) wait_vmcnt<NLD>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    buf = buf + 1 == NBUF ? 0 : buf + 1;
+  } else {
+    for (int jt = jt0; jt < ntiles; ++jt) {
+      if (jt + 1 < ntiles) issue((jt + 1) * BK, buf ^ 1);
+      bool any = true;
+      if constexpr (MASK)                          // the mask leaves the wave some key of the tile
+        any = __ballot((sM[(buf * NW + w) * 64 + 2 * n] | sM[(buf * NW + w) * 64 + 2 * n + 1]) != 0) != 0;
+      if (visible(jt) && any) {
+        s_phase(buf);
+        dq_phase(jt, buf);
+      }
+      // This wave's loads of tile jt + 1 have landed; the barrier makes every
+      // wave's share visible and frees buffer buf for the loads issued next.
+      wait_vmcnt<0>();
+      __syncthreads();
+      buf ^= 1;
+    }
   }
 
   if (q_ok) {
