@@ -9,7 +9,8 @@ is one of those helper sequences, that no other instruction that reads M0
 appears, and that register-indexing brackets (s_set_gpr_idx_on .. _off, which
 keep their index in M0; the compiler emits them only in the fp32 d = 128
 test-path kernel) contain no direct load.  It also checks that the bf16 kernels keep everything in registers
-(no scratch), which the schedules assume (head dim 256's backward excepted).
+(no scratch), which the schedules assume (head dim 256's backward excepted),
+and that no kernel calls a function (everything is inlined).
 """
 
 import os
@@ -84,3 +85,14 @@ def test_bf16_kernels_use_no_scratch(asm):
                 continue
             size = int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", desc).group(1))
             assert size == 0, f"{src}:{name} uses {size} bytes of scratch per lane"
+
+
+def test_kernels_make_no_calls(asm):
+    # Every helper and lambda is inlined into its kernel: a call would pass the
+    # kernel's register arrays through scratch and break the hand-ordered
+    # schedules (a lambda called from two places once stayed out of line and
+    # ran twenty times slower).
+    for src, text in asm.items():
+        for name, body in kernels(text):
+            # (s_setpc_b64 alone is the compiler's long branch inside a large kernel, not a call)
+            assert not re.search(r"^\s*s_swappc_b64", body, flags=re.M), f"{src}:{name} calls a function"
