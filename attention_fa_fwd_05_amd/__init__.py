@@ -8,5 +8,5 @@ from ._binding import (EXPORTS, FA_DTYPE_BF16, FA_DTYPE_F32, LIB_PATH, STAGE_ALL
                        STAGE_DKDV, STAGE_DQ, STAGE_PRE, STATUS, FaError, attention, backward, forward,
                        backward_masked, backward_noalloc, backward_paged, backward_varlen, forward_masked,
                        forward_paged, pack_mask, forward_splitk, forward_varlen, forward_varlen_masked,
-                       backward_varlen_masked, load_library,
+                       forward_varlen_splitk, backward_varlen_masked, load_library,
                        splitk_workspace_bytes, status_string, workspace_bytes)

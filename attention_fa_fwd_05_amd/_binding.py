@@ -31,6 +31,7 @@ EXPORTS = ["fa_fwd", "fa_bwd", "fa_bwd_stages", "fa_fwd_window", "fa_bwd_window"
            "fa_fwd_paged_workspace_bytes", "fa_bwd_paged", "fa_bwd_paged_workspace_bytes", "fa_bwd_workspace_bytes",
            "fa_mask_row_words", "fa_mask_pack", "fa_fwd_mask", "fa_bwd_mask", "fa_bwd_mask_workspace_bytes",
            "fa_fwd_mask_splitk", "fa_fwd_mask_splitk_workspace_bytes", "fa_fwd_varlen_mask", "fa_bwd_varlen_mask",
+           "fa_fwd_varlen_splitk", "fa_fwd_varlen_splitk_workspace_bytes",
            "fa_bwd_noalloc", "fa_bwd_noalloc_scratch_bytes",
            "fa_status_string", "fa_hip_error_string", "fa_abi_version"]
 
@@ -117,6 +118,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_bwd_varlen_mask.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, ll, vp, vp,
                                        i, i, i, i, i, i, i, i, i, i, f, i, vp]
     lib.fa_bwd_varlen_mask.restype = i
+    lib.fa_fwd_varlen_splitk.argtypes = [vp, vp, vp, vp, vp, vp, ll, vp, vp, vp, sz, i, i, i, i, i, i, i, i, i, i,
+                                         f, i, i, vp]
+    lib.fa_fwd_varlen_splitk.restype = i
+    lib.fa_fwd_varlen_splitk_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i, i]
+    lib.fa_fwd_varlen_splitk_workspace_bytes.restype = sz
     lib.fa_bwd_mask_workspace_bytes.argtypes = [i, i, i, i, i, i, i, ll]
     lib.fa_bwd_mask_workspace_bytes.restype = sz
     lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
@@ -490,6 +496,34 @@ def pack_mask(mask, Tk: int | None = None, out=None):
     if st != 0:
         raise FaError(st, "fa_mask_pack")
     return bits
+
+
+def forward_varlen_splitk(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                          causal: bool = False, scale: float | None = None, window: int = 0, mask=None,
+                          nsplit: int = 0, workspace=None, out=None, lse=None):
+    """fa_fwd_varlen_splitk: forward_varlen (forward_varlen_masked when ``mask`` is given) with
+    each sequence's keys split over ``nsplit`` slices (0: automatic) and merged; returns
+    (o like q, lse float32 [Hq, total_q])."""
+    import torch
+    lib = load_library()
+    B, Hq, Hkv, total_q, total_k, d = _varlen_shapes(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    mq, mk = int(max_seqlen_q), int(max_seqlen_k)
+    bits, stride = (None, 0) if mask is None else _varlen_mask_bits(lib, mask, q, B, mq, mk)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    code = _dtype_code(q)
+    need = int(lib.fa_fwd_varlen_splitk_workspace_bytes(B, Hq, Hkv, total_q, mq, mk, d, code, int(nsplit),
+                                                        int(mask is not None)))
+    ws = _ws(workspace, need, q)
+    o = torch.empty_like(q) if _out(out, "out", q.shape, q) is None else out
+    L = _out(lse, "lse", (Hq, total_q), q, torch.float32)
+    L = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device) if L is None else L
+    st = lib.fa_fwd_varlen_splitk(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(L), None if bits is None else _ptr(bits),
+                                  stride, cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), ws.data_ptr(),
+                                  _nbytes(ws), B, Hq, Hkv, total_q, total_k, mq, mk, d, int(bool(causal)),
+                                  int(window), scale, code, int(nsplit), _stream(q))
+    if st != 0:
+        raise FaError(st, "fa_fwd_varlen_splitk")
+    return o, L
 
 
 def _mask_bits(lib, mask, q, B, Tq, Tk):

@@ -181,9 +181,13 @@ size_t mask_t_bytes(int B, int Tq, int Tk, long long stride) {
   return align_up((size_t)entries * Tk * (4 * ((Tq + 127) / 128)) * 4);
 }
 
-size_t splitk_ws_bytes(int B, int Hq, int Tq, int d, int ns) {
-  const size_t rows = (size_t)B * Hq * Tq;
+// Split-forward partials for `rows` output rows: ns * rows fp32 rows of d
+// values, then ns * rows logsumexps, each part 256-byte aligned.
+size_t splitk_rows_bytes(size_t rows, int d, int ns) {
   return align_up((size_t)ns * rows * d * 4) + align_up((size_t)ns * rows * 4);
+}
+size_t splitk_ws_bytes(int B, int Hq, int Tq, int d, int ns) {
+  return splitk_rows_bytes((size_t)B * Hq * Tq, d, ns);
 }
 
 // Workspace of the backward through a block table: the backward's own (-D,
@@ -318,7 +322,7 @@ int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, c
                   d, d, causal, 0, scale, dtype, FA_BWD_STAGE_ALL, stream);
 }
 
-int fa_abi_version(void) { return (2 << 16) | 0; }
+int fa_abi_version(void) { return (2 << 16) | 1; }
 
 const char* fa_hip_error_string(void) { return t_hip_error; }
 
@@ -439,12 +443,14 @@ size_t fa_fwd_mask_splitk_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk
 namespace {
 
 // The masked forward for the fixed layout (cu_q == nullptr; Tq, Tk) or a
-// variable-length batch (offsets; Tq, Tk the longest sequences).  Runs the
-// plain shape (its packing only), split over ns key slices when ns > 1.
-int fwd_mask_core(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
-                  long long mask_batch_stride, const int* cu_q, const int* cu_k, int B, int Hq, int Hkv,
-                  int total_q, int total_k, int Tq, int Tk, int d, int dv, int causal, int window, float scale,
-                  int dtype, void* workspace, size_t workspace_bytes, int nsplit, void* stream) {
+// variable-length batch (offsets; Tq, Tk the longest sequences), and the
+// unmasked variable-length forward (masked == false).  A mask runs the plain
+// shape (its packing only); without one the packing of fa_fwd_varlen.  Split
+// over ns key slices when ns > 1, the partials indexed by output row.
+int fwd_split_core(const void* Q, const void* K, const void* V, void* O, float* L, bool masked,
+                   const uint32_t* mask_bits, long long mask_batch_stride, const int* cu_q, const int* cu_k, int B,
+                   int Hq, int Hkv, int total_q, int total_k, int Tq, int Tk, int d, int dv, int causal, int window,
+                   float scale, int dtype, void* workspace, size_t workspace_bytes, int nsplit, void* stream) {
   int st = check_common(B, Hq, Hkv, Tq, Tk, d, dtype);
   if (st != FA_OK) return st;
   if ((st = check_dv(d, dv, dtype)) != FA_OK) return st;
@@ -457,11 +463,12 @@ int fwd_mask_core(const void* Q, const void* K, const void* V, void* O, float* L
       (st = check_ptr(V, krows * dv)) || (st = check_ptr(L, rows)))
     return st;
   const long long rw = fa_mask_row_words(Tk);
-  if ((st = check_mask(mask_bits, mask_batch_stride, B, Tq, Tk))) return st;
+  if (masked && (st = check_mask(mask_bits, mask_batch_stride, B, Tq, Tk))) return st;
   if (bad_scale(scale)) return FA_ERR_SCALE;
-  const int ns = varlen ? 1 : mask_splits(B, Hq, Hkv, Tq, Tk, d, dtype, nsplit);
+  const int ns = masked ? mask_splits(B, Hq, Hkv, Tq, Tk, d, dtype, nsplit)
+                        : fwd_splits(B, Hq, Hkv, Tq, Tk, d, dtype, nsplit);
   if (ns > kMaxSplits) return FA_ERR_TOO_LARGE;
-  const size_t need = ns == 1 ? 0 : splitk_ws_bytes(B, Hq, Tq, dv, ns);
+  const size_t need = ns == 1 ? 0 : splitk_rows_bytes((size_t)rows, dv, ns);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (misaligned(workspace)) return FA_ERR_ALIGNMENT;
@@ -473,20 +480,21 @@ int fwd_mask_core(const void* Q, const void* K, const void* V, void* O, float* L
   a.window = window > 0 ? window : 0;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   const int G = Hq / Hkv, nw = fa::fwd_waves(dtype == FA_DTYPE_BF16, d);
-  a.pack = (G <= nw && Tq <= 32 * (nw / G)) ? 1 : 0;   // the plain shape's packing only
+  a.pack = !masked ? fwd_pack(Hq, Hkv, Tq, d, dtype)
+                   : (G <= nw && Tq <= 32 * (nw / G)) ? 1 : 0;   // a mask: the plain shape's packing only
   a.Opart = nullptr;
   a.Lpart = nullptr;
   a.cu_q = cu_q;
   a.cu_k = cu_k;
   a.total_q = varlen ? total_q : 0;
   a.total_k = varlen ? total_k : 0;
-  a.mask = Tk > 0 ? mask_bits : nullptr;
+  a.mask = masked && Tk > 0 ? mask_bits : nullptr;
   a.mask_bstride = mask_batch_stride;
   a.mask_row_words = (int)rw;
   if (ns > 1) {
     char* wsb = static_cast<char*>(workspace);
     a.Opart = reinterpret_cast<float*>(wsb);
-    a.Lpart = reinterpret_cast<float*>(wsb + align_up((size_t)ns * B * Hq * Tq * dv * 4));
+    a.Lpart = reinterpret_cast<float*>(wsb + align_up((size_t)ns * rows * dv * 4));
   }
   return hip_status(fa::launch_fwd(a, dtype == FA_DTYPE_BF16, d, causal != 0, (hipStream_t)stream, ns, dv));
 }
@@ -497,8 +505,8 @@ int fa_fwd_mask_splitk(const void* Q, const void* K, const void* V, void* O, flo
                        long long mask_batch_stride, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
                        int Tq, int Tk, int d, int dv, int causal, int window, float scale, int dtype, int nsplit,
                        void* stream) {
-  return fwd_mask_core(Q, K, V, O, L, mask_bits, mask_batch_stride, nullptr, nullptr, B, Hq, Hkv, 0, 0, Tq, Tk, d,
-                       dv, causal, window, scale, dtype, workspace, workspace_bytes, nsplit, stream);
+  return fwd_split_core(Q, K, V, O, L, true, mask_bits, mask_batch_stride, nullptr, nullptr, B, Hq, Hkv, 0, 0, Tq,
+                        Tk, d, dv, causal, window, scale, dtype, workspace, workspace_bytes, nsplit, stream);
 }
 
 int fa_fwd_varlen_mask(const void* Q, const void* K, const void* V, void* O, float* L, const uint32_t* mask_bits,
@@ -509,9 +517,33 @@ int fa_fwd_varlen_mask(const void* Q, const void* K, const void* V, void* O, flo
   if (st != FA_OK) return st;
   if ((st = check_varlen(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max_seqlen_k)) != FA_OK)
     return st;
-  return fwd_mask_core(Q, K, V, O, L, mask_bits, mask_seq_stride, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q,
-                       total_k, max_seqlen_q, max_seqlen_k, d, d, causal, window, scale, dtype, nullptr, 0, 1,
-                       stream);
+  return fwd_split_core(Q, K, V, O, L, true, mask_bits, mask_seq_stride, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv,
+                        total_q, total_k, max_seqlen_q, max_seqlen_k, d, d, causal, window, scale, dtype, nullptr, 0,
+                        1, stream);
+}
+
+size_t fa_fwd_varlen_splitk_workspace_bytes(int B, int Hq, int Hkv, int total_q, int max_seqlen_q,
+                                            int max_seqlen_k, int d, int dtype, int nsplit, int masked) {
+  if (check_common(B, Hq, Hkv, max_seqlen_q, max_seqlen_k, d, dtype) != FA_OK) return 0;
+  if (total_q < max_seqlen_q || total_q > kMaxSeq * 64) return 0;
+  const int ns = masked ? mask_splits(B, Hq, Hkv, max_seqlen_q, max_seqlen_k, d, dtype, nsplit)
+                        : fwd_splits(B, Hq, Hkv, max_seqlen_q, max_seqlen_k, d, dtype, nsplit);
+  if (ns > kMaxSplits) return 0;
+  return ns == 1 ? 0 : splitk_rows_bytes((size_t)Hq * total_q, d, ns);
+}
+
+int fa_fwd_varlen_splitk(const void* Q, const void* K, const void* V, void* O, float* L,
+                         const uint32_t* mask_bits, long long mask_seq_stride, const int* cu_seqlens_q,
+                         const int* cu_seqlens_k, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                         int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d, int causal,
+                         int window, float scale, int dtype, int nsplit, void* stream) {
+  int st = check_common(B, Hq, Hkv, max_seqlen_q, max_seqlen_k, d, dtype);
+  if (st != FA_OK) return st;
+  if ((st = check_varlen(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max_seqlen_k)) != FA_OK)
+    return st;
+  return fwd_split_core(Q, K, V, O, L, mask_bits != nullptr, mask_bits, mask_seq_stride, cu_seqlens_q,
+                        cu_seqlens_k, B, Hq, Hkv, total_q, total_k, max_seqlen_q, max_seqlen_k, d, d, causal, window,
+                        scale, dtype, workspace, workspace_bytes, nsplit, stream);
 }
 
 size_t fa_bwd_mask_workspace_bytes(int B, int Hq, int Hkv, int Tq, int Tk, int d, int dtype,

@@ -385,7 +385,8 @@ int fa_bwd_mask(const void* Q, const void* K, const void* V, const void* O, cons
  * mask_seq_stride is 0 (one mask for every sequence) or at least
  * max_seqlen_q * fa_mask_row_words(max_seqlen_k) and a multiple of 4.  The
  * backward's workspace is fa_bwd_mask_workspace_bytes(B, Hq, Hkv,
- * max_seqlen_q, max_seqlen_k, d, dtype, mask_seq_stride).  No key split.
+ * max_seqlen_q, max_seqlen_k, d, dtype, mask_seq_stride).  The key-split
+ * forward is fa_fwd_varlen_splitk.
  * Errors as fa_fwd_varlen / fa_bwd_varlen plus the mask errors of fa_fwd_mask
  * (with max_seqlen_q, max_seqlen_k in place of Tq, Tk).
  */
@@ -398,6 +399,37 @@ int fa_bwd_varlen_mask(const void* Q, const void* K, const void* V, const void* 
                        const uint32_t* mask_bits, long long mask_seq_stride, const int* cu_seqlens_q,
                        const int* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
                        int max_seqlen_k, int d, int causal, int window, float scale, int dtype, void* stream);
+
+/*
+ * The variable-length forward with the keys split over slices and merged as
+ * in fa_fwd_splitk ("The Autograd Memory Trap", section "The Scene": blocks of
+ * few new positions, each against a long prefix of its own length; unsplit,
+ * such a batch gives each compute unit a long run of key tiles or nothing).
+ * Layout, offsets, causal alignment and window as fa_fwd_varlen (d = dv).
+ * mask_bits == NULL: no mask (fa_fwd_varlen's result); otherwise the mask of
+ * fa_fwd_varlen_mask, with its mask_seq_stride.  The key tiles each
+ * workgroup of a sequence would visit are divided into nsplit equal runs, one
+ * per slice; a slice left without tiles of a sequence gives its rows
+ * L_s = -inf, which weighs nothing in the merge.  nsplit == 1 runs the unsplit
+ * kernels with no workspace: bit for bit fa_fwd_varlen / fa_fwd_varlen_mask.
+ * nsplit <= 0 picks the count as fa_fwd_splitk (fa_fwd_mask_splitk with a
+ * mask) would for B sequences of the longest lengths.  Otherwise the workspace
+ * (device memory, 16-byte aligned, at least
+ * fa_fwd_varlen_splitk_workspace_bytes for the same arguments) holds
+ * nsplit * Hq * total_q * (d + 1) floats; it carries nothing between calls.
+ * The size function's `masked` is 1 for a call with a mask (the automatic
+ * count differs).  Errors as fa_fwd_varlen, the mask errors of
+ * fa_fwd_varlen_mask when a mask is given, FA_ERR_WORKSPACE and
+ * FA_ERR_TOO_LARGE (more than 1024 slices); the size function returns 0 for
+ * invalid sizes and when one slice is used.
+ */
+size_t fa_fwd_varlen_splitk_workspace_bytes(int B, int Hq, int Hkv, int total_q, int max_seqlen_q,
+                                            int max_seqlen_k, int d, int dtype, int nsplit, int masked);
+int fa_fwd_varlen_splitk(const void* Q, const void* K, const void* V, void* O, float* L,
+                         const uint32_t* mask_bits, long long mask_seq_stride, const int* cu_seqlens_q,
+                         const int* cu_seqlens_k, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                         int total_q, int total_k, int max_seqlen_q, int max_seqlen_k, int d, int causal,
+                         int window, float scale, int dtype, int nsplit, void* stream);
 
 /*
  * The backward pass of fa_bwd for callers that cannot allocate memory or pass

@@ -254,6 +254,30 @@ def test_mask_splitk_workspace_and_arguments(lib):
                                   0, 0, 0.125, 1, 5000, None) == 9
 
 
+def test_varlen_splitk_workspace_and_arguments(lib):
+    """fa_fwd_varlen_splitk: partials for Hq * total_q rows per slice; B = 2 sequences, Hq = 4,
+    Hkv = 2, total_q = 32, total_k = 300, longest 16 and 200, d = 64, bf16."""
+    size = lambda ns, masked=0, d=64, total_q=32, max_q=16: lib.fa_fwd_varlen_splitk_workspace_bytes(
+        2, 4, 2, total_q, max_q, 200, d, 1, ns, masked)
+    rows = 4 * 32
+    assert size(3) == math.ceil(3 * rows * 64 * 4 / 256) * 256 + math.ceil(3 * rows * 4 / 256) * 256
+    assert size(3, masked=1) == size(3)
+    assert size(1) == 0 and size(1, masked=1) == 0
+    assert size(3, d=96) == 0 and size(3, max_q=40) == 0 and size(5000) == 0
+
+    def call(mask=None, stride=0, cu_q=FAKE, ws=FAKE, wsb=1 << 30, ns=3, d=64, window=0):
+        return lib.fa_fwd_varlen_splitk(*(FAKE,) * 5, mask, stride, cu_q, FAKE, ws, wsb, 2, 4, 2, 32, 300, 16, 200, d,
+                                        1, window, 0.125, 1, ns, None)
+    assert call(ws=None, wsb=0) == 7 and call(wsb=64) == 7 and call(mask=FAKE, ws=None, wsb=0) == 7
+    assert call(ns=5000) == 9
+    assert call(ws=FAKE + 4) == 8
+    assert call(cu_q=None) == 1 and call(d=80) == 4
+    assert call(mask=FAKE, stride=-4) == 2 and call(mask=FAKE, stride=6) == 2
+    # one slice needs no workspace: validation passes and stops at the NULL output
+    assert lib.fa_fwd_varlen_splitk(FAKE, FAKE, FAKE, None, FAKE, None, 0, FAKE, FAKE, None, 0, 2, 4, 2, 32, 300,
+                                    16, 200, 64, 1, 0, 0.125, 1, 1, None) == 1
+
+
 @pytest.mark.parametrize("d,fp32,bf16", [(32, 1, 1), (64, 1, 1), (128, 1, 1), (16, 4, 4), (96, 4, 4), (256, 4, 1)])
 def test_head_dims(lib, d, fp32, bf16):
     # supported head dims pass validation (then fail on the NULL output); 256 is bf16 only
@@ -299,6 +323,8 @@ def _scale_calls(lib, s):
                                                              1, 0, s, 1, None),
         "fa_bwd_varlen_mask": lambda: lib.fa_bwd_varlen_mask(*(FAKE,) * 10, W, FAKE, 0, FAKE, FAKE, 2, 4, 2, 32, 300,
                                                              16, 200, 64, 1, 0, s, 1, None),
+        "fa_fwd_varlen_splitk": lambda: lib.fa_fwd_varlen_splitk(*(FAKE,) * 5, None, 0, FAKE, FAKE, FAKE, W, 2, 4, 2,
+                                                                 32, 300, 16, 200, 64, 1, 0, s, 1, 2, None),
         "fa_bwd": lambda: lib.fa_bwd(*(FAKE,) * 10, W, 1, 2, 1, 16, 16, 64, 1, s, 1, None),
         "fa_bwd_stages": lambda: lib.fa_bwd_stages(*(FAKE,) * 10, W, 1, 2, 1, 16, 16, 64, 1, s, 1, 7, None),
         "fa_bwd_window": lambda: lib.fa_bwd_window(*(FAKE,) * 10, W, 1, 2, 1, 16, 16, 64, 1, 8, s, 1, 7, None),
