@@ -10,8 +10,9 @@ Covered: forward (plain, window, dv != d, fp32 d = 32), backward (same), the
 key-split forward and its merge (bf16, fp32 d = 64 and d = 32), variable-length
 forward and backward, paged forward (one pass and split) and backward, mask packing, masked
 forward (one pass and split) and masked backward (whose workspace holds the
-key-major mask copy), also with a window and dv != d, and the masked varlen
-forward and backward.
+key-major mask copy), also with a window and dv != d, the masked varlen
+forward and backward, and the key-split varlen forward (with and without a
+mask) with its merge.
 """
 
 import math
@@ -259,3 +260,27 @@ def test_varlen_masked_paths_stay_in_bounds(fa):
     fa.backward_varlen_masked(q, k, v, o, lse, do, cu_q, cu_k, mq, mk, mask, True, window=60, workspace=ws,
                               dq=dq, dk=dk, dv=dvv)
     g.check("varlen masked")
+
+
+@pytest.mark.parametrize("dtn,d,masked", [("bf16", 128, False), ("bf16", 128, True), ("fp32", 32, False)])
+def test_varlen_split_stays_in_bounds(fa, dtn, d, masked):
+    import torch
+    t = dt(dtn)
+    lens = [(32, 900), (1, 1), (0, 40), (77, 0), (32, 333)]
+    B, Hq, Hkv = len(lens), 8, 2
+    mq, mk = max(a for a, _ in lens), max(b for _, b in lens)
+    tq, tk = sum(a for a, _ in lens), sum(b for _, b in lens)
+    q, k, v = rnd((Hq, tq, d), t, 23), rnd((Hkv, tk, d), t, 24), rnd((Hkv, tk, d), t, 25)
+    cu_q = torch.tensor(np.concatenate([[0], np.cumsum([a for a, _ in lens])]).astype(np.int32)).cuda()
+    cu_k = torch.tensor(np.concatenate([[0], np.cumsum([b for _, b in lens])]).astype(np.int32)).cuda()
+    mask = torch.from_numpy(np.random.default_rng(11).random((B, mq, mk)) < 0.5).cuda() if masked else None
+    lib = fa.load_library()
+    code = fa.FA_DTYPE_BF16 if dtn == "bf16" else fa.FA_DTYPE_F32
+    g = Guarded()
+    o, lse = g.tensor("O", q.shape, t), g.tensor("L", (Hq, tq), torch.float32)
+    ws = g.workspace("varlen split workspace",
+                     int(lib.fa_fwd_varlen_splitk_workspace_bytes(B, Hq, Hkv, tq, mq, mk, d, code, 3, int(masked))))
+    fa.forward_varlen_splitk(q, k, v, cu_q, cu_k, mq, mk, True, window=200, mask=mask, nsplit=3, workspace=ws,
+                             out=o, lse=lse)
+    g.check(f"varlen split {dtn} d={d} masked={masked}")
+    assert torch.isfinite(o.float()).all()
