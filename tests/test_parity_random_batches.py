@@ -6,7 +6,9 @@ of the cases): 16 batches of 1 to 5 sequences, each with its own query and key
 counts from 0 to 300 (single rows, empty sides and Tq != Tk both ways occur),
 dtype, head dim (32, 64, 128; bf16 256), group size 1, 2 or 4, causal or not,
 a window on some, a boolean mask shared by the batch or per sequence on some;
-the oracle runs on each sequence alone.  Paged (fa_fwd_paged / fa_bwd_paged):
+the oracle runs on each sequence alone; each batch's forward also runs split
+over a drawn number of key slices (automatic, 2, 3 or 7;
+fa_fwd_varlen_splitk, with the batch's mask if any).  Paged (fa_fwd_paged / fa_bwd_paged):
 12 pools with shuffled pages, a first page shared by every sequence and pages
 no entry references, 1 to 3 sequences with 1 to 96 queries against 0 to 700
 keys, page sizes 128 and 256, against oracle/paged.py.  Checked: O, L, dQ, dK,
@@ -106,6 +108,12 @@ def test_random_varlen(fa, c):
            "dQ": pack([r[2][0] for r in refs]), "dK": pack([r[3][0] for r in refs]),
            "dV": pack([r[4][0] for r in refs])}
     check(vname(c), dtype, errors(got, exp))
+    ns = int(np.random.default_rng(c["seed"] + 2).choice([0, 2, 3, 7]))
+    o2, lse2 = fa.forward_varlen_splitk(q, k, v, cq, ck, max_q, max_k, causal, scale, window=window,
+                                        mask=None if mask is None else torch.from_numpy(mask).cuda(), nsplit=ns)
+    torch.cuda.synchronize()
+    got2 = {"O": o2.float().cpu().numpy(), "L": lse2.cpu().numpy()}
+    check(f"{vname(c)} split nsplit={ns}", dtype, errors(got2, {"O": exp["O"], "L": exp["L"]}))
 
 
 def draw_paged(i):
