@@ -14,7 +14,7 @@ Frobenius error 1e-4 (fp32) / 2e-2 (bf16) and the per-row bound of
 parity_tools; rows that see no key give O = 0, L = -inf.  The workspace is
 filled with NaN bytes before each call (every partial the merge reads is
 written first); one slice gives fa_fwd_varlen / fa_fwd_varlen_mask bit for
-bit.
+bit.  At the limit of 1024 slices nearly every slice is empty; 1025 is refused.
 """
 
 import numpy as np
@@ -112,3 +112,36 @@ def test_varlen_splitk_parity(fa, case):
         o2, l2 = fa.forward_varlen_masked(q, k, v, cu_q, cu_k, mq, mk, mask, causal, scale, window=window)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2), f"{name}: one slice differs from the unsplit call"
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_varlen_split_at_the_slice_limit(fa, masked):
+    """1024 slices (the most the library accepts): nearly every slice holds no tile of any
+    sequence and must weigh nothing in the merge; 1025 is rejected."""
+    import torch
+    lens, Hq, Hkv, d = [(32, 300), (5, 0), (17, 1000)], 4, 2, 64
+    B, mq, mk = len(lens), 32, 1000
+    full = np.random.default_rng(331).random((B, mq, mk)) < 0.5 if masked else None
+    seqs, refs = [], []
+    for b, (tq, tk) in enumerate(lens):
+        w = wl.Workload(f"limit[{b}]", 1, Hq, Hkv, tq, tk, d, "bf16", True, 340 + b)
+        inp = wl.make_inputs(w)
+        seqs.append(inp)
+        m = None if full is None else np.ascontiguousarray(full[b, :tq, :tk])
+        refs.append(oa.attention_forward(inp.q, inp.k, inp.v, True, w.scale, mask=m))
+    dev = lambda arrs: torch.from_numpy(pack([a[0] for a in arrs])).to(torch.bfloat16).cuda().contiguous()
+    q, k, v = (dev([getattr(s, n) for s in seqs]) for n in ("q", "k", "v"))
+    cu_q = torch.tensor(np.concatenate([[0], np.cumsum([a for a, _ in lens])]).astype(np.int32)).cuda()
+    cu_k = torch.tensor(np.concatenate([[0], np.cumsum([b for _, b in lens])]).astype(np.int32)).cuda()
+    mask = None if full is None else torch.from_numpy(full).cuda()
+    lib = fa.load_library()
+    need = int(lib.fa_fwd_varlen_splitk_workspace_bytes(B, Hq, Hkv, q.shape[1], mq, mk, d, fa.FA_DTYPE_BF16, 1024,
+                                                        int(masked)))
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    o, lse = fa.forward_varlen_splitk(q, k, v, cu_q, cu_k, mq, mk, True, mask=mask, nsplit=1024, workspace=ws)
+    torch.cuda.synchronize()
+    ref = {"O": pack([r[0][0] for r in refs]), "L": np.concatenate([r[1][0] for r in refs], axis=1)}
+    check(f"varlen split 1024 slices masked={masked}", "bf16",
+          errors({"O": o.float().cpu().numpy(), "L": lse.cpu().numpy()}, ref))
+    with pytest.raises(fa.FaError):
+        fa.forward_varlen_splitk(q, k, v, cu_q, cu_k, mq, mk, True, mask=mask, nsplit=1025, workspace=ws)
