@@ -121,7 +121,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_fwd_varlen_splitk.argtypes = [vp, vp, vp, vp, vp, vp, ll, vp, vp, vp, sz, i, i, i, i, i, i, i, i, i, i,
                                          f, i, i, vp]
     lib.fa_fwd_varlen_splitk.restype = i
-    lib.fa_fwd_varlen_splitk_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i, i]
+    lib.fa_fwd_varlen_splitk_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i, i, i, i]
     lib.fa_fwd_varlen_splitk_workspace_bytes.restype = sz
     lib.fa_bwd_mask_workspace_bytes.argtypes = [i, i, i, i, i, i, i, ll]
     lib.fa_bwd_mask_workspace_bytes.restype = sz
@@ -511,7 +511,7 @@ def forward_varlen_splitk(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int
     bits, stride = (None, 0) if mask is None else _varlen_mask_bits(lib, mask, q, B, mq, mk)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     code = _dtype_code(q)
-    need = int(lib.fa_fwd_varlen_splitk_workspace_bytes(B, Hq, Hkv, total_q, mq, mk, d, code, int(nsplit),
+    need = int(lib.fa_fwd_varlen_splitk_workspace_bytes(B, Hq, Hkv, total_q, total_k, mq, mk, d, code, int(nsplit),
                                                         int(mask is not None)))
     ws = _ws(workspace, need, q)
     o = torch.empty_like(q) if _out(out, "out", q.shape, q) is None else out

@@ -335,15 +335,19 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
       if (active && myq < Tq) {
         const size_t rows_all = (a.cu_q != nullptr) ? (size_t)a.Hq * a.total_q : (size_t)a.B * a.Hq * a.Tq;
         const size_t row = (size_t)blockIdx.y * rows_all + qrow0 + myq;
-        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        float* orow = a.Opart + row * DV;
+        // A row that saw no key of this slice gets L_s = -inf, which the merge
+        // skips without reading O_s: its partial output is not written.
+        if (ltot > 0.f) {
+          const float inv = 1.f / ltot;
+          float* orow = a.Opart + row * DV;
 #pragma unroll
-        for (int t = 0; t < NDT; ++t) {
+          for (int t = 0; t < NDT; ++t) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int d0 = t * 32 + 8 * g + 4 * h;
-            store4(orow + d0, o[u][t][4 * g] * inv, o[u][t][4 * g + 1] * inv, o[u][t][4 * g + 2] * inv,
-                   o[u][t][4 * g + 3] * inv);
+            for (int g = 0; g < 4; ++g) {
+              const int d0 = t * 32 + 8 * g + 4 * h;
+              store4(orow + d0, o[u][t][4 * g] * inv, o[u][t][4 * g + 1] * inv, o[u][t][4 * g + 2] * inv,
+                     o[u][t][4 * g + 3] * inv);
+            }
           }
         }
         if (h == 0) {

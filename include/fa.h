@@ -413,7 +413,10 @@ int fa_bwd_varlen_mask(const void* Q, const void* K, const void* V, const void* 
  * L_s = -inf, which weighs nothing in the merge.  nsplit == 1 runs the unsplit
  * kernels with no workspace: bit for bit fa_fwd_varlen / fa_fwd_varlen_mask.
  * nsplit <= 0 picks the count as fa_fwd_splitk (fa_fwd_mask_splitk with a
- * mask) would for B sequences of the longest lengths.  Otherwise the workspace
+ * mask) would for B sequences of the longest lengths; when the longest key
+ * count is 4 or more times the mean (r = max_seqlen_k * B / total_k), its
+ * workgroup target grows by sqrt(r), as the few long sequences' slices then
+ * set the time.  Otherwise the workspace
  * (device memory, 16-byte aligned, at least
  * fa_fwd_varlen_splitk_workspace_bytes for the same arguments) holds
  * nsplit * Hq * total_q * (d + 1) floats; it carries nothing between calls.
@@ -423,7 +426,7 @@ int fa_bwd_varlen_mask(const void* Q, const void* K, const void* V, const void* 
  * FA_ERR_TOO_LARGE (more than 1024 slices); the size function returns 0 for
  * invalid sizes and when one slice is used.
  */
-size_t fa_fwd_varlen_splitk_workspace_bytes(int B, int Hq, int Hkv, int total_q, int max_seqlen_q,
+size_t fa_fwd_varlen_splitk_workspace_bytes(int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
                                             int max_seqlen_k, int d, int dtype, int nsplit, int masked);
 int fa_fwd_varlen_splitk(const void* Q, const void* K, const void* V, void* O, float* L,
                          const uint32_t* mask_bits, long long mask_seq_stride, const int* cu_seqlens_q,

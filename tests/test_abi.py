@@ -257,13 +257,13 @@ def test_mask_splitk_workspace_and_arguments(lib):
 def test_varlen_splitk_workspace_and_arguments(lib):
     """fa_fwd_varlen_splitk: partials for Hq * total_q rows per slice; B = 2 sequences, Hq = 4,
     Hkv = 2, total_q = 32, total_k = 300, longest 16 and 200, d = 64, bf16."""
-    size = lambda ns, masked=0, d=64, total_q=32, max_q=16: lib.fa_fwd_varlen_splitk_workspace_bytes(
-        2, 4, 2, total_q, max_q, 200, d, 1, ns, masked)
+    size = lambda ns, masked=0, d=64, total_q=32, max_q=16, total_k=300: lib.fa_fwd_varlen_splitk_workspace_bytes(
+        2, 4, 2, total_q, total_k, max_q, 200, d, 1, ns, masked)
     rows = 4 * 32
     assert size(3) == math.ceil(3 * rows * 64 * 4 / 256) * 256 + math.ceil(3 * rows * 4 / 256) * 256
     assert size(3, masked=1) == size(3)
     assert size(1) == 0 and size(1, masked=1) == 0
-    assert size(3, d=96) == 0 and size(3, max_q=40) == 0 and size(5000) == 0
+    assert size(3, d=96) == 0 and size(3, max_q=40) == 0 and size(3, total_k=100) == 0 and size(5000) == 0
 
     def call(mask=None, stride=0, cu_q=FAKE, ws=FAKE, wsb=1 << 30, ns=3, d=64, window=0):
         return lib.fa_fwd_varlen_splitk(*(FAKE,) * 5, mask, stride, cu_q, FAKE, ws, wsb, 2, 4, 2, 32, 300, 16, 200, d,
@@ -276,6 +276,21 @@ def test_varlen_splitk_workspace_and_arguments(lib):
     # one slice needs no workspace: validation passes and stops at the NULL output
     assert lib.fa_fwd_varlen_splitk(FAKE, FAKE, FAKE, None, FAKE, None, 0, FAKE, FAKE, None, 0, 2, 4, 2, 32, 300,
                                     16, 200, 64, 1, 0, 0.125, 1, 1, None) == 1
+
+
+def test_varlen_split_automatic_count(lib):
+    """The automatic slice count of fa_fwd_varlen_splitk, read back through the workspace size
+    (which grows linearly with the count).  16 blocks of 32 queries, Hq = 32, Hkv = 8, d = 128,
+    bf16: with key counts near the mean (longest 7759 of 64000 keys) it is the fixed layout's
+    count for the longest lengths (2); with one 8032-key prefix among short ones (12344 keys in
+    all, longest / mean = 10.4) the workgroup target grows by sqrt(10.4), to 7 slices."""
+    size = lambda total_k, max_k, ns, masked=0: lib.fa_fwd_varlen_splitk_workspace_bytes(
+        16, 32, 8, 512, total_k, 32, max_k, 128, 1, ns, masked)
+    assert size(64000, 7759, 0) == size(64000, 7759, 2) > 0
+    # the same rows as 16 fixed-layout entries of 32 queries: the same count and size
+    assert size(64000, 7759, 0) == lib.fa_fwd_splitk_workspace_bytes(16, 32, 8, 32, 7759, 128, 1, 0)
+    assert size(12344, 8032, 0) == size(12344, 8032, 7)
+    assert size(12344, 8032, 0, masked=1) == size(12344, 8032, 7, masked=1)
 
 
 @pytest.mark.parametrize("d,fp32,bf16", [(32, 1, 1), (64, 1, 1), (128, 1, 1), (16, 4, 4), (96, 4, 4), (256, 4, 1)])

@@ -279,7 +279,8 @@ def test_varlen_split_stays_in_bounds(fa, dtn, d, masked):
     g = Guarded()
     o, lse = g.tensor("O", q.shape, t), g.tensor("L", (Hq, tq), torch.float32)
     ws = g.workspace("varlen split workspace",
-                     int(lib.fa_fwd_varlen_splitk_workspace_bytes(B, Hq, Hkv, tq, mq, mk, d, code, 3, int(masked))))
+                     int(lib.fa_fwd_varlen_splitk_workspace_bytes(B, Hq, Hkv, tq, tk, mq, mk, d, code, 3,
+                                                                  int(masked))))
     fa.forward_varlen_splitk(q, k, v, cu_q, cu_k, mq, mk, True, window=200, mask=mask, nsplit=3, workspace=ws,
                              out=o, lse=lse)
     g.check(f"varlen split {dtn} d={d} masked={masked}")

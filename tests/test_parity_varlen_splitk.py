@@ -90,10 +90,10 @@ def test_varlen_splitk_parity(fa, case):
     ref = {"O": pack([r[0][0] for r in refs]), "L": np.concatenate([r[1][0] for r in refs], axis=1)}
     empty = np.isneginf(ref["L"])
     lib = fa.load_library()
-    total_q = q.shape[1]
+    total_q, total_k = q.shape[1], k.shape[1]
+    code = fa.FA_DTYPE_BF16 if dtype == "bf16" else fa.FA_DTYPE_F32
     for ns in splits:
-        need = int(lib.fa_fwd_varlen_splitk_workspace_bytes(B, Hq, Hkv, total_q, mq, mk, d, fa.FA_DTYPE_BF16
-                                                            if dtype == "bf16" else fa.FA_DTYPE_F32, ns,
+        need = int(lib.fa_fwd_varlen_splitk_workspace_bytes(B, Hq, Hkv, total_q, total_k, mq, mk, d, code, ns,
                                                             int(mask is not None)))
         ws = torch.full((max(need, 1),), 0xFF, dtype=torch.uint8, device="cuda")     # NaN floats
         o, lse = fa.forward_varlen_splitk(q, k, v, cu_q, cu_k, mq, mk, causal, scale, window=window, mask=mask,
@@ -135,8 +135,8 @@ def test_varlen_split_at_the_slice_limit(fa, masked):
     cu_k = torch.tensor(np.concatenate([[0], np.cumsum([b for _, b in lens])]).astype(np.int32)).cuda()
     mask = None if full is None else torch.from_numpy(full).cuda()
     lib = fa.load_library()
-    need = int(lib.fa_fwd_varlen_splitk_workspace_bytes(B, Hq, Hkv, q.shape[1], mq, mk, d, fa.FA_DTYPE_BF16, 1024,
-                                                        int(masked)))
+    need = int(lib.fa_fwd_varlen_splitk_workspace_bytes(B, Hq, Hkv, q.shape[1], k.shape[1], mq, mk, d,
+                                                        fa.FA_DTYPE_BF16, 1024, int(masked)))
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
     o, lse = fa.forward_varlen_splitk(q, k, v, cu_q, cu_k, mq, mk, True, mask=mask, nsplit=1024, workspace=ws)
     torch.cuda.synchronize()
