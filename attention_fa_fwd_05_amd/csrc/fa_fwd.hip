@@ -125,14 +125,21 @@ __global__ __launch_bounds__((64 * FwdShape<T, D, DEC>::NW), (DEC ? 2 : 1)) void
 
   // Key tiles jt0 .. ntiles - 1: those before the sliding window of the
   // block's first query, and those after the causal bound of its last, are
-  // never loaded.  Split over keys, slice blockIdx.y takes an equal share.
+  // never loaded.  Split over keys, slice blockIdx.y takes the next run of
+  // `per` tiles.  Fixed layout: the workgroup's own tiles in equal shares.
+  // Sequences of their own lengths (offsets or a page table): runs as long as
+  // the longest sequence's share, so a short sequence fills the first slices
+  // and leaves the others empty (they store only L_s = -inf) instead of
+  // spreading a few tiles over every slice.
   const int W = WIN ? a.window : 0;               // compile-time 0 without a window
   int kend = Tk;
   if (CAUSAL) kend = min(Tk, max(0, qlast + 1 + off));
   int ntiles = (kend + BK - 1) / BK;
   int jt0 = W > 0 ? min(ntiles, max(0, q0 + off - W + 1) / BK) : 0;
   if (gridDim.y > 1) {
-    const int per = (ntiles - jt0 + (int)gridDim.y - 1) / (int)gridDim.y;
+    const bool own_lengths = a.cu_q != nullptr || a.pages != nullptr;
+    const int span = own_lengths ? (a.Tk + BK - 1) / BK : ntiles - jt0;
+    const int per = (span + (int)gridDim.y - 1) / (int)gridDim.y;
     jt0 = min(ntiles, jt0 + (int)blockIdx.y * per);
     ntiles = min(ntiles, jt0 + per);
   }

@@ -254,7 +254,10 @@ int fa_bwd_dv(const void* Q, const void* K, const void* V, const void* O, const 
  * pool and key counts into [0, pages_per_seq * page_size].  page_size must be a
  * multiple of 128.  nsplit == 1 runs one pass with no workspace; otherwise the
  * keys are split over slices and merged as in fa_fwd_splitk (nsplit <= 0:
- * automatic), with a workspace of fa_fwd_paged_workspace_bytes bytes.  Errors
+ * automatic), with a workspace of fa_fwd_paged_workspace_bytes bytes.  The
+ * slices are equal runs of key tiles sized for the longest sequence the table
+ * holds (pages_per_seq * page_size keys), so a sequence with few keys leaves
+ * the later slices empty.  Errors
  * as fa_fwd_splitk, plus FA_ERR_BAD_SHAPE for a page size that is not a
  * positive multiple of 128 or an empty pool.
  */
@@ -407,10 +410,11 @@ int fa_bwd_varlen_mask(const void* Q, const void* K, const void* V, const void* 
  * such a batch gives each compute unit a long run of key tiles or nothing).
  * Layout, offsets, causal alignment and window as fa_fwd_varlen (d = dv).
  * mask_bits == NULL: no mask (fa_fwd_varlen's result); otherwise the mask of
- * fa_fwd_varlen_mask, with its mask_seq_stride.  The key tiles each
- * workgroup of a sequence would visit are divided into nsplit equal runs, one
- * per slice; a slice left without tiles of a sequence gives its rows
- * L_s = -inf, which weighs nothing in the merge.  nsplit == 1 runs the unsplit
+ * fa_fwd_varlen_mask, with its mask_seq_stride.  Slice s takes the key tiles
+ * s * n .. (s + 1) * n - 1 of the ones a workgroup would visit, with n the
+ * longest sequence's tile count over nsplit (rounded up): a short sequence
+ * fills the first slices and leaves the others without tiles.  Such a slice
+ * gives its rows L_s = -inf, which weighs nothing in the merge.  nsplit == 1 runs the unsplit
  * kernels with no workspace: bit for bit fa_fwd_varlen / fa_fwd_varlen_mask.
  * nsplit <= 0 picks the count as fa_fwd_splitk (fa_fwd_mask_splitk with a
  * mask) would for B sequences of the longest lengths; when the longest key
