@@ -9,6 +9,7 @@ are allocated once, outside the timed region.
     python bench.py [--steps K] [--warmup W] [--workload NAME]
     python bench.py --decode        # key-split forward, 32 queries against 8032 keys
     python bench.py --mask 0.5      # forward + backward under a random boolean mask
+    python bench.py --varlen-decode prefix   # variable-length key-split forward
 
 Prints one JSON line: whole-step throughput in counted TFLOP/s (4*Tq*Tk*d
 forward + 10*Tq*Tk*d backward per query head, halved when causal), the
@@ -244,6 +245,81 @@ def copy_calibration(nbytes: int, reps: int):
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
 
 
+# Variable-length decode batches: 32 new positions per sequence against key
+# counts drawn from a seeded generator (Hq = 32, Hkv = 8, d = 128, bf16,
+# end-aligned causal).  "prefix": one 8032-key prefix among 15 sequences of
+# 32-600 keys; "uniform": 16 sequences of 1000-8032 keys.
+VARLEN_DECODE = {"prefix": lambda rng: [8032] + [int(x) for x in rng.integers(32, 601, 15)],
+                 "uniform": lambda rng: [int(x) for x in rng.integers(1000, 8033, 16)]}
+
+
+def varlen_decode_bench(args, fa, accounting):
+    """Forward only over a variable-length batch of decode blocks: the key-split
+    call (fa_fwd_varlen_splitk, automatic slice count) timed beside the unsplit
+    one (fa_fwd_varlen).  HBM-bound: the roofline is the algorithmic bytes (Q,
+    K, V read; O, L written) over the split call's time against 8 TB/s."""
+    import numpy as np
+    import torch
+    rng = np.random.default_rng(20260)
+    tk = VARLEN_DECODE[args.varlen_decode](rng)
+    Hq, Hkv, d, tq1 = 32, 8, 128, 32
+    B, tq = len(tk), [tq1] * len(tk)
+    g = torch.Generator().manual_seed(20261)
+    mk = lambda *shape: torch.randn(*shape, generator=g).to(torch.bfloat16).cuda()
+    q, k, v = mk(Hq, sum(tq), d), mk(Hkv, sum(tk), d), mk(Hkv, sum(tk), d)
+    cq = torch.tensor(np.concatenate([[0], np.cumsum(tq)]).astype(np.int32)).cuda()
+    ck = torch.tensor(np.concatenate([[0], np.cumsum(tk)]).astype(np.int32)).cuda()
+    o, o1 = torch.empty_like(q), torch.empty_like(q)
+    lse, lse1 = (torch.empty(Hq, sum(tq), dtype=torch.float32, device="cuda") for _ in range(2))
+    lib = fa.load_library()
+    need = int(lib.fa_fwd_varlen_splitk_workspace_bytes(B, Hq, Hkv, sum(tq), sum(tk), max(tq), max(tk), d,
+                                                        fa.FA_DTYPE_BF16, 0, 0))
+    ws = torch.empty(max(1, need), dtype=torch.uint8, device="cuda")
+    rows = Hq * sum(tq)
+    nsplit = max(1, round(need / (rows * (d + 1) * 4))) if need else 1
+    scale = d ** -0.5
+
+    def split():
+        fa.forward_varlen_splitk(q, k, v, cq, ck, max(tq), max(tk), True, scale, nsplit=0, workspace=ws, out=o,
+                                 lse=lse)
+
+    def unsplit():
+        fa.forward_varlen(q, k, v, cq, ck, max(tq), max(tk), True, scale, out=o1, lse=lse1)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev[0].record()
+        for _ in range(args.steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / args.steps, (time.perf_counter() - t0) / args.steps * 1e3
+
+    ms_unsplit, _ = timed(unsplit)
+    ms, wall_ms = timed(split)
+    flops = 4.0 * d * Hq * sum(accounting.visible_pairs(a, b, True) for a, b in zip(tq, tk))
+    algo_bytes = 2 * (2 * Hq * sum(tq) * d + 2 * Hkv * sum(tk) * d) + 4 * Hq * sum(tq)
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
+    out = {"metric": "variable-length decode forward (key-split, merged): TFLOP/s and HBM GB/s",
+           "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) inputs rounded to bf16; seeded key counts)",
+           "config": {"workload": f"varlen_decode_{args.varlen_decode}", "B": B, "Hq": Hq, "Hkv": Hkv,
+                      "Tq_per_seq": tq1, "key_counts": tk, "d": d, "causal": True, "nsplit_auto": nsplit,
+                      "workspace_bytes": ws.numel()},
+           "unsplit_ms": round(ms_unsplit, 4), "speedup_vs_unsplit": round(ms_unsplit / ms, 2),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                        "frac": round(gbs / 8000.0, 4), "traffic": None,
+                        "algorithmic_bytes_per_launch": algo_bytes, "avg_launch_ms": round(ms, 4)}}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,6 +332,8 @@ def main() -> int:
                     help="time the key-split forward on a decode-shaped workload instead")
     ap.add_argument("--mask", type=float, default=0.0, metavar="DENSITY",
                     help="time the boolean-mask forward and backward with a random mask of this density")
+    ap.add_argument("--varlen-decode", choices=sorted(VARLEN_DECODE), default=None,
+                    help="time the variable-length key-split forward on a batch of decode blocks instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run only a device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -284,6 +362,8 @@ def main() -> int:
         return decode_bench(args, fa, accounting, wl)
     if args.mask > 0:
         return mask_bench(args, fa, accounting, wl)
+    if args.varlen_decode:
+        return varlen_decode_bench(args, fa, accounting)
     w = wl.WORKLOADS[args.workload or wl.HEADLINE]
     inp = wl.make_inputs(w)
     q, k, v, do = wl.to_device(inp, w.dtype)

@@ -37,3 +37,15 @@ def test_source_hash_and_stored_traffic():
     got = bench.stored_traffic("gqa_bf16_T4096_d128_causal", "dkdv_pair_kernel")
     # counters are reported only while they were taken on the current kernel sources
     assert got == (entry["bytes_per_launch"] if entry["source_hash"] == h else None)
+
+
+def test_varlen_decode_batches():
+    """The variable-length decode batches of bench.py --varlen-decode: 16 key counts each, from
+    a seeded generator; "prefix" holds one 8032-key prefix and 15 counts of 32-600 keys."""
+    import numpy as np
+    prefix = bench.VARLEN_DECODE["prefix"](np.random.default_rng(20260))
+    uniform = bench.VARLEN_DECODE["uniform"](np.random.default_rng(20260))
+    assert len(prefix) == len(uniform) == 16
+    assert prefix[0] == 8032 and all(32 <= n <= 600 for n in prefix[1:])
+    assert all(1000 <= n <= 8032 for n in uniform)
+    assert prefix == bench.VARLEN_DECODE["prefix"](np.random.default_rng(20260))
