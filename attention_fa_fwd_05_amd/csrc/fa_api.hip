@@ -352,7 +352,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_NULL_PTR: return "a required pointer is NULL";
     case FA_ERR_BAD_SHAPE: return "bad shape: B, Hq, Hkv must be >= 1 and Tq, Tk >= 0";
     case FA_ERR_GQA_RATIO: return "Hq must be a multiple of Hkv";
-    case FA_ERR_HEAD_DIM: return "unsupported head dimension (32, 64 or 128; dv != d as (128, 64) or (64, 128))";
+    case FA_ERR_HEAD_DIM: return "unsupported head dimension (32, 64 or 128, bf16 also 256; dv != d as (128, 64) or (64, 128))";
     case FA_ERR_DTYPE: return "unsupported dtype (FA_DTYPE_F32 or FA_DTYPE_BF16)";
     case FA_ERR_SCALE: return "scale must be finite and positive";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than fa_bwd_workspace_bytes";

@@ -47,6 +47,13 @@ def test_status_strings(lib):
     assert lib.fa_abi_version() >> 16 == 2
 
 
+def test_head_dim_status_names_every_accepted_dim(lib):
+    # the checks accept d = 32, 64, 128 and, in bf16, 256
+    s = fa.status_string(4)
+    for dim in ("32", "64", "128", "256"):
+        assert dim in s, s
+
+
 def test_workspace_bytes(lib):
     # D and L2 per query row, rows padded to a multiple of 64 per head, 256-byte aligned parts
     rows = 4 * 32 * 4096
