@@ -440,6 +440,28 @@ __device__ __forceinline__ void pipelined(F&& fetch, G&& mma, H&& between) {
   }
 }
 
+// As pipelined, with vector work `pre` that the first product needs placed
+// after the first AHEAD operand reads: when `pre` waits on an LDS read of its
+// own, the operand reads are already in flight, so the two round trips
+// overlap instead of following one another.
+template <int NP, int AHEAD, typename Op, typename F, typename P, typename G, typename H>
+__device__ __forceinline__ void pipelined_after(F&& fetch, P&& pre, G&& mma, H&& between) {
+  Op ring[AHEAD];
+#pragma unroll
+  for (int m = 0; m < AHEAD; ++m) ring[m] = fetch(m);
+  __builtin_amdgcn_sched_barrier(0);
+  pre();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int m = 0; m < NP; ++m) {
+    const Op x = ring[m % AHEAD];
+    if (m + AHEAD < NP) ring[m % AHEAD] = fetch(m + AHEAD);
+    mma(m, x);
+    between(m);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Lane l and lane l ^ 32 combined, on the vector ALU: v_permlane32_swap hands

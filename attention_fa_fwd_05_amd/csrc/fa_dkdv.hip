@@ -388,10 +388,14 @@ __global__ __launch_bounds__(512) void dkdv_pair_kernel(BwdArgs a) {
           const float p0 = __uint_as_float(pw[s][e] << 16), p1 = __uint_as_float(pw[s][e] & 0xffff0000u);
           dsw[s][e] = __builtin_bit_cast(uint32_t, bf16x2{(bf16)(p0 * dp[r]), (bf16)(p1 * dp[r + 1])});
         };
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ds_word(0, e);
-        pipelined<NSQ * NDT, 4, Op>(
+        // Step 0's dS words wait on the P read; the first Q^T operand reads
+        // (block it - 1's slot, stable since that block) go out before them.
+        pipelined_after<NSQ * NDT, 4, Op>(
             [&](int m) { return XorFetch<D>::tr(qb + xf.tr0, m % NDT, m / NDT); },
+            [&]() {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ds_word(0, e);
+            },
             [&](int m, const Op& x) {
               dk[m % NDT] = M::mma(x, __builtin_bit_cast(bf16x8, dsw[m / NDT]), dk[m % NDT]);
             },
